@@ -1,0 +1,219 @@
+"""Plain, slow, obviously-correct CPU evaluation of the mLSTM forward pass.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing in the GPU
+library imports or calls this module.
+
+Source: "xLSTM: Extended Long Short-Term Memory", Appendix A.3.
+
+* Eq. 71 forget gate matrix F, Eq. 72 input gate pre-activation matrix I~,
+  Eq. 73 D = F (.) exp(I~), Eq. 76 unstabilized H~ = C V.
+* Eqs. 74-75 and 77: stabilization by the row maximum of log D.
+* Eqs. 79-86 (the stabilized forward pass restated at the start of "Parallel
+  mLSTM Backward Pass"): D~ = logF + I~, m = row max, D' = exp(D~ - m 1^T),
+  C~' = (Q K^T / sqrt(d)) (.) D', b = C~' 1, n = max(|b|, exp(-m)),
+  C = C~' (.) (n^-1 1^T), H~ = C V.
+* Eq. 101: log F_ij = -inf (i < j), 0 (i = j), sum_{k=j+1..i} log sigma(f~_k).
+* Eq. 78: output gate H = sigma(O~) (.) H~.
+* The recurrent form (C_t = f_t C_{t-1} + i_t v_t k_t^T, n_t = f_t n_{t-1} +
+  i_t k_t, h~_t = C_t q_t / max(|n_t^T q_t|, 1)) is read off the recurrent
+  backward pass, Eqs. 59-70, whose forward equations are cited but not shown
+  on the page; the appendix extracts the 1/sqrt(d) of the keys explicitly in
+  the parallel form, so the recurrent keys carry it (k_t / sqrt(d)), and the
+  states start at zero.
+
+Shapes: q, k, v are [B, NH, T, d]; igate (i~), fgate (f~) are [B, NH, T].
+Heads are independent (the page on the xLSTM cell notes there is no memory
+mixing between heads), so every function loops over (b, h) and works on one
+head at a time, exactly as the appendix presents it.
+"""
+
+import math
+
+import numpy as np
+
+
+def log_sigmoid(x):
+    """f-bar = log sigma(x) of Eq. 101, as min(x, 0) - log1p(exp(-|x|)).
+
+    The rewrite is algebraically exact: log sigma(x) = -log(1 + e^-x) for
+    x >= 0 and x - log(1 + e^x) for x < 0; it never forms e^{+|x|}.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+
+
+def _sigmoid(x):
+    x = np.asarray(x, dtype=np.float64)
+    # 1 / (1 + e^-x), evaluated without overflow for either sign.
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def gate_matrices(fgate, igate):
+    """F (Eq. 71) and I~ (Eq. 72) for ONE head, by their definitions.
+
+    F_ij = 0 for i < j, 1 for i = j, prod_{k=j+1..i} sigma(f~_k) for i > j:
+    every entry below the diagonal is the explicit product, formed as a
+    running product down each column.  I~_ij = 0 for i < j, i~_j for i >= j.
+    Returns (F, Itilde) as float64 [T, T].
+    """
+    f = np.asarray(fgate, dtype=np.float64).reshape(-1)
+    ig = np.asarray(igate, dtype=np.float64).reshape(-1)
+    T = f.shape[0]
+    sig = _sigmoid(f)
+    F = np.zeros((T, T), dtype=np.float64)
+    for j in range(T):
+        F[j, j] = 1.0
+        prod = 1.0
+        for i in range(j + 1, T):
+            prod *= sig[i]
+            F[i, j] = prod
+    It = np.zeros((T, T), dtype=np.float64)
+    for i in range(T):
+        It[i, : i + 1] = ig[: i + 1]
+    return F, It
+
+
+def log_gate_matrix(fgate, igate, rows=None, dtype=np.float64):
+    """D~ = log F + I~ (Eqs. 74, 79, with log F from Eq. 101) for ONE head.
+
+    log F_ij is the sum of f-bar_k over k = j+1..i, written as the difference
+    of the inclusive prefix sums cs_i - cs_j of f-bar; -inf above the diagonal.
+    ``rows`` selects row indices (default: all).  Returns [len(rows), T].
+    """
+    fbar = log_sigmoid(fgate).astype(dtype)
+    ig = np.asarray(igate, dtype=np.float64).reshape(-1).astype(dtype)
+    T = fbar.shape[0]
+    cs = np.cumsum(fbar, dtype=dtype)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    Dt = cs[rows][:, None] - cs[None, :] + ig[None, :]
+    upper = np.arange(T)[None, :] > rows[:, None]
+    Dt[upper] = -np.inf
+    # Eq. 101 fixes log F_ii = 0 exactly (cs_i - cs_i is already exactly 0).
+    return Dt
+
+
+def _rows_one_head(q, k, v, ig, fg, rows, dtype):
+    """Eqs. 79-86 for the listed rows of one head.  Rows are independent."""
+    T, d = q.shape
+    rows = np.asarray(rows)
+    ncol = int(rows.max()) + 1  # columns j > every listed row are exactly 0 (Eq. 71)
+    Dt = log_gate_matrix(fg[:ncol], ig[:ncol], rows=rows, dtype=dtype)  # Eq. 79
+    m = Dt.max(axis=1)  # Eq. 80, row-wise maximum
+    Dp = np.exp(Dt - m[:, None])  # Eq. 81, exp(-inf) = 0 above the diagonal
+    S = (q[rows].astype(dtype) @ k[:ncol].astype(dtype).T) / dtype(math.sqrt(d))
+    Ct = S * Dp  # Eq. 82
+    b = Ct.sum(axis=1)  # Eq. 83, row sum over j = 1..T
+    n = np.maximum(np.abs(b), np.exp(-m))  # Eq. 84
+    C = Ct / n[:, None]  # Eq. 85
+    h = C @ v[:ncol].astype(dtype)  # Eq. 86
+    return h, m, n, b, np.abs(Ct).sum(axis=1)
+
+
+def forward_stabilized(q, k, v, igate, fgate, block_rows=256, dtype=np.float64,
+                       return_diag=False):
+    """Stabilized parallel forward pass, Eqs. 79-86, densely, per head.
+
+    Rows are processed in blocks of ``block_rows`` only to bound memory; each
+    row's arithmetic is independent of every other row's.
+    Returns (h [B,NH,T,d], m [B,NH,T], n [B,NH,T]); with ``return_diag`` also
+    (b, rho) where b is the signed row sum (Eq. 83) and rho_i = sum_j |C~'_ij|,
+    so that rho / n is the cancellation factor of row i.
+    """
+    q = np.asarray(q)
+    B, NH, T, d = q.shape
+    h = np.empty((B, NH, T, d), dtype=dtype)
+    m = np.empty((B, NH, T), dtype=dtype)
+    n = np.empty((B, NH, T), dtype=dtype)
+    bsum = np.empty((B, NH, T), dtype=dtype)
+    rho = np.empty((B, NH, T), dtype=dtype)
+    for bi in range(B):
+        for hi in range(NH):
+            qh, kh, vh = (np.asarray(a[bi, hi], dtype=np.float64) for a in (q, k, v))
+            ig = np.asarray(igate[bi, hi], dtype=np.float64)
+            fg = np.asarray(fgate[bi, hi], dtype=np.float64)
+            for r0 in range(0, T, block_rows):
+                rows = np.arange(r0, min(T, r0 + block_rows))
+                hh, mm, nn, bb, rr = _rows_one_head(qh, kh, vh, ig, fg, rows, dtype)
+                h[bi, hi, rows] = hh
+                m[bi, hi, rows] = mm
+                n[bi, hi, rows] = nn
+                bsum[bi, hi, rows] = bb
+                rho[bi, hi, rows] = rr
+    if return_diag:
+        return h, m, n, bsum, rho
+    return h, m, n
+
+
+def forward_rows(q, k, v, igate, fgate, bi, hi, rows, dtype=np.float64):
+    """Eqs. 79-86 for selected rows ``rows`` of head (bi, hi) only.
+
+    Costs O(len(rows) * max(rows) * d): used to check single outputs of very
+    long sequences one by one.  Returns (h [R, d], m [R], n [R], b [R], rho [R]).
+    """
+    qh, kh, vh = (np.asarray(a[bi, hi], dtype=np.float64) for a in (q, k, v))
+    ig = np.asarray(igate[bi, hi], dtype=np.float64)
+    fg = np.asarray(fgate[bi, hi], dtype=np.float64)
+    return _rows_one_head(qh, kh, vh, ig, fg, np.asarray(rows), dtype)
+
+
+def forward_recurrent(q, k, v, igate, fgate):
+    """The recurrent mLSTM, step by step, unstabilized, in float64.
+
+    C_0 = 0 (d x d), n_0 = 0 (d); for t = 1..T: f_t = sigma(f~_t),
+    i_t = exp(i~_t), k'_t = k_t / sqrt(d); C_t = f_t C_{t-1} + i_t v_t k'_t^T;
+    n_t = f_t n_{t-1} + i_t k'_t; h~_t = C_t q_t / max(|n_t^T q_t|, 1).
+    Returns (h [B,NH,T,d], nq [B,NH,T]) with nq_t = n_t^T q_t, the recurrent
+    normalizer argument.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, NH, T, d = q.shape
+    h = np.empty((B, NH, T, d))
+    nq = np.empty((B, NH, T))
+    scale = 1.0 / math.sqrt(d)
+    for bi in range(B):
+        for hi in range(NH):
+            C = np.zeros((d, d))
+            nvec = np.zeros(d)
+            for t in range(T):
+                f_t = float(_sigmoid(fgate[bi, hi, t]))
+                i_t = math.exp(float(igate[bi, hi, t]))
+                kt = k[bi, hi, t] * scale
+                vt = v[bi, hi, t]
+                C = f_t * C + i_t * np.outer(vt, kt)
+                nvec = f_t * nvec + i_t * kt
+                qt = q[bi, hi, t]
+                den = float(nvec @ qt)
+                nq[bi, hi, t] = den
+                h[bi, hi, t] = (C @ qt) / max(abs(den), 1.0)
+    return h, nq
+
+
+def forward_unstabilized(q, k, v, igate, fgate):
+    """Unstabilized parallel form, Eqs. 71-73 and 76, by brute force.
+
+    D = F (.) exp(I~) with F built from explicit products (``gate_matrices``);
+    C~ = (Q K^T / sqrt(d)) (.) D; H~ = C~ V / max(|C~ 1|, 1).  Overflows for
+    large input gates, which is what the stabilization exists to avoid.
+    Returns h [B,NH,T,d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, NH, T, d = q.shape
+    h = np.empty((B, NH, T, d))
+    for bi in range(B):
+        for hi in range(NH):
+            F, It = gate_matrices(fgate[bi, hi], igate[bi, hi])
+            D = F * np.exp(It)  # Eq. 73
+            Ct = (q[bi, hi] @ k[bi, hi].T) / math.sqrt(d) * D
+            den = np.maximum(np.abs(Ct.sum(axis=1)), 1.0)
+            h[bi, hi] = (Ct / den[:, None]) @ v[bi, hi]
+    return h
+
+
+def output_gate(h, ogate):
+    """Eq. 78: H = sigma(O~) (.) H~, elementwise."""
+    return _sigmoid(ogate) * np.asarray(h, dtype=np.float64)

@@ -1,0 +1,432 @@
+"""Pins for the CPU oracle: what the xLSTM appendix and plain mathematics fix.
+
+None of these compares the oracle with a retyped copy of itself.  Each check
+is an independent route to the same number: exact rational arithmetic, a
+different form of the method (recurrent, unstabilized), a special case with a
+textbook closed form, or an identity the equations imply.  The mutation tests
+at the end plant plausible mistakes into the oracle (CPU only) and show that
+the pins catch them.
+
+Equation numbers refer to "xLSTM: Extended Long Short-Term Memory",
+Appendix A.3 (Eqs. 59-70 recurrent backward, 71-78 parallel forward, 79-86
+stabilized forward, 101 log forget gate matrix).
+"""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from oracle import mlstm as om
+from linear_recurrent_sequence_amd import workloads as W
+
+
+def _one_head(q, k, v, ig, fg):
+    """Lift single-head arrays to [1, 1, ...]."""
+    return (np.asarray(q, float)[None, None], np.asarray(k, float)[None, None],
+            np.asarray(v, float)[None, None], np.asarray(ig, float)[None, None],
+            np.asarray(fg, float)[None, None])
+
+
+def _rel(a, b):
+    a = np.asarray(a, float)
+    b = np.asarray(b, float)
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-300))
+
+
+# ---------------------------------------------------------------------------
+# Exact rational worked examples.
+#
+# Forget pre-activations f~ = ln r with r rational give sigma(f~) = r / (1 + r)
+# exactly; input pre-activations i~ = a ln 2 with integer a give exp(i~) = 2^a.
+# With d = 4 (sqrt(d) = 2) and small-integer q, k, v every quantity of the
+# unstabilized form (Eqs. 71-73, 76) is a rational number.  The stabilized
+# quantities follow from monotonicity of log: m_i = log max_j D_ij (Eq. 80),
+# exp(-m_i) = 1 / max_j D_ij, b_i = (sum_j C~_ij) / max_j D_ij (Eqs. 81-83),
+# n_i = max(|b_i|, exp(-m_i)) (Eq. 84).  The float inputs carry only the
+# representation error of ln r and a ln 2 (~1e-16), hence the 1e-12 bounds.
+# ---------------------------------------------------------------------------
+
+EXAMPLES = [
+    # (forget ratios r_t, input exponents a_t, q, k, v) with d = 4
+    dict(r=[Fraction(1), Fraction(2), Fraction(1, 2), Fraction(4), Fraction(1, 4), Fraction(3)],
+         a=[0, 1, -1, 2, 0, -2],
+         q=[[1, 0, 2, -1], [0, 1, 1, 0], [2, -1, 0, 1], [1, 1, 1, 1], [-1, 2, 0, 0], [0, 0, 3, -2]],
+         k=[[1, 1, 0, 0], [0, 2, -1, 1], [1, 0, 1, -1], [2, 0, 0, 1], [0, -1, 1, 2], [1, 1, 1, 0]],
+         v=[[1, 2, 0, -1], [0, 1, 3, 1], [2, 0, 1, 0], [-1, 1, 1, 2], [1, -2, 0, 1], [3, 0, -1, 0]]),
+    # large input gates: unstabilized D spans 2^-12 .. 2^12; many rows hit the floor
+    dict(r=[Fraction(1, 4), Fraction(1, 2), Fraction(1, 4), Fraction(1), Fraction(1, 2)],
+         a=[12, -6, 3, -12, 9],
+         q=[[1, -1, 0, 0], [0, 0, 1, 0], [1, 2, 1, 0], [0, 1, 0, -1], [2, 0, 0, 1]],
+         k=[[0, 1, 1, 0], [1, 0, 0, 0], [0, 0, -1, 1], [1, 1, 1, 1], [-1, 0, 2, 0]],
+         v=[[1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 1, 0], [0, 0, 0, 1], [1, 1, 1, 1]]),
+]
+
+
+def _exact(ex):
+    """Exact values of h~, m (as max D), n for an EXAMPLES entry."""
+    r, a, q, k, v = ex["r"], ex["a"], ex["q"], ex["k"], ex["v"]
+    T, d = len(r), len(q[0])
+    sig = [ri / (1 + ri) for ri in r]
+    H, maxD, N = [], [], []
+    for i in range(T):
+        D = []
+        for j in range(T):
+            if j > i:
+                D.append(Fraction(0))
+                continue
+            F = Fraction(1)
+            for kk in range(j + 1, i + 1):  # Eq. 71: product over k = j+1..i
+                F *= sig[kk]
+            D.append(F * Fraction(2) ** a[j])  # Eq. 73
+        Ct = [Fraction(sum(q[i][c] * k[j][c] for c in range(d)), 2) * D[j] for j in range(T)]
+        rowsum = sum(Ct)
+        den = max(abs(rowsum), Fraction(1))  # Eq. 76
+        H.append([sum(Ct[j] * v[j][c] for j in range(T)) / den for c in range(d)])
+        mD = max(D)
+        maxD.append(mD)
+        N.append(max(abs(rowsum) / mD, 1 / mD))  # Eq. 84 via b = rowsum / max D
+    return H, maxD, N
+
+
+def _example_inputs(ex):
+    fg = np.array([math.log(x) for x in ex["r"]])
+    ig = np.array([ai * math.log(2.0) for ai in ex["a"]])
+    return _one_head(ex["q"], ex["k"], ex["v"], ig, fg)
+
+
+@pytest.mark.parametrize("ex", EXAMPLES)
+def test_exact_rational_example_stabilized(ex):
+    q, k, v, ig, fg = _example_inputs(ex)
+    H, maxD, N = _exact(ex)
+    h, m, n = oracle.forward_stabilized(q, k, v, ig, fg)
+    Hf = np.array([[float(x) for x in row] for row in H])
+    assert np.allclose(h[0, 0], Hf, rtol=1e-12, atol=1e-12 * np.abs(Hf).max())
+    assert np.allclose(m[0, 0], [math.log(float(x)) for x in maxD], rtol=0, atol=1e-12)
+    assert np.allclose(n[0, 0], [float(x) for x in N], rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("ex", EXAMPLES)
+def test_exact_rational_example_recurrent_and_unstabilized(ex):
+    q, k, v, ig, fg = _example_inputs(ex)
+    H, _, _ = _exact(ex)
+    Hf = np.array([[float(x) for x in row] for row in H])
+    hr, _ = oracle.forward_recurrent(q, k, v, ig, fg)
+    hu = oracle.forward_unstabilized(q, k, v, ig, fg)
+    for got in (hr, hu):
+        assert np.allclose(got[0, 0], Hf, rtol=1e-12, atol=1e-12 * np.abs(Hf).max())
+
+
+@pytest.mark.parametrize("ex", EXAMPLES)
+def test_exact_rational_example_rows(ex):
+    q, k, v, ig, fg = _example_inputs(ex)
+    H, maxD, N = _exact(ex)
+    rows = [4, 0, 2]
+    h, m, n, _, _ = oracle.forward_rows(q, k, v, ig, fg, 0, 0, rows)
+    for t, i in enumerate(rows):
+        assert np.allclose(h[t], [float(x) for x in H[i]], rtol=1e-12, atol=1e-12)
+        assert abs(m[t] - math.log(float(maxD[i]))) < 1e-12
+        assert abs(n[t] - float(N[i])) <= 1e-12 * float(N[i])
+
+
+# ---------------------------------------------------------------------------
+# The three forms agree (the appendix states the stabilized and unstabilized
+# H~ are identical, and that the parallel form reformulates the recurrence).
+# ---------------------------------------------------------------------------
+
+def test_tiny_workload_forms_agree():
+    x = W.make("tiny_fp32", seed=0)
+    args = (x["q"], x["k"], x["v"], x["igate"], x["fgate"])
+    h, m, n = oracle.forward_stabilized(*args)
+    hr, nq = oracle.forward_recurrent(*args)
+    hu = oracle.forward_unstabilized(*args)
+    assert _rel(h, hr) < 1e-12
+    assert _rel(h, hu) < 1e-12
+    # recurrent normalizer vs Eq. 84: n_i = exp(-m_i) * max(|n_i^T q_i|, 1)
+    assert _rel(n, np.exp(-m) * np.maximum(np.abs(nq), 1.0)) < 1e-12
+    # the floor exp(-m) is active on some rows of this workload, inactive on others
+    floor = np.isclose(n, np.exp(-m), rtol=1e-14, atol=0)
+    assert 0 < floor.sum() < floor.size
+
+
+@settings(max_examples=40, deadline=None)
+@given(T=st.integers(1, 20), d=st.integers(1, 8), seed=st.integers(0, 2**31 - 1),
+       fmu=st.floats(-3, 6), fsd=st.floats(0.1, 4), imu=st.floats(-4, 4), isd=st.floats(0.1, 4))
+def test_forms_agree_random_tiny(T, d, seed, fmu, fsd, imu, isd):
+    x = W.make(dict(B=1, NH=2, T=T, d=d, dtype="fp32",
+                    igate=("normal", imu, isd), fgate=("normal", fmu, fsd)), seed=seed)
+    args = (x["q"], x["k"], x["v"], x["igate"], x["fgate"])
+    h, m, n = oracle.forward_stabilized(*args, block_rows=7)
+    hr, nq = oracle.forward_recurrent(*args)
+    hu = oracle.forward_unstabilized(*args)
+    scale = max(np.abs(hr).max(), 1e-300)
+    assert np.abs(h - hr).max() <= 1e-10 * scale
+    assert np.abs(h - hu).max() <= 1e-10 * scale
+    assert _rel(n, np.exp(-m) * np.maximum(np.abs(nq), 1.0)) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# Gate matrices (Eqs. 71-75, 101)
+# ---------------------------------------------------------------------------
+
+def test_gate_matrix_structure():
+    rng = np.random.default_rng(1)
+    T = 17
+    fg = rng.normal(1.0, 2.0, T)
+    ig = rng.normal(0.0, 1.0, T)
+    F, It = oracle.gate_matrices(fg, ig)
+    assert np.array_equal(np.diag(F), np.ones(T))  # F_ii = 1
+    assert np.array_equal(np.triu(F, 1), np.zeros((T, T)))  # zero above diagonal
+    assert np.array_equal(np.triu(It, 1), np.zeros((T, T)))
+    assert np.array_equal(np.tril(It), np.tril(np.broadcast_to(ig, (T, T))))
+    sig = 1.0 / (1.0 + np.exp(-fg))
+    for i in range(T):
+        for j in range(i):
+            assert math.isclose(F[i, j], float(np.prod(sig[j + 1:i + 1])), rel_tol=1e-13)
+    Dt = oracle.log_gate_matrix(fg, ig)
+    assert np.all(np.isneginf(Dt[np.triu_indices(T, 1)]))  # log F = -inf above
+    assert np.array_equal(np.diag(Dt), ig)  # log F_ii = 0, so D~_ii = i~_i
+    # exp(D~) = D = F (.) exp(I~) on and below the diagonal (Eqs. 73, 74)
+    low = np.tril_indices(T)
+    assert np.allclose(np.exp(Dt[low]), (F * np.exp(It))[low], rtol=1e-12, atol=0)
+
+
+def test_log_sigmoid_extremes():
+    x = np.array([-800.0, -30.0, -1.0, 0.0, 1e-8, 3.0, 40.0, 800.0])
+    got = oracle.log_sigmoid(x)
+    assert got[0] == -800.0  # log sigma(x) -> x for x -> -inf (no overflow)
+    assert math.isclose(got[3], -math.log(2.0), rel_tol=1e-15)
+    assert math.isclose(got[6], -math.exp(-40.0), rel_tol=1e-12)  # -log1p(e^-40)
+    assert got[7] == 0.0 or abs(got[7]) < 1e-300
+    mid = x[1:6]
+    assert np.allclose(got[1:6], np.log(1.0 / (1.0 + np.exp(-mid))), rtol=1e-13)
+
+
+def test_stabilizer_properties():
+    x = W.make(dict(B=2, NH=2, T=50, d=8, dtype="fp32", igate=("uniform", -20, 20),
+                    fgate=("normal", 0.0, 4.0), fgate_floor=(0.05, -30.0)), seed=3)
+    args = (x["q"], x["k"], x["v"], x["igate"], x["fgate"])
+    h, m, n, b, rho = oracle.forward_stabilized(*args, return_diag=True)
+    # P9: n >= exp(-m), n >= |b|, and n equals one of them (Eq. 84)
+    floor = np.exp(-m)
+    assert np.all(n >= floor) and np.all(n >= np.abs(b))
+    assert np.all((n == floor) | (n == np.abs(b)))
+    assert np.all(rho >= np.abs(b) * (1 - 1e-12))
+    for bi in range(2):
+        for hi in range(2):
+            fg, ig = x["fgate"][bi, hi], x["igate"][bi, hi]
+            Dt = oracle.log_gate_matrix(fg, ig)
+            Dp = np.exp(Dt - m[bi, hi][:, None])
+            # P5: the row maximum of D' is exactly 1 (Eqs. 80-81)
+            assert np.array_equal(Dp.max(axis=1), np.ones(50))
+            # P7: m from the max-plus recurrence m_i = max(m_{i-1} + fbar_i, i~_i),
+            # m_1 = i~_1 (split j = i from j < i in Eq. 80 using Eq. 101)
+            fbar = oracle.log_sigmoid(fg)
+            mm = np.empty(50)
+            mm[0] = ig[0]
+            for i in range(1, 50):
+                mm[i] = max(mm[i - 1] + fbar[i], ig[i])
+            assert np.allclose(m[bi, hi], mm, rtol=0, atol=1e-12 * np.abs(mm).max())
+
+
+def test_first_forget_gate_is_irrelevant():
+    # Eq. 71: products start at k = j+1, so f~_1 never enters any output (P6)
+    x = W.make(dict(B=1, NH=3, T=40, d=8, dtype="fp32", igate=("normal", 0, 2),
+                    fgate=("normal", 2, 2)), seed=5)
+    args = [x["q"], x["k"], x["v"], x["igate"], x["fgate"].copy()]
+    h0, m0, n0 = oracle.forward_stabilized(*args)
+    args[4][:, :, 0] = np.array([-25.0, 0.0, 25.0])
+    h1, m1, n1 = oracle.forward_stabilized(*args)
+    assert _rel(h1, h0) < 1e-13 and _rel(m1, m0) < 1e-13 and _rel(n1, n0) < 1e-13
+
+
+def test_input_gate_shift():
+    # P13: i~ -> i~ + c moves m by c, leaves D' and b unchanged, and leaves H~
+    # unchanged on rows where the floor exp(-m) is inactive both times.
+    x = W.make(dict(B=1, NH=2, T=60, d=8, dtype="fp32", igate=("normal", 0, 1),
+                    fgate=("normal", 3, 1)), seed=7)
+    args = (x["q"], x["k"], x["v"])
+    c = 5.25
+    h0, m0, n0, b0, _ = oracle.forward_stabilized(*args, x["igate"], x["fgate"], return_diag=True)
+    ig1 = x["igate"].astype(np.float64) + c
+    h1, m1, n1, b1, _ = oracle.forward_stabilized(*args, ig1, x["fgate"], return_diag=True)
+    assert np.allclose(m1, m0 + c, rtol=0, atol=1e-12)
+    assert np.allclose(b1, b0, rtol=1e-11, atol=1e-14)
+    ok = (np.abs(b0) >= np.exp(-m0)) & (np.abs(b1) >= np.exp(-m1))
+    assert ok.sum() > 10
+    assert np.allclose(h1[ok], h0[ok], rtol=1e-10, atol=1e-12)
+    assert np.allclose(n1, np.maximum(np.abs(b0), np.exp(-m0 - c)), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Special cases with textbook closed forms
+# ---------------------------------------------------------------------------
+
+def test_no_forgetting_unit_input_is_causal_linear_attention():
+    # f~ = 40 gives log sigma ~ -4e-18 (no forgetting), i~ = 0 gives unit input
+    # gates: D is the lower-triangular ones matrix, m = 0, and H~ is causal
+    # linear attention with normalizer max(|row sum|, 1).
+    rng = np.random.default_rng(11)
+    T, d = 45, 12
+    q, k, v = (rng.standard_normal((T, d)) for _ in range(3))
+    args = _one_head(q, k, v, np.zeros(T), np.full(T, 40.0))
+    h, m, n = oracle.forward_stabilized(*args)
+    A = np.tril(q @ k.T) / math.sqrt(d)
+    ref = (A @ v) / np.maximum(np.abs(A.sum(axis=1)), 1.0)[:, None]
+    assert _rel(h[0, 0], ref) < 1e-13
+    assert np.abs(m).max() < 1e-15
+
+
+def test_constant_forgetting_is_geometric_decay():
+    # constant f~ = c, i~ = 0: F_ij = sigma(c)^(i-j) (a fixed exponential decay)
+    rng = np.random.default_rng(12)
+    T, d, c = 33, 6, 0.7
+    q, k, v = (rng.standard_normal((T, d)) for _ in range(3))
+    args = _one_head(q, k, v, np.zeros(T), np.full(T, c))
+    s = 1.0 / (1.0 + math.exp(-c))
+    i, j = np.indices((T, T))
+    Dgeo = np.where(i >= j, s ** (i - j).astype(float), 0.0)
+    Dt = oracle.log_gate_matrix(np.full(T, c), np.zeros(T))
+    assert np.allclose(np.exp(Dt), Dgeo, rtol=1e-13, atol=0)
+    h, m, n = oracle.forward_stabilized(*args)
+    Ct = (q @ k.T) / math.sqrt(d) * Dgeo
+    ref = (Ct @ v) / np.maximum(np.abs(Ct.sum(axis=1)), 1.0)[:, None]
+    assert _rel(h[0, 0], ref) < 1e-12
+    assert np.allclose(m, 0.0, atol=1e-15)
+
+
+@pytest.mark.parametrize("ig", [-30.0, -2.0, 0.0, 3.5, 20.0])
+def test_single_step_closed_form(ig):
+    # T = 1: m = i~, s = q.k/sqrt(d), n = max(|s|, e^-i~), h~ = s v / n
+    rng = np.random.default_rng(13)
+    d = 9
+    q, k, v = (rng.standard_normal((1, d)) for _ in range(3))
+    args = _one_head(q, k, v, [ig], [1.3])
+    h, m, n = oracle.forward_stabilized(*args)
+    s = float(q[0] @ k[0]) / 3.0
+    nn = max(abs(s), math.exp(-ig))
+    assert m[0, 0, 0] == ig
+    assert math.isclose(n[0, 0, 0], nn, rel_tol=1e-14)
+    assert np.allclose(h[0, 0, 0], s * v[0] / nn, rtol=1e-14)
+
+
+def test_output_gate_closed_forms():
+    rng = np.random.default_rng(14)
+    h = rng.standard_normal((2, 3, 5, 4))
+    assert np.array_equal(oracle.output_gate(h, np.zeros_like(h)), h * 0.5)
+    o = rng.normal(0, 5, h.shape)
+    assert np.allclose(oracle.output_gate(h, o) + oracle.output_gate(h, -o), h, rtol=1e-14)
+    assert np.allclose(oracle.output_gate(h, np.log(3.0) * np.ones_like(h)), 0.75 * h, rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Consistency of the blocking and of the float32 twin (an error-floor
+# instrument, not the reference)
+# ---------------------------------------------------------------------------
+
+def test_row_blocking_and_rows_api_consistent():
+    x = W.make(dict(B=1, NH=2, T=130, d=16, dtype="fp32", igate=("normal", 0, 2),
+                    fgate=("normal", 3, 1.5)), seed=9)
+    args = (x["q"], x["k"], x["v"], x["igate"], x["fgate"])
+    h1, m1, n1 = oracle.forward_stabilized(*args, block_rows=1000)
+    h2, m2, n2 = oracle.forward_stabilized(*args, block_rows=17)
+    assert _rel(h2, h1) < 1e-14 and _rel(m2, m1) < 1e-14 and _rel(n2, n1) < 1e-14
+    rows = [0, 64, 129, 7]
+    h3, m3, n3, _, _ = oracle.forward_rows(*args, 0, 1, rows)
+    assert _rel(h3, h1[0, 1, rows]) < 1e-14
+    assert _rel(m3, m1[0, 1, rows]) < 1e-14 and _rel(n3, n1[0, 1, rows]) < 1e-14
+
+
+def test_float32_twin_is_close():
+    x = W.make("small_bf16", seed=0)
+    sub = {k: x[k][:1, :1, :128] for k in ("q", "k", "v", "igate", "fgate")}
+    args = (sub["q"], sub["k"], sub["v"], sub["igate"], sub["fgate"])
+    h64, m64, n64 = oracle.forward_stabilized(*args)
+    h32, m32, n32 = oracle.forward_stabilized(*args, dtype=np.float32)
+    assert h32.dtype == np.float32
+    assert _rel(h32, h64) < 1e-4 and _rel(n32, n64) < 1e-5
+    assert np.abs(m32 - m64).max() / max(np.abs(m64).max(), 1) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# Mutation tests: plausible mistakes planted in the oracle must fail a pin.
+# ---------------------------------------------------------------------------
+
+def _pins_pass(monkeypatch_target=None):
+    try:
+        for ex in EXAMPLES:
+            test_exact_rational_example_stabilized(ex)
+        test_tiny_workload_forms_agree()
+        test_no_forgetting_unit_input_is_causal_linear_attention()
+        test_constant_forgetting_is_geometric_decay()
+    except AssertionError:
+        return False
+    return True
+
+
+MUTANTS = {
+    # log sigma with a sign error in the correction term
+    "logsig_sign": ("log_sigmoid",
+                    lambda x: np.minimum(np.asarray(x, float), 0) + np.log1p(np.exp(-np.abs(np.asarray(x, float))))),
+    # forget activation exp instead of sigma in the log domain (f-bar = f~)
+    "logsig_identity": ("log_sigmoid", lambda x: np.asarray(x, float)),
+    # prefix sum off by one (cs_i - cs_j would then cover k = j..i-1)
+    "cumsum_shift": ("log_gate_matrix", None),
+    # the 1/sqrt(d) of the keys dropped
+    "no_sqrt_d": ("_rows_one_head", None),
+    # Q K^T transposed to K Q^T
+    "transposed": ("_rows_one_head", None),
+    # floor uses exp(+m)
+    "floor_sign": ("_rows_one_head", None),
+}
+
+
+def _mutant_rows(kind):
+    def rows(q, k, v, ig, fg, rows, dtype):
+        T, d = q.shape
+        rows = np.asarray(rows)
+        ncol = int(rows.max()) + 1
+        Dt = om.log_gate_matrix(fg[:ncol], ig[:ncol], rows=rows, dtype=dtype)
+        m = Dt.max(axis=1)
+        Dp = np.exp(Dt - m[:, None])
+        scale = 1.0 if kind == "no_sqrt_d" else math.sqrt(d)
+        if kind == "transposed":
+            S = (k[rows] @ q[:ncol].T) / scale
+        else:
+            S = (q[rows] @ k[:ncol].T) / scale
+        Ct = S * Dp
+        b = Ct.sum(axis=1)
+        floor = np.exp(m) if kind == "floor_sign" else np.exp(-m)
+        n = np.maximum(np.abs(b), floor)
+        h = (Ct / n[:, None]) @ v[:ncol]
+        return h, m, n, b, np.abs(Ct).sum(axis=1)
+    return rows
+
+
+def _mutant_lgm(fgate, igate, rows=None, dtype=np.float64):
+    fbar = om.log_sigmoid(fgate)
+    ig = np.asarray(igate, float).reshape(-1)
+    T = fbar.shape[0]
+    cs = np.concatenate([[0.0], np.cumsum(fbar)[:-1]])  # exclusive: wrong by one
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    Dt = cs[rows][:, None] - cs[None, :] + ig[None, :]
+    Dt[np.arange(T)[None, :] > rows[:, None]] = -np.inf
+    return Dt
+
+
+def test_pins_pass_unmutated():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    if attr == "_rows_one_head":
+        fn = _mutant_rows(name)
+    elif attr == "log_gate_matrix":
+        fn = _mutant_lgm
+    monkeypatch.setattr(om, attr, fn)
+    assert not _pins_pass(), f"mutant {name} survived every pin"
