@@ -1,0 +1,151 @@
+/*
+ * mlstm.h -- C ABI of the MI355X (gfx950) stabilized parallel mLSTM forward pass.
+ *
+ * The operation is the stabilized parallel forward pass of the mLSTM cell of
+ * "xLSTM: Extended Long Short-Term Memory", Appendix A.3: the parallel form
+ * ("Parallel mLSTM Forward Pass", Eqs. 71-77) in the stabilized version that
+ * opens "Parallel mLSTM Backward Pass" (Eqs. 79-86), with the log forget gate
+ * matrix of Eq. 101.  For one head with queries, keys, values Q, K, V (T x d)
+ * and gate pre-activations f~, i~ (length T):
+ *
+ *   fbar_k   = log sigmoid(f~_k)                                   (Eq. 101)
+ *   D~_ij    = sum_{k=j+1..i} fbar_k + i~_j  for j <= i, -inf above (Eqs. 79, 101, 72)
+ *   m_i      = max_j D~_ij                                         (Eq. 80)
+ *   D'_ij    = exp(D~_ij - m_i)                                    (Eq. 81)
+ *   C~'_ij   = (q_i . k_j / sqrt(d)) D'_ij                          (Eq. 82)
+ *   b_i      = sum_j C~'_ij                                        (Eq. 83)
+ *   n_i      = max(|b_i|, exp(-m_i))                               (Eq. 84)
+ *   h~_i     = sum_j C~'_ij v_j / n_i                              (Eqs. 85, 86)
+ *
+ * Heads are independent (the xLSTM cell has no memory mixing across heads),
+ * so every call processes B x NH heads at once.
+ *
+ * Layouts (all row-major, contiguous, no strides):
+ *   q, k, v, h_out  [B][NH][T][d]   element type given by `dtype`
+ *   igate, fgate    [B][NH][T]      float32 (i~ and f~ pre-activations)
+ *   m_out, n_out    [B][NH][T]      float32
+ * k is passed UNSCALED: the library applies the 1/sqrt(d) of Eq. 82.
+ *
+ * Ownership: every pointer is device memory owned by the caller, on the
+ * device that is current when the call is made.  The library never frees or
+ * retains a caller pointer beyond the work it enqueues.  Outputs are fully
+ * overwritten.  Inputs and outputs must not alias.
+ *
+ * Ordering: calls are asynchronous on the given HIP stream (NULL = the null
+ * stream); results are valid once that stream has synchronized.  No host
+ * synchronization happens inside the library.
+ *
+ * Errors: every argument check runs before any device work; on error nothing
+ * is launched, no output is touched, and a negative status is returned.
+ * Faults inside a kernel surface at the caller's next synchronization, as for
+ * any stream API.  No C++ exception crosses this interface.
+ *
+ * Numerics: gates, m and n are float32.  For MLSTM_BF16 the two contractions
+ * run on bf16 matrix cores with float32 accumulation; the row sums b are taken
+ * from the float32 C~' before it is rounded to bf16; h_out is rounded to
+ * nearest even.  Inputs must be finite; NaN/Inf propagate and are not checked.
+ * Results are bitwise reproducible run to run (fixed reduction order, no
+ * atomics).
+ */
+#ifndef MLSTM_H
+#define MLSTM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of q, k, v, h_out */
+enum { MLSTM_FP32 = 0, MLSTM_BF16 = 1 };
+
+/* tile-kernel selector for mlstm_causal_tiles */
+enum {
+  MLSTM_KERNEL_AUTO = 0,   /* bf16 -> matrix-core kernel, fp32 -> vector kernel */
+  MLSTM_KERNEL_MFMA = 1,   /* bf16 only: bf16 MFMA tiles (the production path) */
+  MLSTM_KERNEL_VECTOR = 2  /* any dtype: float32 vector-ALU tiles, no bf16 rounding of C~' */
+};
+
+/* status codes */
+enum {
+  MLSTM_OK = 0,
+  MLSTM_ERR_NULL = -1,        /* a required pointer is NULL */
+  MLSTM_ERR_SHAPE = -2,       /* B, NH, T or d < 1, or a size overflows */
+  MLSTM_ERR_DTYPE = -3,       /* dtype not MLSTM_FP32 / MLSTM_BF16 */
+  MLSTM_ERR_HEAD_DIM = -4,    /* d not a multiple of 16 in [16, 512] */
+  MLSTM_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+  MLSTM_ERR_HIP = -6,         /* a HIP allocation or launch failed */
+  MLSTM_ERR_WORKSPACE = -7,   /* caller workspace smaller than mlstm_workspace_bytes */
+  MLSTM_ERR_KERNEL = -8       /* unknown kernel selector, or MFMA asked for fp32 */
+};
+
+/*
+ * mlstm_parallel_fwd -- the whole forward pass (Eqs. 79-86) for B x NH heads.
+ *   q, k, v   in   [B][NH][T][d], dtype
+ *   igate     in   [B][NH][T] float32, i~ (input gate pre-activations, Eq. 72)
+ *   fgate     in   [B][NH][T] float32, f~ (forget gate pre-activations, Eq. 71;
+ *                  sigmoid forget activation; f~ at t = 0 never affects a result)
+ *   h_out     out  [B][NH][T][d], dtype: h~ (Eq. 86), before any output gate
+ *   m_out     out  [B][NH][T] float32: the row maximum m (Eq. 80)
+ *   n_out     out  [B][NH][T] float32: the normalizer n (Eq. 84)
+ *   B, NH, T  >= 1;  d a multiple of 16 in [16, 512]
+ *   dtype     MLSTM_FP32 or MLSTM_BF16
+ * Runs on the null stream with a library-allocated, stream-ordered workspace.
+ * Returns MLSTM_OK or a negative status.
+ */
+int mlstm_parallel_fwd(const void* q, const void* k, const void* v,
+                       const float* igate, const float* fgate,
+                       void* h_out, float* m_out, float* n_out,
+                       int64_t B, int64_t NH, int64_t T, int64_t d, int dtype);
+
+/* As mlstm_parallel_fwd, enqueued on `stream` (a hipStream_t; NULL = null stream). */
+int mlstm_parallel_fwd_stream(const void* q, const void* k, const void* v,
+                              const float* igate, const float* fgate,
+                              void* h_out, float* m_out, float* n_out,
+                              int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
+                              void* stream);
+
+/*
+ * The same pass split into its two stages with a caller-owned workspace, for
+ * callers that time or schedule the stages separately.
+ *
+ * mlstm_workspace_bytes: bytes of device workspace the two stages need for
+ * B x NH heads of length T (0 if the sizes are invalid).
+ */
+size_t mlstm_workspace_bytes(int64_t B, int64_t NH, int64_t T);
+
+/*
+ * mlstm_gate_scan -- stage 1: the gate-only part of Eqs. 79-81 and 101.
+ * Computes log sigmoid(f~), its prefix sums, and the row maximum
+ *   m_i = max_{j<=i} (sum_{k=j+1..i} fbar_k + i~_j)                 (Eq. 80)
+ * through the equivalent recurrence m_i = max(m_{i-1} + fbar_i, i~_i),
+ * m_0 = i~_0, before any Q K^T work.  Writes m_out and the per-row and
+ * per-column exponent terms and block anchors the tile stage reads into
+ * `workspace` (device memory, >= mlstm_workspace_bytes(B, NH, T) bytes,
+ * 256-byte aligned).  `d` is needed for the 1/sqrt(d) folded into the
+ * exponent terms.
+ */
+int mlstm_gate_scan(const float* igate, const float* fgate, float* m_out,
+                    void* workspace, size_t workspace_bytes,
+                    int64_t B, int64_t NH, int64_t T, int64_t d, void* stream);
+
+/*
+ * mlstm_causal_tiles -- stage 2: Eqs. 81-86 over causal tiles.  Reads q, k,
+ * v, m (from stage 1) and the workspace stage 1 wrote on the same stream, and
+ * writes h_out and n_out.  `kernel` is an MLSTM_KERNEL_* selector.
+ */
+int mlstm_causal_tiles(const void* q, const void* k, const void* v, const float* m,
+                       const void* workspace, size_t workspace_bytes,
+                       void* h_out, float* n_out,
+                       int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
+                       int kernel, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* mlstm_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLSTM_H */

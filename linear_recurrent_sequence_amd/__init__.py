@@ -7,14 +7,12 @@ library; the first call into the binding does, and fails loudly if it is
 missing.  ``workloads`` draws the seeded synthetic inputs.
 """
 
+import importlib
+
 __all__ = ["mlstm", "workloads"]
 
 
 def __getattr__(name):
-    if name == "mlstm":
-        from . import mlstm
-        return mlstm
-    if name == "workloads":
-        from . import workloads
-        return workloads
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

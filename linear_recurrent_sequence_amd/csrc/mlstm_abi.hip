@@ -1,0 +1,152 @@
+// C ABI of libmlstm (declared in include/mlstm.h): argument validation,
+// workspace handling, and the two kernel launches of the stabilized parallel
+// mLSTM forward pass (xLSTM appendix A.3, Eqs. 79-86).
+#include "mlstm.h"
+#include "mlstm_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+using mlstm::Workspace;
+
+constexpr int64_t kMaxT = int64_t(1) << 30;
+constexpr int64_t kMaxElems = int64_t(1) << 46;
+
+int check_shape(int64_t B, int64_t NH, int64_t T, int64_t d) {
+  if (B < 1 || NH < 1 || T < 1 || d < 1) return MLSTM_ERR_SHAPE;
+  if (T > kMaxT || B > (int64_t(1) << 31) || NH > (int64_t(1) << 31)) return MLSTM_ERR_SHAPE;
+  const int64_t H = B * NH;
+  if (H > (int64_t(1) << 31) - 1) return MLSTM_ERR_SHAPE;
+  const int64_t Tp = mlstm::padded_len(T);
+  if (H > kMaxElems / Tp) return MLSTM_ERR_SHAPE;
+  // launch grids are one-dimensional: (T / 16) x H workgroups at most
+  if (((Tp / 16) * H) > int64_t(0xFFFFFFFF)) return MLSTM_ERR_SHAPE;
+  if (d % 16 != 0 || d > 512) return MLSTM_ERR_HEAD_DIM;
+  if (H * Tp > kMaxElems / d) return MLSTM_ERR_SHAPE;
+  return MLSTM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MLSTM_OK : MLSTM_ERR_HIP; }
+
+int check_scan_args(const float* igate, const float* fgate, const float* m_out, const void* ws) {
+  if (!igate || !fgate || !m_out || !ws) return MLSTM_ERR_NULL;
+  if (!aligned16(igate) || !aligned16(fgate) || !aligned16(m_out)) return MLSTM_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return MLSTM_ERR_ALIGN;
+  return MLSTM_OK;
+}
+
+int check_tile_args(const void* q, const void* k, const void* v, const float* m, const void* ws,
+                    const void* h_out, const float* n_out, int dtype, int kernel) {
+  if (!q || !k || !v || !m || !ws || !h_out || !n_out) return MLSTM_ERR_NULL;
+  if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
+  if (kernel != MLSTM_KERNEL_AUTO && kernel != MLSTM_KERNEL_MFMA && kernel != MLSTM_KERNEL_VECTOR)
+    return MLSTM_ERR_KERNEL;
+  if (kernel == MLSTM_KERNEL_MFMA && dtype != MLSTM_BF16) return MLSTM_ERR_KERNEL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(m) || !aligned16(h_out) ||
+      !aligned16(n_out))
+    return MLSTM_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return MLSTM_ERR_ALIGN;
+  return MLSTM_OK;
+}
+
+int run_tiles(const void* q, const void* k, const void* v, const float* m, const Workspace& w,
+              void* h_out, float* n_out, int64_t H, int64_t T, int64_t d, int dtype, int kernel,
+              hipStream_t stream) {
+  const bool use_mfma =
+      kernel == MLSTM_KERNEL_MFMA || (kernel == MLSTM_KERNEL_AUTO && dtype == MLSTM_BF16);
+  if (use_mfma)
+    return hip_status(mlstm::launch_tiles_mfma(q, k, v, m, w, h_out, n_out, H, T, d, stream));
+  return hip_status(mlstm::launch_tiles_vector(q, k, v, m, w, h_out, n_out, H, T, d,
+                                               dtype == MLSTM_BF16, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mlstm_workspace_bytes(int64_t B, int64_t NH, int64_t T) {
+  if (check_shape(B, NH, T, 16) != MLSTM_OK) return 0;
+  return mlstm::workspace_bytes(B * NH, T);
+}
+
+int mlstm_gate_scan(const float* igate, const float* fgate, float* m_out, void* workspace,
+                    size_t workspace_bytes, int64_t B, int64_t NH, int64_t T, int64_t d,
+                    void* stream) {
+  int st = check_scan_args(igate, fgate, m_out, workspace);
+  if (st != MLSTM_OK) return st;
+  if ((st = check_shape(B, NH, T, d)) != MLSTM_OK) return st;
+  const int64_t H = B * NH;
+  if (workspace_bytes < mlstm::workspace_bytes(H, T)) return MLSTM_ERR_WORKSPACE;
+  const Workspace w = mlstm::carve(workspace, H, T);
+  return hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int mlstm_causal_tiles(const void* q, const void* k, const void* v, const float* m,
+                       const void* workspace, size_t workspace_bytes, void* h_out, float* n_out,
+                       int64_t B, int64_t NH, int64_t T, int64_t d, int dtype, int kernel,
+                       void* stream) {
+  int st = check_tile_args(q, k, v, m, workspace, h_out, n_out, dtype, kernel);
+  if (st != MLSTM_OK) return st;
+  if ((st = check_shape(B, NH, T, d)) != MLSTM_OK) return st;
+  const int64_t H = B * NH;
+  if (workspace_bytes < mlstm::workspace_bytes(H, T)) return MLSTM_ERR_WORKSPACE;
+  const Workspace w = mlstm::carve(const_cast<void*>(workspace), H, T);
+  return run_tiles(q, k, v, m, w, h_out, n_out, H, T, d, dtype, kernel,
+                   static_cast<hipStream_t>(stream));
+}
+
+int mlstm_parallel_fwd_stream(const void* q, const void* k, const void* v, const float* igate,
+                              const float* fgate, void* h_out, float* m_out, float* n_out,
+                              int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
+                              void* stream) {
+  if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
+  int st = check_shape(B, NH, T, d);
+  if (st != MLSTM_OK) return st;
+  if (!q || !k || !v || !igate || !fgate || !h_out || !m_out || !n_out) return MLSTM_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(igate) ||
+      !aligned16(fgate) || !aligned16(h_out) || !aligned16(m_out) || !aligned16(n_out))
+    return MLSTM_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t H = B * NH;
+  const size_t bytes = mlstm::workspace_bytes(H, T);
+  void* ws = nullptr;
+  // stream-ordered allocation: safe under concurrent calls on different streams
+  if (hipMallocAsync(&ws, bytes, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return MLSTM_ERR_HIP;
+  }
+  const Workspace w = mlstm::carve(ws, H, T);
+  st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d, s));
+  if (st == MLSTM_OK)
+    st = run_tiles(q, k, v, m_out, w, h_out, n_out, H, T, d, dtype, MLSTM_KERNEL_AUTO, s);
+  if (hipFreeAsync(ws, s) != hipSuccess && st == MLSTM_OK) st = MLSTM_ERR_HIP;
+  return st;
+}
+
+int mlstm_parallel_fwd(const void* q, const void* k, const void* v, const float* igate,
+                       const float* fgate, void* h_out, float* m_out, float* n_out, int64_t B,
+                       int64_t NH, int64_t T, int64_t d, int dtype) {
+  return mlstm_parallel_fwd_stream(q, k, v, igate, fgate, h_out, m_out, n_out, B, NH, T, d,
+                                   dtype, nullptr);
+}
+
+const char* mlstm_strerror(int status) {
+  switch (status) {
+    case MLSTM_OK: return "success";
+    case MLSTM_ERR_NULL: return "a required pointer is NULL";
+    case MLSTM_ERR_SHAPE: return "invalid shape: B, NH, T, d must be >= 1 and sizes must not overflow";
+    case MLSTM_ERR_DTYPE: return "invalid dtype: expected MLSTM_FP32 or MLSTM_BF16";
+    case MLSTM_ERR_HEAD_DIM: return "unsupported head dimension: d must be a multiple of 16 in [16, 512]";
+    case MLSTM_ERR_ALIGN: return "misaligned pointer: tensors need 16-byte, workspaces 256-byte alignment";
+    case MLSTM_ERR_HIP: return "HIP allocation or kernel launch failed";
+    case MLSTM_ERR_WORKSPACE: return "workspace smaller than mlstm_workspace_bytes()";
+    case MLSTM_ERR_KERNEL: return "unknown kernel selector, or the MFMA kernel asked for float32";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

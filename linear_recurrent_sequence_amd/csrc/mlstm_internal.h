@@ -1,0 +1,77 @@
+// Internal declarations shared by the HIP translation units of libmlstm.
+//
+// Workspace written by the gate scan and read by the tile kernels, for H
+// heads of length T, padded to Tp = ceil(T / 128) * 128 positions:
+//
+//   anchor [H][Tp/64]  float64  A_b = (sum of fbar over positions < 64 b) * log2(e)
+//   rowt   [H][Tp]     float32  r_i = (loc_i - m_i - ln(d)/2) * log2(e)
+//   colt   [H][Tp]     float32  c_j = (i~_j - loc_j) * log2(e)    (-inf on padding)
+//
+// where fbar = log sigmoid(f~) and loc_i = (inclusive prefix sum of fbar up to
+// i) - (the same sum up to the start of i's 64-position block), so that, for
+// j <= i (Eqs. 79-82 and 101 of the xLSTM appendix),
+//
+//   log2( D'_ij / sqrt(d) ) = (A_{i/64} - A_{j/64}) + r_i + c_j.
+//
+// The block anchors keep the difference of two long prefix sums out of
+// float32: the anchor difference is taken in float64 and rounded once, and
+// every other term is bounded by one block's worth of forget gates.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlstm {
+
+constexpr int kRowPad = 128;     // T is padded to a multiple of this
+constexpr int kAnchorBlock = 64; // positions per float64 anchor
+
+struct Workspace {
+  double* anchor;
+  float* rowt;
+  float* colt;
+  int64_t Tp;
+  int64_t nblk;
+};
+
+inline int64_t padded_len(int64_t T) { return (T + kRowPad - 1) / kRowPad * kRowPad; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline size_t workspace_bytes(int64_t H, int64_t T) {
+  const int64_t Tp = padded_len(T);
+  return align256(size_t(H) * size_t(Tp / kAnchorBlock) * sizeof(double)) +
+         2 * align256(size_t(H) * size_t(Tp) * sizeof(float));
+}
+
+inline Workspace carve(void* base, int64_t H, int64_t T) {
+  Workspace w;
+  w.Tp = padded_len(T);
+  w.nblk = w.Tp / kAnchorBlock;
+  char* p = static_cast<char*>(base);
+  w.anchor = reinterpret_cast<double*>(p);
+  p += align256(size_t(H) * size_t(w.nblk) * sizeof(double));
+  w.rowt = reinterpret_cast<float*>(p);
+  p += align256(size_t(H) * size_t(w.Tp) * sizeof(float));
+  w.colt = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// Stage 1: gate scan (one workgroup per head).
+hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out,
+                            const Workspace& ws, int64_t H, int64_t T, int64_t d,
+                            hipStream_t stream);
+
+// Stage 2, bf16 matrix-core tiles.  Returns hipErrorInvalidValue for an
+// unsupported head dimension (none for d % 16 == 0, 16 <= d <= 512).
+hipError_t launch_tiles_mfma(const void* q, const void* k, const void* v, const float* m,
+                             const Workspace& ws, void* h_out, float* n_out,
+                             int64_t H, int64_t T, int64_t d, hipStream_t stream);
+
+// Stage 2, float32 vector-ALU tiles; is_bf16 selects the element type.
+hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, const float* m,
+                               const Workspace& ws, void* h_out, float* n_out,
+                               int64_t H, int64_t T, int64_t d, bool is_bf16,
+                               hipStream_t stream);
+
+}  // namespace mlstm

@@ -1,0 +1,126 @@
+// Stage 2, float32 vector-ALU variant: Eqs. 81-86 of the xLSTM appendix
+// ("Parallel mLSTM Backward Pass" opens with the stabilized forward pass) over
+// causal 16 x 16 tiles.
+//
+// This is the path for float32 inputs and a second, independent GPU
+// evaluation for bf16 inputs: both contractions run on the vector ALUs in
+// float32 and C~' is never rounded to bf16.  One workgroup of 256 threads owns
+// 16 query rows of one head; thread (r, c) of the 16 x 16 grid forms one
+// entry of S = Q K^T and of C~' per key tile, and then accumulates output
+// columns c, c + 16, ... of row r.
+#include "mlstm_internal.h"
+
+#include <hip/hip_bf16.h>
+
+namespace mlstm {
+namespace {
+
+constexpr int kVT = 16;        // query rows per workgroup and keys per tile
+constexpr int kVMaxD = 512;
+constexpr int kVPad = kVMaxD + 1;
+
+__device__ inline float load_elem(const float* p) { return *p; }
+__device__ inline float load_elem(const __hip_bfloat16* p) { return __bfloat162float(*p); }
+__device__ inline void store_elem(float* p, float x) { *p = x; }
+__device__ inline void store_elem(__hip_bfloat16* p, float x) { *p = __float2bfloat16(x); }
+
+template <typename Tin>
+__global__ __launch_bounds__(256) void tiles_vector_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const float* __restrict__ m_in, const double* __restrict__ anchor,
+    const float* __restrict__ rowt, const float* __restrict__ colt, Tin* __restrict__ h_out,
+    float* __restrict__ n_out, int64_t T, int d, int64_t Tp, int64_t nblk, int64_t row_tiles) {
+  __shared__ float Qs[kVT][kVPad];
+  __shared__ float Ks[kVT][kVPad];
+  __shared__ float Vs[kVT][kVMaxD];
+  __shared__ float Ps[kVT][kVT + 1];
+
+  const int tid = threadIdx.x;
+  const int rl = tid / kVT;  // local query row
+  const int cl = tid % kVT;  // local key (S phase) / column group (PV phase)
+  const int64_t head = blockIdx.x / row_tiles;
+  const int64_t q0 = (blockIdx.x % row_tiles) * kVT;
+  const int64_t qi = q0 + rl;
+  const int64_t hoff = head * T * int64_t(d);
+
+  for (int idx = tid; idx < kVT * d; idx += 256) {
+    const int r = idx / d, c = idx % d;
+    Qs[r][c] = (q0 + r < T) ? load_elem(q + hoff + (q0 + r) * d + c) : 0.0f;
+  }
+  const float r_i = rowt[head * Tp + qi];  // qi < Tp: Tp is T rounded up to 128
+  const double a_i = anchor[head * nblk + q0 / kAnchorBlock];
+
+  float acc[kVMaxD / kVT];
+#pragma unroll
+  for (int u = 0; u < kVMaxD / kVT; ++u) acc[u] = 0.0f;
+  float bsum = 0.0f;
+
+  const int64_t last_key = (q0 + kVT - 1 < T ? q0 + kVT - 1 : T - 1);
+  for (int64_t k0 = 0; k0 <= last_key; k0 += kVT) {
+    __syncthreads();  // previous tile fully consumed
+    for (int idx = tid; idx < kVT * d; idx += 256) {
+      const int r = idx / d, c = idx % d;
+      const bool in = k0 + r < T;
+      Ks[r][c] = in ? load_elem(k + hoff + (k0 + r) * d + c) : 0.0f;
+      Vs[r][c] = in ? load_elem(v + hoff + (k0 + r) * d + c) : 0.0f;
+    }
+    __syncthreads();
+    const int64_t kj = k0 + cl;
+    float s = 0.0f;
+    for (int c = 0; c < d; ++c) s = fmaf(Qs[rl][c], Ks[cl][c], s);
+    // log2(D'_ij / sqrt(d)) = (A_{i/64} - A_{j/64}) + r_i + c_j   (Eqs. 79, 81, 82)
+    const float delta = float(a_i - anchor[head * nblk + k0 / kAnchorBlock]);
+    const float ex = delta + r_i + colt[head * Tp + kj];
+    const bool valid = (kj <= qi) && (kj < T) && (qi < T);
+    const float cv = valid ? s * exp2f(ex) : 0.0f;  // C~'_ij (Eq. 82)
+    bsum += cv;                                     // b_i (Eq. 83), float32
+    Ps[rl][cl] = cv;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kVMaxD / kVT; ++u) {
+      const int c = cl + kVT * u;
+      if (c < d) {
+        float a = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kVT; ++t) a = fmaf(Ps[rl][t], Vs[t][c], a);
+        acc[u] += a;
+      }
+    }
+  }
+  // the 16 threads of a row are 16 consecutive lanes of one wave
+#pragma unroll
+  for (int off = kVT / 2; off > 0; off >>= 1) bsum += __shfl_xor(bsum, off, 64);
+  if (qi < T) {
+    const float nn = fmaxf(fabsf(bsum), expf(-m_in[head * T + qi]));  // Eq. 84
+    if (cl == 0) n_out[head * T + qi] = nn;
+#pragma unroll
+    for (int u = 0; u < kVMaxD / kVT; ++u) {
+      const int c = cl + kVT * u;
+      if (c < d) store_elem(h_out + hoff + qi * d + c, acc[u] / nn);  // Eqs. 85, 86
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, const float* m,
+                               const Workspace& ws, void* h_out, float* n_out, int64_t H,
+                               int64_t T, int64_t d, bool is_bf16, hipStream_t stream) {
+  const int64_t row_tiles = (T + kVT - 1) / kVT;
+  const dim3 grid(unsigned(row_tiles * H));
+  if (is_bf16) {
+    using B16 = __hip_bfloat16;
+    hipLaunchKernelGGL(tiles_vector_kernel<B16>, grid, dim3(256), 0, stream,
+                       static_cast<const B16*>(q), static_cast<const B16*>(k),
+                       static_cast<const B16*>(v), m, ws.anchor, ws.rowt, ws.colt,
+                       static_cast<B16*>(h_out), n_out, T, int(d), ws.Tp, ws.nblk, row_tiles);
+  } else {
+    hipLaunchKernelGGL(tiles_vector_kernel<float>, grid, dim3(256), 0, stream,
+                       static_cast<const float*>(q), static_cast<const float*>(k),
+                       static_cast<const float*>(v), m, ws.anchor, ws.rowt, ws.colt,
+                       static_cast<float*>(h_out), n_out, T, int(d), ws.Tp, ws.nblk, row_tiles);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mlstm

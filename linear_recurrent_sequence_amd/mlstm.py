@@ -1,0 +1,179 @@
+"""Thin ctypes binding over libmlstm.so (the C ABI in include/mlstm.h).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or the tensors are
+not on a GPU, the call raises.
+
+    h, m, n = parallel_fwd(q, k, v, igate, fgate)
+
+q, k, v: [B, NH, T, d] contiguous, float32 or bfloat16, on the current GPU.
+igate, fgate: [B, NH, T] contiguous float32 (input / forget gate pre-activations).
+Returns h~ (same dtype as q), m and n (float32), as defined by Eqs. 80, 84 and
+86 of the xLSTM appendix ("Parallel mLSTM Backward Pass" restates the
+stabilized forward pass).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmlstm.so")
+
+MLSTM_FP32, MLSTM_BF16 = 0, 1
+KERNELS = {"auto": 0, "mfma": 1, "vector": 2}
+
+_lib = None
+
+
+class MlstmError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def load_library():
+    """Load libmlstm.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m linear_recurrent_sequence_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.mlstm_parallel_fwd.argtypes = [vp] * 8 + [i64] * 4 + [i32]
+    lib.mlstm_parallel_fwd.restype = i32
+    lib.mlstm_parallel_fwd_stream.argtypes = [vp] * 8 + [i64] * 4 + [i32, vp]
+    lib.mlstm_parallel_fwd_stream.restype = i32
+    lib.mlstm_workspace_bytes.argtypes = [i64] * 3
+    lib.mlstm_workspace_bytes.restype = f
+    lib.mlstm_gate_scan.argtypes = [vp] * 4 + [f] + [i64] * 4 + [vp]
+    lib.mlstm_gate_scan.restype = i32
+    lib.mlstm_causal_tiles.argtypes = [vp] * 5 + [f] + [vp] * 2 + [i64] * 4 + [i32, i32, vp]
+    lib.mlstm_causal_tiles.restype = i32
+    lib.mlstm_strerror.argtypes = [i32]
+    lib.mlstm_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(status):
+    return load_library().mlstm_strerror(int(status)).decode()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return MLSTM_FP32
+    if t.dtype == torch.bfloat16:
+        return MLSTM_BF16
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check_inputs(q, k, v, igate, fgate):
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, NH, T, d], got shape {tuple(q.shape)}")
+    B, NH, T, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    for name, t in (("igate", igate), ("fgate", fgate)):
+        if tuple(t.shape) != (B, NH, T) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [B, NH, T] = {(B, NH, T)}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("igate", igate), ("fgate", fgate)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device:
+            raise ValueError("all tensors must be on the same device")
+    return B, NH, T, d
+
+
+def _stream_ptr(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def parallel_fwd(q, k, v, igate, fgate, out=None):
+    """Stabilized parallel mLSTM forward for B x NH heads -> (h, m, n).
+
+    ``out`` may be a tuple (h, m, n) of preallocated outputs.
+    """
+    lib = load_library()
+    B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
+    if out is None:
+        h = torch.empty_like(q)
+        m = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
+        n = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
+    else:
+        h, m, n = out
+    with torch.cuda.device(q.device):
+        st = lib.mlstm_parallel_fwd_stream(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
+            h.data_ptr(), m.data_ptr(), n.data_ptr(), B, NH, T, d, _dtype_code(q),
+            _stream_ptr(q.device))
+    if st != 0:
+        raise MlstmError(st, "mlstm_parallel_fwd")
+    return h, m, n
+
+
+def workspace_bytes(B, NH, T):
+    return int(load_library().mlstm_workspace_bytes(B, NH, T))
+
+
+def alloc_workspace(B, NH, T, device):
+    """A device workspace for gate_scan / causal_tiles (256-byte aligned)."""
+    nbytes = workspace_bytes(B, NH, T)
+    if nbytes == 0:
+        raise ValueError("invalid sizes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def gate_scan(igate, fgate, d, workspace, m=None):
+    """Stage 1: m (Eq. 80) and the exponent terms, written into ``workspace``."""
+    lib = load_library()
+    if igate.dim() != 3 or igate.shape != fgate.shape:
+        raise ValueError("igate and fgate must both be [B, NH, T]")
+    B, NH, T = igate.shape
+    for t in (igate, fgate):
+        if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32):
+            raise ValueError("gates must be contiguous float32 GPU tensors")
+    if m is None:
+        m = torch.empty((B, NH, T), dtype=torch.float32, device=igate.device)
+    with torch.cuda.device(igate.device):
+        st = lib.mlstm_gate_scan(igate.data_ptr(), fgate.data_ptr(), m.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel(), B, NH, T, d,
+                                 _stream_ptr(igate.device))
+    if st != 0:
+        raise MlstmError(st, "mlstm_gate_scan")
+    return m
+
+
+def causal_tiles(q, k, v, m, workspace, kernel="auto", out=None):
+    """Stage 2: h~ and n from q, k, v and the stage-1 results -> (h, n)."""
+    lib = load_library()
+    B, NH, T, d = _check_inputs(q, k, v, m, m)
+    if out is None:
+        h = torch.empty_like(q)
+        n = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
+    else:
+        h, n = out
+    with torch.cuda.device(q.device):
+        st = lib.mlstm_causal_tiles(q.data_ptr(), k.data_ptr(), v.data_ptr(), m.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel(), h.data_ptr(),
+                                    n.data_ptr(), B, NH, T, d, _dtype_code(q), KERNELS[kernel],
+                                    _stream_ptr(q.device))
+    if st != 0:
+        raise MlstmError(st, "mlstm_causal_tiles")
+    return h, n
+
+
+def parallel_fwd_staged(q, k, v, igate, fgate, kernel="auto"):
+    """Both stages with an explicit workspace and a chosen tile kernel."""
+    B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
+    ws = alloc_workspace(B, NH, T, q.device)
+    m = gate_scan(igate, fgate, d, ws)
+    h, n = causal_tiles(q, k, v, m, ws, kernel=kernel)
+    return h, m, n

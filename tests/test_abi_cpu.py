@@ -1,0 +1,93 @@
+"""The C-ABI library loads and exports every symbol include/mlstm.h declares,
+and its host-side argument checks reject bad calls before any device work.
+
+No call here reaches the HIP runtime: every call fails validation, which runs
+first and touches no device state.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_recurrent_sequence_amd import mlstm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlstm.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(mlstm.LIB_PATH),
+                               reason="libmlstm.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlstm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("mlstm_parallel_fwd", "mlstm_parallel_fwd_stream", "mlstm_gate_scan",
+                 "mlstm_causal_tiles", "mlstm_workspace_bytes", "mlstm_strerror"):
+        assert want in names
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mlstm.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+@needs_lib
+def test_strerror_and_workspace_size():
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        msg = mlstm.strerror(st)
+        assert msg and msg != "unknown status"
+    assert mlstm.strerror(-99) == "unknown status"
+    lib = mlstm.load_library()
+    # anchors (8 B per 64 positions) + two float32 terms per position, T padded to 128
+    assert lib.mlstm_workspace_bytes(1, 1, 64) == 256 + 2 * 512
+    assert lib.mlstm_workspace_bytes(8, 4, 2048) == 32 * 32 * 8 + 2 * 32 * 2048 * 4
+    assert lib.mlstm_workspace_bytes(0, 4, 2048) == 0
+    assert lib.mlstm_workspace_bytes(1, 1, 0) == 0
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced
+
+
+@needs_lib
+@pytest.mark.parametrize("case,status", [
+    (dict(q=0), -1), (dict(igate=0), -1), (dict(n_out=0), -1),
+    (dict(B=0), -2), (dict(T=0), -2), (dict(NH=-3), -2), (dict(d=0), -2),
+    (dict(dtype=2), -3), (dict(dtype=-1), -3),
+    (dict(d=8), -4), (dict(d=24), -4), (dict(d=528), -4),
+    (dict(q=FAKE + 8), -5), (dict(m_out=FAKE + 4), -5),
+])
+def test_parallel_fwd_rejects_before_device_work(case, status):
+    lib = mlstm.load_library()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, igate=FAKE, fgate=FAKE, h_out=FAKE, m_out=FAKE,
+                n_out=FAKE, B=1, NH=1, T=64, d=16, dtype=1)
+    args.update(case)
+    order = ["q", "k", "v", "igate", "fgate", "h_out", "m_out", "n_out", "B", "NH", "T", "d", "dtype"]
+    st = lib.mlstm_parallel_fwd(*[args[k] or None if k in order[:8] else args[k] for k in order])
+    assert st == status
+
+
+@needs_lib
+def test_staged_entry_points_reject_before_device_work():
+    lib = mlstm.load_library()
+    # workspace too small
+    assert lib.mlstm_gate_scan(FAKE, FAKE, FAKE, FAKE, 10, 1, 1, 64, 16, None) == -7
+    # misaligned workspace (needs 256 bytes)
+    assert lib.mlstm_gate_scan(FAKE, FAKE, FAKE, FAKE + 16, 1 << 20, 1, 1, 64, 16, None) == -5
+    # MFMA kernel for float32 inputs
+    assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE,
+                                  1, 1, 64, 16, 0, 1, None) == -8
+    # unknown kernel selector
+    assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE,
+                                  1, 1, 64, 16, 1, 7, None) == -8
+    assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, None, FAKE, 1 << 20, FAKE, FAKE,
+                                  1, 1, 64, 16, 1, 0, None) == -1
+    assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE,
+                                  1, 1, 64, 16, 1, 0, None) == -7
