@@ -12,22 +12,25 @@
 // applied once at the end.
 //
 // Transposed products keep every intermediate in registers:
-//   S^T (32 keys x 32 queries)  = K_J  Q^T          A = K from LDS, B = Q^T held in VGPRs
+//   S^T (32 keys x 32 queries)  = K_J  Q^T      A = K rows from LDS, B = Q^T in VGPRs
 //   C~'^T = S^T (.) D'^T, row sums b from the float32 C~' (Eq. 83)
-//   O^T (d x 32 queries)       += V_J^T C~'^T       A = V^T from LDS, B = bf16(C~'^T)
+//   O^T (d x 32 queries)       += V_J^T C~'^T   A = V^T via LDS transpose reads,
+//                                               B = bf16(C~'^T) straight from S^T
 // In the 32x32 accumulator layout a lane holds one query column and 16 key
-// rows, which is exactly the B-operand layout of the second product once the
-// 16 keys are listed in the order the lane holds them; V^T is stored in LDS
-// with its key axis permuted the same way (bits 2 and 3 of the key index
-// swapped), so the contraction pairs each V row with its own C~' entry.
+// rows; listed in the order the lane holds them, those 16 keys are the
+// B-operand slots of the second product, and the V^T operand is gathered in
+// the same key order by ds_read_b64_tr_b16 from V stored row-major in LDS.
+//
+// Data movement.  K, V (row-major, padded rows) and the column exponent terms
+// of tile J+1 are copied global -> LDS by the load-to-LDS path
+// (buffer_load_dwordx4 ... lds: no staging registers, no VALU) while tile J is
+// computed from the other buffer; one barrier per tile.  The copies go through
+// buffer resources whose range ends at the sequence end, so rows past it and
+// head-dimension padding arrive as zeros.
 //
 // Exponents: log2(D'_ij / sqrt(d)) = (A_{i/64} - A_{j/64}) + r_i + c_j with the
 // terms of the gate scan; the anchor difference is formed in float64 once per
-// (wave, tile).
-//
-// Pipelining: K, V^T and c of tile J+1 are fetched into registers while tile J
-// is computed from the other half of a double-buffered LDS area, then stored;
-// one barrier per tile.
+// (wave, tile), the key-tile anchor travelling with the tile into LDS.
 #include "mlstm_internal.h"
 
 namespace mlstm {
@@ -35,33 +38,33 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kBM = 128;   // query rows per workgroup
-constexpr int kBN = 32;    // keys per tile
+constexpr int kBM = 128;    // query rows per workgroup
+constexpr int kBN = 32;     // keys per tile
 constexpr int kThreads = 256;
-constexpr int kPf = 3;     // LDS fragment prefetch distance (MFMA steps)
+constexpr int kWaves = kThreads / 64;
+constexpr int kPf = 3;      // LDS fragment prefetch distance (MFMA steps)
+constexpr int kRsrcFlags = 0x00020000;  // buffer resource word 3: 32-bit data format
+constexpr unsigned kOutOfRange = 0x40000000u;  // a buffer offset that reads zeros
 
 template <int DP>
 struct Cfg {
   static_assert(DP % 32 == 0 && DP >= 32 && DP <= 512, "padded head dim");
-  static constexpr int KS = DP * 2 + 16;           // K tile row stride, bytes
-  static constexpr int VS = kBN * 2 + 16;          // V^T tile row stride, bytes
-  static constexpr int K_BYTES = kBN * KS;
-  static constexpr int V_BYTES = DP * VS;
-  static constexpr int C_BYTES = kBN * 4;
-  static constexpr int BUF = (K_BYTES + V_BYTES + C_BYTES + 15) / 16 * 16;
-  static constexpr int K_CHUNKS = kBN * DP / 8;    // 16-byte chunks of a K tile
-  static constexpr int K_PER = (K_CHUNKS + kThreads - 1) / kThreads;
-  static constexpr int V_UNITS = (kBN / 2) * (DP / 8);  // (key pair, 8 columns)
-  static constexpr int V_PER = (V_UNITS + kThreads - 1) / kThreads;
+  static constexpr int CH = DP / 8;               // 16-byte chunks per row
+  static constexpr int RSK = DP * 2 + 16;         // K row stride: 16 rows hit 16 distinct bank groups
+  static constexpr int RSV = DP * 2 + 64;         // V row stride: transpose reads 2-way at most
+  static constexpr int K_BYTES = kBN * RSK;
+  static constexpr int V_BYTES = kBN * RSV;
+  static constexpr int C_OFF = K_BYTES + V_BYTES;
+  static constexpr int A_OFF = C_OFF + kBN * 4;  // float64 anchor of the key tile
+  static constexpr int BUF = (A_OFF + 8 + 15) / 16 * 16;
 };
-
-// key position inside a 32-key tile as stored in V^T: swap bits 2 and 3
-__device__ __host__ constexpr int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
 
 // Heaviest row tiles first (a row tile I costs ~I + 1 key tiles), and when the
 // head count allows, every row tile of a head on the same XCD (workgroups are
@@ -78,22 +81,39 @@ __device__ inline void map_tile(int64_t wg, int64_t row_tiles, int64_t H, int64_
   }
 }
 
-__device__ inline bf16x8 load16(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+// 16 bytes per lane, global -> LDS at (wave-uniform) dst + 16 * lane, through
+// a buffer resource: offsets at or past `num_records` bytes read as zeros.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t num_records) {
+  const int n = num_records > 0x7FFFFFFF ? 0x7FFFFFFF : int(num_records);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcFlags);
+}
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voffset, 0, 0, 0);
+}
+// 4 bytes per lane, to dst + 4 * lane
+__device__ inline void dma4(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, voffset, 0, 0, 0);
+}
+
+__device__ inline i16x4 tr_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
 
 template <int DP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void tiles_mfma_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ m_in, const double* __restrict__ anchor,
-    const float* __restrict__ rowt, const float* __restrict__ colt, u16* __restrict__ h_out,
-    float* __restrict__ n_out, int64_t T, int d, int64_t Tp, int64_t nblk, int64_t row_tiles,
-    int64_t H) {
+    const float* __restrict__ rowt, const float* __restrict__ colt, u16* __restrict__ h_out, float* __restrict__ n_out, int64_t T,
+    int d, int64_t Tp, int64_t nblk, int64_t row_tiles, int64_t H) {
   using C = Cfg<DP>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::BUF];
+  // two distinct buffers, so the loads into one never alias reads of the other
+  __shared__ __attribute__((aligned(1024))) char smem0[C::BUF];
+  __shared__ __attribute__((aligned(1024))) char smem1[C::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;    // half-wave: selects 8 of the 16 reduction indices
   const int l32 = lane & 31;  // query column of this lane
   int64_t I, head;
@@ -102,10 +122,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int64_t q0 = I * kBM;
   const int64_t qw = q0 + 32 * w;  // first query row of this wave
   const int64_t qi = qw + l32;     // query row of this lane
+  const int dch = d / 8;           // real 16-byte chunks per row
 
-  // Q^T fragments: B operand of S^T = K Q^T, reduction index = head dim
-  // (branch-free: out-of-range rows and padded columns read a valid address
-  // and are replaced by zeros)
+  // Q^T fragments: B operand of S^T = K Q^T, reduction index = head dim.
+  // Branch-free: out-of-range rows and padded columns read a valid address
+  // and are replaced by zeros.
   bf16x8 qf[DP / 16];
   {
     const int64_t qrow = qi < T ? qi : T - 1;
@@ -114,8 +135,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       const int col = 16 * s + 8 * g;
       const bool ok = qi < T && col < d;
       const uint4 raw = *reinterpret_cast<const uint4*>(q + hoff + qrow * d + (ok ? col : 0));
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      const uint4 val = ok ? raw : z;
+      const uint4 val = ok ? raw : make_uint4(0, 0, 0, 0);
       qf[s] = *reinterpret_cast<const bf16x8*>(&val);
     }
   }
@@ -131,155 +151,127 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int64_t last_tile = (4 * I + 3 < n_key_tiles - 1) ? 4 * I + 3 : n_key_tiles - 1;
   const int64_t wave_last = (4 * I + w < n_key_tiles - 1) ? 4 * I + w : n_key_tiles - 1;
 
-  // ---- tile fetch (global -> registers) and store (registers -> LDS) ----
-  uint4 kreg[C::K_PER];
-  uint4 vreg[C::V_PER][2];
-  float4 creg;
-  auto fetch_k = [&](int64_t J) {
+  // ---- global -> LDS copy of tile J: each wave copies 8 K rows and 8 V rows.
+  // The buffer range ends at the last key of the sequence, so rows past it
+  // arrive as zeros; head-dimension padding reads an out-of-range offset.
+  auto load_tile = [&](int64_t J, char* buf) {
     const int64_t k0 = J * kBN;
+    const int64_t nrec = (T - k0 < kBN ? T - k0 : kBN) * int64_t(d) * 2;
+    const auto rk = make_rsrc(k + hoff + k0 * d, nrec);
+    const auto rv = make_rsrc(v + hoff + k0 * d, nrec);
 #pragma unroll
-    for (int it = 0; it < C::K_PER; ++it) {
-      const int u = tid + kThreads * it;
-      const int key = u / (DP / 8), dc = u % (DP / 8);
-      const bool ok = u < C::K_CHUNKS && k0 + key < T && 8 * dc < d;
-      const uint4 raw =
-          *reinterpret_cast<const uint4*>(k + hoff + (ok ? (k0 + key) * d + 8 * dc : 0));
-      kreg[it] = ok ? raw : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < kBN / 4) creg = *reinterpret_cast<const float4*>(colt + head * Tp + k0 + 4 * tid);
-  };
-  auto fetch_v = [&](int64_t J) {
-    const int64_t k0 = J * kBN;
-#pragma unroll
-    for (int it = 0; it < C::V_PER; ++it) {
-      const int u = tid + kThreads * it;
-      const int kp = u % (kBN / 2), dc = u / (kBN / 2);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t key = k0 + 2 * kp + e;
-        const bool ok = u < C::V_UNITS && key < T && 8 * dc < d;
-        const uint4 raw = *reinterpret_cast<const uint4*>(v + hoff + (ok ? key * d + 8 * dc : 0));
-        vreg[it][e] = ok ? raw : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kBN / kWaves; ++i) {
+      const int r = w * (kBN / kWaves) + i;
+      if (lane < C::CH) {
+        const unsigned off = lane < dch ? unsigned(r * d * 2 + 16 * lane) : kOutOfRange;
+        dma16(rk, off, buf + r * C::RSK);
+        dma16(rv, off, buf + C::K_BYTES + r * C::RSV);
       }
     }
-  };
-  auto store_k = [&](int buf) {
-    char* kb = smem + buf * C::BUF;
-    char* cb = kb + C::K_BYTES + C::V_BYTES;
-#pragma unroll
-    for (int it = 0; it < C::K_PER; ++it) {
-      const int u = tid + kThreads * it;
-      const int key = u / (DP / 8), dc = u % (DP / 8);
-      if (u < C::K_CHUNKS) *reinterpret_cast<uint4*>(kb + key * C::KS + 16 * dc) = kreg[it];
-    }
-    if (tid < kBN / 4) *reinterpret_cast<float4*>(cb + 16 * tid) = creg;
-  };
-  auto store_v = [&](int buf) {
-    char* vb = smem + buf * C::BUF + C::K_BYTES;
-#pragma unroll
-    for (int it = 0; it < C::V_PER; ++it) {
-      const int u = tid + kThreads * it;
-      const int kp = u % (kBN / 2), dc = u / (kBN / 2);
-      if (u < C::V_UNITS) {
-        const u16* r0 = reinterpret_cast<const u16*>(&vreg[it][0]);
-        const u16* r1 = reinterpret_cast<const u16*>(&vreg[it][1]);
-        const int pos = vt_pos(2 * kp);  // keys 2kp, 2kp+1 stay adjacent
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const unsigned pair = unsigned(r0[e]) | (unsigned(r1[e]) << 16);
-          *reinterpret_cast<unsigned*>(vb + (8 * dc + e) * C::VS + 2 * pos) = pair;
-        }
-      }
-    }
+    if (w == 0 && lane < kBN / 4)
+      dma16(make_rsrc(colt + head * Tp, Tp * 4), unsigned((k0 + 4 * lane) * 4), buf + C::C_OFF);
+    if (w == 1 && lane < 2)
+      dma4(make_rsrc(anchor + head * nblk, nblk * 8),
+           unsigned((k0 / kAnchorBlock) * 8 + 4 * lane), buf + C::A_OFF);
   };
 
-  fetch_k(0);
-  fetch_v(0);
-  store_k(0);
-  store_v(0);
-  __syncthreads();
+  // per-lane LDS offsets of the operand reads
+  const int koff = l32 * C::RSK + 16 * g;
+  const int j16 = l32 & 15;
+  const int voff = (4 * g + (j16 >> 2)) * C::RSV + 32 * (l32 >> 4) + 8 * (j16 & 3);
 
-  for (int64_t J = 0; J <= last_tile; ++J) {
-    const int buf = int(J & 1);
-    const bool more = J + 1 <= last_tile;
-    const bool active = J <= wave_last;
-    if (more) fetch_k(J + 1);
+  auto compute = [&](const char* buf, int64_t J) {
+    // S^T = K_J Q^T, K fragments read kPf steps ahead (the scheduling
+    // barriers stop the compiler from hoisting every LDS read of the
+    // unrolled loop, which would cost a register per read)
     f32x16 st = f32x16{};
-    if (active) {
-      const char* kb = smem + buf * C::BUF;
-      const char* vb = kb + C::K_BYTES;
-      const float* cb = reinterpret_cast<const float*>(vb + C::V_BYTES);
-      // S^T = K_J Q^T: two partial accumulators keep two MFMA chains in flight;
-      // K fragments are read kPf steps ahead (the scheduling barriers stop the
-      // compiler from hoisting every LDS read of the unrolled loop)
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
-      const char* kp = kb + l32 * C::KS + 16 * g;
+    {
+      const char* kp = buf + koff;
       constexpr int NS = DP / 16;
       bf16x8 kf[kPf + 1];
 #pragma unroll
       for (int t = 0; t < kPf && t < NS; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(kp + 32 * t);
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
-        if (t + kPf < NS) kf[(t + kPf) % (kPf + 1)] = *reinterpret_cast<const bf16x8*>(kp + 32 * (t + kPf));
-        if (t & 1)
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kPf + 1)], qf[t], s1, 0, 0, 0);
-        else
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kPf + 1)], qf[t], s0, 0, 0, 0);
+        if (t + kPf < NS)
+          kf[(t + kPf) % (kPf + 1)] = *reinterpret_cast<const bf16x8*>(kp + 32 * (t + kPf));
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kPf + 1)], qf[t], st, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      st = s0 + s1;
     }
-    if (more) {
-      store_k(buf ^ 1);
-      fetch_v(J + 1);
+    // lane (g, l32), register r holds S^T[key 8(r/4) + 4g + r%4][query l32]
+    const double a_j = *reinterpret_cast<const double*>(buf + C::A_OFF);
+    const float base = float(a_i - a_j) + r_i;
+    const bool diag = (J * kBN == qw);
+    const float* cb = reinterpret_cast<const float*>(buf + C::C_OFF);
+    float cv[16];
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const float4 c4 = *reinterpret_cast<const float4*>(cb + 8 * rq + 4 * g);
+      const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 8 * rq + 4 * g + e;
+        float ex = base + cc[e];
+        if (diag && key > l32) ex = -INFINITY;  // above the diagonal (Eq. 71)
+        const float c = st[4 * rq + e] * __builtin_amdgcn_exp2f(ex);  // C~' (Eq. 82)
+        bsum += c;                                                 // b (Eq. 83)
+        cv[4 * rq + e] = c;
+      }
     }
-    if (active) {
-      const char* kb = smem + buf * C::BUF;
-      const char* vb = kb + C::K_BYTES;
-      const float* cb = reinterpret_cast<const float*>(vb + C::V_BYTES);
-      // lane (g, l32), register r holds S^T[key 8(r/4) + 4g + r%4][query l32]
-      const float base = float(a_i - anchor[head * nblk + (J * kBN) / kAnchorBlock]) + r_i;
-      const bool diag = (J * kBN == qw);
-      float cv[16];
+    bf16x8 p[2];
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const float4 c4 = *reinterpret_cast<const float4*>(cb + 8 * rq + 4 * g);
-        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+    for (int e = 0; e < 8; ++e) {
+      p[0][e] = (__bf16)cv[e];
+      p[1][e] = (__bf16)cv[8 + e];
+    }
+    // O^T += V_J^T C~'^T.  Step t = (column block b, key half s): the A operand
+    // holds V[16s + 4g + 0..3][32b + l32] and V[16s + 8 + 4g + 0..3][32b + l32],
+    // the keys of B-operand registers 8s..8s+7.
+    {
+      const char* vp = buf + C::K_BYTES + voff;
+      constexpr int NV = DP / 16;
+      i16x4 vlo[kPf + 1], vhi[kPf + 1];
+      auto vaddr = [&](int t) { return vp + 16 * (t & 1) * C::RSV + 64 * (t >> 1); };
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = 8 * rq + 4 * g + e;
-          float ex = base + cc[e];
-          if (diag && key > l32) ex = -INFINITY;  // above the diagonal (Eq. 71)
-          const float c = st[4 * rq + e] * __builtin_amdgcn_exp2f(ex);  // C~' (Eq. 82)
-          bsum += c;                                                 // b (Eq. 83)
-          cv[4 * rq + e] = c;
-        }
+      for (int t = 0; t < kPf && t < NV; ++t) {
+        vlo[t] = tr_read(vaddr(t));
+        vhi[t] = tr_read(vaddr(t) + 8 * C::RSV);
       }
-      bf16x8 p0, p1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p0[e] = (__bf16)cv[e];
-        p1[e] = (__bf16)cv[8 + e];
-      }
-      // O^T += V_J^T C~'^T, V^T fragments read kPf steps ahead
-      const char* vp = vb + l32 * C::VS + 16 * g;
-      constexpr int NV = DP / 16;  // (column block, key half) steps
-      bf16x8 vf[kPf + 1];
-#pragma unroll
-      for (int t = 0; t < kPf && t < NV; ++t)
-        vf[t] = *reinterpret_cast<const bf16x8*>(vp + 32 * (t >> 1) * C::VS + 32 * (t & 1));
 #pragma unroll
       for (int t = 0; t < NV; ++t) {
         const int tn = t + kPf;
-        if (tn < NV)
-          vf[tn % (kPf + 1)] =
-              *reinterpret_cast<const bf16x8*>(vp + 32 * (tn >> 1) * C::VS + 32 * (tn & 1));
-        acc[t >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t % (kPf + 1)], (t & 1) ? p1 : p0,
-                                                              acc[t >> 1], 0, 0, 0);
+        if (tn < NV) {
+          vlo[tn % (kPf + 1)] = tr_read(vaddr(tn));
+          vhi[tn % (kPf + 1)] = tr_read(vaddr(tn) + 8 * C::RSV);
+        }
+        const i16x8 a16 = __builtin_shufflevector(vlo[t % (kPf + 1)], vhi[t % (kPf + 1)], 0, 1,
+                                                  2, 3, 4, 5, 6, 7);
+        acc[t >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, a16), p[t & 1], acc[t >> 1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (more) store_v(buf ^ 1);
+  };
+
+  load_tile(0, smem0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // No plain global load is issued inside the loop: everything a tile needs
+  // (K, V, c and the key-tile anchor) arrives by the copies into LDS, so the
+  // waits on those copies stay exact.
+  for (int64_t J = 0; J <= last_tile; J += 2) {
+    // even tile from smem0, prefetch into smem1
+    if (J + 1 <= last_tile) load_tile(J + 1, smem1);
+    if (J <= wave_last) compute(smem0, J);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (J + 1 > last_tile) break;
+    // odd tile from smem1, prefetch into smem0
+    if (J + 2 <= last_tile) load_tile(J + 2, smem0);
+    if (J + 1 <= wave_last) compute(smem1, J + 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -314,7 +306,8 @@ hipError_t launch_dp(const void* q, const void* k, const void* v, const float* m
   hipLaunchKernelGGL(tiles_mfma_kernel<DP>, dim3(unsigned(row_tiles * H)), dim3(kThreads), 0,
                      stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), m, ws.anchor, ws.rowt, ws.colt,
-                     static_cast<u16*>(h_out), n_out, T, int(d), ws.Tp, ws.nblk, row_tiles, H);
+                     static_cast<u16*>(h_out), n_out, T,
+                     int(d), ws.Tp, ws.nblk, row_tiles, H);
   return hipGetLastError();
 }
 

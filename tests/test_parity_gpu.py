@@ -111,13 +111,15 @@ def test_small_bf16_workload():
 @pytest.mark.parametrize("s", [spec(1, 2, 257, 128), spec(1, 1, 150, 384),
                                spec(1, 1, 200, 64, ig=("uniform", -20, 20), fg=("normal", 0, 4))],
                          ids=_id)
-def test_vector_kernel_bf16_inputs_at_fp32_bar(s):
-    """The float32 vector kernel on bf16 inputs never rounds C~' to bf16, so it
-    meets the float32 bar; an independent GPU evaluation of the same pass."""
+def test_vector_kernel_bf16_inputs(s):
+    """The float32 vector kernel on bf16 inputs never rounds C~' to bf16: its
+    only bf16 rounding is that of the stored h~ (half an ulp, 2^-8 relative),
+    so it meets a 4e-3 bar on h~ and the float32 bars on m and n.  An
+    independent GPU evaluation of the same pass."""
     x = W.make(s, seed=3)
     h, m, n = run_gpu(x, kernel="vector")
     hr, mr, nr = oracle_full(x)[:3]
-    print(check(h, m, n, hr, mr, nr, TOL_H["fp32"]))
+    print(check(h, m, n, hr, mr, nr, 4e-3))
 
 
 def test_gate_scan_m_matches_oracle():
