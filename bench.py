@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU ("2.5 PFLOP/s")
 PEAK_HBM_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "tiles_mfma_xlstm125m_counters.json")
+COPY_BYTES = 512 << 20
 TILE_SRC = os.path.join(ROOT, "linear_recurrent_sequence_amd", "csrc", "tiles_mfma.hip")
 
 
@@ -39,6 +40,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="approximate CPU seconds for the oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 512 MiB float32 device copy (a torch neg kernel) "
+                        "three times, the reference for rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
 
 
@@ -190,6 +194,14 @@ def main():
                       "frac_of_hbm": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "output_finite": finite,
     }
+    if args.copy_calibration:
+        # reads and writes exactly COPY_BYTES each per launch
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = COPY_BYTES
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
