@@ -107,6 +107,25 @@ int mlstm_parallel_fwd_stream(const void* q, const void* k, const void* v,
                               void* stream);
 
 /*
+ * mlstm_parallel_fwd_gated -- the forward pass followed by the output gate of
+ * "Parallel mLSTM Forward Pass" (Eq. 78): H = sigma(O~) (.) H~, elementwise,
+ * with the logistic sigmoid.  The gate is applied to the float32 h~ inside
+ * the tile kernel's epilogue, before the result is rounded to `dtype`.
+ *   ogate       in   [B][NH][T][d], dtype: O~ (output gate pre-activations); required
+ *   h_out       out  [B][NH][T][d], dtype: H (Eq. 78)
+ *   htilde_out  out  [B][NH][T][d], dtype: H~ (Eq. 86), bitwise what
+ *                    mlstm_parallel_fwd writes to its h_out; may be NULL (not stored)
+ *   all other arguments as for mlstm_parallel_fwd_stream.
+ * ogate and htilde_out must be 16-byte aligned and must not alias any other
+ * argument.  Errors as for mlstm_parallel_fwd (MLSTM_ERR_NULL for ogate NULL).
+ */
+int mlstm_parallel_fwd_gated(const void* q, const void* k, const void* v,
+                             const float* igate, const float* fgate, const void* ogate,
+                             void* h_out, void* htilde_out, float* m_out, float* n_out,
+                             int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
+                             void* stream);
+
+/*
  * The same pass split into its two stages with a caller-owned workspace, for
  * callers that time or schedule the stages separately.
  *

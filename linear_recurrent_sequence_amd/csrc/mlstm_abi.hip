@@ -53,14 +53,49 @@ int check_tile_args(const void* q, const void* k, const void* v, const float* m,
 }
 
 int run_tiles(const void* q, const void* k, const void* v, const float* m, const Workspace& w,
-              void* h_out, float* n_out, int64_t H, int64_t T, int64_t d, int dtype, int kernel,
-              hipStream_t stream) {
+              void* h_out, float* n_out, const mlstm::Epilogue& ep, int64_t H, int64_t T,
+              int64_t d, int dtype, int kernel, hipStream_t stream) {
   const bool use_mfma =
       kernel == MLSTM_KERNEL_MFMA || (kernel == MLSTM_KERNEL_AUTO && dtype == MLSTM_BF16);
   if (use_mfma)
-    return hip_status(mlstm::launch_tiles_mfma(q, k, v, m, w, h_out, n_out, H, T, d, stream));
-  return hip_status(mlstm::launch_tiles_vector(q, k, v, m, w, h_out, n_out, H, T, d,
+    return hip_status(
+        mlstm::launch_tiles_mfma(q, k, v, m, w, h_out, n_out, ep, H, T, d, stream));
+  return hip_status(mlstm::launch_tiles_vector(q, k, v, m, w, h_out, n_out, ep, H, T, d,
                                                dtype == MLSTM_BF16, stream));
+}
+
+// Both stages with a stream-ordered workspace (safe under concurrent calls on
+// different streams).  Arguments are checked by the caller.
+int forward(const void* q, const void* k, const void* v, const float* igate, const float* fgate,
+            const mlstm::Epilogue& ep, void* h_out, float* m_out, float* n_out, int64_t B,
+            int64_t NH, int64_t T, int64_t d, int dtype, hipStream_t s) {
+  const int64_t H = B * NH;
+  const size_t bytes = mlstm::workspace_bytes(H, T);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, bytes, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return MLSTM_ERR_HIP;
+  }
+  const Workspace w = mlstm::carve(ws, H, T);
+  int st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d, s));
+  if (st == MLSTM_OK)
+    st = run_tiles(q, k, v, m_out, w, h_out, n_out, ep, H, T, d, dtype, MLSTM_KERNEL_AUTO, s);
+  if (hipFreeAsync(ws, s) != hipSuccess && st == MLSTM_OK) st = MLSTM_ERR_HIP;
+  return st;
+}
+
+int check_forward_args(const void* q, const void* k, const void* v, const float* igate,
+                       const float* fgate, const void* h_out, const float* m_out,
+                       const float* n_out, int64_t B, int64_t NH, int64_t T, int64_t d,
+                       int dtype) {
+  if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
+  int st = check_shape(B, NH, T, d);
+  if (st != MLSTM_OK) return st;
+  if (!q || !k || !v || !igate || !fgate || !h_out || !m_out || !n_out) return MLSTM_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(igate) ||
+      !aligned16(fgate) || !aligned16(h_out) || !aligned16(m_out) || !aligned16(n_out))
+    return MLSTM_ERR_ALIGN;
+  return MLSTM_OK;
 }
 
 }  // namespace
@@ -95,7 +130,7 @@ int mlstm_causal_tiles(const void* q, const void* k, const void* v, const float*
   const int64_t H = B * NH;
   if (workspace_bytes < mlstm::workspace_bytes(H, T)) return MLSTM_ERR_WORKSPACE;
   const Workspace w = mlstm::carve(const_cast<void*>(workspace), H, T);
-  return run_tiles(q, k, v, m, w, h_out, n_out, H, T, d, dtype, kernel,
+  return run_tiles(q, k, v, m, w, h_out, n_out, mlstm::Epilogue{}, H, T, d, dtype, kernel,
                    static_cast<hipStream_t>(stream));
 }
 
@@ -103,28 +138,26 @@ int mlstm_parallel_fwd_stream(const void* q, const void* k, const void* v, const
                               const float* fgate, void* h_out, float* m_out, float* n_out,
                               int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
                               void* stream) {
-  if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
-  int st = check_shape(B, NH, T, d);
+  const int st = check_forward_args(q, k, v, igate, fgate, h_out, m_out, n_out, B, NH, T, d,
+                                    dtype);
   if (st != MLSTM_OK) return st;
-  if (!q || !k || !v || !igate || !fgate || !h_out || !m_out || !n_out) return MLSTM_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(igate) ||
-      !aligned16(fgate) || !aligned16(h_out) || !aligned16(m_out) || !aligned16(n_out))
-    return MLSTM_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t H = B * NH;
-  const size_t bytes = mlstm::workspace_bytes(H, T);
-  void* ws = nullptr;
-  // stream-ordered allocation: safe under concurrent calls on different streams
-  if (hipMallocAsync(&ws, bytes, s) != hipSuccess) {
-    (void)hipGetLastError();
-    return MLSTM_ERR_HIP;
-  }
-  const Workspace w = mlstm::carve(ws, H, T);
-  st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d, s));
-  if (st == MLSTM_OK)
-    st = run_tiles(q, k, v, m_out, w, h_out, n_out, H, T, d, dtype, MLSTM_KERNEL_AUTO, s);
-  if (hipFreeAsync(ws, s) != hipSuccess && st == MLSTM_OK) st = MLSTM_ERR_HIP;
-  return st;
+  return forward(q, k, v, igate, fgate, mlstm::Epilogue{}, h_out, m_out, n_out, B, NH, T, d,
+                 dtype, static_cast<hipStream_t>(stream));
+}
+
+int mlstm_parallel_fwd_gated(const void* q, const void* k, const void* v, const float* igate,
+                             const float* fgate, const void* ogate, void* h_out,
+                             void* htilde_out, float* m_out, float* n_out, int64_t B,
+                             int64_t NH, int64_t T, int64_t d, int dtype, void* stream) {
+  int st = check_forward_args(q, k, v, igate, fgate, h_out, m_out, n_out, B, NH, T, d, dtype);
+  if (st != MLSTM_OK) return st;
+  if (!ogate) return MLSTM_ERR_NULL;
+  if (!aligned16(ogate) || (htilde_out && !aligned16(htilde_out))) return MLSTM_ERR_ALIGN;
+  mlstm::Epilogue ep;
+  ep.ogate = ogate;
+  ep.htilde = htilde_out;
+  return forward(q, k, v, igate, fgate, ep, h_out, m_out, n_out, B, NH, T, d, dtype,
+                 static_cast<hipStream_t>(stream));
 }
 
 int mlstm_parallel_fwd(const void* q, const void* k, const void* v, const float* igate,

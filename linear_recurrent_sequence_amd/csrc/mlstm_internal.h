@@ -57,6 +57,15 @@ inline Workspace carve(void* base, int64_t H, int64_t T) {
   return w;
 }
 
+// Optional epilogue of the tile kernels: the output gate H = sigma(O~) (.) H~
+// (Eq. 78), applied to the float32 h~ before it is rounded and stored.
+// ogate = NULL: h_out receives h~.  htilde != NULL: h~ is stored there too.
+// Both are [H][T][d] in the element type of q.
+struct Epilogue {
+  const void* ogate = nullptr;
+  void* htilde = nullptr;
+};
+
 // Stage 1: gate scan (one workgroup per head).
 hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out,
                             const Workspace& ws, int64_t H, int64_t T, int64_t d,
@@ -66,12 +75,13 @@ hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out
 // unsupported head dimension (none for d % 16 == 0, 16 <= d <= 512).
 hipError_t launch_tiles_mfma(const void* q, const void* k, const void* v, const float* m,
                              const Workspace& ws, void* h_out, float* n_out,
-                             int64_t H, int64_t T, int64_t d, hipStream_t stream);
+                             const Epilogue& ep, int64_t H, int64_t T, int64_t d,
+                             hipStream_t stream);
 
 // Stage 2, float32 vector-ALU tiles; is_bf16 selects the element type.
 hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, const float* m,
                                const Workspace& ws, void* h_out, float* n_out,
-                               int64_t H, int64_t T, int64_t d, bool is_bf16,
-                               hipStream_t stream);
+                               const Epilogue& ep, int64_t H, int64_t T, int64_t d,
+                               bool is_bf16, hipStream_t stream);
 
 }  // namespace mlstm

@@ -104,7 +104,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void tiles_mfma_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ m_in, const double* __restrict__ anchor,
-    const float* __restrict__ rowt, const float* __restrict__ colt, u16* __restrict__ h_out, float* __restrict__ n_out, int64_t T,
+    const float* __restrict__ rowt, const float* __restrict__ colt, u16* __restrict__ h_out,
+    float* __restrict__ n_out, const u16* __restrict__ ogate, u16* __restrict__ htilde, int64_t T,
     int d, int64_t Tp, int64_t nblk, int64_t row_tiles, int64_t H) {
   using C = Cfg<DP>;
   // two distinct buffers, so the loads into one never alias reads of the other
@@ -275,23 +276,37 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     __syncthreads();
   }
 
-  // ---- epilogue: n (Eq. 84), h~ = acc / n (Eqs. 85, 86) ----
+  // ---- epilogue: n (Eq. 84), h~ = acc / n (Eqs. 85, 86), and with an
+  // output gate H = sigma(O~) (.) h~ (Eq. 78) from the float32 h~ ----
   bsum += __shfl_xor(bsum, 32, 64);
   if (qi < T) {
     const float nn = fmaxf(fabsf(bsum), expf(-m_in[head * T + qi]));
     if (g == 0) n_out[head * T + qi] = nn;
     const float inv = 1.0f / nn;
-    u16* hrow = h_out + hoff + qi * d;
+    const int64_t row = hoff + qi * d;
 #pragma unroll
     for (int b = 0; b < DP / 32; ++b) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int col = 32 * b + 8 * rq + 4 * g;
         if (col < d) {
-          bf16x4 o;
+          float hv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[b][4 * rq + e] * inv);
-          *reinterpret_cast<bf16x4*>(hrow + col) = o;
+          for (int e = 0; e < 4; ++e) hv[e] = acc[b][4 * rq + e] * inv;
+          bf16x4 o;
+          if (htilde) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (__bf16)hv[e];
+            *reinterpret_cast<bf16x4*>(htilde + row + col) = o;
+          }
+          if (ogate) {
+            const bf16x4 og = *reinterpret_cast<const bf16x4*>(ogate + row + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hv[e] *= 1.0f / (1.0f + __expf(-float(og[e])));
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (__bf16)hv[e];
+          *reinterpret_cast<bf16x4*>(h_out + row + col) = o;
         }
       }
     }
@@ -300,40 +315,41 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 
 template <int DP>
 hipError_t launch_dp(const void* q, const void* k, const void* v, const float* m,
-                     const Workspace& ws, void* h_out, float* n_out, int64_t H, int64_t T,
-                     int64_t d, hipStream_t stream) {
+                     const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,
+                     int64_t H, int64_t T, int64_t d, hipStream_t stream) {
   const int64_t row_tiles = (T + kBM - 1) / kBM;
   hipLaunchKernelGGL(tiles_mfma_kernel<DP>, dim3(unsigned(row_tiles * H)), dim3(kThreads), 0,
                      stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), m, ws.anchor, ws.rowt, ws.colt,
-                     static_cast<u16*>(h_out), n_out, T,
-                     int(d), ws.Tp, ws.nblk, row_tiles, H);
+                     static_cast<u16*>(h_out), n_out, static_cast<const u16*>(ep.ogate),
+                     static_cast<u16*>(ep.htilde), T, int(d), ws.Tp, ws.nblk, row_tiles, H);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_tiles_mfma(const void* q, const void* k, const void* v, const float* m,
-                             const Workspace& ws, void* h_out, float* n_out, int64_t H,
-                             int64_t T, int64_t d, hipStream_t stream) {
+                             const Workspace& ws, void* h_out, float* n_out,
+                             const Epilogue& ep, int64_t H, int64_t T, int64_t d,
+                             hipStream_t stream) {
   // head dims are padded up to a multiple of 32 (zero columns add nothing)
   switch ((d + 31) / 32) {
-    case 1: return launch_dp<32>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 2: return launch_dp<64>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 3: return launch_dp<96>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 4: return launch_dp<128>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 5: return launch_dp<160>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 6: return launch_dp<192>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 7: return launch_dp<224>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 8: return launch_dp<256>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 9: return launch_dp<288>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 10: return launch_dp<320>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 11: return launch_dp<352>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 12: return launch_dp<384>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 13: return launch_dp<416>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 14: return launch_dp<448>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 15: return launch_dp<480>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
-    case 16: return launch_dp<512>(q, k, v, m, ws, h_out, n_out, H, T, d, stream);
+    case 1: return launch_dp<32>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 2: return launch_dp<64>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 3: return launch_dp<96>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 4: return launch_dp<128>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 5: return launch_dp<160>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 6: return launch_dp<192>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 7: return launch_dp<224>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 8: return launch_dp<256>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 9: return launch_dp<288>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 10: return launch_dp<320>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 11: return launch_dp<352>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 12: return launch_dp<384>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 13: return launch_dp<416>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 14: return launch_dp<448>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 15: return launch_dp<480>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 16: return launch_dp<512>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
     default: return hipErrorInvalidValue;
   }
 }

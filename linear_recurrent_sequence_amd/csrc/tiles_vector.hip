@@ -29,7 +29,8 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ m_in, const double* __restrict__ anchor,
     const float* __restrict__ rowt, const float* __restrict__ colt, Tin* __restrict__ h_out,
-    float* __restrict__ n_out, int64_t T, int d, int64_t Tp, int64_t nblk, int64_t row_tiles) {
+    float* __restrict__ n_out, const Tin* __restrict__ ogate, Tin* __restrict__ htilde, int64_t T,
+    int d, int64_t Tp, int64_t nblk, int64_t row_tiles) {
   __shared__ float Qs[kVT][kVPad];
   __shared__ float Ks[kVT][kVPad];
   __shared__ float Vs[kVT][kVMaxD];
@@ -96,7 +97,13 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
 #pragma unroll
     for (int u = 0; u < kVMaxD / kVT; ++u) {
       const int c = cl + kVT * u;
-      if (c < d) store_elem(h_out + hoff + qi * d + c, acc[u] / nn);  // Eqs. 85, 86
+      if (c < d) {
+        const int64_t at = hoff + qi * d + c;
+        float hv = acc[u] / nn;  // Eqs. 85, 86
+        if (htilde) store_elem(htilde + at, hv);
+        if (ogate) hv *= 1.0f / (1.0f + __expf(-load_elem(ogate + at)));  // Eq. 78
+        store_elem(h_out + at, hv);
+      }
     }
   }
 }
@@ -104,8 +111,9 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
 }  // namespace
 
 hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, const float* m,
-                               const Workspace& ws, void* h_out, float* n_out, int64_t H,
-                               int64_t T, int64_t d, bool is_bf16, hipStream_t stream) {
+                               const Workspace& ws, void* h_out, float* n_out,
+                               const Epilogue& ep, int64_t H, int64_t T, int64_t d,
+                               bool is_bf16, hipStream_t stream) {
   const int64_t row_tiles = (T + kVT - 1) / kVT;
   const dim3 grid(unsigned(row_tiles * H));
   if (is_bf16) {
@@ -113,12 +121,14 @@ hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, cons
     hipLaunchKernelGGL(tiles_vector_kernel<B16>, grid, dim3(256), 0, stream,
                        static_cast<const B16*>(q), static_cast<const B16*>(k),
                        static_cast<const B16*>(v), m, ws.anchor, ws.rowt, ws.colt,
-                       static_cast<B16*>(h_out), n_out, T, int(d), ws.Tp, ws.nblk, row_tiles);
+                       static_cast<B16*>(h_out), n_out, static_cast<const B16*>(ep.ogate),
+                       static_cast<B16*>(ep.htilde), T, int(d), ws.Tp, ws.nblk, row_tiles);
   } else {
     hipLaunchKernelGGL(tiles_vector_kernel<float>, grid, dim3(256), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), m, ws.anchor, ws.rowt, ws.colt,
-                       static_cast<float*>(h_out), n_out, T, int(d), ws.Tp, ws.nblk, row_tiles);
+                       static_cast<float*>(h_out), n_out, static_cast<const float*>(ep.ogate),
+                       static_cast<float*>(ep.htilde), T, int(d), ws.Tp, ws.nblk, row_tiles);
   }
   return hipGetLastError();
 }

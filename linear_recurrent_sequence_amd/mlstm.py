@@ -48,6 +48,8 @@ def load_library():
     lib.mlstm_parallel_fwd.restype = i32
     lib.mlstm_parallel_fwd_stream.argtypes = [vp] * 8 + [i64] * 4 + [i32, vp]
     lib.mlstm_parallel_fwd_stream.restype = i32
+    lib.mlstm_parallel_fwd_gated.argtypes = [vp] * 10 + [i64] * 4 + [i32, vp]
+    lib.mlstm_parallel_fwd_gated.restype = i32
     lib.mlstm_workspace_bytes.argtypes = [i64] * 3
     lib.mlstm_workspace_bytes.restype = f
     lib.mlstm_gate_scan.argtypes = [vp] * 4 + [f] + [i64] * 4 + [vp]
@@ -117,6 +119,32 @@ def parallel_fwd(q, k, v, igate, fgate, out=None):
     if st != 0:
         raise MlstmError(st, "mlstm_parallel_fwd")
     return h, m, n
+
+
+def parallel_fwd_gated(q, k, v, igate, fgate, ogate, htilde=False):
+    """Forward pass with the output gate of Eq. 78 fused into the epilogue.
+
+    ogate: O~, same shape, dtype and device as q.  Returns (h, m, n), or
+    (h, h_tilde, m, n) with ``htilde=True``, where h = sigmoid(O~) * h_tilde.
+    """
+    lib = load_library()
+    B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
+    if ogate.shape != q.shape or ogate.dtype != q.dtype or ogate.device != q.device:
+        raise ValueError("ogate must match q in shape, dtype and device")
+    if not ogate.is_contiguous():
+        raise ValueError("ogate must be contiguous")
+    h = torch.empty_like(q)
+    ht = torch.empty_like(q) if htilde else None
+    m = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
+    n = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib.mlstm_parallel_fwd_gated(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
+            ogate.data_ptr(), h.data_ptr(), ht.data_ptr() if htilde else None, m.data_ptr(),
+            n.data_ptr(), B, NH, T, d, _dtype_code(q), _stream_ptr(q.device))
+    if st != 0:
+        raise MlstmError(st, "mlstm_parallel_fwd_gated")
+    return (h, ht, m, n) if htilde else (h, m, n)
 
 
 def workspace_bytes(B, NH, T):

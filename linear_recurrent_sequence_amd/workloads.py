@@ -101,6 +101,19 @@ def make(spec, seed=0):
     return dict(q=q, k=k, v=v, igate=igate, fgate=fgate, spec=spec)
 
 
+def make_ogate(spec, seed=0, loc=0.0, scale=2.0):
+    """Output gate pre-activations O~ [B,NH,T,d] for a drawn batch's spec.
+
+    Drawn from a generator of its own, seeded (seed, 78), so that adding an
+    output gate never changes the other inputs of the same seed.  N(loc, scale),
+    float32, rounded to bf16 for bf16 workloads.
+    """
+    B, NH, T, d = spec["B"], spec["NH"], spec["T"], spec["d"]
+    rng = np.random.Generator(np.random.PCG64([seed, 78]))
+    o = (loc + scale * rng.standard_normal((B, NH, T, d))).astype(np.float32)
+    return round_bf16(o) if spec["dtype"] == "bf16" else o
+
+
 def counted_flops(B, NH, T, d):
     """Causal work counted as 2 * T^2 * d per head (both contractions, causal half)."""
     return 2.0 * T * T * d * B * NH

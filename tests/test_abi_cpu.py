@@ -91,3 +91,20 @@ def test_staged_entry_points_reject_before_device_work():
                                   1, 1, 64, 16, 1, 0, None) == -1
     assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE,
                                   1, 1, 64, 16, 1, 0, None) == -7
+
+
+@needs_lib
+@pytest.mark.parametrize("case,status", [
+    (dict(ogate=0), -1), (dict(q=0), -1), (dict(ogate=FAKE + 8), -5),
+    (dict(htilde_out=FAKE + 2), -5), (dict(d=24), -4), (dict(dtype=3), -3), (dict(T=0), -2),
+])
+def test_gated_forward_rejects_before_device_work(case, status):
+    lib = mlstm.load_library()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, igate=FAKE, fgate=FAKE, ogate=FAKE, h_out=FAKE,
+                htilde_out=0, m_out=FAKE, n_out=FAKE, B=1, NH=1, T=64, d=16, dtype=1)
+    args.update(case)
+    ptrs = ["q", "k", "v", "igate", "fgate", "ogate", "h_out", "htilde_out", "m_out", "n_out"]
+    st = lib.mlstm_parallel_fwd_gated(*[args[k] or None for k in ptrs],
+                                      args["B"], args["NH"], args["T"], args["d"], args["dtype"],
+                                      None)
+    assert st == status

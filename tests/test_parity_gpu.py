@@ -245,3 +245,43 @@ def test_errors_raise_on_gpu():
         g = torch.zeros((1, 1, 0), dtype=torch.float32, device="cuda")
         mlstm.parallel_fwd(z, z, z, g, g)
     assert e.value.status == -2
+
+
+# ---------------------------------------------------------------------------
+# output gate fused into the epilogue (Eq. 78)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("s", [spec(1, 2, 257, 128), spec(2, 1, 160, 384), spec(1, 1, 140, 512),
+                               spec(1, 2, 100, 48), spec(1, 2, 130, 64, "fp32")], ids=_id)
+def test_output_gate_fused(s):
+    """h = sigmoid(O~) * h~ against the oracle's Eq. 78 on its h~; the h~ the
+    gated call stores is bitwise the ungated call's h."""
+    x = W.make(s, seed=12)
+    og = W.make_ogate(x["spec"], seed=12)
+    q, k, v, ig, fg = _dev(x)
+    dt = q.dtype
+    o_dev = torch.from_numpy(og).to("cuda").to(dt).contiguous()
+    h, ht, m, n = mlstm.parallel_fwd_gated(q, k, v, ig, fg, o_dev, htilde=True)
+    h0, m0, n0 = mlstm.parallel_fwd(q, k, v, ig, fg)
+    h2, m2, n2 = mlstm.parallel_fwd_gated(q, k, v, ig, fg, o_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(ht, h0) and torch.equal(m, m0) and torch.equal(n, n0)
+    assert torch.equal(h, h2) and torch.equal(m2, m0) and torch.equal(n2, n0)
+    hr, mr, nr = oracle_full(x)[:3]
+    gated_ref = oracle.output_gate(hr, og)
+    tol = TOL_H["bf16"] if s["dtype"] == "bf16" else TOL_H["fp32"]
+    print(check(_host(h), _host(m), _host(n), gated_ref, mr, nr, tol))
+
+
+def test_output_gate_language_model_sampled():
+    x = W.make("xlstm125m_layer", seed=0)
+    og = W.make_ogate(x["spec"], seed=0)
+    q, k, v, ig, fg = _dev(x)
+    o_dev = torch.from_numpy(og).to("cuda").to(torch.bfloat16).contiguous()
+    h, m, n = mlstm.parallel_fwd_gated(q, k, v, ig, fg, o_dev)
+    torch.cuda.synchronize()
+    h, m, n = _host(h), _host(m), _host(n)
+    rows = _sample_rows(x["spec"]["T"], np.random.default_rng(13), count=20)
+    hr, mr, nr, _ = _sampled_reference(x, rows)
+    gated_ref = oracle.output_gate(hr, og[:, :, rows])
+    print(check(h[:, :, rows], m[:, :, rows], n[:, :, rows], gated_ref, mr, nr, TOL_H["bf16"]))
