@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="xlstm125m_layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-long-context", action="store_true",
+                   help="skip the tile-skipping comparison on the 16K stress workload")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="approximate CPU seconds for the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -94,6 +96,40 @@ def cpu_baseline(x, budget_s):
             "kind": "oracle",
             "sample": f"{done} of {B * NH} heads (full T={T}, d={d} each), float64 NumPy, "
                       f"{dt:.1f} s"}
+
+
+def long_context_skipping(torch, mlstm, workloads, dev, reps):
+    """Stage-2 time on long_context_16k with and without decay-aware skipping."""
+    x = workloads.make("long_context_16k", seed=0)
+    spec = x["spec"]
+    B, NH, T, d = spec["B"], spec["NH"], spec["T"], spec["d"]
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16).contiguous()
+               for n in ("q", "k", "v"))
+    ig = torch.from_numpy(x["igate"]).to(dev).contiguous()
+    fg = torch.from_numpy(x["fgate"]).to(dev).contiguous()
+    ws = mlstm.alloc_workspace(B, NH, T, dev)
+    m = mlstm.gate_scan(ig, fg, d, ws)
+    h = torch.empty_like(q)
+    n = torch.empty_like(m)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for kernel in ("mfma", "mfma_all_tiles"):
+        mlstm.causal_tiles(q, k, v, m, ws, kernel=kernel, out=(h, n))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            mlstm.causal_tiles(q, k, v, m, ws, kernel=kernel, out=(h, n))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[kernel] = e0.elapsed_time(e1) / reps
+    flops = workloads.counted_flops(B, NH, T, d)
+    return {"workload": "long_context_16k", "B": B, "NH": NH, "T": T, "d": d,
+            "tile_ms_skipping": round(out["mfma"], 4),
+            "tile_ms_all_tiles": round(out["mfma_all_tiles"], 4),
+            "counted_TFLOP/s_skipping": round(flops / (out["mfma"] * 1e-3) / 1e12, 1),
+            "counted_TFLOP/s_all_tiles": round(flops / (out["mfma_all_tiles"] * 1e-3) / 1e12, 1),
+            "speedup": round(out["mfma_all_tiles"] / out["mfma"], 2)}
 
 
 def main():
@@ -161,6 +197,12 @@ def main():
     scan_ms = e0.elapsed_time(e1) / reps
     scan_bytes = B * NH * T * (4 + 4 + 4 + 4 + 4) + B * NH * (T // 64 + 2) * 8
 
+    # decay-aware tile skipping on the long-context stress workload: the same
+    # call with skipping (default) and visiting every causal tile
+    skip_rec = None
+    if not args.no_long_context:
+        skip_rec = long_context_skipping(torch, mlstm, workloads, dev, reps=10)
+
     # correctness spot check of the timed output (not part of the timing)
     mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
     torch.cuda.synchronize()
@@ -194,6 +236,8 @@ def main():
                       "frac_of_hbm": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "output_finite": finite,
     }
+    if skip_rec is not None:
+        line["tile_skipping"] = skip_rec
     if args.copy_calibration:
         # reads and writes exactly COPY_BYTES each per launch
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

@@ -64,8 +64,19 @@ enum { MLSTM_FP32 = 0, MLSTM_BF16 = 1 };
 enum {
   MLSTM_KERNEL_AUTO = 0,   /* bf16 -> matrix-core kernel, fp32 -> vector kernel */
   MLSTM_KERNEL_MFMA = 1,   /* bf16 only: bf16 MFMA tiles (the production path) */
-  MLSTM_KERNEL_VECTOR = 2  /* any dtype: float32 vector-ALU tiles, no bf16 rounding of C~' */
+  MLSTM_KERNEL_VECTOR = 2, /* any dtype: float32 vector-ALU tiles, no bf16 rounding of C~' */
+  MLSTM_KERNEL_MFMA_ALL_TILES = 3  /* as MLSTM_KERNEL_MFMA, but visiting every causal tile */
 };
+/*
+ * Decay-aware tile skipping (MLSTM_KERNEL_AUTO and _MFMA on bf16).  From the
+ * gate scan's terms the tile kernel bounds log2(D'_ij / sqrt(d)) over each
+ * 32 x 32 block of Eqs. 79-81; where the bound is below -200 every entry's
+ * float32 exponential is exactly 0, so the block adds nothing to b (Eq. 83)
+ * or to C~'V and is not visited.  Outputs equal those of
+ * MLSTM_KERNEL_MFMA_ALL_TILES (up to the sign of exact zeros).  Long
+ * sequences with strong forgetting skip most of the causal triangle; the
+ * counted work (2 T^2 d per head) is unchanged.
+ */
 
 /* status codes */
 enum {
@@ -77,7 +88,7 @@ enum {
   MLSTM_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
   MLSTM_ERR_HIP = -6,         /* a HIP allocation or launch failed */
   MLSTM_ERR_WORKSPACE = -7,   /* caller workspace smaller than mlstm_workspace_bytes */
-  MLSTM_ERR_KERNEL = -8       /* unknown kernel selector, or MFMA asked for fp32 */
+  MLSTM_ERR_KERNEL = -8       /* unknown kernel selector, or an MFMA selector for fp32 */
 };
 
 /*

@@ -47,7 +47,8 @@ __device__ inline float log_sigmoid(float x) {
 __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     const float* __restrict__ igate, const float* __restrict__ fgate, float* __restrict__ m_out,
     double* __restrict__ anchor, float* __restrict__ rowt, float* __restrict__ colt,
-    int64_t T, int64_t Tp, int64_t nblk, double half_ln_d) {
+    float* __restrict__ rowb, float* __restrict__ keyb, int64_t T, int64_t Tp, int64_t nblk,
+    double half_ln_d) {
   const double kLog2e = 1.4426950408889634074;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -59,6 +60,8 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
   double* anc = anchor + head * nblk;
   float* rt = rowt + head * Tp;
   float* ct = colt + head * Tp;
+  float* rb = rowb + head * (Tp / kBoundTile);
+  float* kb = keyb + head * (Tp / kBoundTile);
 
   __shared__ double s_sum[kScanWaves];
   __shared__ double s_a[kScanWaves];
@@ -133,6 +136,7 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     // held by the first of the 8 threads that share the block
     const double blk_anchor = __shfl(cs, lane & ~7, 64);
     if (p0 < Tp && (p0 & (kAnchorBlock - 1)) == 0) anc[p0 / kAnchorBlock] = blk_anchor * kLog2e;
+    float rmax = -INFINITY, cmax = -INFINITY;  // of the values stored below
 #pragma unroll
     for (int e = 0; e < kScanPer; ++e) {
       const int64_t p = p0 + e;
@@ -140,13 +144,27 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
       m = fmax(m + double(fb[e]), double(iv[e]));
       const double loc = cs - blk_anchor;
       if (p < T) {
+        const float r = float((loc - m - half_ln_d) * kLog2e);
+        const float c = float((double(iv[e]) - loc) * kLog2e);
         mo[p] = float(m);
-        rt[p] = float((loc - m - half_ln_d) * kLog2e);
-        ct[p] = float((double(iv[e]) - loc) * kLog2e);
+        rt[p] = r;
+        ct[p] = c;
+        rmax = fmaxf(rmax, r);
+        cmax = fmaxf(cmax, c);
       } else if (p < Tp) {
         rt[p] = 0.0f;
         ct[p] = -INFINITY;
+        rmax = fmaxf(rmax, 0.0f);
       }
+    }
+    // tile bounds: the 4 threads of a 32-position tile are 4 consecutive lanes
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 1, 64));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 2, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 1, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 2, 64));
+    if (p0 < Tp && (p0 & (kBoundTile - 1)) == 0) {
+      rb[p0 / kBoundTile] = rmax;
+      kb[p0 / kBoundTile] = cmax;
     }
     carry_cs += tot_sum;
     carry_m = apply(tot_map, carry_m);
@@ -160,7 +178,7 @@ hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out
                             const Workspace& ws, int64_t H, int64_t T, int64_t d,
                             hipStream_t stream) {
   hipLaunchKernelGGL(gate_scan_kernel, dim3(unsigned(H)), dim3(kScanThreads), 0, stream, igate,
-                     fgate, m_out, ws.anchor, ws.rowt, ws.colt, T, ws.Tp, ws.nblk,
+                     fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.rowb, ws.keyb, T, ws.Tp, ws.nblk,
                      0.5 * log(double(d)));
   return hipGetLastError();
 }

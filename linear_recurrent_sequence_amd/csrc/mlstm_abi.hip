@@ -42,9 +42,12 @@ int check_tile_args(const void* q, const void* k, const void* v, const float* m,
                     const void* h_out, const float* n_out, int dtype, int kernel) {
   if (!q || !k || !v || !m || !ws || !h_out || !n_out) return MLSTM_ERR_NULL;
   if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
-  if (kernel != MLSTM_KERNEL_AUTO && kernel != MLSTM_KERNEL_MFMA && kernel != MLSTM_KERNEL_VECTOR)
+  if (kernel != MLSTM_KERNEL_AUTO && kernel != MLSTM_KERNEL_MFMA &&
+      kernel != MLSTM_KERNEL_VECTOR && kernel != MLSTM_KERNEL_MFMA_ALL_TILES)
     return MLSTM_ERR_KERNEL;
-  if (kernel == MLSTM_KERNEL_MFMA && dtype != MLSTM_BF16) return MLSTM_ERR_KERNEL;
+  if ((kernel == MLSTM_KERNEL_MFMA || kernel == MLSTM_KERNEL_MFMA_ALL_TILES) &&
+      dtype != MLSTM_BF16)
+    return MLSTM_ERR_KERNEL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(m) || !aligned16(h_out) ||
       !aligned16(n_out))
     return MLSTM_ERR_ALIGN;
@@ -55,11 +58,12 @@ int check_tile_args(const void* q, const void* k, const void* v, const float* m,
 int run_tiles(const void* q, const void* k, const void* v, const float* m, const Workspace& w,
               void* h_out, float* n_out, const mlstm::Epilogue& ep, int64_t H, int64_t T,
               int64_t d, int dtype, int kernel, hipStream_t stream) {
-  const bool use_mfma =
-      kernel == MLSTM_KERNEL_MFMA || (kernel == MLSTM_KERNEL_AUTO && dtype == MLSTM_BF16);
+  const bool use_mfma = kernel == MLSTM_KERNEL_MFMA || kernel == MLSTM_KERNEL_MFMA_ALL_TILES ||
+                        (kernel == MLSTM_KERNEL_AUTO && dtype == MLSTM_BF16);
   if (use_mfma)
-    return hip_status(
-        mlstm::launch_tiles_mfma(q, k, v, m, w, h_out, n_out, ep, H, T, d, stream));
+    return hip_status(mlstm::launch_tiles_mfma(q, k, v, m, w, h_out, n_out, ep,
+                                               kernel != MLSTM_KERNEL_MFMA_ALL_TILES, H, T, d,
+                                               stream));
   return hip_status(mlstm::launch_tiles_vector(q, k, v, m, w, h_out, n_out, ep, H, T, d,
                                                dtype == MLSTM_BF16, stream));
 }

@@ -6,6 +6,8 @@
 //   anchor [H][Tp/64]  float64  A_b = (sum of fbar over positions < 64 b) * log2(e)
 //   rowt   [H][Tp]     float32  r_i = (loc_i - m_i - ln(d)/2) * log2(e)
 //   colt   [H][Tp]     float32  c_j = (i~_j - loc_j) * log2(e)    (-inf on padding)
+//   rowb   [H][Tp/32]  float32  max of r_i over each 32-row block
+//   keyb   [H][Tp/32]  float32  max of c_j over each 32-key tile (-inf if all padding)
 //
 // where fbar = log sigmoid(f~) and loc_i = (inclusive prefix sum of fbar up to
 // i) - (the same sum up to the start of i's 64-position block), so that, for
@@ -16,6 +18,14 @@
 // The block anchors keep the difference of two long prefix sums out of
 // float32: the anchor difference is taken in float64 and rounded once, and
 // every other term is bounded by one block's worth of forget gates.
+//
+// Tile bound: the tile kernels form each exponent as
+// fl(fl(float(A_{i/64} - A_{j/64}) + r_i) + c_j).  Rounding is monotone, so
+// fl(fl(float(A_W - A_J) + rowb_W) + keyb_J), with the anchors of a 32-row
+// block W and a 32-key tile J, is at least every computed exponent of the
+// 32 x 32 tile.  Where it is below kSkipLog2 every exponential of the tile is
+// exactly 0 in float32, every C~' entry is 0, and the tile contributes
+// nothing: the tile kernels skip it without changing any result.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,11 +35,15 @@ namespace mlstm {
 
 constexpr int kRowPad = 128;     // T is padded to a multiple of this
 constexpr int kAnchorBlock = 64; // positions per float64 anchor
+constexpr int kBoundTile = 32;   // rows / keys per entry of rowb and keyb
+constexpr float kSkipLog2 = -200.0f;
 
 struct Workspace {
   double* anchor;
   float* rowt;
   float* colt;
+  float* rowb;
+  float* keyb;
   int64_t Tp;
   int64_t nblk;
 };
@@ -41,7 +55,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline size_t workspace_bytes(int64_t H, int64_t T) {
   const int64_t Tp = padded_len(T);
   return align256(size_t(H) * size_t(Tp / kAnchorBlock) * sizeof(double)) +
-         2 * align256(size_t(H) * size_t(Tp) * sizeof(float));
+         2 * align256(size_t(H) * size_t(Tp) * sizeof(float)) +
+         2 * align256(size_t(H) * size_t(Tp / kBoundTile) * sizeof(float));
 }
 
 inline Workspace carve(void* base, int64_t H, int64_t T) {
@@ -54,6 +69,10 @@ inline Workspace carve(void* base, int64_t H, int64_t T) {
   w.rowt = reinterpret_cast<float*>(p);
   p += align256(size_t(H) * size_t(w.Tp) * sizeof(float));
   w.colt = reinterpret_cast<float*>(p);
+  p += align256(size_t(H) * size_t(w.Tp) * sizeof(float));
+  w.rowb = reinterpret_cast<float*>(p);
+  p += align256(size_t(H) * size_t(w.Tp / kBoundTile) * sizeof(float));
+  w.keyb = reinterpret_cast<float*>(p);
   return w;
 }
 
@@ -71,11 +90,13 @@ hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out
                             const Workspace& ws, int64_t H, int64_t T, int64_t d,
                             hipStream_t stream);
 
-// Stage 2, bf16 matrix-core tiles.  Returns hipErrorInvalidValue for an
-// unsupported head dimension (none for d % 16 == 0, 16 <= d <= 512).
+// Stage 2, bf16 matrix-core tiles; `skip` enables the decay-aware skipping
+// of tiles whose bound is below kSkipLog2 (results are identical either way).
+// Returns hipErrorInvalidValue for an unsupported head dimension (none for
+// d % 16 == 0, 16 <= d <= 512).
 hipError_t launch_tiles_mfma(const void* q, const void* k, const void* v, const float* m,
                              const Workspace& ws, void* h_out, float* n_out,
-                             const Epilogue& ep, int64_t H, int64_t T, int64_t d,
+                             const Epilogue& ep, bool skip, int64_t H, int64_t T, int64_t d,
                              hipStream_t stream);
 
 // Stage 2, float32 vector-ALU tiles; is_bf16 selects the element type.

@@ -63,7 +63,8 @@ struct Cfg {
   static constexpr int V_BYTES = kBN * RSV;
   static constexpr int C_OFF = K_BYTES + V_BYTES;
   static constexpr int A_OFF = C_OFF + kBN * 4;  // float64 anchor of the key tile
-  static constexpr int BUF = (A_OFF + 8 + 15) / 16 * 16;
+  static constexpr int KB_OFF = A_OFF + 8;       // max of c_j over the key tile
+  static constexpr int BUF = (KB_OFF + 4 + 15) / 16 * 16;
 };
 
 // Heaviest row tiles first (a row tile I costs ~I + 1 key tiles), and when the
@@ -105,8 +106,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ m_in, const double* __restrict__ anchor,
     const float* __restrict__ rowt, const float* __restrict__ colt, u16* __restrict__ h_out,
-    float* __restrict__ n_out, const u16* __restrict__ ogate, u16* __restrict__ htilde, int64_t T,
-    int d, int64_t Tp, int64_t nblk, int64_t row_tiles, int64_t H) {
+    const float* __restrict__ rowb, const float* __restrict__ keyb, float* __restrict__ n_out,
+    const u16* __restrict__ ogate, u16* __restrict__ htilde, int64_t T, int d, int64_t Tp,
+    int64_t nblk, int64_t row_tiles, int64_t H, int skip) {
   using C = Cfg<DP>;
   // two distinct buffers, so the loads into one never alias reads of the other
   __shared__ __attribute__((aligned(1024))) char smem0[C::BUF];
@@ -152,6 +154,54 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int64_t last_tile = (4 * I + 3 < n_key_tiles - 1) ? 4 * I + 3 : n_key_tiles - 1;
   const int64_t wave_last = (4 * I + w < n_key_tiles - 1) ? 4 * I + w : n_key_tiles - 1;
 
+  // ---- decay-aware tile skipping.  A key tile J whose exponent bound (see
+  // the workspace notes) is below kSkipLog2 for a wave's 32 rows contributes
+  // exactly zero to them.  The workgroup starts its key loop at the first
+  // tile some wave needs, and inside the loop each wave skips the products
+  // of tiles it does not need.
+  const int64_t nb32 = Tp / kBoundTile;
+  const float rb_w = rowb[head * nb32 + qw / kBoundTile];
+  auto tile_needed = [&](double a_row, float rb, double a_key, float kb) {
+    return float(a_row - a_key) + rb + kb >= kSkipLog2;
+  };
+  int64_t first_tile = 0;
+  if (skip) {
+    __shared__ int64_t s_first[kWaves];
+    double a_rows[kWaves];
+    float rb_rows[kWaves];
+    int64_t last_w[kWaves];
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) {
+      const int64_t qu = q0 + 32 * u;
+      a_rows[u] = anchor[head * nblk + qu / kAnchorBlock];
+      rb_rows[u] = rowb[head * nb32 + qu / kBoundTile];
+      last_w[u] = (4 * I + u < n_key_tiles - 1) ? 4 * I + u : n_key_tiles - 1;
+    }
+    int64_t mine = last_tile;  // the diagonal tile of wave 0 bounds the answer
+    for (int64_t J = tid; J < last_tile; J += kThreads) {
+      const double a_key = anchor[head * nblk + (J * kBN) / kAnchorBlock];
+      const float kb = keyb[head * nb32 + J];
+      bool need = false;
+#pragma unroll
+      for (int u = 0; u < kWaves; ++u)
+        need = need || (J <= last_w[u] && tile_needed(a_rows[u], rb_rows[u], a_key, kb));
+      if (need) {
+        mine = J;
+        break;  // J grows with each iteration: the first hit is this thread's least
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const int64_t o = __shfl_xor(mine, off, 64);
+      mine = o < mine ? o : mine;
+    }
+    if (lane == 0) s_first[w] = mine;
+    __syncthreads();
+    first_tile = s_first[0];
+#pragma unroll
+    for (int u = 1; u < kWaves; ++u) first_tile = s_first[u] < first_tile ? s_first[u] : first_tile;
+  }
+
   // ---- global -> LDS copy of tile J: each wave copies 8 K rows and 8 V rows.
   // The buffer range ends at the last key of the sequence, so rows past it
   // arrive as zeros; head-dimension padding reads an out-of-range offset.
@@ -170,10 +220,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       }
     }
     if (w == 0 && lane < kBN / 4)
-      dma16(make_rsrc(colt + head * Tp, Tp * 4), unsigned((k0 + 4 * lane) * 4), buf + C::C_OFF);
+      dma16(make_rsrc(colt + head * Tp + k0, kBN * 4), unsigned(16 * lane), buf + C::C_OFF);
     if (w == 1 && lane < 2)
-      dma4(make_rsrc(anchor + head * nblk, nblk * 8),
-           unsigned((k0 / kAnchorBlock) * 8 + 4 * lane), buf + C::A_OFF);
+      dma4(make_rsrc(anchor + head * nblk + k0 / kAnchorBlock, 8), unsigned(4 * lane),
+           buf + C::A_OFF);
+    if (w == 2 && lane < 1) dma4(make_rsrc(keyb + head * nb32 + J, 4), 0u, buf + C::KB_OFF);
+  };
+  // whether this wave's rows need tile J (copied into `buf`)
+  auto wave_needs = [&](const char* buf, int64_t J) {
+    if (J > wave_last) return false;
+    if (!skip) return true;
+    const double a_key = *reinterpret_cast<const double*>(buf + C::A_OFF);
+    const float kb = *reinterpret_cast<const float*>(buf + C::KB_OFF);
+    return tile_needed(a_i, rb_w, a_key, kb);
   };
 
   // per-lane LDS offsets of the operand reads
@@ -255,23 +314,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     }
   };
 
-  load_tile(0, smem0);
+  load_tile(first_tile, smem0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // No plain global load is issued inside the loop: everything a tile needs
   // (K, V, c and the key-tile anchor) arrives by the copies into LDS, so the
   // waits on those copies stay exact.
-  for (int64_t J = 0; J <= last_tile; J += 2) {
+  for (int64_t J = first_tile; J <= last_tile; J += 2) {
     // even tile from smem0, prefetch into smem1
     if (J + 1 <= last_tile) load_tile(J + 1, smem1);
-    if (J <= wave_last) compute(smem0, J);
+    if (wave_needs(smem0, J)) compute(smem0, J);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (J + 1 > last_tile) break;
     // odd tile from smem1, prefetch into smem0
     if (J + 2 <= last_tile) load_tile(J + 2, smem0);
-    if (J + 1 <= wave_last) compute(smem1, J + 1);
+    if (wave_needs(smem1, J + 1)) compute(smem1, J + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -316,13 +375,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 template <int DP>
 hipError_t launch_dp(const void* q, const void* k, const void* v, const float* m,
                      const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,
-                     int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+                     bool skip, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
   const int64_t row_tiles = (T + kBM - 1) / kBM;
   hipLaunchKernelGGL(tiles_mfma_kernel<DP>, dim3(unsigned(row_tiles * H)), dim3(kThreads), 0,
                      stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), m, ws.anchor, ws.rowt, ws.colt,
-                     static_cast<u16*>(h_out), n_out, static_cast<const u16*>(ep.ogate),
-                     static_cast<u16*>(ep.htilde), T, int(d), ws.Tp, ws.nblk, row_tiles, H);
+                     static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
+                     static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), T, int(d),
+                     ws.Tp, ws.nblk, row_tiles, H, int(skip));
   return hipGetLastError();
 }
 
@@ -330,26 +390,26 @@ hipError_t launch_dp(const void* q, const void* k, const void* v, const float* m
 
 hipError_t launch_tiles_mfma(const void* q, const void* k, const void* v, const float* m,
                              const Workspace& ws, void* h_out, float* n_out,
-                             const Epilogue& ep, int64_t H, int64_t T, int64_t d,
-                             hipStream_t stream) {
+                             const Epilogue& ep, bool skip, int64_t H, int64_t T,
+                             int64_t d, hipStream_t stream) {
   // head dims are padded up to a multiple of 32 (zero columns add nothing)
   switch ((d + 31) / 32) {
-    case 1: return launch_dp<32>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 2: return launch_dp<64>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 3: return launch_dp<96>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 4: return launch_dp<128>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 5: return launch_dp<160>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 6: return launch_dp<192>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 7: return launch_dp<224>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 8: return launch_dp<256>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 9: return launch_dp<288>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 10: return launch_dp<320>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 11: return launch_dp<352>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 12: return launch_dp<384>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 13: return launch_dp<416>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 14: return launch_dp<448>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 15: return launch_dp<480>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
-    case 16: return launch_dp<512>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    case 1: return launch_dp<32>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 2: return launch_dp<64>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 3: return launch_dp<96>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 4: return launch_dp<128>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 5: return launch_dp<160>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 6: return launch_dp<192>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 7: return launch_dp<224>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 8: return launch_dp<256>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 9: return launch_dp<288>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 10: return launch_dp<320>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 11: return launch_dp<352>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 12: return launch_dp<384>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 13: return launch_dp<416>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 14: return launch_dp<448>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 15: return launch_dp<480>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 16: return launch_dp<512>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
     default: return hipErrorInvalidValue;
   }
 }

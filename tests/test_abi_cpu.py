@@ -46,9 +46,12 @@ def test_strerror_and_workspace_size():
         assert msg and msg != "unknown status"
     assert mlstm.strerror(-99) == "unknown status"
     lib = mlstm.load_library()
-    # anchors (8 B per 64 positions) + two float32 terms per position, T padded to 128
-    assert lib.mlstm_workspace_bytes(1, 1, 64) == 256 + 2 * 512
-    assert lib.mlstm_workspace_bytes(8, 4, 2048) == 32 * 32 * 8 + 2 * 32 * 2048 * 4
+    # float64 anchors (one per 64 positions), two float32 terms per position and
+    # two float32 tile bounds per 32 positions, T padded to 128, each region
+    # 256-byte aligned
+    assert lib.mlstm_workspace_bytes(1, 1, 64) == 256 + 2 * 512 + 2 * 256
+    assert lib.mlstm_workspace_bytes(8, 4, 2048) == (32 * 32 * 8 + 2 * 32 * 2048 * 4
+                                                     + 2 * 32 * 64 * 4)
     assert lib.mlstm_workspace_bytes(0, 4, 2048) == 0
     assert lib.mlstm_workspace_bytes(1, 1, 0) == 0
 
@@ -84,6 +87,8 @@ def test_staged_entry_points_reject_before_device_work():
     # MFMA kernel for float32 inputs
     assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE,
                                   1, 1, 64, 16, 0, 1, None) == -8
+    assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE,
+                                  1, 1, 64, 16, 0, 3, None) == -8
     # unknown kernel selector
     assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE,
                                   1, 1, 64, 16, 1, 7, None) == -8

@@ -285,3 +285,39 @@ def test_output_gate_language_model_sampled():
     hr, mr, nr, _ = _sampled_reference(x, rows)
     gated_ref = oracle.output_gate(hr, og[:, :, rows])
     print(check(h[:, :, rows], m[:, :, rows], n[:, :, rows], gated_ref, mr, nr, TOL_H["bf16"]))
+
+
+# ---------------------------------------------------------------------------
+# decay-aware tile skipping: identical results to visiting every causal tile
+# ---------------------------------------------------------------------------
+
+def _staged(x, kernel):
+    q, k, v, ig, fg = _dev(x)
+    h, m, n = mlstm.parallel_fwd_staged(q, k, v, ig, fg, kernel=kernel)
+    torch.cuda.synchronize()
+    return h, m, n
+
+
+@pytest.mark.parametrize("s", [
+    spec(1, 4, 3000, 64, ig=("uniform", -20, 20), fg=("normal", 0, 4), fgate_floor=(0.01, -30.0)),
+    spec(2, 2, 1500, 128, ig=("uniform", -40, 40), fg=("normal", -2, 3)),
+    spec(1, 2, 2100, 256, ig=("normal", 0, 1), fg=("normal", -4, 1)),
+    spec(1, 1, 700, 384),  # slow decay: nothing to skip
+], ids=_id)
+def test_tile_skipping_matches_all_tiles_and_oracle(s):
+    x = W.make(s, seed=14)
+    a = _staged(x, "mfma")
+    b = _staged(x, "mfma_all_tiles")
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta, tb)  # equal values (an exact zero may differ in sign)
+    hr, mr, nr, _, rho = oracle_full(x)
+    print(check(_host(a[0]), _host(a[1]), _host(a[2]), hr, mr, nr, TOL_H["bf16"],
+                kappa=rho / nr, kappa_max=1e3))
+
+
+def test_tile_skipping_long_context_full_size():
+    x = W.make("long_context_16k", seed=0)
+    a = _staged(x, "auto")
+    b = _staged(x, "mfma_all_tiles")
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta, tb)
