@@ -24,6 +24,11 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
 * ``forward_unstabilized`` pinned: exact rational examples.
 * ``gate_matrices``        pinned: F_ii = 1, zero above the diagonal, explicit
   products, log F = -inf / 0 / partial sums (Eqs. 71, 72, 101).
+* ``recurrent_step_stabilized`` / ``forward_recurrent_stabilized``  pinned:
+  h equals the unstabilized recurrent form, m and the normalizer equal the
+  parallel form's m and n, and exp(m_T) times the final states equals their
+  definition as gate-weighted sums of v k^T and k (brute force on tiny
+  inputs), also where exp(i~) overflows the unstabilized form.
 * ``output_gate``          pinned: sigma(0) = 1/2 and sigma(-x) = 1 - sigma(x)
   closed forms (Eq. 78).
 """
@@ -35,6 +40,8 @@ from .mlstm import (  # noqa: F401
     forward_stabilized,
     forward_rows,
     forward_recurrent,
+    recurrent_step_stabilized,
+    forward_recurrent_stabilized,
     forward_unstabilized,
     output_gate,
 )

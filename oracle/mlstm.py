@@ -191,6 +191,72 @@ def forward_recurrent(q, k, v, igate, fgate):
     return h, nq
 
 
+def recurrent_step_stabilized(q_t, k_t, v_t, ig_t, fg_t, C, nvec, m):
+    """One step of the recurrent mLSTM for ONE head with stabilized states,
+    float64.
+
+    The pages stabilize the recurrent mLSTM as the sLSTM (its Eq. 15 is not on
+    the pages); the reading used here is the plainest one consistent with the
+    parallel form: the stabilizer is the running maximum of the log gates,
+        m_t = max(fbar_t + m_{t-1}, i~_t),   m_0 = -inf,
+    which is the row maximum m of Eq. 80 (split j = t from j < t), and the
+    states are the unstabilized ones of the recurrent form scaled by
+    exp(-m_t):
+        f'_t = exp(fbar_t + m_{t-1} - m_t),   i'_t = exp(i~_t - m_t),
+        C_t = f'_t C_{t-1} + i'_t v_t k'_t^T,  n_t = f'_t n_{t-1} + i'_t k'_t,
+    with k'_t = k_t / sqrt(d).  Dividing C_t q_t by max(|n_t . q_t|, 1) in the
+    unstabilized scale is then dividing by max(|n_t . q_t|, exp(-m_t)) here,
+    the normalizer of Eq. 84.
+
+    Inputs: vectors q_t, k_t, v_t (d), scalars ig_t (i~), fg_t (f~), state
+    C (d x d, rows indexed by the value dimension), nvec (d), m (scalar;
+    -inf for a fresh state).  Returns (h_t, C_t, n_t, m_t, den_t).
+    """
+    q_t = np.asarray(q_t, dtype=np.float64)
+    k_t = np.asarray(k_t, dtype=np.float64)
+    v_t = np.asarray(v_t, dtype=np.float64)
+    d = q_t.shape[0]
+    fbar = float(log_sigmoid(fg_t))
+    ig = float(ig_t)
+    m_new = max(fbar + m, ig)
+    f_p = math.exp(fbar + m - m_new) if m != -math.inf else 0.0
+    i_p = math.exp(ig - m_new)
+    kp = k_t / math.sqrt(d)
+    C_new = f_p * np.asarray(C, dtype=np.float64) + i_p * np.outer(v_t, kp)
+    n_new = f_p * np.asarray(nvec, dtype=np.float64) + i_p * kp
+    den = max(abs(float(n_new @ q_t)), math.exp(-m_new))
+    h = (C_new @ q_t) / den
+    return h, C_new, n_new, m_new, den
+
+
+def forward_recurrent_stabilized(q, k, v, igate, fgate):
+    """``recurrent_step_stabilized`` from a fresh state (C = 0, n = 0,
+    m = -inf) over every position of every head.
+
+    Returns (h [B,NH,T,d], m [B,NH,T], den [B,NH,T], C_T [B,NH,d,d],
+    n_T [B,NH,d]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, NH, T, d = q.shape
+    h = np.empty((B, NH, T, d))
+    mm = np.empty((B, NH, T))
+    den = np.empty((B, NH, T))
+    CT = np.empty((B, NH, d, d))
+    nT = np.empty((B, NH, d))
+    for bi in range(B):
+        for hi in range(NH):
+            C = np.zeros((d, d))
+            nvec = np.zeros(d)
+            m = -math.inf
+            for t in range(T):
+                h[bi, hi, t], C, nvec, m, den[bi, hi, t] = recurrent_step_stabilized(
+                    q[bi, hi, t], k[bi, hi, t], v[bi, hi, t], igate[bi, hi, t], fgate[bi, hi, t],
+                    C, nvec, m)
+                mm[bi, hi, t] = m
+            CT[bi, hi], nT[bi, hi] = C, nvec
+    return h, mm, den, CT, nT
+
+
 def forward_unstabilized(q, k, v, igate, fgate):
     """Unstabilized parallel form, Eqs. 71-73 and 76, by brute force.
 

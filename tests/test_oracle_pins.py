@@ -430,3 +430,70 @@ def test_pins_catch_mutant(name, monkeypatch):
         fn = _mutant_lgm
     monkeypatch.setattr(om, attr, fn)
     assert not _pins_pass(), f"mutant {name} survived every pin"
+
+
+# ---------------------------------------------------------------------------
+# stabilized recurrent step (the generation step of the recurrent form)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,ig_scale", [(0, 1.0), (1, 10.0), (2, 30.0)])
+def test_recurrent_stabilized_matches_unstabilized_and_parallel(seed, ig_scale):
+    rng = np.random.default_rng(seed)
+    B, NH, T, d = 1, 2, 19, 8
+    q, k, v = (rng.standard_normal((B, NH, T, d)) for _ in range(3))
+    ig = ig_scale * rng.standard_normal((B, NH, T))
+    fg = 2.0 + 2.0 * rng.standard_normal((B, NH, T))
+    h, m, den, CT, nT = om.forward_recurrent_stabilized(q, k, v, ig, fg)
+    hu, _ = om.forward_recurrent(q, k, v, ig, fg)
+    hp, mp, npar = om.forward_stabilized(q, k, v, ig, fg)
+    assert np.allclose(h, hu, rtol=1e-11, atol=1e-12)
+    assert np.allclose(h, hp, rtol=1e-11, atol=1e-12)
+    assert np.allclose(m, mp, rtol=1e-13, atol=1e-13)
+    assert np.allclose(den, npar, rtol=1e-11, atol=0)
+
+
+def test_recurrent_stabilized_states_are_scaled_gate_sums():
+    """exp(m_T) C_T = sum_j F_Tj exp(i~_j) v_j k_j^T / sqrt(d) and likewise
+    for n_T (the definitions of the recurrent states unrolled), by brute
+    force with the explicit products of Eq. 71."""
+    rng = np.random.default_rng(3)
+    B, NH, T, d = 1, 1, 11, 6
+    q, k, v = (rng.standard_normal((B, NH, T, d)) for _ in range(3))
+    ig = 3.0 * rng.standard_normal((B, NH, T))
+    fg = 1.0 + rng.standard_normal((B, NH, T))
+    _, m, _, CT, nT = om.forward_recurrent_stabilized(q, k, v, ig, fg)
+    F, _ = om.gate_matrices(fg[0, 0], ig[0, 0])
+    kp = k[0, 0] / math.sqrt(d)
+    Cdef = sum(F[T - 1, j] * math.exp(ig[0, 0, j]) * np.outer(v[0, 0, j], kp[j]) for j in range(T))
+    ndef = sum(F[T - 1, j] * math.exp(ig[0, 0, j]) * kp[j] for j in range(T))
+    scale = math.exp(m[0, 0, T - 1])
+    assert np.allclose(scale * CT[0, 0], Cdef, rtol=1e-12, atol=1e-12)
+    assert np.allclose(scale * nT[0, 0], ndef, rtol=1e-12, atol=1e-12)
+
+
+def test_recurrent_stabilized_survives_exp_overflow():
+    """Input gates far past exp's float64 range: the stabilized step stays
+    finite and equal to the stabilized parallel form."""
+    rng = np.random.default_rng(4)
+    B, NH, T, d = 1, 1, 16, 8
+    q, k, v = (rng.standard_normal((B, NH, T, d)) for _ in range(3))
+    ig = rng.uniform(-800.0, 800.0, (B, NH, T))
+    fg = 4.0 * rng.standard_normal((B, NH, T))
+    h, m, den, _, _ = om.forward_recurrent_stabilized(q, k, v, ig, fg)
+    hp, mp, npar = om.forward_stabilized(q, k, v, ig, fg)
+    assert np.isfinite(h).all()
+    assert np.allclose(h, hp, rtol=1e-10, atol=1e-12)
+    assert np.allclose(m, mp, rtol=1e-13, atol=1e-13)
+    assert np.allclose(den, npar, rtol=1e-10, atol=0)
+
+
+def test_recurrent_step_fresh_state_is_the_single_step_closed_form():
+    rng = np.random.default_rng(5)
+    d = 5
+    q, k, v = rng.standard_normal((3, d))
+    h, C, n, m, den = om.recurrent_step_stabilized(q, k, v, 2.5, -1.0, np.zeros((d, d)),
+                                                   np.zeros(d), -math.inf)
+    s = float(q @ k) / math.sqrt(d)
+    assert m == 2.5
+    assert np.allclose(h, s * v / max(abs(s), math.exp(-2.5)), rtol=1e-14)
+    assert np.allclose(C, np.outer(v, k) / math.sqrt(d), rtol=1e-14)
