@@ -132,6 +132,36 @@ def long_context_skipping(torch, mlstm, workloads, dev, reps):
             "speedup": round(out["mfma_all_tiles"] / out["mfma"], 2)}
 
 
+def recurrent_decode(torch, mlstm, dev, B, NH, d, reps=50):
+    """Time mlstm_recurrent_step (bf16 q/k/v, float32 state updated in place)."""
+    g = torch.Generator(device="cpu").manual_seed(0)
+    q, k, v = (torch.randn((B, NH, d), generator=g).to(dev).to(torch.bfloat16) for _ in range(3))
+    ig = torch.randn((B, NH), generator=g).to(dev)
+    fg = (3.0 + torch.randn((B, NH), generator=g)).to(dev)
+    C, n, m = mlstm.recurrent_state(B, NH, d, dev)
+    n2, m2 = torch.empty_like(n), torch.empty_like(m)
+    states = [(C, n, m), (C, n2, m2)]
+    for i in range(3):
+        mlstm.recurrent_step(q, k, v, ig, fg, states[i % 2], out_state=states[(i + 1) % 2])
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        mlstm.recurrent_step(q, k, v, ig, fg, states[i % 2], out_state=states[(i + 1) % 2])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    H = B * NH
+    # state read + written once, plus the step's vectors and scalars
+    nbytes = H * (2 * d * d * 4 + 2 * d * 4 + 4 * d * 2 + 5 * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"B": B, "NH": NH, "d": d, "us_per_step": round(ms * 1e3, 2),
+            "algorithmic_bytes": nbytes, "GB/s": round(gbs, 1),
+            "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "state_MB": round(H * d * d * 4 / 1e6, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -203,6 +233,12 @@ def main():
     if not args.no_long_context:
         skip_rec = long_context_skipping(torch, mlstm, workloads, dev, reps=10)
 
+    # recurrent (generation) step on the same layer shape: the 8 x 4 heads'
+    # state (19 MB) stays in the 256 MB last-level cache between steps; a
+    # batch of 256 (604 MB of state) has to stream it from HBM
+    rec = [recurrent_decode(torch, mlstm, dev, B, NH, d),
+           recurrent_decode(torch, mlstm, dev, 256, NH, d, reps=20)]
+
     # correctness spot check of the timed output (not part of the timing)
     mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
     torch.cuda.synchronize()
@@ -238,6 +274,7 @@ def main():
     }
     if skip_rec is not None:
         line["tile_skipping"] = skip_rec
+    line["recurrent_step"] = rec
     if args.copy_calibration:
         # reads and writes exactly COPY_BYTES each per launch
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

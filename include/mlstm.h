@@ -88,7 +88,8 @@ enum {
   MLSTM_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
   MLSTM_ERR_HIP = -6,         /* a HIP allocation or launch failed */
   MLSTM_ERR_WORKSPACE = -7,   /* caller workspace smaller than mlstm_workspace_bytes */
-  MLSTM_ERR_KERNEL = -8       /* unknown kernel selector, or an MFMA selector for fp32 */
+  MLSTM_ERR_KERNEL = -8,      /* unknown kernel selector, or an MFMA selector for fp32 */
+  MLSTM_ERR_ALIAS = -9        /* an output overlaps an input it must not alias */
 };
 
 /*
@@ -170,6 +171,41 @@ int mlstm_causal_tiles(const void* q, const void* k, const void* v, const float*
                        void* h_out, float* n_out,
                        int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
                        int kernel, void* stream);
+
+/*
+ * mlstm_recurrent_step -- one step of the recurrent mLSTM (the generation
+ * form that the parallel pass reformulates; its equations are those the
+ * recurrent backward pass of appendix A.3 differentiates, Eqs. 59-70), with
+ * the states stabilized by the running maximum of the log gates, the same
+ * recurrence as the parallel form's row maximum (Eq. 80):
+ *   m_t  = max(log sigmoid(f~_t) + m_{t-1}, i~_t)
+ *   f'_t = exp(log sigmoid(f~_t) + m_{t-1} - m_t),  i'_t = exp(i~_t - m_t)
+ *   C_t  = f'_t C_{t-1} + i'_t v_t (k_t / sqrt(d))^T
+ *   n_t  = f'_t n_{t-1} + i'_t k_t / sqrt(d)
+ *   h~_t = C_t q_t / max(|n_t . q_t|, exp(-m_t))
+ * These states are the unstabilized ones times exp(-m_t); h~_t, m_t and the
+ * denominator equal row t of mlstm_parallel_fwd's h~, m and n.
+ *   q, k, v      in   [B][NH][d], dtype: this step's query, key, value
+ *   igate, fgate in   [B][NH] float32: i~_t, f~_t
+ *   C_in, n_in, m_in   in  [B][NH][d][d], [B][NH][d], [B][NH] float32: the
+ *                state after step t-1 (C rows index the value dimension);
+ *                a fresh state is C = 0, n = 0, m = -inf
+ *   C_out, n_out, m_out out: the state after step t.  C_out may be C_in
+ *                (updated in place); n_out and m_out must not overlap n_in and
+ *                m_in (MLSTM_ERR_ALIAS)
+ *   h_out        out  [B][NH][d], dtype: h~_t (before any output gate)
+ *   den_out      out  [B][NH] float32: max(|n_t . q_t|, exp(-m_t)); may be NULL
+ *   d            a multiple of 16 in [16, 512]
+ * Vectors and C need 16-byte alignment, scalars 4-byte.  Asynchronous on
+ * `stream`; no workspace.  Bound by memory bandwidth: the state is read and
+ * written once per step.
+ */
+int mlstm_recurrent_step(const void* q, const void* k, const void* v,
+                         const float* igate, const float* fgate,
+                         const float* C_in, const float* n_in, const float* m_in,
+                         float* C_out, float* n_out, float* m_out,
+                         void* h_out, float* den_out,
+                         int64_t B, int64_t NH, int64_t d, int dtype, void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* mlstm_strerror(int status);

@@ -29,6 +29,11 @@ int check_shape(int64_t B, int64_t NH, int64_t T, int64_t d) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? MLSTM_OK : MLSTM_ERR_HIP; }
 
 int check_scan_args(const float* igate, const float* fgate, const float* m_out, const void* ws) {
@@ -171,6 +176,38 @@ int mlstm_parallel_fwd(const void* q, const void* k, const void* v, const float*
                                    dtype, nullptr);
 }
 
+int mlstm_recurrent_step(const void* q, const void* k, const void* v, const float* igate,
+                         const float* fgate, const float* C_in, const float* n_in,
+                         const float* m_in, float* C_out, float* n_out, float* m_out,
+                         void* h_out, float* den_out, int64_t B, int64_t NH, int64_t d,
+                         int dtype, void* stream) {
+  if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
+  int st = check_shape(B, NH, 1, d);
+  if (st != MLSTM_OK) return st;
+  if (!q || !k || !v || !igate || !fgate || !C_in || !n_in || !m_in || !C_out || !n_out ||
+      !m_out || !h_out)
+    return MLSTM_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(C_in) || !aligned16(n_in) ||
+      !aligned16(C_out) || !aligned16(n_out) || !aligned16(h_out) ||
+      (reinterpret_cast<uintptr_t>(igate) & 3) || (reinterpret_cast<uintptr_t>(fgate) & 3) ||
+      (reinterpret_cast<uintptr_t>(m_in) & 3) || (reinterpret_cast<uintptr_t>(m_out) & 3) ||
+      (reinterpret_cast<uintptr_t>(den_out) & 3))
+    return MLSTM_ERR_ALIGN;
+  const int64_t H = B * NH;
+  // C may be updated in place, but not through a shifted window; n and m are
+  // read by every workgroup while the first of each head writes them
+  const size_t cb = size_t(H) * size_t(d) * size_t(d) * sizeof(float);
+  const size_t nb = size_t(H) * size_t(d) * sizeof(float);
+  const size_t mb = size_t(H) * sizeof(float);
+  if ((C_out != C_in && overlaps(C_in, cb, C_out, cb)) || overlaps(n_in, nb, n_out, nb) ||
+      overlaps(m_in, mb, m_out, mb))
+    return MLSTM_ERR_ALIAS;
+  return hip_status(mlstm::launch_recurrent_step(q, k, v, igate, fgate, C_in, n_in, m_in, C_out,
+                                                 n_out, m_out, h_out, den_out, H, d,
+                                                 dtype == MLSTM_BF16,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 const char* mlstm_strerror(int status) {
   switch (status) {
     case MLSTM_OK: return "success";
@@ -182,6 +219,7 @@ const char* mlstm_strerror(int status) {
     case MLSTM_ERR_HIP: return "HIP allocation or kernel launch failed";
     case MLSTM_ERR_WORKSPACE: return "workspace smaller than mlstm_workspace_bytes()";
     case MLSTM_ERR_KERNEL: return "unknown kernel selector, or the MFMA kernel asked for float32";
+    case MLSTM_ERR_ALIAS: return "an output overlaps an input it must not alias";
     default: return "unknown status";
   }
 }

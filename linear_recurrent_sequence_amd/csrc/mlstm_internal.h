@@ -105,4 +105,14 @@ hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, cons
                                const Epilogue& ep, int64_t H, int64_t T, int64_t d,
                                bool is_bf16, hipStream_t stream);
 
+// Recurrent step (generation), stabilized states in float32: C [H][d][d],
+// n [H][d], m [H].  C_out may equal C_in; n_out / m_out must not overlap
+// n_in / m_in.  den_out [H] is optional.  hipErrorInvalidValue for an
+// unsupported d (a multiple of 16 in [16, 512] is supported).
+hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, const float* igate,
+                                 const float* fgate, const float* C_in, const float* n_in,
+                                 const float* m_in, float* C_out, float* n_out, float* m_out,
+                                 void* h_out, float* den_out, int64_t H, int64_t d, bool is_bf16,
+                                 hipStream_t stream);
+
 }  // namespace mlstm

@@ -50,6 +50,8 @@ def load_library():
     lib.mlstm_parallel_fwd_stream.restype = i32
     lib.mlstm_parallel_fwd_gated.argtypes = [vp] * 10 + [i64] * 4 + [i32, vp]
     lib.mlstm_parallel_fwd_gated.restype = i32
+    lib.mlstm_recurrent_step.argtypes = [vp] * 13 + [i64] * 3 + [i32, vp]
+    lib.mlstm_recurrent_step.restype = i32
     lib.mlstm_workspace_bytes.argtypes = [i64] * 3
     lib.mlstm_workspace_bytes.restype = f
     lib.mlstm_gate_scan.argtypes = [vp] * 4 + [f] + [i64] * 4 + [vp]
@@ -205,3 +207,50 @@ def parallel_fwd_staged(q, k, v, igate, fgate, kernel="auto"):
     m = gate_scan(igate, fgate, d, ws)
     h, n = causal_tiles(q, k, v, m, ws, kernel=kernel)
     return h, m, n
+
+
+def recurrent_state(B, NH, d, device):
+    """A fresh recurrent state (C = 0, n = 0, m = -inf), float32."""
+    C = torch.zeros((B, NH, d, d), dtype=torch.float32, device=device)
+    n = torch.zeros((B, NH, d), dtype=torch.float32, device=device)
+    m = torch.full((B, NH), float("-inf"), dtype=torch.float32, device=device)
+    return C, n, m
+
+
+def recurrent_step(q, k, v, igate, fgate, state, out_state=None, den=False):
+    """One stabilized recurrent step -> (h, new_state[, den]).
+
+    q, k, v: [B, NH, d] (float32 or bfloat16); igate, fgate: [B, NH] float32;
+    state = (C [B,NH,d,d], n [B,NH,d], m [B,NH]) float32.  ``out_state``
+    receives the new state (its C may be the input C: updated in place); by
+    default C is updated in place and new n, m are allocated.
+    """
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, NH, d], got {tuple(q.shape)}")
+    B, NH, d = q.shape
+    C, n, m = state
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    for name, t, shp in (("igate", igate, (B, NH)), ("fgate", fgate, (B, NH)),
+                         ("C", C, (B, NH, d, d)), ("n", n, (B, NH, d)), ("m", m, (B, NH))):
+        if tuple(t.shape) != shp or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 {shp}")
+    for t in (q, k, v, igate, fgate, C, n, m):
+        if not (t.is_cuda and t.is_contiguous() and t.device == q.device):
+            raise ValueError("all tensors must be contiguous on the same GPU")
+    if out_state is None:
+        out_state = (C, torch.empty_like(n), torch.empty_like(m))
+    Co, no, mo = out_state
+    h = torch.empty_like(q)
+    dn = torch.empty((B, NH), dtype=torch.float32, device=q.device) if den else None
+    with torch.cuda.device(q.device):
+        st = lib.mlstm_recurrent_step(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
+            C.data_ptr(), n.data_ptr(), m.data_ptr(), Co.data_ptr(), no.data_ptr(), mo.data_ptr(),
+            h.data_ptr(), dn.data_ptr() if den else None, B, NH, d, _dtype_code(q),
+            _stream_ptr(q.device))
+    if st != 0:
+        raise MlstmError(st, "mlstm_recurrent_step")
+    return (h, out_state, dn) if den else (h, out_state)

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_strerror_and_workspace_size():
-    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         msg = mlstm.strerror(st)
         assert msg and msg != "unknown status"
     assert mlstm.strerror(-99) == "unknown status"
@@ -112,4 +112,27 @@ def test_gated_forward_rejects_before_device_work(case, status):
     st = lib.mlstm_parallel_fwd_gated(*[args[k] or None for k in ptrs],
                                       args["B"], args["NH"], args["T"], args["d"], args["dtype"],
                                       None)
+    assert st == status
+
+
+@needs_lib
+@pytest.mark.parametrize("case,status", [
+    (dict(q=0), -1), (dict(C_in=0), -1), (dict(h_out=0), -1),
+    (dict(d=24), -4), (dict(d=528), -4), (dict(B=0), -2), (dict(dtype=5), -3),
+    (dict(C_in=FAKE + 8), -5), (dict(igate=FAKE + 2), -5),
+    (dict(n_out=FAKE), -9),                       # n_out is n_in
+    (dict(m_out=FAKE + (1 << 16)), -9),           # m_out is m_in
+    (dict(C_out=FAKE + (1 << 12)), -9),           # C_out overlaps C_in, shifted
+])
+def test_recurrent_step_rejects_before_device_work(case, status):
+    lib = mlstm.load_library()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, igate=FAKE, fgate=FAKE,
+                C_in=FAKE, n_in=FAKE, m_in=FAKE + (1 << 16),
+                C_out=FAKE, n_out=FAKE + (1 << 24), m_out=FAKE + (1 << 25),
+                h_out=FAKE, den_out=0, B=1, NH=1, d=64, dtype=1)
+    args.update(case)
+    ptrs = ["q", "k", "v", "igate", "fgate", "C_in", "n_in", "m_in", "C_out", "n_out", "m_out",
+            "h_out", "den_out"]
+    st = lib.mlstm_recurrent_step(*[args[k] or None for k in ptrs], args["B"], args["NH"],
+                                  args["d"], args["dtype"], None)
     assert st == status

@@ -321,3 +321,99 @@ def test_tile_skipping_long_context_full_size():
     b = _staged(x, "mfma_all_tiles")
     for ta, tb in zip(a, b):
         assert torch.equal(ta, tb)
+
+
+# ---------------------------------------------------------------------------
+# recurrent step (generation): T steps from a fresh state against the oracle
+# ---------------------------------------------------------------------------
+
+def _run_steps(x, in_place=True):
+    q, k, v, ig, fg = _dev(x)
+    B, NH, T, d = q.shape
+    state = mlstm.recurrent_state(B, NH, d, "cuda")
+    hs, ms, dens = [], [], []
+    for t in range(T):
+        C, n, m = state
+        out = (C if in_place else torch.empty_like(C), torch.empty_like(n), torch.empty_like(m))
+        h, state, den = mlstm.recurrent_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(),
+                                             v[:, :, t].contiguous(), ig[:, :, t].contiguous(),
+                                             fg[:, :, t].contiguous(), state, out_state=out,
+                                             den=True)
+        hs.append(h)
+        ms.append(state[2].clone())
+        dens.append(den)
+    torch.cuda.synchronize()
+    H = torch.stack(hs, dim=2)
+    M = torch.stack(ms, dim=2)
+    N = torch.stack(dens, dim=2)
+    return _host(H), _host(M), _host(N), tuple(_host(s) for s in state)
+
+
+@pytest.mark.parametrize("s", [
+    spec(1, 2, 40, 64, "fp32"), spec(2, 1, 33, 128, "fp32"),
+    spec(1, 2, 40, 64), spec(1, 1, 30, 384), spec(1, 1, 20, 512), spec(1, 3, 25, 16),
+    spec(1, 2, 60, 64, "fp32", ig=("uniform", -20, 20), fg=("normal", 0, 4),
+         fgate_floor=(0.05, -30.0)),
+], ids=_id)
+def test_recurrent_steps_match_oracle(s):
+    x = W.make(s, seed=15)
+    h, m, den, (C, n, mT) = _run_steps(x)
+    hr, mr, denr, CT, nT = oracle.forward_recurrent_stabilized(
+        x["q"], x["k"], x["v"], x["igate"], x["fgate"])
+    tol = TOL_H["bf16"] if s["dtype"] == "bf16" else TOL_H["fp32"]
+    print(check(h, m, den, hr, mr, denr, tol))
+    # final states (float32 recurrences; states are not rounded to bf16)
+    assert head_normwise(C.reshape(C.shape[0], C.shape[1], -1),
+                         CT.reshape(CT.shape[0], CT.shape[1], -1)) <= 1e-4
+    assert head_normwise(n, nT) <= 1e-4
+    # the recurrent step and the parallel pass agree on h~, m and n
+    hp, mp, npar = oracle.forward_stabilized(x["q"], x["k"], x["v"], x["igate"], x["fgate"])
+    print(check(h, m, den, hp, mp, npar, tol))
+
+
+def test_recurrent_step_in_place_equals_out_of_place_bitwise():
+    x = W.make(spec(2, 2, 12, 128), seed=16)
+    a = _run_steps(x, in_place=True)
+    b = _run_steps(x, in_place=False)
+    for ta, tb in zip(a[:3], b[:3]):
+        assert np.array_equal(ta, tb)
+    for ta, tb in zip(a[3], b[3]):
+        assert np.array_equal(ta, tb)
+
+
+def test_recurrent_step_full_size_decode_shape():
+    """One step of the 125M-shaped layer (B=8, NH=4, d=384) from a random
+    state; sampled heads against the oracle step."""
+    rng = np.random.default_rng(17)
+    B, NH, d = 8, 4, 384
+    q, k, v = (W.round_bf16(rng.standard_normal((B, NH, d)).astype(np.float32)) for _ in range(3))
+    ig = rng.standard_normal((B, NH)).astype(np.float32)
+    fg = (3.0 + rng.standard_normal((B, NH))).astype(np.float32)
+    C0 = (0.1 * rng.standard_normal((B, NH, d, d))).astype(np.float32)
+    n0 = (0.1 * rng.standard_normal((B, NH, d))).astype(np.float32)
+    m0 = rng.standard_normal((B, NH)).astype(np.float32)
+    dev = lambda a, dt=torch.float32: torch.from_numpy(a).to("cuda").to(dt).contiguous()
+    state = (dev(C0), dev(n0), dev(m0))
+    h, (C1, n1, m1), den = mlstm.recurrent_step(dev(q, torch.bfloat16), dev(k, torch.bfloat16),
+                                                dev(v, torch.bfloat16), dev(ig), dev(fg), state,
+                                                den=True)
+    torch.cuda.synchronize()
+    h, C1, n1, m1, den = (_host(t) for t in (h, C1, n1, m1, den))
+    for bi, hi in [(0, 0), (3, 2), (7, 3)]:
+        hr, Cr, nr, mr, dr = oracle.recurrent_step_stabilized(
+            q[bi, hi], k[bi, hi], v[bi, hi], ig[bi, hi], fg[bi, hi], C0[bi, hi], n0[bi, hi],
+            float(m0[bi, hi]))
+        assert abs(m1[bi, hi] - mr) <= 1e-5 * max(abs(mr), 1.0)
+        assert abs(den[bi, hi] - dr) <= 1e-5 * dr
+        assert np.abs(h[bi, hi] - hr).max() <= 2e-2 * np.abs(hr).max()
+        assert np.abs(C1[bi, hi] - Cr).max() <= 1e-5 * np.abs(Cr).max()
+        assert np.abs(n1[bi, hi] - nr).max() <= 1e-5 * np.abs(nr).max()
+
+
+def test_recurrent_step_alias_rejected_on_gpu():
+    q = torch.zeros((1, 1, 64), dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros((1, 1), dtype=torch.float32, device="cuda")
+    state = mlstm.recurrent_state(1, 1, 64, "cuda")
+    with pytest.raises(mlstm.MlstmError) as e:
+        mlstm.recurrent_step(q, q, q, g, g, state, out_state=state)
+    assert e.value.status == -9
