@@ -29,6 +29,10 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
   parallel form's m and n, and exp(m_T) times the final states equals their
   definition as gate-weighted sums of v k^T and k (brute force on tiny
   inputs), also where exp(i~) overflows the unstabilized form.
+* ``backward_stabilized``  pinned: central finite differences of
+  ``forward_stabilized`` for every input (q, k, v, i~, f~), on inputs with
+  rows on both sides of the normalizer floor, and the derivative identity
+  d/dx log sigma(x) = sigma(-x) (Eq. 104).
 * ``output_gate``          pinned: sigma(0) = 1/2 and sigma(-x) = 1 - sigma(x)
   closed forms (Eq. 78).
 """
@@ -44,4 +48,5 @@ from .mlstm import (  # noqa: F401
     forward_recurrent_stabilized,
     forward_unstabilized,
     output_gate,
+    backward_stabilized,
 )

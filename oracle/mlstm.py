@@ -280,6 +280,61 @@ def forward_unstabilized(q, k, v, igate, fgate):
     return h
 
 
+def backward_stabilized(q, k, v, igate, fgate, dh):
+    """Gradients of the stabilized parallel forward pass (Eqs. 87-105) for
+    every head, float64, dense T x T per head.
+
+    Given dh = dL/dH~ ([B,NH,T,d]), returns (dq, dk, dv [B,NH,T,d],
+    digate, dfgate [B,NH,T]).  The forward quantities (D', C~', b, n, m) are
+    recomputed from the inputs exactly as in ``forward_stabilized``.  m is held
+    constant: its contributions cancel (H~ does not depend on the stabilizer).
+
+    Reading of Eq. 90: the page writes sign(n), but n = max(|b|, exp(-m)) is
+    positive; the derivative of |b| is sign(b), which is what is used here.
+    Eq. 102 is evaluated literally as the double sum over j < k <= i.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dh = np.asarray(dh, dtype=np.float64)
+    B, NH, T, d = q.shape
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    di = np.empty((B, NH, T))
+    df = np.empty((B, NH, T))
+    rs = 1.0 / math.sqrt(d)
+    for bi in range(B):
+        for hi in range(NH):
+            Dt = log_gate_matrix(fgate[bi, hi], igate[bi, hi])             # Eq. 79
+            m = Dt.max(axis=1)                                             # Eq. 80
+            Dp = np.exp(Dt - m[:, None])                                   # Eq. 81
+            S = (q[bi, hi] @ k[bi, hi].T) * rs
+            Ct = S * Dp                                                    # Eq. 82
+            b = Ct.sum(axis=1)                                             # Eq. 83
+            n = np.maximum(np.abs(b), np.exp(-m))                          # Eq. 84
+            Cn = Ct / n[:, None]                                           # Eq. 85
+            dC = dh[bi, hi] @ v[bi, hi].T                                  # Eq. 87 (dC, T x T)
+            dn = -((Ct * dC).sum(axis=1)) / n ** 2                         # Eqs. 88-89
+            db = np.sign(b) * dn * (np.abs(b) > np.exp(-m))                # Eq. 90 (sign(b))
+            dCt = dC / n[:, None] + db[:, None]                            # Eqs. 91-93
+            dDp = S * dCt                                                  # Eq. 94
+            dDt = Dp * dDp                                                 # Eq. 95
+            P = Dp * dCt
+            dq[bi, hi] = (P @ k[bi, hi]) * rs                              # Eq. 98
+            dk[bi, hi] = (P.T @ q[bi, hi]) * rs                            # Eq. 99
+            dv[bi, hi] = Cn.T @ dh[bi, hi]                                 # Eq. 100
+            # Eqs. 96-97: dFbar = dI = dD~ (zero above the diagonal, where
+            # D' = 0); Eq. 105: column sums; Eq. 102: double sum
+            di[bi, hi] = dDt.sum(axis=0)
+            dfbar = np.zeros(T)
+            for kk in range(T):
+                dfbar[kk] = dDt[kk:, :kk].sum()
+            fg = np.asarray(fgate[bi, hi], dtype=np.float64)
+            df[bi, hi] = _sigmoid(-fg) * dfbar                             # Eqs. 103-104
+    return dq, dk, dv, di, df
+
+
 def output_gate(h, ogate):
     """Eq. 78: H = sigma(O~) (.) H~, elementwise."""
     return _sigmoid(ogate) * np.asarray(h, dtype=np.float64)

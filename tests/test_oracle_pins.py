@@ -497,3 +497,66 @@ def test_recurrent_step_fresh_state_is_the_single_step_closed_form():
     assert m == 2.5
     assert np.allclose(h, s * v / max(abs(s), math.exp(-2.5)), rtol=1e-14)
     assert np.allclose(C, np.outer(v, k) / math.sqrt(d), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# backward pass (Eqs. 87-105) against finite differences of the forward pass
+# ---------------------------------------------------------------------------
+
+def _loss(q, k, v, ig, fg, dh):
+    h, _, _ = om.forward_stabilized(q, k, v, ig, fg)
+    return float((h * dh).sum())
+
+
+def _fd(f, x, eps=1e-6):
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        xp = x.copy(); xp[idx] += eps
+        xm = x.copy(); xm[idx] -= eps
+        g[idx] = (f(xp) - f(xm)) / (2 * eps)
+    return g
+
+
+@pytest.mark.parametrize("seed,ig_scale,fg_mu", [(0, 1.0, 2.0), (1, 3.0, 0.0), (2, 0.5, 4.0)])
+def test_backward_matches_finite_differences(seed, ig_scale, fg_mu):
+    rng = np.random.default_rng(seed)
+    B, NH, T, d = 1, 1, 9, 4
+    q, k, v = (rng.standard_normal((B, NH, T, d)) for _ in range(3))
+    ig = ig_scale * rng.standard_normal((B, NH, T))
+    fg = fg_mu + 2.0 * rng.standard_normal((B, NH, T))
+    dh = rng.standard_normal((B, NH, T, d))
+    # rows on both sides of the floor exp(-m) (Eq. 84)
+    _, m, n, b, _ = om.forward_stabilized(q, k, v, ig, fg, return_diag=True)
+    dq, dk, dv, di, df = om.backward_stabilized(q, k, v, ig, fg, dh)
+    L = lambda **kw: _loss(kw.get("q", q), kw.get("k", k), kw.get("v", v), kw.get("ig", ig),
+                           kw.get("fg", fg), dh)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("ig", ig, di), ("fg", fg, df)):
+        num = _fd(lambda y: L(**{name: y}), x)
+        assert np.allclose(g, num, rtol=1e-5, atol=1e-7), name
+
+
+def test_backward_floor_rows_and_sign_of_b():
+    """Inputs chosen so that b is negative on some rows above the floor and
+    some rows sit on the floor: only sign(b) (not sign(n) = 1) matches finite
+    differences of the input-gate gradient."""
+    rng = np.random.default_rng(7)
+    B, NH, T, d = 1, 1, 8, 3
+    q, k, v = (rng.standard_normal((B, NH, T, d)) for _ in range(3))
+    ig = 2.0 * rng.standard_normal((B, NH, T))
+    fg = 1.0 + rng.standard_normal((B, NH, T))
+    _, m, n, b, _ = om.forward_stabilized(q, k, v, ig, fg, return_diag=True)
+    assert (b < -np.exp(-m)).any() and (np.abs(b) < np.exp(-m)).any()
+    dh = rng.standard_normal((B, NH, T, d))
+    _, _, _, di, _ = om.backward_stabilized(q, k, v, ig, fg, dh)
+    num = _fd(lambda y: _loss(q, k, v, y, fg, dh), ig)
+    assert np.allclose(di, num, rtol=1e-5, atol=1e-7)
+
+
+def test_log_sigmoid_derivative_identity():
+    """Eq. 104: d/dx log sigma(x) = sigma(-x)."""
+    x = np.linspace(-30, 30, 61)
+    eps = 1e-6
+    num = (om.log_sigmoid(x + eps) - om.log_sigmoid(x - eps)) / (2 * eps)
+    assert np.allclose(num, 1.0 / (1.0 + np.exp(x)), rtol=1e-6, atol=1e-12)
