@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="xlstm125m_layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip timing the backward pass")
     p.add_argument("--no-long-context", action="store_true",
                    help="skip the tile-skipping comparison on the 16K stress workload")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
@@ -162,6 +164,35 @@ def recurrent_decode(torch, mlstm, dev, B, NH, d, reps=50):
             "state_MB": round(H * d * d * 4 / 1e6, 1)}
 
 
+def backward_timing(torch, mlstm, workloads, x, dev, reps=3):
+    """Time mlstm_parallel_bwd (float32 vector tiles) on the benchmarked layer."""
+    spec = x["spec"]
+    B, NH, T, d = spec["B"], spec["NH"], spec["T"], spec["d"]
+    dt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(dt).contiguous() for n in ("q", "k", "v"))
+    ig = torch.from_numpy(x["igate"]).to(dev).contiguous()
+    fg = torch.from_numpy(x["fgate"]).to(dev).contiguous()
+    h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg)
+    dh = torch.randn(q.shape, generator=torch.Generator().manual_seed(1)).to(dev).to(dt)
+    mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, dh)
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, dh)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    counted = 2.5 * workloads.counted_flops(B, NH, T, d)   # 5 causal contractions
+    executed = 3.5 * workloads.counted_flops(B, NH, T, d)  # 7: S and dh v^T recomputed twice
+    return {"ms_per_call": round(ms, 3), "counted_flops": counted,
+            "counted_TFLOP/s": round(counted / (ms * 1e-3) / 1e12, 2),
+            "executed_TFLOP/s": round(executed / (ms * 1e-3) / 1e12, 2),
+            "bound": "alu", "peak_fp32_vector_TFLOP/s": 157.3,
+            "frac": round(executed / (ms * 1e-3) / 1e12 / 157.3, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -239,6 +270,8 @@ def main():
     rec = [recurrent_decode(torch, mlstm, dev, B, NH, d),
            recurrent_decode(torch, mlstm, dev, 256, NH, d, reps=20)]
 
+    bwd = None if args.no_backward else backward_timing(torch, mlstm, workloads, x, dev)
+
     # correctness spot check of the timed output (not part of the timing)
     mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
     torch.cuda.synchronize()
@@ -275,6 +308,8 @@ def main():
     if skip_rec is not None:
         line["tile_skipping"] = skip_rec
     line["recurrent_step"] = rec
+    if bwd is not None:
+        line["backward"] = bwd
     if args.copy_calibration:
         # reads and writes exactly COPY_BYTES each per launch
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

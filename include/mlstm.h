@@ -173,6 +173,45 @@ int mlstm_causal_tiles(const void* q, const void* k, const void* v, const float*
                        int kernel, void* stream);
 
 /*
+ * mlstm_parallel_fwd_train -- mlstm_parallel_fwd_stream that also stores the
+ * row sums b = C~' 1 (Eq. 83), which the backward pass needs (Eq. 90).
+ *   b_out  out  [B][NH][T] float32 (required, 16-byte aligned)
+ * Other arguments, layouts and errors as for mlstm_parallel_fwd_stream.
+ */
+int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v,
+                             const float* igate, const float* fgate,
+                             void* h_out, float* m_out, float* n_out, float* b_out,
+                             int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
+                             void* stream);
+
+/*
+ * mlstm_parallel_bwd -- gradients of the stabilized parallel forward pass
+ * ("Parallel mLSTM Backward Pass", Eqs. 87-105) with respect to q, k, v and
+ * the gate pre-activations, given dh = dL/dH~.
+ *   q, k, v, igate, fgate   in: the forward inputs
+ *   h, m, n, b              in: the forward outputs of mlstm_parallel_fwd_train
+ *                           (h~ before any output gate, [B][NH][T][d] dtype;
+ *                           m, n, b [B][NH][T] float32)
+ *   dh                      in  [B][NH][T][d], dtype
+ *   dq, dk, dv              out [B][NH][T][d], dtype (float32 accumulation)
+ *   digate, dfgate          out [B][NH][T] float32
+ * m is held constant (its contributions cancel, as the pages note).  Eq. 90
+ * is applied with the derivative of |b|, sign(b): the printed sign(n) is 1
+ * for every row, since n > 0.  d(log sigma(x))/dx = sigma(-x) (Eq. 104).
+ * dL/dn uses sum_j C~'_ij v_j = n_i h~_i, so for bf16 it carries the
+ * rounding of the stored h~.  Arithmetic is float32 on the vector ALUs
+ * (tiles of 16 x 16); the library allocates a stream-ordered workspace.
+ * Pointers 16-byte aligned; no output may alias an input.  Errors as for
+ * mlstm_parallel_fwd.
+ */
+int mlstm_parallel_bwd(const void* q, const void* k, const void* v,
+                       const float* igate, const float* fgate,
+                       const void* h, const float* m, const float* n, const float* b,
+                       const void* dh, void* dq, void* dk, void* dv,
+                       float* digate, float* dfgate,
+                       int64_t B, int64_t NH, int64_t T, int64_t d, int dtype, void* stream);
+
+/*
  * mlstm_recurrent_step -- one step of the recurrent mLSTM (the generation
  * form that the parallel pass reformulates; its equations are those the
  * recurrent backward pass of appendix A.3 differentiates, Eqs. 59-70), with

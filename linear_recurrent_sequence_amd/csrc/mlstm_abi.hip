@@ -176,6 +176,61 @@ int mlstm_parallel_fwd(const void* q, const void* k, const void* v, const float*
                                    dtype, nullptr);
 }
 
+int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v, const float* igate,
+                             const float* fgate, void* h_out, float* m_out, float* n_out,
+                             float* b_out, int64_t B, int64_t NH, int64_t T, int64_t d,
+                             int dtype, void* stream) {
+  int st = check_forward_args(q, k, v, igate, fgate, h_out, m_out, n_out, B, NH, T, d, dtype);
+  if (st != MLSTM_OK) return st;
+  if (!b_out) return MLSTM_ERR_NULL;
+  if (!aligned16(b_out)) return MLSTM_ERR_ALIGN;
+  mlstm::Epilogue ep;
+  ep.b = b_out;
+  return forward(q, k, v, igate, fgate, ep, h_out, m_out, n_out, B, NH, T, d, dtype,
+                 static_cast<hipStream_t>(stream));
+}
+
+int mlstm_parallel_bwd(const void* q, const void* k, const void* v, const float* igate,
+                       const float* fgate, const void* h, const float* m, const float* n,
+                       const float* b, const void* dh, void* dq, void* dk, void* dv,
+                       float* digate, float* dfgate, int64_t B, int64_t NH, int64_t T,
+                       int64_t d, int dtype, void* stream) {
+  if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
+  int st = check_shape(B, NH, T, d);
+  if (st != MLSTM_OK) return st;
+  const void* ins[] = {q, k, v, igate, fgate, h, m, n, b, dh};
+  const void* outs[] = {dq, dk, dv, digate, dfgate};
+  for (const void* p : ins)
+    if (!p) return MLSTM_ERR_NULL;
+  for (const void* p : outs)
+    if (!p) return MLSTM_ERR_NULL;
+  for (const void* p : ins)
+    if (!aligned16(p)) return MLSTM_ERR_ALIGN;
+  for (const void* p : outs)
+    if (!aligned16(p)) return MLSTM_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t H = B * NH;
+  const size_t wsb = mlstm::workspace_bytes(H, T);
+  const size_t mb = mlstm::align256(size_t(H) * size_t(T) * sizeof(float));
+  const size_t scb = mlstm::backward_scratch_bytes(H, T);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, wsb + mb + scb, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return MLSTM_ERR_HIP;
+  }
+  const Workspace w = mlstm::carve(ws, H, T);
+  float* m_scan = reinterpret_cast<float*>(static_cast<char*>(ws) + wsb);
+  void* scratch = static_cast<char*>(ws) + wsb + mb;
+  // the exponent terms of D' are recomputed from the gates (the scan's m is
+  // bitwise the forward's)
+  st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_scan, w, H, T, d, s));
+  if (st == MLSTM_OK)
+    st = hip_status(mlstm::launch_backward(q, k, v, fgate, h, m, n, b, dh, w, scratch, dq, dk,
+                                           dv, digate, dfgate, H, T, d, dtype == MLSTM_BF16, s));
+  if (hipFreeAsync(ws, s) != hipSuccess && st == MLSTM_OK) st = MLSTM_ERR_HIP;
+  return st;
+}
+
 int mlstm_recurrent_step(const void* q, const void* k, const void* v, const float* igate,
                          const float* fgate, const float* C_in, const float* n_in,
                          const float* m_in, float* C_out, float* n_out, float* m_out,

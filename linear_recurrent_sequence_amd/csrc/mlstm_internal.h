@@ -80,9 +80,12 @@ inline Workspace carve(void* base, int64_t H, int64_t T) {
 // (Eq. 78), applied to the float32 h~ before it is rounded and stored.
 // ogate = NULL: h_out receives h~.  htilde != NULL: h~ is stored there too.
 // Both are [H][T][d] in the element type of q.
+// b != NULL: the row sums b (Eq. 83), float32 [H][T], are stored too (the
+// backward pass needs their sign).
 struct Epilogue {
   const void* ogate = nullptr;
   void* htilde = nullptr;
+  float* b = nullptr;
 };
 
 // Stage 1: gate scan (one workgroup per head).
@@ -104,6 +107,16 @@ hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, cons
                                const Workspace& ws, void* h_out, float* n_out,
                                const Epilogue& ep, int64_t H, int64_t T, int64_t d,
                                bool is_bf16, hipStream_t stream);
+
+// Backward pass (Eqs. 87-105), float32 vector tiles.  `ws` holds the gate
+// scan's terms for the same inputs; `scratch` holds backward_scratch_bytes(H,
+// T) bytes (256-byte aligned) of per-row temporaries.
+size_t backward_scratch_bytes(int64_t H, int64_t T);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const float* fgate,
+                           const void* h, const float* m, const float* n, const float* b,
+                           const void* dh, const Workspace& ws, void* scratch, void* dq, void* dk,
+                           void* dv, float* digate, float* dfgate, int64_t H, int64_t T,
+                           int64_t d, bool is_bf16, hipStream_t stream);
 
 // Recurrent step (generation), stabilized states in float32: C [H][d][d],
 // n [H][d], m [H].  C_out may equal C_in; n_out / m_out must not overlap

@@ -107,7 +107,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const float* __restrict__ m_in, const double* __restrict__ anchor,
     const float* __restrict__ rowt, const float* __restrict__ colt, u16* __restrict__ h_out,
     const float* __restrict__ rowb, const float* __restrict__ keyb, float* __restrict__ n_out,
-    const u16* __restrict__ ogate, u16* __restrict__ htilde, int64_t T, int d, int64_t Tp,
+    const u16* __restrict__ ogate, u16* __restrict__ htilde, float* __restrict__ b_out,
+    int64_t T, int d, int64_t Tp,
     int64_t nblk, int64_t row_tiles, int64_t H, int skip) {
   using C = Cfg<DP>;
   // two distinct buffers, so the loads into one never alias reads of the other
@@ -341,6 +342,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   if (qi < T) {
     const float nn = fmaxf(fabsf(bsum), expf(-m_in[head * T + qi]));
     if (g == 0) n_out[head * T + qi] = nn;
+    if (g == 0 && b_out) b_out[head * T + qi] = bsum;
     const float inv = 1.0f / nn;
     const int64_t row = hoff + qi * d;
 #pragma unroll
@@ -381,8 +383,8 @@ hipError_t launch_dp(const void* q, const void* k, const void* v, const float* m
                      stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), m, ws.anchor, ws.rowt, ws.colt,
                      static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
-                     static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), T, int(d),
-                     ws.Tp, ws.nblk, row_tiles, H, int(skip));
+                     static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), ep.b, T,
+                     int(d), ws.Tp, ws.nblk, row_tiles, H, int(skip));
   return hipGetLastError();
 }
 

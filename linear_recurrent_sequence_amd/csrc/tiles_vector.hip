@@ -29,8 +29,8 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ m_in, const double* __restrict__ anchor,
     const float* __restrict__ rowt, const float* __restrict__ colt, Tin* __restrict__ h_out,
-    float* __restrict__ n_out, const Tin* __restrict__ ogate, Tin* __restrict__ htilde, int64_t T,
-    int d, int64_t Tp, int64_t nblk, int64_t row_tiles) {
+    float* __restrict__ n_out, const Tin* __restrict__ ogate, Tin* __restrict__ htilde,
+    float* __restrict__ b_out, int64_t T, int d, int64_t Tp, int64_t nblk, int64_t row_tiles) {
   __shared__ float Qs[kVT][kVPad];
   __shared__ float Ks[kVT][kVPad];
   __shared__ float Vs[kVT][kVMaxD];
@@ -94,6 +94,7 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
   if (qi < T) {
     const float nn = fmaxf(fabsf(bsum), expf(-m_in[head * T + qi]));  // Eq. 84
     if (cl == 0) n_out[head * T + qi] = nn;
+    if (cl == 0 && b_out) b_out[head * T + qi] = bsum;
 #pragma unroll
     for (int u = 0; u < kVMaxD / kVT; ++u) {
       const int c = cl + kVT * u;
@@ -122,13 +123,14 @@ hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, cons
                        static_cast<const B16*>(q), static_cast<const B16*>(k),
                        static_cast<const B16*>(v), m, ws.anchor, ws.rowt, ws.colt,
                        static_cast<B16*>(h_out), n_out, static_cast<const B16*>(ep.ogate),
-                       static_cast<B16*>(ep.htilde), T, int(d), ws.Tp, ws.nblk, row_tiles);
+                       static_cast<B16*>(ep.htilde), ep.b, T, int(d), ws.Tp, ws.nblk, row_tiles);
   } else {
     hipLaunchKernelGGL(tiles_vector_kernel<float>, grid, dim3(256), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), m, ws.anchor, ws.rowt, ws.colt,
                        static_cast<float*>(h_out), n_out, static_cast<const float*>(ep.ogate),
-                       static_cast<float*>(ep.htilde), T, int(d), ws.Tp, ws.nblk, row_tiles);
+                       static_cast<float*>(ep.htilde), ep.b, T, int(d), ws.Tp, ws.nblk,
+                       row_tiles);
   }
   return hipGetLastError();
 }

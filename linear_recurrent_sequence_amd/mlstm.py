@@ -52,6 +52,10 @@ def load_library():
     lib.mlstm_parallel_fwd_gated.restype = i32
     lib.mlstm_recurrent_step.argtypes = [vp] * 13 + [i64] * 3 + [i32, vp]
     lib.mlstm_recurrent_step.restype = i32
+    lib.mlstm_parallel_fwd_train.argtypes = [vp] * 9 + [i64] * 4 + [i32, vp]
+    lib.mlstm_parallel_fwd_train.restype = i32
+    lib.mlstm_parallel_bwd.argtypes = [vp] * 15 + [i64] * 4 + [i32, vp]
+    lib.mlstm_parallel_bwd.restype = i32
     lib.mlstm_workspace_bytes.argtypes = [i64] * 3
     lib.mlstm_workspace_bytes.restype = f
     lib.mlstm_gate_scan.argtypes = [vp] * 4 + [f] + [i64] * 4 + [vp]
@@ -254,3 +258,43 @@ def recurrent_step(q, k, v, igate, fgate, state, out_state=None, den=False):
     if st != 0:
         raise MlstmError(st, "mlstm_recurrent_step")
     return (h, out_state, dn) if den else (h, out_state)
+
+
+def parallel_fwd_train(q, k, v, igate, fgate):
+    """Forward pass that also returns the row sums b -> (h, m, n, b)."""
+    lib = load_library()
+    B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
+    h = torch.empty_like(q)
+    m, n, b = (torch.empty((B, NH, T), dtype=torch.float32, device=q.device) for _ in range(3))
+    with torch.cuda.device(q.device):
+        st = lib.mlstm_parallel_fwd_train(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
+            h.data_ptr(), m.data_ptr(), n.data_ptr(), b.data_ptr(), B, NH, T, d, _dtype_code(q),
+            _stream_ptr(q.device))
+    if st != 0:
+        raise MlstmError(st, "mlstm_parallel_fwd_train")
+    return h, m, n, b
+
+
+def parallel_bwd(q, k, v, igate, fgate, h, m, n, b, dh):
+    """Gradients (dq, dk, dv, digate, dfgate) of the forward pass given dh = dL/dh~."""
+    lib = load_library()
+    B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
+    for name, t in (("h", h), ("dh", dh)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must match q in shape and dtype, contiguous on the GPU")
+    for name, t in (("m", m), ("n", n), ("b", b)):
+        if tuple(t.shape) != (B, NH, T) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32 [B, NH, T]")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dig, dfg = torch.empty_like(igate), torch.empty_like(fgate)
+    with torch.cuda.device(q.device):
+        st = lib.mlstm_parallel_bwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
+            h.data_ptr(), m.data_ptr(), n.data_ptr(), b.data_ptr(), dh.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dig.data_ptr(), dfg.data_ptr(),
+            B, NH, T, d, _dtype_code(q), _stream_ptr(q.device))
+    if st != 0:
+        raise MlstmError(st, "mlstm_parallel_bwd")
+    return dq, dk, dv, dig, dfg
+
