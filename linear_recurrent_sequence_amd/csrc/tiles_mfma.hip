@@ -32,26 +32,16 @@
 // terms of the gate scan; the anchor difference is formed in float64 once per
 // (wave, tile), the key-tile anchor travelling with the tile into LDS.
 #include "mlstm_internal.h"
+#include "tile_common.h"
 
 namespace mlstm {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned short u16;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+using namespace tilecommon;
 
-constexpr int kBM = 128;    // query rows per workgroup
-constexpr int kBN = 32;     // keys per tile
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPf = 3;      // LDS fragment prefetch distance (MFMA steps)
-constexpr int kRsrcFlags = 0x00020000;  // buffer resource word 3: 32-bit data format
-constexpr unsigned kOutOfRange = 0x40000000u;  // a buffer offset that reads zeros
 
 template <int DP>
 struct Cfg {
@@ -66,39 +56,6 @@ struct Cfg {
   static constexpr int KB_OFF = A_OFF + 8;       // max of c_j over the key tile
   static constexpr int BUF = (KB_OFF + 4 + 15) / 16 * 16;
 };
-
-// Heaviest row tiles first (a row tile I costs ~I + 1 key tiles), and when the
-// head count allows, every row tile of a head on the same XCD (workgroups are
-// dealt to the 8 XCDs round-robin), so a head's K and V stay in one L2.
-__device__ inline void map_tile(int64_t wg, int64_t row_tiles, int64_t H, int64_t& I,
-                                int64_t& head) {
-  if ((H & 7) == 0) {
-    const int64_t x = wg & 7, s = wg >> 3, hpx = H >> 3;
-    head = x + 8 * (s % hpx);
-    I = row_tiles - 1 - s / hpx;
-  } else {
-    I = row_tiles - 1 - wg / H;
-    head = wg % H;
-  }
-}
-
-// 16 bytes per lane, global -> LDS at (wave-uniform) dst + 16 * lane, through
-// a buffer resource: offsets at or past `num_records` bytes read as zeros.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t num_records) {
-  const int n = num_records > 0x7FFFFFFF ? 0x7FFFFFFF : int(num_records);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcFlags);
-}
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, char* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voffset, 0, 0, 0);
-}
-// 4 bytes per lane, to dst + 4 * lane
-__device__ inline void dma4(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, char* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, voffset, 0, 0, 0);
-}
-
-__device__ inline i16x4 tr_read(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-}
 
 template <int DP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
