@@ -33,12 +33,18 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
   ``forward_stabilized`` for every input (q, k, v, i~, f~), on inputs with
   rows on both sides of the normalizer floor, and the derivative identity
   d/dx log sigma(x) = sigma(-x) (Eq. 104).
+* every function above takes ``forget="sigmoid"`` (default) or ``"exp"``:
+  the exponential forget gate is pinned the same way (all forms agree, the
+  closed form of F, finite differences of the backward).
 * ``output_gate``          pinned: sigma(0) = 1/2 and sigma(-x) = 1 - sigma(x)
   closed forms (Eq. 78).
 """
 
 from .mlstm import (  # noqa: F401
     log_sigmoid,
+    forget_gate,
+    log_forget,
+    FORGET_ACTIVATIONS,
     gate_matrices,
     log_gate_matrix,
     forward_stabilized,

@@ -49,7 +49,39 @@ def _sigmoid(x):
     return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
 
 
-def gate_matrices(fgate, igate):
+FORGET_ACTIVATIONS = ("sigmoid", "exp")
+
+
+def forget_gate(fgate, forget="sigmoid"):
+    """The forget gate f_t from its pre-activation: sigma(f~) (Eq. 71's
+    activation, the one the parallel form fixes) or exp(f~) (the other
+    activation the pages allow for the forget gate)."""
+    if forget == "sigmoid":
+        return _sigmoid(fgate)
+    if forget == "exp":
+        return np.exp(np.asarray(fgate, dtype=np.float64))
+    raise ValueError(f"unknown forget activation {forget!r}")
+
+
+def log_forget(fgate, forget="sigmoid"):
+    """f-bar = log f_t (Eq. 101): log sigma(f~), or f~ itself for exp."""
+    if forget == "sigmoid":
+        return log_sigmoid(fgate)
+    if forget == "exp":
+        return np.asarray(fgate, dtype=np.float64)
+    raise ValueError(f"unknown forget activation {forget!r}")
+
+
+def dlog_forget(fgate, forget="sigmoid"):
+    """d f-bar / d f~: sigma(-f~) (Eq. 104) for sigmoid, 1 for exp."""
+    if forget == "sigmoid":
+        return _sigmoid(-np.asarray(fgate, dtype=np.float64))
+    if forget == "exp":
+        return np.ones_like(np.asarray(fgate, dtype=np.float64))
+    raise ValueError(f"unknown forget activation {forget!r}")
+
+
+def gate_matrices(fgate, igate, forget="sigmoid"):
     """F (Eq. 71) and I~ (Eq. 72) for ONE head, by their definitions.
 
     F_ij = 0 for i < j, 1 for i = j, prod_{k=j+1..i} sigma(f~_k) for i > j:
@@ -60,7 +92,7 @@ def gate_matrices(fgate, igate):
     f = np.asarray(fgate, dtype=np.float64).reshape(-1)
     ig = np.asarray(igate, dtype=np.float64).reshape(-1)
     T = f.shape[0]
-    sig = _sigmoid(f)
+    sig = forget_gate(f, forget)
     F = np.zeros((T, T), dtype=np.float64)
     for j in range(T):
         F[j, j] = 1.0
@@ -74,14 +106,14 @@ def gate_matrices(fgate, igate):
     return F, It
 
 
-def log_gate_matrix(fgate, igate, rows=None, dtype=np.float64):
+def log_gate_matrix(fgate, igate, rows=None, dtype=np.float64, forget="sigmoid"):
     """D~ = log F + I~ (Eqs. 74, 79, with log F from Eq. 101) for ONE head.
 
     log F_ij is the sum of f-bar_k over k = j+1..i, written as the difference
     of the inclusive prefix sums cs_i - cs_j of f-bar; -inf above the diagonal.
     ``rows`` selects row indices (default: all).  Returns [len(rows), T].
     """
-    fbar = log_sigmoid(fgate).astype(dtype)
+    fbar = log_forget(fgate, forget).astype(dtype)
     ig = np.asarray(igate, dtype=np.float64).reshape(-1).astype(dtype)
     T = fbar.shape[0]
     cs = np.cumsum(fbar, dtype=dtype)
@@ -93,12 +125,12 @@ def log_gate_matrix(fgate, igate, rows=None, dtype=np.float64):
     return Dt
 
 
-def _rows_one_head(q, k, v, ig, fg, rows, dtype):
+def _rows_one_head(q, k, v, ig, fg, rows, dtype, forget="sigmoid"):
     """Eqs. 79-86 for the listed rows of one head.  Rows are independent."""
     T, d = q.shape
     rows = np.asarray(rows)
     ncol = int(rows.max()) + 1  # columns j > every listed row are exactly 0 (Eq. 71)
-    Dt = log_gate_matrix(fg[:ncol], ig[:ncol], rows=rows, dtype=dtype)  # Eq. 79
+    Dt = log_gate_matrix(fg[:ncol], ig[:ncol], rows=rows, dtype=dtype, forget=forget)  # Eq. 79
     m = Dt.max(axis=1)  # Eq. 80, row-wise maximum
     Dp = np.exp(Dt - m[:, None])  # Eq. 81, exp(-inf) = 0 above the diagonal
     S = (q[rows].astype(dtype) @ k[:ncol].astype(dtype).T) / dtype(math.sqrt(d))
@@ -111,7 +143,7 @@ def _rows_one_head(q, k, v, ig, fg, rows, dtype):
 
 
 def forward_stabilized(q, k, v, igate, fgate, block_rows=256, dtype=np.float64,
-                       return_diag=False):
+                       return_diag=False, forget="sigmoid"):
     """Stabilized parallel forward pass, Eqs. 79-86, densely, per head.
 
     Rows are processed in blocks of ``block_rows`` only to bound memory; each
@@ -134,7 +166,7 @@ def forward_stabilized(q, k, v, igate, fgate, block_rows=256, dtype=np.float64,
             fg = np.asarray(fgate[bi, hi], dtype=np.float64)
             for r0 in range(0, T, block_rows):
                 rows = np.arange(r0, min(T, r0 + block_rows))
-                hh, mm, nn, bb, rr = _rows_one_head(qh, kh, vh, ig, fg, rows, dtype)
+                hh, mm, nn, bb, rr = _rows_one_head(qh, kh, vh, ig, fg, rows, dtype, forget)
                 h[bi, hi, rows] = hh
                 m[bi, hi, rows] = mm
                 n[bi, hi, rows] = nn
@@ -145,7 +177,7 @@ def forward_stabilized(q, k, v, igate, fgate, block_rows=256, dtype=np.float64,
     return h, m, n
 
 
-def forward_rows(q, k, v, igate, fgate, bi, hi, rows, dtype=np.float64):
+def forward_rows(q, k, v, igate, fgate, bi, hi, rows, dtype=np.float64, forget="sigmoid"):
     """Eqs. 79-86 for selected rows ``rows`` of head (bi, hi) only.
 
     Costs O(len(rows) * max(rows) * d): used to check single outputs of very
@@ -154,10 +186,10 @@ def forward_rows(q, k, v, igate, fgate, bi, hi, rows, dtype=np.float64):
     qh, kh, vh = (np.asarray(a[bi, hi], dtype=np.float64) for a in (q, k, v))
     ig = np.asarray(igate[bi, hi], dtype=np.float64)
     fg = np.asarray(fgate[bi, hi], dtype=np.float64)
-    return _rows_one_head(qh, kh, vh, ig, fg, np.asarray(rows), dtype)
+    return _rows_one_head(qh, kh, vh, ig, fg, np.asarray(rows), dtype, forget)
 
 
-def forward_recurrent(q, k, v, igate, fgate):
+def forward_recurrent(q, k, v, igate, fgate, forget="sigmoid"):
     """The recurrent mLSTM, step by step, unstabilized, in float64.
 
     C_0 = 0 (d x d), n_0 = 0 (d); for t = 1..T: f_t = sigma(f~_t),
@@ -178,7 +210,7 @@ def forward_recurrent(q, k, v, igate, fgate):
             C = np.zeros((d, d))
             nvec = np.zeros(d)
             for t in range(T):
-                f_t = float(_sigmoid(fgate[bi, hi, t]))
+                f_t = float(forget_gate(fgate[bi, hi, t], forget))
                 i_t = math.exp(float(igate[bi, hi, t]))
                 kt = k[bi, hi, t] * scale
                 vt = v[bi, hi, t]
@@ -191,7 +223,7 @@ def forward_recurrent(q, k, v, igate, fgate):
     return h, nq
 
 
-def recurrent_step_stabilized(q_t, k_t, v_t, ig_t, fg_t, C, nvec, m):
+def recurrent_step_stabilized(q_t, k_t, v_t, ig_t, fg_t, C, nvec, m, forget="sigmoid"):
     """One step of the recurrent mLSTM for ONE head with stabilized states,
     float64.
 
@@ -216,7 +248,7 @@ def recurrent_step_stabilized(q_t, k_t, v_t, ig_t, fg_t, C, nvec, m):
     k_t = np.asarray(k_t, dtype=np.float64)
     v_t = np.asarray(v_t, dtype=np.float64)
     d = q_t.shape[0]
-    fbar = float(log_sigmoid(fg_t))
+    fbar = float(log_forget(fg_t, forget))
     ig = float(ig_t)
     m_new = max(fbar + m, ig)
     f_p = math.exp(fbar + m - m_new) if m != -math.inf else 0.0
@@ -229,7 +261,7 @@ def recurrent_step_stabilized(q_t, k_t, v_t, ig_t, fg_t, C, nvec, m):
     return h, C_new, n_new, m_new, den
 
 
-def forward_recurrent_stabilized(q, k, v, igate, fgate):
+def forward_recurrent_stabilized(q, k, v, igate, fgate, forget="sigmoid"):
     """``recurrent_step_stabilized`` from a fresh state (C = 0, n = 0,
     m = -inf) over every position of every head.
 
@@ -251,13 +283,13 @@ def forward_recurrent_stabilized(q, k, v, igate, fgate):
             for t in range(T):
                 h[bi, hi, t], C, nvec, m, den[bi, hi, t] = recurrent_step_stabilized(
                     q[bi, hi, t], k[bi, hi, t], v[bi, hi, t], igate[bi, hi, t], fgate[bi, hi, t],
-                    C, nvec, m)
+                    C, nvec, m, forget)
                 mm[bi, hi, t] = m
             CT[bi, hi], nT[bi, hi] = C, nvec
     return h, mm, den, CT, nT
 
 
-def forward_unstabilized(q, k, v, igate, fgate):
+def forward_unstabilized(q, k, v, igate, fgate, forget="sigmoid"):
     """Unstabilized parallel form, Eqs. 71-73 and 76, by brute force.
 
     D = F (.) exp(I~) with F built from explicit products (``gate_matrices``);
@@ -272,7 +304,7 @@ def forward_unstabilized(q, k, v, igate, fgate):
     h = np.empty((B, NH, T, d))
     for bi in range(B):
         for hi in range(NH):
-            F, It = gate_matrices(fgate[bi, hi], igate[bi, hi])
+            F, It = gate_matrices(fgate[bi, hi], igate[bi, hi], forget)
             D = F * np.exp(It)  # Eq. 73
             Ct = (q[bi, hi] @ k[bi, hi].T) / math.sqrt(d) * D
             den = np.maximum(np.abs(Ct.sum(axis=1)), 1.0)
@@ -280,7 +312,7 @@ def forward_unstabilized(q, k, v, igate, fgate):
     return h
 
 
-def backward_stabilized(q, k, v, igate, fgate, dh):
+def backward_stabilized(q, k, v, igate, fgate, dh, forget="sigmoid"):
     """Gradients of the stabilized parallel forward pass (Eqs. 87-105) for
     every head, float64, dense T x T per head.
 
@@ -306,7 +338,7 @@ def backward_stabilized(q, k, v, igate, fgate, dh):
     rs = 1.0 / math.sqrt(d)
     for bi in range(B):
         for hi in range(NH):
-            Dt = log_gate_matrix(fgate[bi, hi], igate[bi, hi])             # Eq. 79
+            Dt = log_gate_matrix(fgate[bi, hi], igate[bi, hi], forget=forget)  # Eq. 79
             m = Dt.max(axis=1)                                             # Eq. 80
             Dp = np.exp(Dt - m[:, None])                                   # Eq. 81
             S = (q[bi, hi] @ k[bi, hi].T) * rs
@@ -331,7 +363,7 @@ def backward_stabilized(q, k, v, igate, fgate, dh):
             for kk in range(T):
                 dfbar[kk] = dDt[kk:, :kk].sum()
             fg = np.asarray(fgate[bi, hi], dtype=np.float64)
-            df[bi, hi] = _sigmoid(-fg) * dfbar                             # Eqs. 103-104
+            df[bi, hi] = dlog_forget(fg, forget) * dfbar                   # Eqs. 103-104
     return dq, dk, dv, di, df
 
 

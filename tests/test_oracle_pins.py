@@ -385,7 +385,7 @@ MUTANTS = {
 
 
 def _mutant_rows(kind):
-    def rows(q, k, v, ig, fg, rows, dtype):
+    def rows(q, k, v, ig, fg, rows, dtype, forget="sigmoid"):
         T, d = q.shape
         rows = np.asarray(rows)
         ncol = int(rows.max()) + 1
@@ -406,7 +406,7 @@ def _mutant_rows(kind):
     return rows
 
 
-def _mutant_lgm(fgate, igate, rows=None, dtype=np.float64):
+def _mutant_lgm(fgate, igate, rows=None, dtype=np.float64, forget="sigmoid"):
     fbar = om.log_sigmoid(fgate)
     ig = np.asarray(igate, float).reshape(-1)
     T = fbar.shape[0]
@@ -560,3 +560,57 @@ def test_log_sigmoid_derivative_identity():
     eps = 1e-6
     num = (om.log_sigmoid(x + eps) - om.log_sigmoid(x - eps)) / (2 * eps)
     assert np.allclose(num, 1.0 / (1.0 + np.exp(x)), rtol=1e-6, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# exponential forget gate: f_t = exp(f~_t), f-bar = f~
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,fmu", [(0, -0.5), (1, 0.3)])
+def test_exp_forget_gate_forms_agree(seed, fmu):
+    """Parallel stabilized = recurrent = unstabilized (explicit products of
+    exp(f~)) = stabilized recurrent step, for f_t = exp(f~_t), which may
+    exceed 1."""
+    rng = np.random.default_rng(seed)
+    B, NH, T, d = 1, 2, 17, 6
+    q, k, v = (rng.standard_normal((B, NH, T, d)) for _ in range(3))
+    ig = rng.standard_normal((B, NH, T))
+    fg = fmu + 0.5 * rng.standard_normal((B, NH, T))
+    hp, mp, npar = om.forward_stabilized(q, k, v, ig, fg, forget="exp")
+    hr, _ = om.forward_recurrent(q, k, v, ig, fg, forget="exp")
+    hu = om.forward_unstabilized(q, k, v, ig, fg, forget="exp")
+    hs, ms, dens, _, _ = om.forward_recurrent_stabilized(q, k, v, ig, fg, forget="exp")
+    assert np.allclose(hp, hr, rtol=1e-11, atol=1e-12)
+    assert np.allclose(hp, hu, rtol=1e-11, atol=1e-12)
+    assert np.allclose(hp, hs, rtol=1e-11, atol=1e-12)
+    assert np.allclose(mp, ms, rtol=1e-13, atol=1e-13)
+    assert np.allclose(npar, dens, rtol=1e-11)
+    # and it is a different function from the sigmoid gate
+    assert not np.allclose(hp, om.forward_stabilized(q, k, v, ig, fg)[0], rtol=1e-3)
+
+
+def test_exp_forget_gate_matrix_closed_form():
+    rng = np.random.default_rng(2)
+    fg = rng.standard_normal(9)
+    F, _ = om.gate_matrices(fg, np.zeros(9), forget="exp")
+    for i in range(9):
+        for j in range(9):
+            want = 0.0 if i < j else math.exp(fg[j + 1:i + 1].sum())
+            assert F[i, j] == pytest.approx(want, rel=1e-13, abs=0)
+
+
+def test_exp_forget_gate_backward_finite_differences():
+    rng = np.random.default_rng(3)
+    B, NH, T, d = 1, 1, 8, 3
+    q, k, v = (rng.standard_normal((B, NH, T, d)) for _ in range(3))
+    ig = rng.standard_normal((B, NH, T))
+    fg = -0.3 + 0.6 * rng.standard_normal((B, NH, T))
+    dh = rng.standard_normal((B, NH, T, d))
+    _, _, _, di, df = om.backward_stabilized(q, k, v, ig, fg, dh, forget="exp")
+
+    def L(ig_, fg_):
+        h, _, _ = om.forward_stabilized(q, k, v, ig_, fg_, forget="exp")
+        return float((h * dh).sum())
+    assert np.allclose(di, _fd(lambda y: L(y, fg), ig), rtol=1e-5, atol=1e-7)
+    assert np.allclose(df, _fd(lambda y: L(ig, y), fg), rtol=1e-5, atol=1e-7)
+
