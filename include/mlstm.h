@@ -89,8 +89,21 @@ enum {
   MLSTM_ERR_HIP = -6,         /* a HIP allocation or launch failed */
   MLSTM_ERR_WORKSPACE = -7,   /* caller workspace smaller than mlstm_workspace_bytes */
   MLSTM_ERR_KERNEL = -8,      /* unknown kernel selector, or an MFMA selector for fp32 */
-  MLSTM_ERR_ALIAS = -9        /* an output overlaps an input it must not alias */
+  MLSTM_ERR_ALIAS = -9,       /* an output overlaps an input it must not alias */
+  MLSTM_ERR_ACTIVATION = -10  /* unknown forget-gate activation */
 };
+
+/*
+ * Forget-gate activation (the `forget_activation` argument of
+ * mlstm_gate_scan, mlstm_parallel_fwd_train, mlstm_parallel_bwd and
+ * mlstm_recurrent_step).  The mLSTM forward equations (Eq. 71) allow the
+ * forget gate to be either sigma(f~) or exp(f~); every formula of the
+ * parallel and recurrent forms uses it only through its logarithm
+ * fbar = log f, which is log sigma(f~) or f~ itself.  With MLSTM_FORGET_EXP
+ * the caller keeps f~ <= 0 if it wants f <= 1; nothing here requires it.
+ * mlstm_parallel_fwd, _stream and _gated use MLSTM_FORGET_SIGMOID.
+ */
+enum { MLSTM_FORGET_SIGMOID = 0, MLSTM_FORGET_EXP = 1 };
 
 /*
  * mlstm_parallel_fwd -- the whole forward pass (Eqs. 79-86) for B x NH heads.
@@ -148,7 +161,8 @@ size_t mlstm_workspace_bytes(int64_t B, int64_t NH, int64_t T);
 
 /*
  * mlstm_gate_scan -- stage 1: the gate-only part of Eqs. 79-81 and 101.
- * Computes log sigmoid(f~), its prefix sums, and the row maximum
+ * Computes fbar = log f (log sigmoid(f~), or f~ for MLSTM_FORGET_EXP), its
+ * prefix sums, and the row maximum
  *   m_i = max_{j<=i} (sum_{k=j+1..i} fbar_k + i~_j)                 (Eq. 80)
  * through the equivalent recurrence m_i = max(m_{i-1} + fbar_i, i~_i),
  * m_0 = i~_0, before any Q K^T work.  Writes m_out and the per-row and
@@ -159,7 +173,8 @@ size_t mlstm_workspace_bytes(int64_t B, int64_t NH, int64_t T);
  */
 int mlstm_gate_scan(const float* igate, const float* fgate, float* m_out,
                     void* workspace, size_t workspace_bytes,
-                    int64_t B, int64_t NH, int64_t T, int64_t d, void* stream);
+                    int64_t B, int64_t NH, int64_t T, int64_t d,
+                    int forget_activation, void* stream);
 
 /*
  * mlstm_causal_tiles -- stage 2: Eqs. 81-86 over causal tiles.  Reads q, k,
@@ -175,14 +190,15 @@ int mlstm_causal_tiles(const void* q, const void* k, const void* v, const float*
 /*
  * mlstm_parallel_fwd_train -- mlstm_parallel_fwd_stream that also stores the
  * row sums b = C~' 1 (Eq. 83), which the backward pass needs (Eq. 90).
- *   b_out  out  [B][NH][T] float32 (required, 16-byte aligned)
+ *   b_out              out  [B][NH][T] float32 (required, 16-byte aligned)
+ *   forget_activation  MLSTM_FORGET_SIGMOID or MLSTM_FORGET_EXP
  * Other arguments, layouts and errors as for mlstm_parallel_fwd_stream.
  */
 int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v,
                              const float* igate, const float* fgate,
                              void* h_out, float* m_out, float* n_out, float* b_out,
                              int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
-                             void* stream);
+                             int forget_activation, void* stream);
 
 /*
  * mlstm_parallel_bwd -- gradients of the stabilized parallel forward pass
@@ -197,7 +213,9 @@ int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v,
  *   digate, dfgate          out [B][NH][T] float32
  * m is held constant (its contributions cancel, as the pages note).  Eq. 90
  * is applied with the derivative of |b|, sign(b): the printed sign(n) is 1
- * for every row, since n > 0.  d(log sigma(x))/dx = sigma(-x) (Eq. 104).
+ * for every row, since n > 0.  d(log sigma(x))/dx = sigma(-x) (Eq. 104);
+ * with forget_activation MLSTM_FORGET_EXP, d(log f)/df~ = 1.  The forward
+ * outputs must come from the same forget_activation.
  * dL/dn uses sum_j C~'_ij v_j = n_i h~_i, so for bf16 it carries the
  * rounding of the stored h~.  Arithmetic is float32 on the vector ALUs
  * (tiles of 16 x 16); the library allocates a stream-ordered workspace.
@@ -209,7 +227,8 @@ int mlstm_parallel_bwd(const void* q, const void* k, const void* v,
                        const void* h, const float* m, const float* n, const float* b,
                        const void* dh, void* dq, void* dk, void* dv,
                        float* digate, float* dfgate,
-                       int64_t B, int64_t NH, int64_t T, int64_t d, int dtype, void* stream);
+                       int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
+                       int forget_activation, void* stream);
 
 /*
  * mlstm_recurrent_step -- one step of the recurrent mLSTM (the generation
@@ -217,8 +236,9 @@ int mlstm_parallel_bwd(const void* q, const void* k, const void* v,
  * recurrent backward pass of appendix A.3 differentiates, Eqs. 59-70), with
  * the states stabilized by the running maximum of the log gates, the same
  * recurrence as the parallel form's row maximum (Eq. 80):
- *   m_t  = max(log sigmoid(f~_t) + m_{t-1}, i~_t)
- *   f'_t = exp(log sigmoid(f~_t) + m_{t-1} - m_t),  i'_t = exp(i~_t - m_t)
+ *   m_t  = max(fbar_t + m_{t-1}, i~_t),  fbar_t = log f_t (log sigmoid(f~_t),
+ *          or f~_t with forget_activation MLSTM_FORGET_EXP)
+ *   f'_t = exp(fbar_t + m_{t-1} - m_t),  i'_t = exp(i~_t - m_t)
  *   C_t  = f'_t C_{t-1} + i'_t v_t (k_t / sqrt(d))^T
  *   n_t  = f'_t n_{t-1} + i'_t k_t / sqrt(d)
  *   h~_t = C_t q_t / max(|n_t . q_t|, exp(-m_t))
@@ -244,7 +264,8 @@ int mlstm_recurrent_step(const void* q, const void* k, const void* v,
                          const float* C_in, const float* n_in, const float* m_in,
                          float* C_out, float* n_out, float* m_out,
                          void* h_out, float* den_out,
-                         int64_t B, int64_t NH, int64_t d, int dtype, void* stream);
+                         int64_t B, int64_t NH, int64_t d, int dtype,
+                         int forget_activation, void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* mlstm_strerror(int status);

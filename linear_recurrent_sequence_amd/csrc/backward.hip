@@ -15,7 +15,7 @@
 //   dD~_ij = C~'_ij dC~'_ij                                       (Eqs. 94-95)
 //   di~_j  = sum_i dD~_ij                                         (Eqs. 97, 105)
 //   dfbar_k = sum_{j<k<=i} dD~_ij = sum_{i>=k} (r_i - c_i)        (Eqs. 96, 102)
-//   df~_k  = sigma(-f~_k) dfbar_k                                  (Eqs. 103, 104)
+//   df~_k  = sigma(-f~_k) dfbar_k  (dfbar_k for an exponential gate) (Eqs. 103, 104)
 //
 // with r_i = sum_j dD~_ij and c_j = di~_j: splitting the sum over i >= k of
 // the row sums r_i into the entries with j < k (Eq. 102) and those with
@@ -260,7 +260,7 @@ constexpr int kGPer = 8;
 __global__ __launch_bounds__(kGThreads) void bwd_gates_kernel(
     const float* __restrict__ fgate, const float* __restrict__ rsum,
     const float* __restrict__ csum, float* __restrict__ digate, float* __restrict__ dfgate,
-    int64_t T) {
+    int64_t T, int exp_forget) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t head = blockIdx.x;
   const float* r = rsum + head * T;
@@ -298,8 +298,9 @@ __global__ __launch_bounds__(kGThreads) void bwd_gates_kernel(
       run += x[e];
       if (p >= 0) {
         const float f = fgate[head * T + p];
-        const double sig_neg = 1.0 / (1.0 + exp(double(f)));  // sigma(-f~)
-        dfgate[head * T + p] = float(sig_neg * run);
+        // d(log f)/d f~: sigma(-f~) (Eq. 104), or 1 for the exponential gate
+        const double dlogf = exp_forget ? 1.0 : 1.0 / (1.0 + exp(double(f)));
+        dfgate[head * T + p] = float(dlogf * run);
         digate[head * T + p] = c[p];
       }
     }
@@ -313,7 +314,7 @@ hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* f
                         const Tin* h, const float* m, const float* n, const float* b,
                         const Tin* dh, const Workspace& ws, float* inv_n, float* db, float* rsum,
                         float* csum, Tin* dq, Tin* dk, Tin* dv, float* digate, float* dfgate,
-                        int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+                        int64_t H, int64_t T, int64_t d, bool exp_forget, hipStream_t stream) {
   const int64_t rows = H * T;
   hipLaunchKernelGGL(bwd_rows_prep_kernel<Tin>, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
                      stream, h, dh, m, n, b, inv_n, db, rows, int(d));
@@ -325,7 +326,7 @@ hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* f
                      k, v, dh, inv_n, db, ws.anchor, ws.rowt, ws.colt, dk, dv, csum, T, int(d),
                      ws.Tp, ws.nblk, tiles);
   hipLaunchKernelGGL(bwd_gates_kernel, dim3(unsigned(H)), dim3(kGThreads), 0, stream, fgate,
-                     rsum, csum, digate, dfgate, T);
+                     rsum, csum, digate, dfgate, T, int(exp_forget));
   return hipGetLastError();
 }
 
@@ -339,7 +340,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                            const void* h, const float* m, const float* n, const float* b,
                            const void* dh, const Workspace& ws, void* scratch, void* dq, void* dk,
                            void* dv, float* digate, float* dfgate, int64_t H, int64_t T,
-                           int64_t d, bool is_bf16, hipStream_t stream) {
+                           int64_t d, bool is_bf16, bool exp_forget, hipStream_t stream) {
   if (d % 16 != 0 || d < 16 || d > kBMaxD) return hipErrorInvalidValue;
   char* p = static_cast<char*>(scratch);
   const size_t one = align256(size_t(H) * size_t(T) * sizeof(float));
@@ -353,13 +354,14 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                              static_cast<const B16*>(v), fgate, static_cast<const B16*>(h), m, n,
                              b, static_cast<const B16*>(dh), ws, inv_n, db, rsum, csum,
                              static_cast<B16*>(dq), static_cast<B16*>(dk), static_cast<B16*>(dv),
-                             digate, dfgate, H, T, d, stream);
+                             digate, dfgate, H, T, d, exp_forget, stream);
   }
   return launch_typed<float>(static_cast<const float*>(q), static_cast<const float*>(k),
                              static_cast<const float*>(v), fgate, static_cast<const float*>(h), m,
                              n, b, static_cast<const float*>(dh), ws, inv_n, db, rsum, csum,
                              static_cast<float*>(dq), static_cast<float*>(dk),
-                             static_cast<float*>(dv), digate, dfgate, H, T, d, stream);
+                             static_cast<float*>(dv), digate, dfgate, H, T, d, exp_forget,
+                             stream);
 }
 
 }  // namespace mlstm

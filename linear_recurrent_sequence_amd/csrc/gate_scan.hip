@@ -3,7 +3,7 @@
 // Everything in Eqs. 79-81 of the xLSTM appendix that depends only on the
 // gates is computed here, before any Q K^T work:
 //
-//   fbar_k = log sigmoid(f~_k)                                  (Eq. 101)
+//   fbar_k = log sigmoid(f~_k)   (f~_k for an exponential forget gate) (Eq. 101)
 //   m_i    = max_{j<=i} (sum_{k=j+1..i} fbar_k + i~_j)          (Eqs. 79, 80)
 //
 // The row maximum is evaluated through the recurrence obtained by splitting
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     const float* __restrict__ igate, const float* __restrict__ fgate, float* __restrict__ m_out,
     double* __restrict__ anchor, float* __restrict__ rowt, float* __restrict__ colt,
     float* __restrict__ rowb, float* __restrict__ keyb, int64_t T, int64_t Tp, int64_t nblk,
-    double half_ln_d) {
+    double half_ln_d, int exp_forget) {
   const double kLog2e = 1.4426950408889634074;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     for (int e = 0; e < kScanPer; ++e) {
       const int64_t p = p0 + e;
       if (p < T) {
-        fb[e] = log_sigmoid(f[p]);
+        fb[e] = exp_forget ? f[p] : log_sigmoid(f[p]);  // log f_t
         iv[e] = ig[p];
       } else {  // padding: no forgetting, no input; never reaches a real row
         fb[e] = 0.0f;
@@ -176,10 +176,10 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
 
 hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out,
                             const Workspace& ws, int64_t H, int64_t T, int64_t d,
-                            hipStream_t stream) {
+                            bool exp_forget, hipStream_t stream) {
   hipLaunchKernelGGL(gate_scan_kernel, dim3(unsigned(H)), dim3(kScanThreads), 0, stream, igate,
                      fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.rowb, ws.keyb, T, ws.Tp, ws.nblk,
-                     0.5 * log(double(d)));
+                     0.5 * log(double(d)), int(exp_forget));
   return hipGetLastError();
 }
 

@@ -77,7 +77,8 @@ int run_tiles(const void* q, const void* k, const void* v, const float* m, const
 // different streams).  Arguments are checked by the caller.
 int forward(const void* q, const void* k, const void* v, const float* igate, const float* fgate,
             const mlstm::Epilogue& ep, void* h_out, float* m_out, float* n_out, int64_t B,
-            int64_t NH, int64_t T, int64_t d, int dtype, hipStream_t s) {
+            int64_t NH, int64_t T, int64_t d, int dtype, hipStream_t s,
+            bool exp_forget = false) {
   const int64_t H = B * NH;
   const size_t bytes = mlstm::workspace_bytes(H, T);
   void* ws = nullptr;
@@ -86,7 +87,7 @@ int forward(const void* q, const void* k, const void* v, const float* igate, con
     return MLSTM_ERR_HIP;
   }
   const Workspace w = mlstm::carve(ws, H, T);
-  int st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d, s));
+  int st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d, exp_forget, s));
   if (st == MLSTM_OK)
     st = run_tiles(q, k, v, m_out, w, h_out, n_out, ep, H, T, d, dtype, MLSTM_KERNEL_AUTO, s);
   if (hipFreeAsync(ws, s) != hipSuccess && st == MLSTM_OK) st = MLSTM_ERR_HIP;
@@ -118,7 +119,9 @@ size_t mlstm_workspace_bytes(int64_t B, int64_t NH, int64_t T) {
 
 int mlstm_gate_scan(const float* igate, const float* fgate, float* m_out, void* workspace,
                     size_t workspace_bytes, int64_t B, int64_t NH, int64_t T, int64_t d,
-                    void* stream) {
+                    int forget_activation, void* stream) {
+  if (forget_activation != MLSTM_FORGET_SIGMOID && forget_activation != MLSTM_FORGET_EXP)
+    return MLSTM_ERR_ACTIVATION;
   int st = check_scan_args(igate, fgate, m_out, workspace);
   if (st != MLSTM_OK) return st;
   if ((st = check_shape(B, NH, T, d)) != MLSTM_OK) return st;
@@ -126,6 +129,7 @@ int mlstm_gate_scan(const float* igate, const float* fgate, float* m_out, void* 
   if (workspace_bytes < mlstm::workspace_bytes(H, T)) return MLSTM_ERR_WORKSPACE;
   const Workspace w = mlstm::carve(workspace, H, T);
   return hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d,
+                                            forget_activation == MLSTM_FORGET_EXP,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -179,23 +183,28 @@ int mlstm_parallel_fwd(const void* q, const void* k, const void* v, const float*
 int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v, const float* igate,
                              const float* fgate, void* h_out, float* m_out, float* n_out,
                              float* b_out, int64_t B, int64_t NH, int64_t T, int64_t d,
-                             int dtype, void* stream) {
+                             int dtype, int forget_activation, void* stream) {
   int st = check_forward_args(q, k, v, igate, fgate, h_out, m_out, n_out, B, NH, T, d, dtype);
   if (st != MLSTM_OK) return st;
+  if (forget_activation != MLSTM_FORGET_SIGMOID && forget_activation != MLSTM_FORGET_EXP)
+    return MLSTM_ERR_ACTIVATION;
   if (!b_out) return MLSTM_ERR_NULL;
   if (!aligned16(b_out)) return MLSTM_ERR_ALIGN;
   mlstm::Epilogue ep;
   ep.b = b_out;
   return forward(q, k, v, igate, fgate, ep, h_out, m_out, n_out, B, NH, T, d, dtype,
-                 static_cast<hipStream_t>(stream));
+                 static_cast<hipStream_t>(stream), forget_activation == MLSTM_FORGET_EXP);
 }
 
 int mlstm_parallel_bwd(const void* q, const void* k, const void* v, const float* igate,
                        const float* fgate, const void* h, const float* m, const float* n,
                        const float* b, const void* dh, void* dq, void* dk, void* dv,
                        float* digate, float* dfgate, int64_t B, int64_t NH, int64_t T,
-                       int64_t d, int dtype, void* stream) {
+                       int64_t d, int dtype, int forget_activation, void* stream) {
   if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
+  if (forget_activation != MLSTM_FORGET_SIGMOID && forget_activation != MLSTM_FORGET_EXP)
+    return MLSTM_ERR_ACTIVATION;
+  const bool exp_forget = forget_activation == MLSTM_FORGET_EXP;
   int st = check_shape(B, NH, T, d);
   if (st != MLSTM_OK) return st;
   const void* ins[] = {q, k, v, igate, fgate, h, m, n, b, dh};
@@ -223,10 +232,11 @@ int mlstm_parallel_bwd(const void* q, const void* k, const void* v, const float*
   void* scratch = static_cast<char*>(ws) + wsb + mb;
   // the exponent terms of D' are recomputed from the gates (the scan's m is
   // bitwise the forward's)
-  st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_scan, w, H, T, d, s));
+  st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_scan, w, H, T, d, exp_forget, s));
   if (st == MLSTM_OK)
     st = hip_status(mlstm::launch_backward(q, k, v, fgate, h, m, n, b, dh, w, scratch, dq, dk,
-                                           dv, digate, dfgate, H, T, d, dtype == MLSTM_BF16, s));
+                                           dv, digate, dfgate, H, T, d, dtype == MLSTM_BF16,
+                                           exp_forget, s));
   if (hipFreeAsync(ws, s) != hipSuccess && st == MLSTM_OK) st = MLSTM_ERR_HIP;
   return st;
 }
@@ -235,8 +245,10 @@ int mlstm_recurrent_step(const void* q, const void* k, const void* v, const floa
                          const float* fgate, const float* C_in, const float* n_in,
                          const float* m_in, float* C_out, float* n_out, float* m_out,
                          void* h_out, float* den_out, int64_t B, int64_t NH, int64_t d,
-                         int dtype, void* stream) {
+                         int dtype, int forget_activation, void* stream) {
   if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
+  if (forget_activation != MLSTM_FORGET_SIGMOID && forget_activation != MLSTM_FORGET_EXP)
+    return MLSTM_ERR_ACTIVATION;
   int st = check_shape(B, NH, 1, d);
   if (st != MLSTM_OK) return st;
   if (!q || !k || !v || !igate || !fgate || !C_in || !n_in || !m_in || !C_out || !n_out ||
@@ -260,6 +272,7 @@ int mlstm_recurrent_step(const void* q, const void* k, const void* v, const floa
   return hip_status(mlstm::launch_recurrent_step(q, k, v, igate, fgate, C_in, n_in, m_in, C_out,
                                                  n_out, m_out, h_out, den_out, H, d,
                                                  dtype == MLSTM_BF16,
+                                                 forget_activation == MLSTM_FORGET_EXP,
                                                  static_cast<hipStream_t>(stream)));
 }
 
@@ -275,6 +288,7 @@ const char* mlstm_strerror(int status) {
     case MLSTM_ERR_WORKSPACE: return "workspace smaller than mlstm_workspace_bytes()";
     case MLSTM_ERR_KERNEL: return "unknown kernel selector, or the MFMA kernel asked for float32";
     case MLSTM_ERR_ALIAS: return "an output overlaps an input it must not alias";
+    case MLSTM_ERR_ACTIVATION: return "unknown forget-gate activation";
     default: return "unknown status";
   }
 }

@@ -88,10 +88,11 @@ struct Epilogue {
   float* b = nullptr;
 };
 
-// Stage 1: gate scan (one workgroup per head).
+// Stage 1: gate scan (one workgroup per head).  exp_forget: the forget gate
+// is exp(f~) (log f = f~) instead of sigmoid(f~).
 hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out,
                             const Workspace& ws, int64_t H, int64_t T, int64_t d,
-                            hipStream_t stream);
+                            bool exp_forget, hipStream_t stream);
 
 // Stage 2, bf16 matrix-core tiles; `skip` enables the decay-aware skipping
 // of tiles whose bound is below kSkipLog2 (results are identical either way).
@@ -116,7 +117,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                            const void* h, const float* m, const float* n, const float* b,
                            const void* dh, const Workspace& ws, void* scratch, void* dq, void* dk,
                            void* dv, float* digate, float* dfgate, int64_t H, int64_t T,
-                           int64_t d, bool is_bf16, hipStream_t stream);
+                           int64_t d, bool is_bf16, bool exp_forget, hipStream_t stream);
 
 // Recurrent step (generation), stabilized states in float32: C [H][d][d],
 // n [H][d], m [H].  C_out may equal C_in; n_out / m_out must not overlap
@@ -126,6 +127,6 @@ hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, co
                                  const float* fgate, const float* C_in, const float* n_in,
                                  const float* m_in, float* C_out, float* n_out, float* m_out,
                                  void* h_out, float* den_out, int64_t H, int64_t d, bool is_bf16,
-                                 hipStream_t stream);
+                                 bool exp_forget, hipStream_t stream);
 
 }  // namespace mlstm

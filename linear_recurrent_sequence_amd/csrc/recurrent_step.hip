@@ -7,7 +7,7 @@
 // maximum of the log gates -- the same recurrence that gives the parallel
 // form's row maximum (Eq. 80):
 //
-//   fbar_t = log sigmoid(f~_t)                              (Eq. 101)
+//   fbar_t = log sigmoid(f~_t)  (or f~_t for an exponential forget gate, Eq. 101)
 //   m_t    = max(fbar_t + m_{t-1}, i~_t),   m_0 = -inf
 //   f'_t   = exp(fbar_t + m_{t-1} - m_t),   i'_t = exp(i~_t - m_t)
 //   C_t    = f'_t C_{t-1} + i'_t v_t k'_t^T,  k'_t = k_t / sqrt(d)
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(
     const float* __restrict__ igate, const float* __restrict__ fgate, const float* C_in,
     const float* __restrict__ n_in, const float* __restrict__ m_in, float* C_out,
     float* __restrict__ n_out, float* __restrict__ m_out, Tin* __restrict__ h_out,
-    float* __restrict__ den_out, int d, int blocks_per_head) {
+    float* __restrict__ den_out, int d, int blocks_per_head, int exp_forget) {
   const int64_t head = blockIdx.x / blocks_per_head;
   const int rb = blockIdx.x % blocks_per_head;
   const int lane = threadIdx.x & 63;
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(
   const int npairs = d / 2;
 
   // gates and stabilizer
-  const float fbar = log_sigmoid(fgate[head]);
+  const float fbar = exp_forget ? fgate[head] : log_sigmoid(fgate[head]);  // log f_t
   const float ig = igate[head];
   const float m_old = m_in[head];
   const float m_new = fmaxf(fbar + m_old, ig);
@@ -156,7 +156,7 @@ hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, co
                                  const float* fgate, const float* C_in, const float* n_in,
                                  const float* m_in, float* C_out, float* n_out, float* m_out,
                                  void* h_out, float* den_out, int64_t H, int64_t d, bool is_bf16,
-                                 hipStream_t stream) {
+                                 bool exp_forget, hipStream_t stream) {
   if (d % 16 != 0 || d < 16 || d > 2 * 64 * kPairsPerLane) return hipErrorInvalidValue;
   const int blocks_per_head = int((d + kStepRows - 1) / kStepRows);
   const dim3 grid(unsigned(H * blocks_per_head));
@@ -165,13 +165,14 @@ hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, co
     hipLaunchKernelGGL(recurrent_step_kernel<B16>, grid, dim3(kStepThreads), 0, stream,
                        static_cast<const B16*>(q), static_cast<const B16*>(k),
                        static_cast<const B16*>(v), igate, fgate, C_in, n_in, m_in, C_out, n_out,
-                       m_out, static_cast<B16*>(h_out), den_out, int(d), blocks_per_head);
+                       m_out, static_cast<B16*>(h_out), den_out, int(d), blocks_per_head,
+                       int(exp_forget));
   } else {
     hipLaunchKernelGGL(recurrent_step_kernel<float>, grid, dim3(kStepThreads), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), igate, fgate, C_in, n_in, m_in, C_out,
                        n_out, m_out, static_cast<float*>(h_out), den_out, int(d),
-                       blocks_per_head);
+                       blocks_per_head, int(exp_forget));
   }
   return hipGetLastError();
 }

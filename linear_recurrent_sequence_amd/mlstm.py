@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libmlstm.so")
 
 MLSTM_FP32, MLSTM_BF16 = 0, 1
 KERNELS = {"auto": 0, "mfma": 1, "vector": 2, "mfma_all_tiles": 3}
+FORGET_ACTIVATIONS = {"sigmoid": 0, "exp": 1}
 
 _lib = None
 
@@ -50,15 +51,15 @@ def load_library():
     lib.mlstm_parallel_fwd_stream.restype = i32
     lib.mlstm_parallel_fwd_gated.argtypes = [vp] * 10 + [i64] * 4 + [i32, vp]
     lib.mlstm_parallel_fwd_gated.restype = i32
-    lib.mlstm_recurrent_step.argtypes = [vp] * 13 + [i64] * 3 + [i32, vp]
+    lib.mlstm_recurrent_step.argtypes = [vp] * 13 + [i64] * 3 + [i32, i32, vp]
     lib.mlstm_recurrent_step.restype = i32
-    lib.mlstm_parallel_fwd_train.argtypes = [vp] * 9 + [i64] * 4 + [i32, vp]
+    lib.mlstm_parallel_fwd_train.argtypes = [vp] * 9 + [i64] * 4 + [i32, i32, vp]
     lib.mlstm_parallel_fwd_train.restype = i32
-    lib.mlstm_parallel_bwd.argtypes = [vp] * 15 + [i64] * 4 + [i32, vp]
+    lib.mlstm_parallel_bwd.argtypes = [vp] * 15 + [i64] * 4 + [i32, i32, vp]
     lib.mlstm_parallel_bwd.restype = i32
     lib.mlstm_workspace_bytes.argtypes = [i64] * 3
     lib.mlstm_workspace_bytes.restype = f
-    lib.mlstm_gate_scan.argtypes = [vp] * 4 + [f] + [i64] * 4 + [vp]
+    lib.mlstm_gate_scan.argtypes = [vp] * 4 + [f] + [i64] * 4 + [i32, vp]
     lib.mlstm_gate_scan.restype = i32
     lib.mlstm_causal_tiles.argtypes = [vp] * 5 + [f] + [vp] * 2 + [i64] * 4 + [i32, i32, vp]
     lib.mlstm_causal_tiles.restype = i32
@@ -78,6 +79,13 @@ def _dtype_code(t):
     if t.dtype == torch.bfloat16:
         return MLSTM_BF16
     raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _forget_code(forget):
+    """The C-ABI code of a forget-gate activation name ("sigmoid" or "exp")."""
+    if forget not in FORGET_ACTIVATIONS:
+        raise ValueError(f"forget must be one of {tuple(FORGET_ACTIVATIONS)}, got {forget!r}")
+    return FORGET_ACTIVATIONS[forget]
 
 
 def _check_inputs(q, k, v, igate, fgate):
@@ -165,7 +173,7 @@ def alloc_workspace(B, NH, T, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def gate_scan(igate, fgate, d, workspace, m=None):
+def gate_scan(igate, fgate, d, workspace, m=None, forget="sigmoid"):
     """Stage 1: m (Eq. 80) and the exponent terms, written into ``workspace``."""
     lib = load_library()
     if igate.dim() != 3 or igate.shape != fgate.shape:
@@ -179,7 +187,7 @@ def gate_scan(igate, fgate, d, workspace, m=None):
     with torch.cuda.device(igate.device):
         st = lib.mlstm_gate_scan(igate.data_ptr(), fgate.data_ptr(), m.data_ptr(),
                                  workspace.data_ptr(), workspace.numel(), B, NH, T, d,
-                                 _stream_ptr(igate.device))
+                                 _forget_code(forget), _stream_ptr(igate.device))
     if st != 0:
         raise MlstmError(st, "mlstm_gate_scan")
     return m
@@ -204,11 +212,11 @@ def causal_tiles(q, k, v, m, workspace, kernel="auto", out=None):
     return h, n
 
 
-def parallel_fwd_staged(q, k, v, igate, fgate, kernel="auto"):
+def parallel_fwd_staged(q, k, v, igate, fgate, kernel="auto", forget="sigmoid"):
     """Both stages with an explicit workspace and a chosen tile kernel."""
     B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
     ws = alloc_workspace(B, NH, T, q.device)
-    m = gate_scan(igate, fgate, d, ws)
+    m = gate_scan(igate, fgate, d, ws, forget=forget)
     h, n = causal_tiles(q, k, v, m, ws, kernel=kernel)
     return h, m, n
 
@@ -221,7 +229,7 @@ def recurrent_state(B, NH, d, device):
     return C, n, m
 
 
-def recurrent_step(q, k, v, igate, fgate, state, out_state=None, den=False):
+def recurrent_step(q, k, v, igate, fgate, state, out_state=None, den=False, forget="sigmoid"):
     """One stabilized recurrent step -> (h, new_state[, den]).
 
     q, k, v: [B, NH, d] (float32 or bfloat16); igate, fgate: [B, NH] float32;
@@ -254,13 +262,13 @@ def recurrent_step(q, k, v, igate, fgate, state, out_state=None, den=False):
             q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
             C.data_ptr(), n.data_ptr(), m.data_ptr(), Co.data_ptr(), no.data_ptr(), mo.data_ptr(),
             h.data_ptr(), dn.data_ptr() if den else None, B, NH, d, _dtype_code(q),
-            _stream_ptr(q.device))
+            _forget_code(forget), _stream_ptr(q.device))
     if st != 0:
         raise MlstmError(st, "mlstm_recurrent_step")
     return (h, out_state, dn) if den else (h, out_state)
 
 
-def parallel_fwd_train(q, k, v, igate, fgate):
+def parallel_fwd_train(q, k, v, igate, fgate, forget="sigmoid"):
     """Forward pass that also returns the row sums b -> (h, m, n, b)."""
     lib = load_library()
     B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
@@ -270,13 +278,13 @@ def parallel_fwd_train(q, k, v, igate, fgate):
         st = lib.mlstm_parallel_fwd_train(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
             h.data_ptr(), m.data_ptr(), n.data_ptr(), b.data_ptr(), B, NH, T, d, _dtype_code(q),
-            _stream_ptr(q.device))
+            _forget_code(forget), _stream_ptr(q.device))
     if st != 0:
         raise MlstmError(st, "mlstm_parallel_fwd_train")
     return h, m, n, b
 
 
-def parallel_bwd(q, k, v, igate, fgate, h, m, n, b, dh):
+def parallel_bwd(q, k, v, igate, fgate, h, m, n, b, dh, forget="sigmoid"):
     """Gradients (dq, dk, dv, digate, dfgate) of the forward pass given dh = dL/dh~."""
     lib = load_library()
     B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
@@ -293,7 +301,7 @@ def parallel_bwd(q, k, v, igate, fgate, h, m, n, b, dh):
             q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
             h.data_ptr(), m.data_ptr(), n.data_ptr(), b.data_ptr(), dh.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dig.data_ptr(), dfg.data_ptr(),
-            B, NH, T, d, _dtype_code(q), _stream_ptr(q.device))
+            B, NH, T, d, _dtype_code(q), _forget_code(forget), _stream_ptr(q.device))
     if st != 0:
         raise MlstmError(st, "mlstm_parallel_bwd")
     return dq, dk, dv, dig, dfg

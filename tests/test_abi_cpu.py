@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_strerror_and_workspace_size():
-    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10):
         msg = mlstm.strerror(st)
         assert msg and msg != "unknown status"
     assert mlstm.strerror(-99) == "unknown status"
@@ -81,9 +81,12 @@ def test_parallel_fwd_rejects_before_device_work(case, status):
 def test_staged_entry_points_reject_before_device_work():
     lib = mlstm.load_library()
     # workspace too small
-    assert lib.mlstm_gate_scan(FAKE, FAKE, FAKE, FAKE, 10, 1, 1, 64, 16, None) == -7
+    assert lib.mlstm_gate_scan(FAKE, FAKE, FAKE, FAKE, 10, 1, 1, 64, 16, 0, None) == -7
     # misaligned workspace (needs 256 bytes)
-    assert lib.mlstm_gate_scan(FAKE, FAKE, FAKE, FAKE + 16, 1 << 20, 1, 1, 64, 16, None) == -5
+    assert lib.mlstm_gate_scan(FAKE, FAKE, FAKE, FAKE + 16, 1 << 20, 1, 1, 64, 16, 0, None) == -5
+    # unknown forget-gate activation
+    assert lib.mlstm_gate_scan(FAKE, FAKE, FAKE, FAKE, 1 << 20, 1, 1, 64, 16, 2, None) == -10
+    assert lib.mlstm_gate_scan(FAKE, FAKE, FAKE, FAKE, 1 << 20, 1, 1, 64, 16, -1, None) == -10
     # MFMA kernel for float32 inputs
     assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, FAKE,
                                   1, 1, 64, 16, 0, 1, None) == -8
@@ -123,16 +126,28 @@ def test_gated_forward_rejects_before_device_work(case, status):
     (dict(n_out=FAKE), -9),                       # n_out is n_in
     (dict(m_out=FAKE + (1 << 16)), -9),           # m_out is m_in
     (dict(C_out=FAKE + (1 << 12)), -9),           # C_out overlaps C_in, shifted
+    (dict(forget=2), -10),
 ])
 def test_recurrent_step_rejects_before_device_work(case, status):
     lib = mlstm.load_library()
     args = dict(q=FAKE, k=FAKE, v=FAKE, igate=FAKE, fgate=FAKE,
                 C_in=FAKE, n_in=FAKE, m_in=FAKE + (1 << 16),
                 C_out=FAKE, n_out=FAKE + (1 << 24), m_out=FAKE + (1 << 25),
-                h_out=FAKE, den_out=0, B=1, NH=1, d=64, dtype=1)
+                h_out=FAKE, den_out=0, B=1, NH=1, d=64, dtype=1, forget=0)
     args.update(case)
     ptrs = ["q", "k", "v", "igate", "fgate", "C_in", "n_in", "m_in", "C_out", "n_out", "m_out",
             "h_out", "den_out"]
     st = lib.mlstm_recurrent_step(*[args[k] or None for k in ptrs], args["B"], args["NH"],
-                                  args["d"], args["dtype"], None)
+                                  args["d"], args["dtype"], args["forget"], None)
     assert st == status
+
+
+@needs_lib
+def test_training_entry_points_reject_unknown_forget_activation():
+    lib = mlstm.load_library()
+    assert lib.mlstm_parallel_fwd_train(*[FAKE] * 9, 1, 1, 64, 16, 1, 2, None) == -10
+    assert lib.mlstm_parallel_bwd(*[FAKE] * 15, 1, 1, 64, 16, 1, 7, None) == -10
+    # the activation is checked after the other arguments' own checks
+    assert lib.mlstm_parallel_fwd_train(*[FAKE] * 8, None, 1, 1, 64, 16, 1, 0, None) == -1
+    with pytest.raises(ValueError):
+        mlstm._forget_code("tanh")

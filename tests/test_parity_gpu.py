@@ -491,3 +491,82 @@ def test_backward_deterministic_bitwise():
     torch.cuda.synchronize()
     for ta, tc in zip(a, c):
         assert torch.equal(ta, tc)
+
+
+# ---------------------------------------------------------------------------
+# exponential forget gate (f = exp(f~)): forward, recurrent step and backward
+# ---------------------------------------------------------------------------
+
+EXP_CASES = [
+    spec(1, 2, 130, 64, "fp32", fg=("normal", -0.05, 0.03)),
+    spec(1, 2, 257, 128, fg=("normal", -0.05, 0.03)),
+    spec(1, 1, 160, 384, fg=("normal", -0.02, 0.02)),
+    spec(2, 1, 200, 64, ig=("uniform", -10, 10), fg=("uniform", -3.0, 0.5)),  # some f > 1
+]
+
+
+@pytest.mark.parametrize("s", EXP_CASES, ids=_id)
+def test_exp_forget_forward_matches_oracle(s):
+    x = W.make(s, seed=22)
+    q, k, v, ig, fg = _dev(x)
+    h, m, n = mlstm.parallel_fwd_staged(q, k, v, ig, fg, forget="exp")
+    ht, mt, nt, b = mlstm.parallel_fwd_train(q, k, v, ig, fg, forget="exp")
+    hs, ms, ns = mlstm.parallel_fwd_staged(q, k, v, ig, fg)  # sigmoid: must differ
+    torch.cuda.synchronize()
+    assert torch.equal(h, ht) and torch.equal(m, mt) and torch.equal(n, nt)
+    assert not torch.equal(m, ms)
+    hr, mr, nr, br, rho = oracle.forward_stabilized(x["q"], x["k"], x["v"], x["igate"],
+                                                    x["fgate"], return_diag=True, forget="exp")
+    print(check(_host(h), _host(m), _host(n), hr, mr, nr, TOL_H[s["dtype"]],
+                kappa=rho / nr, kappa_max=1e3))
+    assert head_normwise(_host(b), br) <= 1e-5
+
+
+@pytest.mark.parametrize("s", [spec(1, 2, 40, 64, "fp32", fg=("normal", -0.05, 0.03)),
+                               spec(1, 1, 30, 384, fg=("uniform", -2.0, 0.3))], ids=_id)
+def test_exp_forget_recurrent_steps_match_oracle(s):
+    x = W.make(s, seed=23)
+    q, k, v, ig, fg = _dev(x)
+    B, NH, T, d = q.shape
+    state = mlstm.recurrent_state(B, NH, d, "cuda")
+    hs, ms, dens = [], [], []
+    for t in range(T):
+        h, state, den = mlstm.recurrent_step(
+            q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
+            ig[:, :, t].contiguous(), fg[:, :, t].contiguous(), state, den=True, forget="exp")
+        hs.append(h)
+        ms.append(state[2].clone())
+        dens.append(den)
+    torch.cuda.synchronize()
+    h, m, den = (_host(torch.stack(a, dim=2)) for a in (hs, ms, dens))
+    hr, mr, denr, CT, nT = oracle.forward_recurrent_stabilized(
+        x["q"], x["k"], x["v"], x["igate"], x["fgate"], forget="exp")
+    print(check(h, m, den, hr, mr, denr, TOL_H[s["dtype"]]))
+    C = _host(state[0])
+    assert head_normwise(C.reshape(B, NH, -1), CT.reshape(B, NH, -1)) <= 1e-4
+    assert head_normwise(_host(state[1]), nT) <= 1e-4
+
+
+@pytest.mark.parametrize("s", [spec(1, 2, 77, 64, "fp32", fg=("normal", -0.05, 0.03)),
+                               spec(1, 1, 100, 128, fg=("uniform", -2.0, 0.3))], ids=_id)
+def test_exp_forget_backward_matches_oracle(s):
+    x = W.make(s, seed=24)
+    q, k, v, ig, fg = _dev(x)
+    rng = np.random.default_rng(25)
+    dh_np = rng.standard_normal(x["q"].shape).astype(np.float32)
+    if s["dtype"] == "bf16":
+        dh_np = W.round_bf16(dh_np)
+    dh = torch.from_numpy(dh_np).to("cuda").to(q.dtype).contiguous()
+    h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg, forget="exp")
+    grads = mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, dh, forget="exp")
+    torch.cuda.synchronize()
+    ref = oracle.backward_stabilized(x["q"], x["k"], x["v"], x["igate"], x["fgate"], dh_np,
+                                     forget="exp")
+    hr = oracle.forward_stabilized(x["q"], x["k"], x["v"], x["igate"], x["fgate"],
+                                   forget="exp")[0]
+    tol = max(2e-2 if s["dtype"] == "bf16" else 1e-4, 3.0 * head_normwise(_host(h), hr))
+    errs = {name: head_normwise(_host(g), r) for name, g, r in
+            zip(("dq", "dk", "dv", "digate", "dfgate"), grads, ref)}
+    print(errs)
+    for name, e in errs.items():
+        assert e <= (tol if name in ("dq", "dk", "dv") else 10 * tol), (name, errs)
