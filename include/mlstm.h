@@ -65,8 +65,18 @@ enum {
   MLSTM_KERNEL_AUTO = 0,   /* bf16 -> matrix-core kernel, fp32 -> vector kernel */
   MLSTM_KERNEL_MFMA = 1,   /* bf16 only: bf16 MFMA tiles (the production path) */
   MLSTM_KERNEL_VECTOR = 2, /* any dtype: float32 vector-ALU tiles, no bf16 rounding of C~' */
-  MLSTM_KERNEL_MFMA_ALL_TILES = 3  /* as MLSTM_KERNEL_MFMA, but visiting every causal tile */
+  MLSTM_KERNEL_MFMA_ALL_TILES = 3, /* as MLSTM_KERNEL_MFMA, but visiting every causal tile */
+  MLSTM_KERNEL_MFMA_SINGLE = 4     /* bf16 only: the one-wave-per-SIMD MFMA kernel */
 };
+/*
+ * The bf16 MFMA path has two tile kernels.  For d <= 384 it runs 8 waves per
+ * workgroup, two per SIMD: the two waves that share a SIMD share 32 query
+ * rows, each forms C~' for its own 32 of every 64 keys and accumulates half
+ * of the output columns, so one wave's copies and exponentials overlap the
+ * other's matrix-core work.  For d > 384 (and with MLSTM_KERNEL_MFMA_SINGLE)
+ * it runs 4 waves, one per SIMD, each with 32 query rows and all columns.
+ * Both give the same results up to float32 summation order.
+ */
 /*
  * Decay-aware tile skipping (MLSTM_KERNEL_AUTO and _MFMA on bf16).  From the
  * gate scan's terms the tile kernel bounds log2(D'_ij / sqrt(d)) over each

@@ -47,7 +47,8 @@ __device__ inline float log_sigmoid(float x) {
 __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     const float* __restrict__ igate, const float* __restrict__ fgate, float* __restrict__ m_out,
     double* __restrict__ anchor, float* __restrict__ rowt, float* __restrict__ colt,
-    float* __restrict__ rowb, float* __restrict__ keyb, int64_t T, int64_t Tp, int64_t nblk,
+    float* __restrict__ colx, float* __restrict__ rowb, float* __restrict__ keyb, int64_t T,
+    int64_t Tp, int64_t nblk,
     double half_ln_d, int exp_forget) {
   const double kLog2e = 1.4426950408889634074;
   const int tid = threadIdx.x;
@@ -60,6 +61,7 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
   double* anc = anchor + head * nblk;
   float* rt = rowt + head * Tp;
   float* ct = colt + head * Tp;
+  float* cx = colx + head * Tp;
   float* rb = rowb + head * (Tp / kBoundTile);
   float* kb = keyb + head * (Tp / kBoundTile);
 
@@ -137,8 +139,10 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     const double blk_anchor = __shfl(cs, lane & ~7, 64);
     if (p0 < Tp && (p0 & (kAnchorBlock - 1)) == 0) anc[p0 / kAnchorBlock] = blk_anchor * kLog2e;
     float rmax = -INFINITY, cmax = -INFINITY;  // of the values stored below
+    float cvals[kScanPer];
 #pragma unroll
     for (int e = 0; e < kScanPer; ++e) {
+      cvals[e] = -INFINITY;
       const int64_t p = p0 + e;
       cs += double(fb[e]);
       m = fmax(m + double(fb[e]), double(iv[e]));
@@ -149,6 +153,7 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
         mo[p] = float(m);
         rt[p] = r;
         ct[p] = c;
+        cvals[e] = c;
         rmax = fmaxf(rmax, r);
         cmax = fmaxf(cmax, c);
       } else if (p < Tp) {
@@ -166,6 +171,12 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
       rb[p0 / kBoundTile] = rmax;
       kb[p0 / kBoundTile] = cmax;
     }
+    // the key factor of the factored exponent, relative to its tile's maximum
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e) {
+      const int64_t p = p0 + e;
+      if (p < Tp) cx[p] = p < T ? float(exp2(double(cvals[e]) - double(cmax))) : 0.0f;
+    }
     carry_cs += tot_sum;
     carry_m = apply(tot_map, carry_m);
     __syncthreads();  // s_* are rewritten by the next chunk
@@ -178,7 +189,8 @@ hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out
                             const Workspace& ws, int64_t H, int64_t T, int64_t d,
                             bool exp_forget, hipStream_t stream) {
   hipLaunchKernelGGL(gate_scan_kernel, dim3(unsigned(H)), dim3(kScanThreads), 0, stream, igate,
-                     fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.rowb, ws.keyb, T, ws.Tp, ws.nblk,
+                     fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb, ws.keyb, T, ws.Tp,
+                     ws.nblk,
                      0.5 * log(double(d)), int(exp_forget));
   return hipGetLastError();
 }

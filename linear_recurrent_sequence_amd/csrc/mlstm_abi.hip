@@ -48,9 +48,11 @@ int check_tile_args(const void* q, const void* k, const void* v, const float* m,
   if (!q || !k || !v || !m || !ws || !h_out || !n_out) return MLSTM_ERR_NULL;
   if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
   if (kernel != MLSTM_KERNEL_AUTO && kernel != MLSTM_KERNEL_MFMA &&
-      kernel != MLSTM_KERNEL_VECTOR && kernel != MLSTM_KERNEL_MFMA_ALL_TILES)
+      kernel != MLSTM_KERNEL_VECTOR && kernel != MLSTM_KERNEL_MFMA_ALL_TILES &&
+      kernel != MLSTM_KERNEL_MFMA_SINGLE)
     return MLSTM_ERR_KERNEL;
-  if ((kernel == MLSTM_KERNEL_MFMA || kernel == MLSTM_KERNEL_MFMA_ALL_TILES) &&
+  if ((kernel == MLSTM_KERNEL_MFMA || kernel == MLSTM_KERNEL_MFMA_ALL_TILES ||
+       kernel == MLSTM_KERNEL_MFMA_SINGLE) &&
       dtype != MLSTM_BF16)
     return MLSTM_ERR_KERNEL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(m) || !aligned16(h_out) ||
@@ -64,10 +66,14 @@ int run_tiles(const void* q, const void* k, const void* v, const float* m, const
               void* h_out, float* n_out, const mlstm::Epilogue& ep, int64_t H, int64_t T,
               int64_t d, int dtype, int kernel, hipStream_t stream) {
   const bool use_mfma = kernel == MLSTM_KERNEL_MFMA || kernel == MLSTM_KERNEL_MFMA_ALL_TILES ||
+                        kernel == MLSTM_KERNEL_MFMA_SINGLE ||
                         (kernel == MLSTM_KERNEL_AUTO && dtype == MLSTM_BF16);
+  const bool skip = kernel != MLSTM_KERNEL_MFMA_ALL_TILES;
+  if (use_mfma && kernel != MLSTM_KERNEL_MFMA_SINGLE && mlstm::tiles_pairs_supports(d))
+    return hip_status(mlstm::launch_tiles_pairs(q, k, v, m, w, h_out, n_out, ep, skip, H, T, d,
+                                                stream));
   if (use_mfma)
-    return hip_status(mlstm::launch_tiles_mfma(q, k, v, m, w, h_out, n_out, ep,
-                                               kernel != MLSTM_KERNEL_MFMA_ALL_TILES, H, T, d,
+    return hip_status(mlstm::launch_tiles_mfma(q, k, v, m, w, h_out, n_out, ep, skip, H, T, d,
                                                stream));
   return hip_status(mlstm::launch_tiles_vector(q, k, v, m, w, h_out, n_out, ep, H, T, d,
                                                dtype == MLSTM_BF16, stream));

@@ -6,6 +6,7 @@
 //   anchor [H][Tp/64]  float64  A_b = (sum of fbar over positions < 64 b) * log2(e)
 //   rowt   [H][Tp]     float32  r_i = (loc_i - m_i - ln(d)/2) * log2(e)
 //   colt   [H][Tp]     float32  c_j = (i~_j - loc_j) * log2(e)    (-inf on padding)
+//   colx   [H][Tp]     float32  e_j = 2^(c_j - keyb_{j/32})        (0 on padding)
 //   rowb   [H][Tp/32]  float32  max of r_i over each 32-row block
 //   keyb   [H][Tp/32]  float32  max of c_j over each 32-key tile (-inf if all padding)
 //
@@ -18,6 +19,12 @@
 // The block anchors keep the difference of two long prefix sums out of
 // float32: the anchor difference is taken in float64 and rounded once, and
 // every other term is bounded by one block's worth of forget gates.
+//
+// Factored exponent: below the diagonal (every key of a 32-key tile J before
+// every query of a 32-row block), 2^((A_i - A_J) + r_i + c_j) equals
+// 2^((A_i - A_J) + r_i + keyb_J) * e_j, and neither factor can overflow:
+// the first is at most 1 (D' <= 1 and keyb_J is attained by a key of the
+// tile), the second lies in (0, 1].
 //
 // Tile bound: the tile kernels form each exponent as
 // fl(fl(float(A_{i/64} - A_{j/64}) + r_i) + c_j).  Rounding is monotone, so
@@ -42,6 +49,7 @@ struct Workspace {
   double* anchor;
   float* rowt;
   float* colt;
+  float* colx;
   float* rowb;
   float* keyb;
   int64_t Tp;
@@ -55,7 +63,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline size_t workspace_bytes(int64_t H, int64_t T) {
   const int64_t Tp = padded_len(T);
   return align256(size_t(H) * size_t(Tp / kAnchorBlock) * sizeof(double)) +
-         2 * align256(size_t(H) * size_t(Tp) * sizeof(float)) +
+         3 * align256(size_t(H) * size_t(Tp) * sizeof(float)) +
          2 * align256(size_t(H) * size_t(Tp / kBoundTile) * sizeof(float));
 }
 
@@ -69,6 +77,8 @@ inline Workspace carve(void* base, int64_t H, int64_t T) {
   w.rowt = reinterpret_cast<float*>(p);
   p += align256(size_t(H) * size_t(w.Tp) * sizeof(float));
   w.colt = reinterpret_cast<float*>(p);
+  p += align256(size_t(H) * size_t(w.Tp) * sizeof(float));
+  w.colx = reinterpret_cast<float*>(p);
   p += align256(size_t(H) * size_t(w.Tp) * sizeof(float));
   w.rowb = reinterpret_cast<float*>(p);
   p += align256(size_t(H) * size_t(w.Tp / kBoundTile) * sizeof(float));
@@ -102,6 +112,14 @@ hipError_t launch_tiles_mfma(const void* q, const void* k, const void* v, const 
                              const Workspace& ws, void* h_out, float* n_out,
                              const Epilogue& ep, bool skip, int64_t H, int64_t T, int64_t d,
                              hipStream_t stream);
+
+// Stage 2, bf16 matrix-core tiles with two waves per SIMD (d <= 384), the
+// same results up to float32 rounding order.
+bool tiles_pairs_supports(int64_t d);
+hipError_t launch_tiles_pairs(const void* q, const void* k, const void* v, const float* m,
+                              const Workspace& ws, void* h_out, float* n_out,
+                              const Epilogue& ep, bool skip, int64_t H, int64_t T, int64_t d,
+                              hipStream_t stream);
 
 // Stage 2, float32 vector-ALU tiles; is_bf16 selects the element type.
 hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, const float* m,

@@ -1,0 +1,585 @@
+// Stage 2, bf16 matrix-core variant with two waves per SIMD: Eqs. 81-86 of
+// the xLSTM appendix over causal tiles, both contractions on gfx950 MFMA
+// (v_mfma_f32_32x32x16_bf16, float32 accumulation).
+//
+// Why two waves per SIMD.  A wave that issues a global -> LDS copy, or a run
+// of exponentials, cannot issue matrix instructions meanwhile; with one wave
+// per SIMD the matrix core idles for that time.  With two, one wave's copies
+// and exponentials run while the other wave's products keep the matrix core
+// busy.  The register file then holds two waves of at most 256 registers, so
+// a wave cannot keep both all of its queries' Q^T fragments and all of their
+// output columns; the two waves of a SIMD share 32 query rows instead.
+//
+// Work decomposition.  A workgroup of 8 waves owns 128 query rows of one head.
+// Wave w serves query block pq = w % 4 (rows 32 pq .. 32 pq + 31) as member
+// hh = w / 4 of a pair.  The key axis is walked in super-steps of 64 keys;
+// member hh owns key tile hh (32 keys) of each super-step for the first
+// product and the 32-column output blocks 2b + hh for the second:
+//   S^T_hh  = K_hh Q^T                      32 keys x 32 queries, full head dim
+//   C~'^T_hh = S^T_hh (.) D'^T_hh,  b += column sums            (Eqs. 81-83)
+//   members swap bf16(C~'^T) through LDS (2 KiB each)
+//   O^T[own columns] += V^T[own columns, 64 keys] C~'^T[64 keys]
+// so the matrix-core work per SIMD equals that of one wave with all columns,
+// nothing is computed twice, and a wave holds the full Q^T (the B operand of
+// the first product) but only half of the accumulators.  The row sums b of
+// the two members are added once, at the end, in a fixed order.
+//
+// Data movement.  One K tile and one V tile of 64 keys live in LDS, each
+// refilled while the other is read: during the first product of super-step
+// s the copies bring V_s, during the second they bring K_{s+1} and its gate
+// terms; each refill is spread over the matrix instructions of that phase.
+// Copies are buffer_load_dwordx4 ... lds (global -> LDS, no registers), 1 KiB
+// per instruction, issued through inline assembly so that the compiler does
+// not wait for them before unrelated LDS reads; the kernel waits for its own
+// copies (vmcnt) before each barrier.  The 16-byte chunks of a row are
+// permuted (XOR with a function of the row) so that the fragment reads of
+// both products are free of bank conflicts; the permutation is applied by
+// choosing which global chunk each lane fetches.
+//
+// Exponents.  On a tile below the diagonal the exponent factors as
+// 2^(base_i + keyb_J) * e_j with e_j from the gate scan (one exponential per
+// query row and tile); on a diagonal tile every entry takes its own
+// exponential under the causal mask (Eq. 71).
+#include "mlstm_internal.h"
+#include "tile_common.h"
+
+namespace mlstm {
+namespace {
+
+using namespace tilecommon;
+
+constexpr int kWThreads = 512;  // 8 waves: two per SIMD
+constexpr int kWWaves = kWThreads / 64;
+constexpr int kSK = 64;   // keys per super-step (two 32-key tiles)
+constexpr int kWPf = 2;   // LDS fragment prefetch distance (MFMA steps)
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// buffer resource words: offsets at or past num_records bytes read as zeros
+__device__ inline i32x4 rsrc_words(const void* base, int64_t num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const int n = num_records > 0x7FFFFFFF ? 0x7FFFFFFF : int(num_records);
+  return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xFFFFu), n, kRsrcFlags};
+}
+__device__ inline unsigned lds_addr(const char* p) {
+  return unsigned(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+// 16 bytes per active lane, global -> LDS at (wave-uniform) dst + 16 * lane.
+// M0 holds the LDS destination; one wait state separates its write from the copy.
+__device__ inline void copy16(i32x4 rsrc, unsigned voffset, unsigned dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(dst), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+// 4 bytes per active lane to dst + 4 * lane
+__device__ inline void copy4(i32x4 rsrc, unsigned voffset, unsigned dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(dst), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// LDS layout of a tile: rows of ROW bytes, ROW = 2 DP rounded up to an odd
+// multiple of 128 (rows alternate between bank offsets 0 and 128); the 16-byte
+// chunk p of row r sits at slot p ^ sw(r), a permutation inside aligned groups
+// of 8 chunks.  LDS serves 256 bytes per clock in 64 banks: a 16-byte read of
+// 16 lanes, or an 8-byte read of 32 lanes, is free of conflicts when the lanes
+// hit distinct 16-byte (8-byte) slots modulo 256 bytes.
+//  K (and Q, and the output staging): the fragment read of 16 lanes takes one
+//   chunk of 16 consecutive rows; row parity and sw_k = (r / 2) % 8 separate
+//   them.
+//  V: the transpose read of 32 lanes takes one 64-byte group (4 chunks) of the
+//   4 rows of an aligned quad; row parity and sw_v = 4 ((r / 2) % 2) put the
+//   four groups apart.  sw_v only flips chunk bit 2, i.e. byte bit 6.
+__device__ inline int swizzle_k(int r) { return (r >> 1) & 7; }
+__device__ inline int swizzle_v(int r) { return 4 * ((r >> 1) & 1); }
+
+template <int DP>
+struct WCfg {
+  static_assert(DP % 64 == 0 && DP >= 64 && DP <= 384, "head dim of the two-wave kernel");
+  static constexpr int CH = DP / 8;          // 16-byte chunks of data per row (a multiple of 8)
+  static constexpr int ROW = (2 * DP) % 256 == 0 ? 2 * DP + 128 : 2 * DP;  // LDS row bytes
+  static constexpr int CHP = ROW / 16;       // chunks per LDS row, padding included
+  static constexpr int TILE = kSK * ROW;     // one K or V tile of 64 keys
+  static constexpr int NCOPY = TILE / 1024;  // 1 KiB copies per tile
+  static constexpr int CPW = NCOPY / kWWaves;  // copies per wave per tile
+  static constexpr int NB = DP / 64;         // 32-column output blocks per wave
+  static constexpr int NS = DP / 16;         // MFMA steps of S^T
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = TILE;
+  static constexpr int GC = 2 * TILE;        // c_j of the K tile's 64 keys (float32)
+  static constexpr int GE = GC + 256;        // e_j (float32)
+  static constexpr int GA = GC + 512;        // float64 anchor of the 64 keys
+  static constexpr int GB = GC + 528;        // keyb of the two 32-key tiles
+  static constexpr int X_OFF = GC + 544;     // bf16(C~'^T) exchange, 2 KiB per wave
+  static constexpr int BYTES = X_OFF + kWWaves * 2048;
+  static_assert(NCOPY % kWWaves == 0, "copies divide among the waves");
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// global byte offset fetched by `lane` for copy n of a 64-key tile: LDS slot
+// 64 n + lane holds row r, slot q, i.e. logical chunk q ^ sw(r) of key row r
+template <int DP, bool IS_V>
+__device__ inline unsigned tile_src(int n, int lane, int d, int dch) {
+  constexpr int CHP = WCfg<DP>::CHP;
+  const int idx = 64 * n + lane;
+  const int r = idx / CHP;
+  const int slot = idx - r * CHP;
+  const int p = slot ^ (IS_V ? swizzle_v(r) : swizzle_k(r));  // padding maps to padding
+  return p < dch ? unsigned(r * d * 2 + 16 * p) : kOutOfRange;
+}
+
+template <int DP>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
+                          amdgpu_waves_per_eu(2, 2))) void tiles_pairs_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    const float* __restrict__ m_in, const double* __restrict__ anchor,
+    const float* __restrict__ rowt, const float* __restrict__ colt,
+    const float* __restrict__ colx, u16* __restrict__ h_out, const float* __restrict__ rowb,
+    const float* __restrict__ keyb, float* __restrict__ n_out, const u16* __restrict__ ogate,
+    u16* __restrict__ htilde, float* __restrict__ b_out, int T, int d, int Tp, int nblk,
+    int row_tiles, int H, int skip) {
+  using C = WCfg<DP>;
+  __shared__ __attribute__((aligned(1024))) char lds[C::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pq = w & 3;       // query block of this wave's pair
+  const int hh = w >> 2;      // member: key tile of each super-step, output-column half
+  const int g = lane >> 5;    // half-wave: selects 8 of the 16 reduction indices
+  const int l32 = lane & 31;  // query column of this lane
+  const int j16 = l32 & 15;
+  int64_t I64, head64;
+  map_tile(blockIdx.x, row_tiles, H, I64, head64);
+  const int I = int(I64), head = int(head64);
+  const int64_t hoff = int64_t(head) * T * d;
+  const int q0 = I * kBM;
+  const int qw = q0 + 32 * pq;  // first query row of this pair
+  const int qi = qw + l32;      // query row of this lane
+  const int dch = d / 8;            // real 16-byte chunks per row
+
+  // Q^T fragments (full head dim): B operand of S^T = K Q^T, read from the
+  // workgroup's Q block staged in LDS by the prologue
+  bf16x8 qf[C::NS];
+  const float r_i = rowt[int64_t(head) * Tp + qi];
+  // the pair's anchor (uniform across the wave)
+  double a_i = anchor[int64_t(head) * nblk + qw / kAnchorBlock];
+  {
+    const uint64_t bits = __builtin_bit_cast(uint64_t, a_i);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(bits));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(bits >> 32));
+    a_i = __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+  }
+
+  f32x16 acc[C::NB];
+#pragma unroll
+  for (int b = 0; b < C::NB; ++b) acc[b] = f32x16{};
+  float bsum = 0.0f;
+
+  const int n_key_tiles = int((T + kBN - 1) / kBN);
+  const int It = int(I);
+  const int last_tile = (4 * It + 3 < n_key_tiles - 1) ? 4 * It + 3 : n_key_tiles - 1;
+  const int pair_last = (4 * It + pq < n_key_tiles - 1) ? 4 * It + pq : n_key_tiles - 1;
+
+  const int nb32 = Tp / kBoundTile;
+  // ---- copies.  Tile of super-step s: key rows [64 s, 64 s + 64); the
+  // buffer range ends at the sequence end, so rows past it arrive as zeros.
+  auto tile_rsrc = [&](const u16* base, int s) {
+    const int k0 = s * kSK;
+    const int rows = T - k0 < kSK ? T - k0 : kSK;
+    return rsrc_words(base + hoff + int64_t(k0) * d, int64_t(rows) * d * 2);
+  };
+  // copy u of this wave: slot w + 8u of the tile whose first slot of this wave
+  // is `dst`.  dst is made opaque once per phase, so that the compiler forms
+  // each copy's LDS address there instead of keeping all of them in scalar
+  // registers across the loop.
+  // The lane index is made opaque at each copy too: the source offsets are
+  // then formed next to their copy, not held in registers across the loop.
+  auto copy_k = [&](const i32x4& rs, unsigned dst, int u) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    copy16(rs, tile_src<DP, false>(w + kWWaves * u, ln, d, dch), dst + 1024 * kWWaves * u);
+  };
+  auto copy_v = [&](const i32x4& rs, unsigned dst, int u) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    copy16(rs, tile_src<DP, true>(w + kWWaves * u, ln, d, dch), dst + 1024 * kWWaves * u);
+  };
+  auto wave_slot = [&](int region) {
+    unsigned a = lds_addr(lds + region) + 1024 * w;
+    asm volatile("" : "+s"(a));
+    return a;
+  };
+  // gate terms of super-step s: one small copy each for waves 0..3
+  auto copy_gates = [&](int s) {
+    const int k0 = s * kSK;
+    if (w == 0 && lane < 16)
+      copy16(rsrc_words(colt + int64_t(head) * Tp + k0, kSK * 4), unsigned(16 * lane),
+             lds_addr(lds + C::GC));
+    if (w == 1 && lane < 16)
+      copy16(rsrc_words(colx + int64_t(head) * Tp + k0, kSK * 4), unsigned(16 * lane),
+             lds_addr(lds + C::GE));
+    if (w == 2 && lane < 2)
+      copy4(rsrc_words(anchor + int64_t(head) * nblk + k0 / kAnchorBlock, 8), unsigned(4 * lane),
+            lds_addr(lds + C::GA));
+    if (w == 3 && lane < 2)
+      copy4(rsrc_words(keyb + int64_t(head) * nb32 + k0 / kBoundTile, 8), unsigned(4 * lane),
+            lds_addr(lds + C::GB));
+  };
+
+  // ---- the workgroup's Q block (128 rows, contiguous in memory) is copied
+  // into the K and V regions with the tiles' chunk permutation, overlapping
+  // the first-tile search; the prologue reads the Q^T fragments from there.
+  {
+    const int rows = T - q0 < kBM ? T - q0 : kBM;
+    const i32x4 rq = rsrc_words(q + hoff + int64_t(q0) * d, int64_t(rows) * d * 2);
+    const unsigned qdst = wave_slot(C::K_OFF);
+#pragma unroll
+    for (int u = 0; u < 2 * C::CPW; ++u) copy_k(rq, qdst, u);
+  }
+
+  // ---- decay-aware start of the key loop: the first 32-key tile some pair
+  // needs (the bound of mlstm_internal.h); inside the loop each member skips
+  // the products of tiles its rows do not need.
+  const float rb_w = __builtin_bit_cast(
+      float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, rowb[int64_t(head) * nb32 + qw / kBoundTile])));
+  auto tile_needed = [&](double a_row, float rb, double a_key, float kb) {
+    return float(a_row - a_key) + rb + kb >= kSkipLog2;
+  };
+  int first_tile = 0;
+  if (skip) {
+    __shared__ int s_first[kWWaves];
+    double a_rows[4];
+    float rb_rows[4];
+    int last_p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int qu = q0 + 32 * u;
+      a_rows[u] = anchor[int64_t(head) * nblk + qu / kAnchorBlock];
+      rb_rows[u] = rowb[int64_t(head) * nb32 + qu / kBoundTile];
+      last_p[u] = (4 * It + u < n_key_tiles - 1) ? 4 * It + u : n_key_tiles - 1;
+    }
+    int mine = last_tile;
+    for (int J = tid; J < last_tile; J += kWThreads) {
+      const double a_key = anchor[int64_t(head) * nblk + (J * kBN) / kAnchorBlock];
+      const float kb = keyb[int64_t(head) * nb32 + J];
+      bool need = false;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        need = need || (J <= last_p[u] && tile_needed(a_rows[u], rb_rows[u], a_key, kb));
+      if (need) {
+        mine = J;
+        break;  // J grows with each iteration: the first hit is this thread's least
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const int o = __shfl_xor(mine, off, 64);
+      mine = o < mine ? o : mine;
+    }
+    if (lane == 0) s_first[w] = mine;
+    __syncthreads();
+    first_tile = s_first[0];
+#pragma unroll
+    for (int u = 1; u < kWWaves; ++u) first_tile = s_first[u] < first_tile ? s_first[u] : first_tile;
+    first_tile = __builtin_amdgcn_readfirstlane(first_tile);
+  }
+  const int s_first_step = first_tile / 2;
+  const int s_last_step = last_tile / 2;
+
+  // per-lane LDS offsets of the fragment reads.
+  // K: row R = 32 hh + l32, logical chunk 2t + g at slot (2t + g) ^ sw_k(R),
+  //    sw_k(R) = sw_k(l32); the byte offset within the row is
+  //    128 (t / 4) + ((32 (t % 4)) ^ 16 (g ^ sw_k)), and the row start is a
+  //    multiple of 128, so the XOR acts on the sum: four bases, t / 4 is an
+  //    immediate offset.
+  const int kx = 16 * (g ^ swizzle_k(l32));
+  int kb4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) kb4[u] = (C::K_OFF + (32 * hh + l32) * C::ROW + kx) ^ (32 * u);
+  // V^T gather (ds_read_b64_tr_b16): rows 16c + 4g + j (+8) of a key tile,
+  // j = j16 / 4, bytes 64 m + 16 y + 8 (j16 % 2) with m the 64-byte index of
+  // the 32-column block and y = 2 (l32 / 16) + (j16 % 4) / 2.  Member hh owns
+  // the blocks m = 2b + hh, so the permutation (flip byte bit 6 when
+  // sw_v(row) = 4, i.e. when j >= 2) combines with m % 2 = hh into one
+  // per-wave base; block b adds 128 b.
+  const int vj = j16 >> 2;
+  const int vrow = C::V_OFF + (4 * g + vj) * C::ROW +
+                   ((32 * (l32 >> 4) + 16 * ((j16 & 3) >> 1)) ^ (16 * swizzle_v(vj)) ^ (64 * hh)) +
+                   8 * (j16 & 1);
+  const int vown = vrow + 32 * hh * C::ROW;
+  const int vpart = vrow + 32 * (hh ^ 1) * C::ROW;
+  char* const xmine = lds + C::X_OFF + 2048 * w;
+  const char* const xpart = lds + C::X_OFF + 2048 * (w ^ 4);
+
+  // ---- prologue: each wave reads its Q^T fragments (like K fragments) from
+  // the staged Q block; then K and the gate terms of the first super-step are
+  // copied into the K region.
+  {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int qbase = C::K_OFF + (32 * pq + l32) * C::ROW + kx;
+#pragma unroll
+    for (int t = 0; t < C::NS; ++t)
+      qf[t] = *reinterpret_cast<const bf16x8*>(lds + (qbase ^ (32 * (t & 3))) + 128 * (t >> 2));
+    __syncthreads();  // the region is refilled below
+  }
+  {
+    const i32x4 rk = tile_rsrc(k, s_first_step);
+    const unsigned kdst = wave_slot(C::K_OFF);
+#pragma unroll
+    for (int u = 0; u < C::CPW; ++u) copy_k(rk, kdst, u);
+    copy_gates(s_first_step);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  for (int s = s_first_step; s <= s_last_step; ++s) {
+    // ===== phase 1: K_s and its gate terms are resident; copies bring V_s =====
+    const double a_key = *reinterpret_cast<const double*>(lds + C::GA);
+    // whether this member's and the partner's key tiles reach the pair's rows
+    auto member_needs = [&](int hk) {
+      const int J = 2 * s + hk;
+      const float kb = *reinterpret_cast<const float*>(lds + C::GB + 4 * hk);
+      const bool nd = J <= pair_last && (!skip || tile_needed(a_i, rb_w, a_key, kb));
+      return __builtin_amdgcn_readfirstlane(int(nd)) != 0;
+    };
+    const bool need_own = member_needs(hh);
+    const bool need_part = member_needs(hh ^ 1);
+    const i32x4 rv = tile_rsrc(v, s);
+    const unsigned vdst = wave_slot(C::V_OFF);
+    constexpr int STRIDE1 = C::NS / C::CPW;  // MFMA steps between two copies
+    bf16x8 pown[2];
+    if (need_own) {
+      f32x16 st = f32x16{};
+      bf16x8 kf[kWPf + 1];
+      auto kaddr = [&](int t) { return lds + kb4[t & 3] + 128 * (t >> 2); };
+#pragma unroll
+      for (int t = 0; t < kWPf && t < C::NS; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(kaddr(t));
+#pragma unroll
+      for (int t = 0; t < C::NS; ++t) {
+        if (t + kWPf < C::NS)
+          kf[(t + kWPf) % (kWPf + 1)] = *reinterpret_cast<const bf16x8*>(kaddr(t + kWPf));
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kWPf + 1)], qf[t], st, 0, 0, 0);
+        if (t % STRIDE1 == 0 && t / STRIDE1 < C::CPW) copy_v(rv, vdst, t / STRIDE1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // lane (g, l32), register r holds S^T[key 8(r/4) + 4g + r%4][query l32]
+      const float base = float(a_i - a_key) + r_i;
+      const bool diag = (2 * s + hh) * kBN == qw;
+      const float* gc = reinterpret_cast<const float*>(lds + C::GC) + 32 * hh;
+      const float* ge = reinterpret_cast<const float*>(lds + C::GE) + 32 * hh;
+      // C~' = S (.) D' in place of S (Eq. 82), b += C~' (Eq. 83)
+      if (diag) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const float4 c4 = *reinterpret_cast<const float4*>(gc + 8 * rq + 4 * g);
+          const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = 8 * rq + 4 * g + e;
+            const float ex = key > l32 ? -INFINITY : base + cc[e];  // causal mask (Eq. 71)
+            st[4 * rq + e] *= __builtin_amdgcn_exp2f(ex);
+            bsum += st[4 * rq + e];
+          }
+        }
+      } else {
+        const float kb = *reinterpret_cast<const float*>(lds + C::GB + 4 * hh);
+        const float ei = __builtin_amdgcn_exp2f(base + kb);
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const float4 e4 = *reinterpret_cast<const float4*>(ge + 8 * rq + 4 * g);
+          const float ee[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            st[4 * rq + e] *= ei * ee[e];
+            bsum += st[4 * rq + e];
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pown[0][e] = (__bf16)st[e];
+        pown[1][e] = (__bf16)st[8 + e];
+      }
+      *reinterpret_cast<bf16x8*>(xmine + 16 * lane) = pown[0];
+      *reinterpret_cast<bf16x8*>(xmine + 1024 + 16 * lane) = pown[1];
+    } else {
+#pragma unroll
+      for (int u = 0; u < C::CPW; ++u) copy_v(rv, vdst, u);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ===== phase 2: V_s is resident; copies bring K_{s+1} and its gate terms =====
+    const bool more = s < s_last_step;
+    const i32x4 rk = tile_rsrc(k, more ? s + 1 : s);
+    const unsigned kdst = wave_slot(C::K_OFF);
+    // The products run even when neither key tile reaches the pair's rows
+    // (their operands are then zero): a branch around them would make the
+    // compiler copy the accumulators.
+    {
+      const bf16x8 zero8 = bf16x8{};
+      bf16x8 ppart[2] = {zero8, zero8};
+      if (need_part) {
+        ppart[0] = *reinterpret_cast<const bf16x8*>(xpart + 16 * lane);
+        ppart[1] = *reinterpret_cast<const bf16x8*>(xpart + 1024 + 16 * lane);
+      }
+      if (!need_own) pown[0] = pown[1] = zero8;
+      // O^T[own columns] += V^T C~'^T over the 64 keys, this member's key
+      // tile first.  Step t = (column block b, key quarter c4): quarters 0, 1
+      // are the own tile's keys 16 c + [0, 16), quarters 2, 3 the partner's;
+      // the A operand holds V[16 c + 4g + 0..3][col + l32] and
+      // V[16 c + 8 + 4g + 0..3][col + l32] of that tile.
+      constexpr int NV = 4 * C::NB;
+      constexpr int STRIDE2 = NV / C::CPW;
+      auto vaddr = [&](int t) {
+        const int b = t >> 2, c4 = t & 3;
+        return lds + (c4 < 2 ? vown : vpart) + 128 * b + 16 * (c4 & 1) * C::ROW;
+      };
+      i16x4 vlo[kWPf + 1], vhi[kWPf + 1];
+#pragma unroll
+      for (int t = 0; t < kWPf && t < NV; ++t) {
+        vlo[t] = tr_read(vaddr(t));
+        vhi[t] = tr_read(vaddr(t) + 8 * C::ROW);
+      }
+#pragma unroll
+      for (int t = 0; t < NV; ++t) {
+        const int tn = t + kWPf;
+        if (tn < NV) {
+          vlo[tn % (kWPf + 1)] = tr_read(vaddr(tn));
+          vhi[tn % (kWPf + 1)] = tr_read(vaddr(tn) + 8 * C::ROW);
+        }
+        const i16x8 a16 = __builtin_shufflevector(vlo[t % (kWPf + 1)], vhi[t % (kWPf + 1)], 0, 1,
+                                                  2, 3, 4, 5, 6, 7);
+        const int c4 = t & 3;
+        const bf16x8 bop = c4 == 0 ? pown[0] : c4 == 1 ? pown[1] : c4 == 2 ? ppart[0] : ppart[1];
+        acc[t >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16), bop,
+                                                              acc[t >> 2], 0, 0, 0);
+        if (more && t % STRIDE2 == 0 && t / STRIDE2 < C::CPW) copy_k(rk, kdst, t / STRIDE2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (more) copy_gates(s + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // ---- epilogue: b of the pair (member 0's keys first), n (Eq. 84),
+  // h~ = acc / n (Eqs. 85, 86), output gate (Eq. 78) on this member's columns
+  bsum += __shfl_xor(bsum, 32, 64);
+  const float m_q = qi < T ? m_in[int64_t(head) * T + qi] : 0.0f;
+  reinterpret_cast<float*>(xmine)[lane] = bsum;
+  __syncthreads();
+  const float bpart = reinterpret_cast<const float*>(xpart)[lane];
+  const float btot = hh == 0 ? bsum + bpart : bpart + bsum;
+  const float nn = fmaxf(fabsf(btot), expf(-m_q));
+  const float inv = 1.0f / nn;
+  if (qi < T && g == 0 && hh == 0) {
+    n_out[int64_t(head) * T + qi] = nn;
+    if (b_out) b_out[int64_t(head) * T + qi] = btot;
+  }
+  if (ogate == nullptr && htilde == nullptr) {
+    // bf16(h~) goes through LDS (the tile regions are free now): row
+    // 32 pq + l32 of the block, logical 16-byte chunk c at slot c ^ sw(row);
+    // then the block's rows, contiguous in memory, are stored 1 KiB per
+    // instruction.  Rows past the sequence end fall outside the buffer range
+    // and are not written.
+    const int orow = C::K_OFF + (32 * pq + l32) * C::ROW + 8 * g;
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int col = 32 * (2 * b + hh) + 8 * rq + 4 * g;
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[b][4 * rq + e] * inv);
+        *reinterpret_cast<bf16x4*>(lds + orow + 16 * ((col >> 3) ^ swizzle_k(l32))) = o;
+      }
+    }
+    __syncthreads();
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const int rows = T - q0 < kBM ? T - q0 : kBM;
+    const auto rh = make_rsrc(h_out + hoff + int64_t(q0) * d, int64_t(rows) * d * 2);
+    const int nstore = d / 4;  // 1 KiB stores of the 128 x d block
+    const int row_bytes = 2 * d;
+#pragma unroll
+    for (int u = 0; u < (DP / 4 + kWWaves - 1) / kWWaves; ++u) {
+      const int n = w + kWWaves * u;
+      if (n < nstore) {
+        const int gb = 1024 * n + 16 * lane;
+        const int r = gb / row_bytes;
+        const int c = (gb - r * row_bytes) >> 4;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(
+            lds + C::K_OFF + r * C::ROW + 16 * (c ^ swizzle_k(r)));
+        __builtin_amdgcn_raw_buffer_store_b128(val, rh, gb, 0, 0);
+      }
+    }
+  } else if (qi < T) {
+    const int64_t row = hoff + int64_t(qi) * d;
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int col = 32 * (2 * b + hh) + 8 * rq + 4 * g;
+        if (col < d) {
+          float hv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] = acc[b][4 * rq + e] * inv;
+          bf16x4 o;
+          if (htilde) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (__bf16)hv[e];
+            *reinterpret_cast<bf16x4*>(htilde + row + col) = o;
+          }
+          if (ogate) {
+            const bf16x4 og = *reinterpret_cast<const bf16x4*>(ogate + row + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hv[e] *= 1.0f / (1.0f + __expf(-float(og[e])));
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (__bf16)hv[e];
+          *reinterpret_cast<bf16x4*>(h_out + row + col) = o;
+        }
+      }
+    }
+  }
+}
+
+template <int DP>
+hipError_t launch_w(const void* q, const void* k, const void* v, const float* m,
+                    const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep, bool skip,
+                    int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+  const int64_t row_tiles = (T + kBM - 1) / kBM;
+  hipLaunchKernelGGL(tiles_pairs_kernel<DP>, dim3(unsigned(row_tiles * H)), dim3(kWThreads), 0,
+                     stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                     static_cast<const u16*>(v), m, ws.anchor, ws.rowt, ws.colt, ws.colx,
+                     static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
+                     static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), ep.b, T,
+                     int(d), int(ws.Tp), int(ws.nblk), int(row_tiles), int(H), int(skip));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool tiles_pairs_supports(int64_t d) { return d % 16 == 0 && d >= 16 && d <= 384; }
+
+hipError_t launch_tiles_pairs(const void* q, const void* k, const void* v, const float* m,
+                              const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,
+                              bool skip, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+  if (!tiles_pairs_supports(d)) return hipErrorInvalidValue;
+  // head dims are padded up to a multiple of 64 (zero columns add nothing)
+  switch ((d + 63) / 64) {
+    case 1: return launch_w<64>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 2: return launch_w<128>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 3: return launch_w<192>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 4: return launch_w<256>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 5: return launch_w<320>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 6: return launch_w<384>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mlstm
