@@ -28,13 +28,10 @@
 // refilled while the other is read: during the first product of super-step
 // s the copies bring V_s, during the second they bring K_{s+1} and its gate
 // terms; each refill is spread over the matrix instructions of that phase.
-// Copies are buffer_load_dwordx4 ... lds (global -> LDS, no registers), 1 KiB
-// per instruction, issued through inline assembly so that the compiler does
-// not wait for them before unrelated LDS reads; the kernel waits for its own
-// copies (vmcnt) before each barrier.  The 16-byte chunks of a row are
-// permuted (XOR with a function of the row) so that the fragment reads of
-// both products are free of bank conflicts; the permutation is applied by
-// choosing which global chunk each lane fetches.
+// Copies are buffer_load_dwordx4 ... lds (global -> LDS, no registers), one
+// padded row per instruction, issued through inline assembly so that the
+// compiler does not wait for them before unrelated LDS reads; the kernel
+// waits for its own copies (vmcnt) before each barrier.
 //
 // Exponents.  On a tile below the diagonal the exponent factors as
 // 2^(base_i + keyb_J) * e_j with e_j from the gate scan (one exponential per
@@ -80,55 +77,38 @@ __device__ inline void copy4(i32x4 rsrc, unsigned voffset, unsigned dst) {
                : "memory", "m0");
 }
 
-// LDS layout of a tile: rows of ROW bytes, ROW = 2 DP rounded up to an odd
-// multiple of 128 (rows alternate between bank offsets 0 and 128); the 16-byte
-// chunk p of row r sits at slot p ^ sw(r), a permutation inside aligned groups
-// of 8 chunks.  LDS serves 256 bytes per clock in 64 banks: a 16-byte read of
-// 16 lanes, or an 8-byte read of 32 lanes, is free of conflicts when the lanes
-// hit distinct 16-byte (8-byte) slots modulo 256 bytes.
-//  K (and Q, and the output staging): the fragment read of 16 lanes takes one
-//   chunk of 16 consecutive rows; row parity and sw_k = (r / 2) % 8 separate
-//   them.
-//  V: the transpose read of 32 lanes takes one 64-byte group (4 chunks) of the
-//   4 rows of an aligned quad; row parity and sw_v = 4 ((r / 2) % 2) put the
-//   four groups apart.  sw_v only flips chunk bit 2, i.e. byte bit 6.
-__device__ inline int swizzle_k(int r) { return (r >> 1) & 7; }
-__device__ inline int swizzle_v(int r) { return 4 * ((r >> 1) & 1); }
-
+// LDS layout: rows are padded so that the fragment reads are free of bank
+// conflicts (LDS serves 256 bytes per clock in 64 banks; a 16-byte read of
+// 16 lanes, or an 8-byte read of 32 lanes, is conflict-free when the lanes hit
+// distinct 16-byte, resp. 8-byte, slots modulo 256 bytes):
+//  K rows (and the staged Q and output blocks): stride 2 DP + 16; the K
+//   fragment read takes one 16-byte chunk of 16 consecutive rows, which then
+//   start 16 (CH + 1) bytes apart with CH + 1 odd: 16 distinct slots.
+//  V rows: stride 2 DP + 64; the transpose read takes one 64-byte group of
+//   each of the 4 rows of an aligned quad, 64 (DP / 32 + 1) bytes apart with
+//   DP / 32 + 1 odd: 4 distinct groups.
+// Each row is copied by one instruction whose lanes fetch consecutive 16-byte
+// chunks, so a copy needs no per-lane address arithmetic.
 template <int DP>
 struct WCfg {
   static_assert(DP % 64 == 0 && DP >= 64 && DP <= 384, "head dim of the two-wave kernel");
-  static constexpr int CH = DP / 8;          // 16-byte chunks of data per row (a multiple of 8)
-  static constexpr int ROW = (2 * DP) % 256 == 0 ? 2 * DP + 128 : 2 * DP;  // LDS row bytes
-  static constexpr int CHP = ROW / 16;       // chunks per LDS row, padding included
-  static constexpr int TILE = kSK * ROW;     // one K or V tile of 64 keys
-  static constexpr int NCOPY = TILE / 1024;  // 1 KiB copies per tile
-  static constexpr int CPW = NCOPY / kWWaves;  // copies per wave per tile
+  static constexpr int CH = DP / 8;          // 16-byte chunks per row
+  static constexpr int RSK = 2 * DP + 16;    // K row stride (bytes)
+  static constexpr int RSV = 2 * DP + 64;    // V row stride
   static constexpr int NB = DP / 64;         // 32-column output blocks per wave
   static constexpr int NS = DP / 16;         // MFMA steps of S^T
+  static constexpr int RPW = kSK / kWWaves;  // rows of a 64-key tile copied per wave
   static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = TILE;
-  static constexpr int GC = 2 * TILE;        // c_j of the K tile's 64 keys (float32)
+  static constexpr int V_OFF = kSK * RSK;
+  static constexpr int GC = V_OFF + kSK * RSV;  // c_j of the K tile's 64 keys (float32)
   static constexpr int GE = GC + 256;        // e_j (float32)
   static constexpr int GA = GC + 512;        // float64 anchor of the 64 keys
   static constexpr int GB = GC + 528;        // keyb of the two 32-key tiles
   static constexpr int X_OFF = GC + 544;     // bf16(C~'^T) exchange, 2 KiB per wave
   static constexpr int BYTES = X_OFF + kWWaves * 2048;
-  static_assert(NCOPY % kWWaves == 0, "copies divide among the waves");
+  static_assert(2 * kSK * RSK <= GC, "the staged Q block fits in the K and V regions");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
-
-// global byte offset fetched by `lane` for copy n of a 64-key tile: LDS slot
-// 64 n + lane holds row r, slot q, i.e. logical chunk q ^ sw(r) of key row r
-template <int DP, bool IS_V>
-__device__ inline unsigned tile_src(int n, int lane, int d, int dch) {
-  constexpr int CHP = WCfg<DP>::CHP;
-  const int idx = 64 * n + lane;
-  const int r = idx / CHP;
-  const int slot = idx - r * CHP;
-  const int p = slot ^ (IS_V ? swizzle_v(r) : swizzle_k(r));  // padding maps to padding
-  return p < dch ? unsigned(r * d * 2 + 16 * p) : kOutOfRange;
-}
 
 template <int DP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
@@ -186,31 +166,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
   const int nb32 = Tp / kBoundTile;
   // ---- copies.  Tile of super-step s: key rows [64 s, 64 s + 64); the
   // buffer range ends at the sequence end, so rows past it arrive as zeros.
-  auto tile_rsrc = [&](const u16* base, int s) {
-    const int k0 = s * kSK;
-    const int rows = T - k0 < kSK ? T - k0 : kSK;
-    return rsrc_words(base + hoff + int64_t(k0) * d, int64_t(rows) * d * 2);
+  // one row per copy: lanes [0, CH) fetch the row's 16-byte chunks (chunks
+  // past the real head dimension read as zeros), lanes past CH stay idle.  A
+  // row past the sequence end gets an empty buffer range and arrives as zeros.
+  const unsigned vchunk = lane < dch ? unsigned(16 * lane) : kOutOfRange;
+  auto copy_row = [&](const u16* src, int row, unsigned dst) {
+    const i32x4 rs = rsrc_words(src + hoff + int64_t(row) * d, row < T ? 2 * d : 0);
+    if (lane < C::CH) copy16(rs, vchunk, dst);
   };
-  // copy u of this wave: slot w + 8u of the tile whose first slot of this wave
-  // is `dst`.  dst is made opaque once per phase, so that the compiler forms
-  // each copy's LDS address there instead of keeping all of them in scalar
-  // registers across the loop.
-  // The lane index is made opaque at each copy too: the source offsets are
-  // then formed next to their copy, not held in registers across the loop.
-  auto copy_k = [&](const i32x4& rs, unsigned dst, int u) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    copy16(rs, tile_src<DP, false>(w + kWWaves * u, ln, d, dch), dst + 1024 * kWWaves * u);
+  // row i (0 <= i < RPW) of this wave's share of the 64-key tile of super-step s
+  auto copy_k = [&](int s, int i) {
+    const int r = w + kWWaves * i;
+    copy_row(k, s * kSK + r, lds_addr(lds + C::K_OFF + r * C::RSK));
   };
-  auto copy_v = [&](const i32x4& rs, unsigned dst, int u) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    copy16(rs, tile_src<DP, true>(w + kWWaves * u, ln, d, dch), dst + 1024 * kWWaves * u);
-  };
-  auto wave_slot = [&](int region) {
-    unsigned a = lds_addr(lds + region) + 1024 * w;
-    asm volatile("" : "+s"(a));
-    return a;
+  auto copy_v = [&](int s, int i) {
+    const int r = w + kWWaves * i;
+    copy_row(v, s * kSK + r, lds_addr(lds + C::V_OFF + r * C::RSV));
   };
   // gate terms of super-step s: one small copy each for waves 0..3
   auto copy_gates = [&](int s) {
@@ -232,12 +203,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
   // ---- the workgroup's Q block (128 rows, contiguous in memory) is copied
   // into the K and V regions with the tiles' chunk permutation, overlapping
   // the first-tile search; the prologue reads the Q^T fragments from there.
-  {
-    const int rows = T - q0 < kBM ? T - q0 : kBM;
-    const i32x4 rq = rsrc_words(q + hoff + int64_t(q0) * d, int64_t(rows) * d * 2);
-    const unsigned qdst = wave_slot(C::K_OFF);
 #pragma unroll
-    for (int u = 0; u < 2 * C::CPW; ++u) copy_k(rq, qdst, u);
+  for (int i = 0; i < kBM / kWWaves; ++i) {
+    const int r = w + kWWaves * i;
+    copy_row(q, q0 + r, lds_addr(lds + C::K_OFF + r * C::RSK));
   }
 
   // ---- decay-aware start of the key loop: the first 32-key tile some pair
@@ -290,27 +259,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
   const int s_last_step = last_tile / 2;
 
   // per-lane LDS offsets of the fragment reads.
-  // K: row R = 32 hh + l32, logical chunk 2t + g at slot (2t + g) ^ sw_k(R),
-  //    sw_k(R) = sw_k(l32); the byte offset within the row is
-  //    128 (t / 4) + ((32 (t % 4)) ^ 16 (g ^ sw_k)), and the row start is a
-  //    multiple of 128, so the XOR acts on the sum: four bases, t / 4 is an
-  //    immediate offset.
-  const int kx = 16 * (g ^ swizzle_k(l32));
-  int kb4[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) kb4[u] = (C::K_OFF + (32 * hh + l32) * C::ROW + kx) ^ (32 * u);
-  // V^T gather (ds_read_b64_tr_b16): rows 16c + 4g + j (+8) of a key tile,
-  // j = j16 / 4, bytes 64 m + 16 y + 8 (j16 % 2) with m the 64-byte index of
-  // the 32-column block and y = 2 (l32 / 16) + (j16 % 4) / 2.  Member hh owns
-  // the blocks m = 2b + hh, so the permutation (flip byte bit 6 when
-  // sw_v(row) = 4, i.e. when j >= 2) combines with m % 2 = hh into one
-  // per-wave base; block b adds 128 b.
-  const int vj = j16 >> 2;
-  const int vrow = C::V_OFF + (4 * g + vj) * C::ROW +
-                   ((32 * (l32 >> 4) + 16 * ((j16 & 3) >> 1)) ^ (16 * swizzle_v(vj)) ^ (64 * hh)) +
-                   8 * (j16 & 1);
-  const int vown = vrow + 32 * hh * C::ROW;
-  const int vpart = vrow + 32 * (hh ^ 1) * C::ROW;
+  // K: row 32 hh + l32, bytes 32 t + 16 g for MFMA step t (immediate offsets).
+  const int krow = C::K_OFF + (32 * hh + l32) * C::RSK + 16 * g;
+  // V^T gather (ds_read_b64_tr_b16, as in the one-wave kernel): rows
+  // 16 c + 4 g + j16 / 4 (+ 8) of a key tile, bytes 64 m + 32 (l32 / 16) +
+  // 8 (j16 % 4), with m = 2 b + hh the 64-byte index of this member's
+  // 32-column block b.
+  const int vrow = C::V_OFF + (4 * g + (j16 >> 2)) * C::RSV + 32 * (l32 >> 4) + 8 * (j16 & 3) +
+                   64 * hh;
+  const int vown = vrow + 32 * hh * C::RSV;
+  const int vpart = vrow + 32 * (hh ^ 1) * C::RSV;
   char* const xmine = lds + C::X_OFF + 2048 * w;
   const char* const xpart = lds + C::X_OFF + 2048 * (w ^ 4);
 
@@ -320,17 +278,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
   {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int qbase = C::K_OFF + (32 * pq + l32) * C::ROW + kx;
+    const int qrow = C::K_OFF + (32 * pq + l32) * C::RSK + 16 * g;
 #pragma unroll
-    for (int t = 0; t < C::NS; ++t)
-      qf[t] = *reinterpret_cast<const bf16x8*>(lds + (qbase ^ (32 * (t & 3))) + 128 * (t >> 2));
+    for (int t = 0; t < C::NS; ++t) qf[t] = *reinterpret_cast<const bf16x8*>(lds + qrow + 32 * t);
     __syncthreads();  // the region is refilled below
   }
   {
-    const i32x4 rk = tile_rsrc(k, s_first_step);
-    const unsigned kdst = wave_slot(C::K_OFF);
 #pragma unroll
-    for (int u = 0; u < C::CPW; ++u) copy_k(rk, kdst, u);
+    for (int i = 0; i < C::RPW; ++i) copy_k(s_first_step, i);
     copy_gates(s_first_step);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -348,14 +303,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
     };
     const bool need_own = member_needs(hh);
     const bool need_part = member_needs(hh ^ 1);
-    const i32x4 rv = tile_rsrc(v, s);
-    const unsigned vdst = wave_slot(C::V_OFF);
-    constexpr int STRIDE1 = C::NS / C::CPW;  // MFMA steps between two copies
+    // the wave's RPW row copies are spread over the n matrix instructions of a phase
+    auto copies_at = [&](int t, int n, auto&& copy) {
+#pragma unroll
+      for (int i = 0; i < C::RPW; ++i)
+        if ((i * n) / C::RPW == t) copy(i);
+    };
     bf16x8 pown[2];
     if (need_own) {
       f32x16 st = f32x16{};
       bf16x8 kf[kWPf + 1];
-      auto kaddr = [&](int t) { return lds + kb4[t & 3] + 128 * (t >> 2); };
+      auto kaddr = [&](int t) { return lds + krow + 32 * t; };
 #pragma unroll
       for (int t = 0; t < kWPf && t < C::NS; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(kaddr(t));
 #pragma unroll
@@ -363,7 +321,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
         if (t + kWPf < C::NS)
           kf[(t + kWPf) % (kWPf + 1)] = *reinterpret_cast<const bf16x8*>(kaddr(t + kWPf));
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kWPf + 1)], qf[t], st, 0, 0, 0);
-        if (t % STRIDE1 == 0 && t / STRIDE1 < C::CPW) copy_v(rv, vdst, t / STRIDE1);
+        copies_at(t, C::NS, [&](int i) { copy_v(s, i); });
         __builtin_amdgcn_sched_barrier(0);
       }
       // lane (g, l32), register r holds S^T[key 8(r/4) + 4g + r%4][query l32]
@@ -408,15 +366,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
       *reinterpret_cast<bf16x8*>(xmine + 1024 + 16 * lane) = pown[1];
     } else {
 #pragma unroll
-      for (int u = 0; u < C::CPW; ++u) copy_v(rv, vdst, u);
+      for (int i = 0; i < C::RPW; ++i) copy_v(s, i);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // ===== phase 2: V_s is resident; copies bring K_{s+1} and its gate terms =====
     const bool more = s < s_last_step;
-    const i32x4 rk = tile_rsrc(k, more ? s + 1 : s);
-    const unsigned kdst = wave_slot(C::K_OFF);
+
     // The products run even when neither key tile reaches the pair's rows
     // (their operands are then zero): a branch around them would make the
     // compiler copy the accumulators.
@@ -434,23 +391,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
       // the A operand holds V[16 c + 4g + 0..3][col + l32] and
       // V[16 c + 8 + 4g + 0..3][col + l32] of that tile.
       constexpr int NV = 4 * C::NB;
-      constexpr int STRIDE2 = NV / C::CPW;
+
       auto vaddr = [&](int t) {
         const int b = t >> 2, c4 = t & 3;
-        return lds + (c4 < 2 ? vown : vpart) + 128 * b + 16 * (c4 & 1) * C::ROW;
+        return lds + (c4 < 2 ? vown : vpart) + 128 * b + 16 * (c4 & 1) * C::RSV;
       };
       i16x4 vlo[kWPf + 1], vhi[kWPf + 1];
 #pragma unroll
       for (int t = 0; t < kWPf && t < NV; ++t) {
         vlo[t] = tr_read(vaddr(t));
-        vhi[t] = tr_read(vaddr(t) + 8 * C::ROW);
+        vhi[t] = tr_read(vaddr(t) + 8 * C::RSV);
       }
 #pragma unroll
       for (int t = 0; t < NV; ++t) {
         const int tn = t + kWPf;
         if (tn < NV) {
           vlo[tn % (kWPf + 1)] = tr_read(vaddr(tn));
-          vhi[tn % (kWPf + 1)] = tr_read(vaddr(tn) + 8 * C::ROW);
+          vhi[tn % (kWPf + 1)] = tr_read(vaddr(tn) + 8 * C::RSV);
         }
         const i16x8 a16 = __builtin_shufflevector(vlo[t % (kWPf + 1)], vhi[t % (kWPf + 1)], 0, 1,
                                                   2, 3, 4, 5, 6, 7);
@@ -458,7 +415,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
         const bf16x8 bop = c4 == 0 ? pown[0] : c4 == 1 ? pown[1] : c4 == 2 ? ppart[0] : ppart[1];
         acc[t >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16), bop,
                                                               acc[t >> 2], 0, 0, 0);
-        if (more && t % STRIDE2 == 0 && t / STRIDE2 < C::CPW) copy_k(rk, kdst, t / STRIDE2);
+        if (more) copies_at(t, NV, [&](int i) { copy_k(s + 1, i); });
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -487,7 +444,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
     // then the block's rows, contiguous in memory, are stored 1 KiB per
     // instruction.  Rows past the sequence end fall outside the buffer range
     // and are not written.
-    const int orow = C::K_OFF + (32 * pq + l32) * C::ROW + 8 * g;
+    const int orow = C::K_OFF + (32 * pq + l32) * C::RSK;
 #pragma unroll
     for (int b = 0; b < C::NB; ++b) {
 #pragma unroll
@@ -496,7 +453,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
         bf16x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[b][4 * rq + e] * inv);
-        *reinterpret_cast<bf16x4*>(lds + orow + 16 * ((col >> 3) ^ swizzle_k(l32))) = o;
+        *reinterpret_cast<bf16x4*>(lds + orow + 2 * col) = o;
       }
     }
     __syncthreads();
@@ -513,7 +470,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
         const int r = gb / row_bytes;
         const int c = (gb - r * row_bytes) >> 4;
         const u32x4 val = *reinterpret_cast<const u32x4*>(
-            lds + C::K_OFF + r * C::ROW + 16 * (c ^ swizzle_k(r)));
+            lds + C::K_OFF + r * C::RSK + 16 * c);
         __builtin_amdgcn_raw_buffer_store_b128(val, rh, gb, 0, 0);
       }
     }
