@@ -26,9 +26,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU ("2.5 PFLOP/s")
 PEAK_HBM_GBS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "tiles_mfma_xlstm125m_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "tiles_pairs_xlstm125m_counters.json")
 COPY_BYTES = 512 << 20
-TILE_SRC = os.path.join(ROOT, "linear_recurrent_sequence_amd", "csrc", "tiles_mfma.hip")
+TILE_SRC = os.path.join(ROOT, "linear_recurrent_sequence_amd", "csrc", "tiles_pairs.hip")
 
 
 def parse():
@@ -256,7 +256,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     scan_ms = e0.elapsed_time(e1) / reps
-    scan_bytes = B * NH * T * (4 + 4 + 4 + 4 + 4) + B * NH * (T // 64 + 2) * 8
+    scan_bytes = B * NH * T * (4 + 4 + 4 + 4 + 4 + 4) + B * NH * (T // 64 + 2) * 8
 
     # decay-aware tile skipping on the long-context stress workload: the same
     # call with skipping (default) and visiting every causal tile
@@ -294,7 +294,7 @@ def main():
                    "heads": B * NH, "counted_flops": flops,
                    "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {
-            "bound": "mfma", "kernel": "tiles_mfma", "achieved": round(achieved, 2),
+            "bound": "mfma", "kernel": "tiles_pairs", "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_from_counters(), "avg_launch_ms": round(tile_ms, 5),

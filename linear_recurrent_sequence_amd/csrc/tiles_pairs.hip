@@ -48,7 +48,7 @@ using namespace tilecommon;
 constexpr int kWThreads = 512;  // 8 waves: two per SIMD
 constexpr int kWWaves = kWThreads / 64;
 constexpr int kSK = 64;   // keys per super-step (two 32-key tiles)
-constexpr int kWPf = 2;   // LDS fragment prefetch distance (MFMA steps)
+constexpr int kWPf = 3;   // LDS fragment prefetch distance (MFMA steps)
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
