@@ -66,16 +66,21 @@ enum {
   MLSTM_KERNEL_MFMA = 1,   /* bf16 only: bf16 MFMA tiles (the production path) */
   MLSTM_KERNEL_VECTOR = 2, /* any dtype: float32 vector-ALU tiles, no bf16 rounding of C~' */
   MLSTM_KERNEL_MFMA_ALL_TILES = 3, /* as MLSTM_KERNEL_MFMA, but visiting every causal tile */
-  MLSTM_KERNEL_MFMA_SINGLE = 4     /* bf16 only: the one-wave-per-SIMD MFMA kernel */
+  MLSTM_KERNEL_MFMA_SINGLE = 4,    /* bf16 only, d <= 512: the one-wave-per-SIMD MFMA kernel */
+  MLSTM_KERNEL_MFMA_WIDE = 5       /* bf16 only: the wide-head MFMA kernel, for any d */
 };
 /*
- * The bf16 MFMA path has two tile kernels.  For d <= 384 it runs 8 waves per
- * workgroup, two per SIMD: the two waves that share a SIMD share 32 query
+ * The bf16 MFMA path has three tile kernels.  For d <= 384 it runs 8 waves
+ * per workgroup, two per SIMD: the two waves that share a SIMD share 32 query
  * rows, each forms C~' for its own 32 of every 64 keys and accumulates half
  * of the output columns, so one wave's copies and exponentials overlap the
- * other's matrix-core work.  For d > 384 (and with MLSTM_KERNEL_MFMA_SINGLE)
- * it runs 4 waves, one per SIMD, each with 32 query rows and all columns.
- * Both give the same results up to float32 summation order.
+ * other's matrix-core work.  For 384 < d <= 512 (and with
+ * MLSTM_KERNEL_MFMA_SINGLE) it runs 4 waves, one per SIMD, each with 32 query
+ * rows and all columns.  For d > 512 (and with MLSTM_KERNEL_MFMA_WIDE) four
+ * waves share 32 query rows, each holding a quarter of the head dimension:
+ * they add their partial Q K^T products through LDS, and each accumulates a
+ * quarter of the output columns.  All give the same results up to float32
+ * summation order.
  */
 /*
  * Decay-aware tile skipping (MLSTM_KERNEL_AUTO and _MFMA on bf16).  From the
@@ -94,7 +99,7 @@ enum {
   MLSTM_ERR_NULL = -1,        /* a required pointer is NULL */
   MLSTM_ERR_SHAPE = -2,       /* B, NH, T or d < 1, or a size overflows */
   MLSTM_ERR_DTYPE = -3,       /* dtype not MLSTM_FP32 / MLSTM_BF16 */
-  MLSTM_ERR_HEAD_DIM = -4,    /* d not a multiple of 16 in [16, 512] */
+  MLSTM_ERR_HEAD_DIM = -4,    /* d not a multiple of 16 in [16, 1024], or beyond a kernel's limit */
   MLSTM_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
   MLSTM_ERR_HIP = -6,         /* a HIP allocation or launch failed */
   MLSTM_ERR_WORKSPACE = -7,   /* caller workspace smaller than mlstm_workspace_bytes */
@@ -124,7 +129,7 @@ enum { MLSTM_FORGET_SIGMOID = 0, MLSTM_FORGET_EXP = 1 };
  *   h_out     out  [B][NH][T][d], dtype: h~ (Eq. 86), before any output gate
  *   m_out     out  [B][NH][T] float32: the row maximum m (Eq. 80)
  *   n_out     out  [B][NH][T] float32: the normalizer n (Eq. 84)
- *   B, NH, T  >= 1;  d a multiple of 16 in [16, 512]
+ *   B, NH, T  >= 1;  d a multiple of 16 in [16, 1024]
  *   dtype     MLSTM_FP32 or MLSTM_BF16
  * Runs on the null stream with a library-allocated, stream-ordered workspace.
  * Returns MLSTM_OK or a negative status.
@@ -229,8 +234,8 @@ int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v,
  * dL/dn uses sum_j C~'_ij v_j = n_i h~_i, so for bf16 it carries the
  * rounding of the stored h~.  Arithmetic is float32 on the vector ALUs
  * (tiles of 16 x 16); the library allocates a stream-ordered workspace.
- * Pointers 16-byte aligned; no output may alias an input.  Errors as for
- * mlstm_parallel_fwd.
+ * Pointers 16-byte aligned; no output may alias an input.  d <= 512
+ * (MLSTM_ERR_HEAD_DIM above).  Other errors as for mlstm_parallel_fwd.
  */
 int mlstm_parallel_bwd(const void* q, const void* k, const void* v,
                        const float* igate, const float* fgate,
@@ -264,7 +269,7 @@ int mlstm_parallel_bwd(const void* q, const void* k, const void* v,
  *                m_in (MLSTM_ERR_ALIAS)
  *   h_out        out  [B][NH][d], dtype: h~_t (before any output gate)
  *   den_out      out  [B][NH] float32: max(|n_t . q_t|, exp(-m_t)); may be NULL
- *   d            a multiple of 16 in [16, 512]
+ *   d            a multiple of 16 in [16, 1024]
  * Vectors and C need 16-byte alignment, scalars 4-byte.  Asynchronous on
  * `stream`; no workspace.  Bound by memory bandwidth: the state is read and
  * written once per step.

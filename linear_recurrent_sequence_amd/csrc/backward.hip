@@ -34,7 +34,7 @@ namespace mlstm {
 namespace {
 
 constexpr int kBT = 16;  // rows and keys per tile
-constexpr int kBMaxD = 512;
+constexpr int kBMaxD = kBackwardMaxHeadDim;
 constexpr int kBPad = kBMaxD + 1;
 
 __device__ inline float load_elem(const float* p) { return *p; }

@@ -12,6 +12,7 @@ using mlstm::Workspace;
 
 constexpr int64_t kMaxT = int64_t(1) << 30;
 constexpr int64_t kMaxElems = int64_t(1) << 46;
+constexpr int64_t kMaxHeadDim = 1024;
 
 int check_shape(int64_t B, int64_t NH, int64_t T, int64_t d) {
   if (B < 1 || NH < 1 || T < 1 || d < 1) return MLSTM_ERR_SHAPE;
@@ -22,7 +23,7 @@ int check_shape(int64_t B, int64_t NH, int64_t T, int64_t d) {
   if (H > kMaxElems / Tp) return MLSTM_ERR_SHAPE;
   // launch grids are one-dimensional: (T / 16) x H workgroups at most
   if (((Tp / 16) * H) > int64_t(0xFFFFFFFF)) return MLSTM_ERR_SHAPE;
-  if (d % 16 != 0 || d > 512) return MLSTM_ERR_HEAD_DIM;
+  if (d % 16 != 0 || d > kMaxHeadDim) return MLSTM_ERR_HEAD_DIM;
   if (H * Tp > kMaxElems / d) return MLSTM_ERR_SHAPE;
   return MLSTM_OK;
 }
@@ -49,10 +50,10 @@ int check_tile_args(const void* q, const void* k, const void* v, const float* m,
   if (dtype != MLSTM_FP32 && dtype != MLSTM_BF16) return MLSTM_ERR_DTYPE;
   if (kernel != MLSTM_KERNEL_AUTO && kernel != MLSTM_KERNEL_MFMA &&
       kernel != MLSTM_KERNEL_VECTOR && kernel != MLSTM_KERNEL_MFMA_ALL_TILES &&
-      kernel != MLSTM_KERNEL_MFMA_SINGLE)
+      kernel != MLSTM_KERNEL_MFMA_SINGLE && kernel != MLSTM_KERNEL_MFMA_WIDE)
     return MLSTM_ERR_KERNEL;
   if ((kernel == MLSTM_KERNEL_MFMA || kernel == MLSTM_KERNEL_MFMA_ALL_TILES ||
-       kernel == MLSTM_KERNEL_MFMA_SINGLE) &&
+       kernel == MLSTM_KERNEL_MFMA_SINGLE || kernel == MLSTM_KERNEL_MFMA_WIDE) &&
       dtype != MLSTM_BF16)
     return MLSTM_ERR_KERNEL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(m) || !aligned16(h_out) ||
@@ -66,17 +67,25 @@ int run_tiles(const void* q, const void* k, const void* v, const float* m, const
               void* h_out, float* n_out, const mlstm::Epilogue& ep, int64_t H, int64_t T,
               int64_t d, int dtype, int kernel, hipStream_t stream) {
   const bool use_mfma = kernel == MLSTM_KERNEL_MFMA || kernel == MLSTM_KERNEL_MFMA_ALL_TILES ||
-                        kernel == MLSTM_KERNEL_MFMA_SINGLE ||
+                        kernel == MLSTM_KERNEL_MFMA_SINGLE || kernel == MLSTM_KERNEL_MFMA_WIDE ||
                         (kernel == MLSTM_KERNEL_AUTO && dtype == MLSTM_BF16);
   const bool skip = kernel != MLSTM_KERNEL_MFMA_ALL_TILES;
-  if (use_mfma && kernel != MLSTM_KERNEL_MFMA_SINGLE && mlstm::tiles_pairs_supports(d))
-    return hip_status(mlstm::launch_tiles_pairs(q, k, v, m, w, h_out, n_out, ep, skip, H, T, d,
-                                                stream));
-  if (use_mfma)
+  if (!use_mfma)
+    return hip_status(mlstm::launch_tiles_vector(q, k, v, m, w, h_out, n_out, ep, H, T, d,
+                                                 dtype == MLSTM_BF16, stream));
+  if (kernel == MLSTM_KERNEL_MFMA_SINGLE) {
+    if (d > 512) return MLSTM_ERR_HEAD_DIM;
     return hip_status(mlstm::launch_tiles_mfma(q, k, v, m, w, h_out, n_out, ep, skip, H, T, d,
                                                stream));
-  return hip_status(mlstm::launch_tiles_vector(q, k, v, m, w, h_out, n_out, ep, H, T, d,
-                                               dtype == MLSTM_BF16, stream));
+  }
+  if (kernel == MLSTM_KERNEL_MFMA_WIDE || d > 512)
+    return hip_status(mlstm::launch_tiles_wide(q, k, v, m, w, h_out, n_out, ep, skip, H, T, d,
+                                               stream));
+  if (mlstm::tiles_pairs_supports(d))
+    return hip_status(mlstm::launch_tiles_pairs(q, k, v, m, w, h_out, n_out, ep, skip, H, T, d,
+                                                stream));
+  return hip_status(mlstm::launch_tiles_mfma(q, k, v, m, w, h_out, n_out, ep, skip, H, T, d,
+                                             stream));
 }
 
 // Both stages with a stream-ordered workspace (safe under concurrent calls on
@@ -213,6 +222,7 @@ int mlstm_parallel_bwd(const void* q, const void* k, const void* v, const float*
   const bool exp_forget = forget_activation == MLSTM_FORGET_EXP;
   int st = check_shape(B, NH, T, d);
   if (st != MLSTM_OK) return st;
+  if (d > mlstm::kBackwardMaxHeadDim) return MLSTM_ERR_HEAD_DIM;
   const void* ins[] = {q, k, v, igate, fgate, h, m, n, b, dh};
   const void* outs[] = {dq, dk, dv, digate, dfgate};
   for (const void* p : ins)
@@ -288,7 +298,7 @@ const char* mlstm_strerror(int status) {
     case MLSTM_ERR_NULL: return "a required pointer is NULL";
     case MLSTM_ERR_SHAPE: return "invalid shape: B, NH, T, d must be >= 1 and sizes must not overflow";
     case MLSTM_ERR_DTYPE: return "invalid dtype: expected MLSTM_FP32 or MLSTM_BF16";
-    case MLSTM_ERR_HEAD_DIM: return "unsupported head dimension: d must be a multiple of 16 in [16, 512]";
+    case MLSTM_ERR_HEAD_DIM: return "unsupported head dimension: d must be a multiple of 16 in [16, 1024] (and <= 512 for the one-wave MFMA kernel)";
     case MLSTM_ERR_ALIGN: return "misaligned pointer: tensors need 16-byte, workspaces 256-byte alignment";
     case MLSTM_ERR_HIP: return "HIP allocation or kernel launch failed";
     case MLSTM_ERR_WORKSPACE: return "workspace smaller than mlstm_workspace_bytes()";

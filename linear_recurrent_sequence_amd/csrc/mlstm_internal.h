@@ -121,15 +121,25 @@ hipError_t launch_tiles_pairs(const void* q, const void* k, const void* v, const
                               const Epilogue& ep, bool skip, int64_t H, int64_t T, int64_t d,
                               hipStream_t stream);
 
+// Stage 2, bf16 matrix-core tiles for wide heads (d <= 1024): four waves
+// share 32 query rows and split the head dimension in quarters.
+bool tiles_wide_supports(int64_t d);
+hipError_t launch_tiles_wide(const void* q, const void* k, const void* v, const float* m,
+                             const Workspace& ws, void* h_out, float* n_out,
+                             const Epilogue& ep, bool skip, int64_t H, int64_t T, int64_t d,
+                             hipStream_t stream);
+
 // Stage 2, float32 vector-ALU tiles; is_bf16 selects the element type.
 hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, const float* m,
                                const Workspace& ws, void* h_out, float* n_out,
                                const Epilogue& ep, int64_t H, int64_t T, int64_t d,
                                bool is_bf16, hipStream_t stream);
 
-// Backward pass (Eqs. 87-105), float32 vector tiles.  `ws` holds the gate
-// scan's terms for the same inputs; `scratch` holds backward_scratch_bytes(H,
+// Backward pass (Eqs. 87-105), float32 vector tiles, d <= kBackwardMaxHeadDim
+// (four 16-row float32 tiles of the head dimension share the LDS).  `ws` holds
+// the gate scan's terms for the same inputs; `scratch` holds backward_scratch_bytes(H,
 // T) bytes (256-byte aligned) of per-row temporaries.
+constexpr int kBackwardMaxHeadDim = 512;
 size_t backward_scratch_bytes(int64_t H, int64_t T);
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* fgate,
                            const void* h, const float* m, const float* n, const float* b,

@@ -17,7 +17,8 @@
 // The step reads and writes the whole state, d^2 + d + 1 floats per head, so
 // it is bound by memory bandwidth.  One workgroup owns 16 rows of one head's
 // C (rows are indexed by the value dimension, so h~_i = C_i . q); each wave
-// owns 4 rows and each lane a strided pair of columns.  A wave loads all of
+// owns 4 rows and each lane strided pairs of columns (4 pairs for d <= 512,
+// 8 up to 1024).  A wave loads all of
 // its rows before it stores any, so C may be updated in place.  Every
 // workgroup forms n_t . q_t itself (d terms); the first workgroup of a head
 // writes n_t and m_t.  Reductions are fixed-order butterflies: results are
@@ -33,7 +34,6 @@ constexpr int kStepThreads = 256;
 constexpr int kStepWaves = kStepThreads / 64;
 constexpr int kRowsPerWave = 4;
 constexpr int kStepRows = kStepWaves * kRowsPerWave;  // rows of C per workgroup
-constexpr int kPairsPerLane = 4;                       // d <= 512 = 64 lanes x 4 pairs
 
 __device__ inline float load_elem(const float* p) { return *p; }
 __device__ inline float load_elem(const __hip_bfloat16* p) { return __bfloat162float(*p); }
@@ -54,7 +54,7 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-template <typename Tin>
+template <typename Tin, int kPairsPerLane>  // d <= 128 * kPairsPerLane
 __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ igate, const float* __restrict__ fgate, const float* C_in,
@@ -150,6 +150,19 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(
   }
 }
 
+template <typename Tin, int P>
+void launch_r(const void* q, const void* k, const void* v, const float* igate, const float* fgate,
+              const float* C_in, const float* n_in, const float* m_in, float* C_out,
+              float* n_out, float* m_out, void* h_out, float* den_out, int64_t H, int64_t d,
+              bool exp_forget, hipStream_t stream) {
+  const int blocks_per_head = int((d + kStepRows - 1) / kStepRows);
+  hipLaunchKernelGGL((recurrent_step_kernel<Tin, P>), dim3(unsigned(H * blocks_per_head)),
+                     dim3(kStepThreads), 0, stream, static_cast<const Tin*>(q),
+                     static_cast<const Tin*>(k), static_cast<const Tin*>(v), igate, fgate, C_in,
+                     n_in, m_in, C_out, n_out, m_out, static_cast<Tin*>(h_out), den_out, int(d),
+                     blocks_per_head, int(exp_forget));
+}
+
 }  // namespace
 
 hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, const float* igate,
@@ -157,22 +170,22 @@ hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, co
                                  const float* m_in, float* C_out, float* n_out, float* m_out,
                                  void* h_out, float* den_out, int64_t H, int64_t d, bool is_bf16,
                                  bool exp_forget, hipStream_t stream) {
-  if (d % 16 != 0 || d < 16 || d > 2 * 64 * kPairsPerLane) return hipErrorInvalidValue;
-  const int blocks_per_head = int((d + kStepRows - 1) / kStepRows);
-  const dim3 grid(unsigned(H * blocks_per_head));
+  if (d % 16 != 0 || d < 16 || d > 1024) return hipErrorInvalidValue;
+  using B16 = __hip_bfloat16;
   if (is_bf16) {
-    using B16 = __hip_bfloat16;
-    hipLaunchKernelGGL(recurrent_step_kernel<B16>, grid, dim3(kStepThreads), 0, stream,
-                       static_cast<const B16*>(q), static_cast<const B16*>(k),
-                       static_cast<const B16*>(v), igate, fgate, C_in, n_in, m_in, C_out, n_out,
-                       m_out, static_cast<B16*>(h_out), den_out, int(d), blocks_per_head,
-                       int(exp_forget));
+    if (d <= 512)
+      launch_r<B16, 4>(q, k, v, igate, fgate, C_in, n_in, m_in, C_out, n_out, m_out, h_out,
+                       den_out, H, d, exp_forget, stream);
+    else
+      launch_r<B16, 8>(q, k, v, igate, fgate, C_in, n_in, m_in, C_out, n_out, m_out, h_out,
+                       den_out, H, d, exp_forget, stream);
   } else {
-    hipLaunchKernelGGL(recurrent_step_kernel<float>, grid, dim3(kStepThreads), 0, stream,
-                       static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), igate, fgate, C_in, n_in, m_in, C_out,
-                       n_out, m_out, static_cast<float*>(h_out), den_out, int(d),
-                       blocks_per_head, int(exp_forget));
+    if (d <= 512)
+      launch_r<float, 4>(q, k, v, igate, fgate, C_in, n_in, m_in, C_out, n_out, m_out, h_out,
+                         den_out, H, d, exp_forget, stream);
+    else
+      launch_r<float, 8>(q, k, v, igate, fgate, C_in, n_in, m_in, C_out, n_out, m_out, h_out,
+                         den_out, H, d, exp_forget, stream);
   }
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
-// Pieces of the bf16 matrix-core tile kernel kept apart from its body:
+// Pieces of the bf16 matrix-core tile kernels kept apart from their bodies:
 // operand types, tile sizes, the workgroup-to-tile mapping, and the
-// global -> LDS copy and LDS transpose-read helpers.
+// global -> LDS copy and LDS transpose-read helpers shared by the bf16
+// tile kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,6 +51,36 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, char
 // 4 bytes per lane, to dst + 4 * lane
 __device__ inline void dma4(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, char* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, voffset, 0, 0, 0);
+}
+
+// The same copies issued through inline assembly, so that the compiler does
+// not wait for them before unrelated LDS reads; the kernel waits for them
+// (vmcnt) itself before each barrier.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// buffer resource words: offsets at or past num_records bytes read as zeros
+__device__ inline i32x4 rsrc_words(const void* base, int64_t num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const int n = num_records > 0x7FFFFFFF ? 0x7FFFFFFF : int(num_records);
+  return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xFFFFu), n, kRsrcFlags};
+}
+__device__ inline unsigned lds_addr(const char* p) {
+  return unsigned(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+// 16 bytes per active lane, global -> LDS at (wave-uniform) dst + 16 * lane.
+// M0 holds the LDS destination; one wait state separates its write from the copy.
+__device__ inline void copy16(i32x4 rsrc, unsigned voffset, unsigned dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(dst), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+// 4 bytes per active lane to dst + 4 * lane
+__device__ inline void copy4(i32x4 rsrc, unsigned voffset, unsigned dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(dst), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
 }
 
 __device__ inline i16x4 tr_read(const char* p) {

@@ -50,33 +50,6 @@ constexpr int kWWaves = kWThreads / 64;
 constexpr int kSK = 64;   // keys per super-step (two 32-key tiles)
 constexpr int kWPf = 3;   // LDS fragment prefetch distance (MFMA steps)
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// buffer resource words: offsets at or past num_records bytes read as zeros
-__device__ inline i32x4 rsrc_words(const void* base, int64_t num_records) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const int n = num_records > 0x7FFFFFFF ? 0x7FFFFFFF : int(num_records);
-  return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xFFFFu), n, kRsrcFlags};
-}
-__device__ inline unsigned lds_addr(const char* p) {
-  return unsigned(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
-}
-// 16 bytes per active lane, global -> LDS at (wave-uniform) dst + 16 * lane.
-// M0 holds the LDS destination; one wait state separates its write from the copy.
-__device__ inline void copy16(i32x4 rsrc, unsigned voffset, unsigned dst) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(dst), "v"(voffset), "s"(rsrc)
-               : "memory", "m0");
-}
-// 4 bytes per active lane to dst + 4 * lane
-__device__ inline void copy4(i32x4 rsrc, unsigned voffset, unsigned dst) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(dst), "v"(voffset), "s"(rsrc)
-               : "memory", "m0");
-}
-
 // LDS layout: rows are padded so that the fragment reads are free of bank
 // conflicts (LDS serves 256 bytes per clock in 64 banks; a 16-byte read of
 // 16 lanes, or an 8-byte read of 32 lanes, is conflict-free when the lanes hit

@@ -7,7 +7,9 @@
 // float32 and C~' is never rounded to bf16.  One workgroup of 256 threads owns
 // 16 query rows of one head; thread (r, c) of the 16 x 16 grid forms one
 // entry of S = Q K^T and of C~' per key tile, and then accumulates output
-// columns c, c + 16, ... of row r.
+// columns c, c + 16, ... of row r.  For head dims above 512 the K and V
+// tiles take turns in one LDS buffer (Q, K and V tiles of 16 x 1024 float32
+// would not fit together).
 #include "mlstm_internal.h"
 
 #include <hip/hip_bf16.h>
@@ -15,26 +17,26 @@
 namespace mlstm {
 namespace {
 
-constexpr int kVT = 16;        // query rows per workgroup and keys per tile
-constexpr int kVMaxD = 512;
-constexpr int kVPad = kVMaxD + 1;
+constexpr int kVT = 16;  // query rows per workgroup and keys per tile
 
 __device__ inline float load_elem(const float* p) { return *p; }
 __device__ inline float load_elem(const __hip_bfloat16* p) { return __bfloat162float(*p); }
 __device__ inline void store_elem(float* p, float x) { *p = x; }
 __device__ inline void store_elem(__hip_bfloat16* p, float x) { *p = __float2bfloat16(x); }
 
-template <typename Tin>
+template <typename Tin, int MAXD>
 __global__ __launch_bounds__(256) void tiles_vector_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ m_in, const double* __restrict__ anchor,
     const float* __restrict__ rowt, const float* __restrict__ colt, Tin* __restrict__ h_out,
     float* __restrict__ n_out, const Tin* __restrict__ ogate, Tin* __restrict__ htilde,
     float* __restrict__ b_out, int64_t T, int d, int64_t Tp, int64_t nblk, int64_t row_tiles) {
-  __shared__ float Qs[kVT][kVPad];
-  __shared__ float Ks[kVT][kVPad];
-  __shared__ float Vs[kVT][kVMaxD];
+  constexpr bool kShared = MAXD > 512;  // K and V tiles share one buffer
+  __shared__ float Qs[kVT][MAXD + 1];
+  __shared__ float Ks[kVT][MAXD + 1];
+  __shared__ float Vbuf[kShared ? 1 : kVT][kShared ? 1 : MAXD];
   __shared__ float Ps[kVT][kVT + 1];
+  auto Vs = [&](int r, int c) -> float& { return kShared ? Ks[r][c] : Vbuf[r][c]; };
 
   const int tid = threadIdx.x;
   const int rl = tid / kVT;  // local query row
@@ -51,9 +53,9 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
   const float r_i = rowt[head * Tp + qi];  // qi < Tp: Tp is T rounded up to 128
   const double a_i = anchor[head * nblk + q0 / kAnchorBlock];
 
-  float acc[kVMaxD / kVT];
+  float acc[MAXD / kVT];
 #pragma unroll
-  for (int u = 0; u < kVMaxD / kVT; ++u) acc[u] = 0.0f;
+  for (int u = 0; u < MAXD / kVT; ++u) acc[u] = 0.0f;
   float bsum = 0.0f;
 
   const int64_t last_key = (q0 + kVT - 1 < T ? q0 + kVT - 1 : T - 1);
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
       const int r = idx / d, c = idx % d;
       const bool in = k0 + r < T;
       Ks[r][c] = in ? load_elem(k + hoff + (k0 + r) * d + c) : 0.0f;
-      Vs[r][c] = in ? load_elem(v + hoff + (k0 + r) * d + c) : 0.0f;
+      if (!kShared) Vs(r, c) = in ? load_elem(v + hoff + (k0 + r) * d + c) : 0.0f;
     }
     __syncthreads();
     const int64_t kj = k0 + cl;
@@ -77,13 +79,20 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
     bsum += cv;                                     // b_i (Eq. 83), float32
     Ps[rl][cl] = cv;
     __syncthreads();
+    if (kShared) {  // every S entry is formed: the V tile replaces the K tile
+      for (int idx = tid; idx < kVT * d; idx += 256) {
+        const int r = idx / d, c = idx % d;
+        Vs(r, c) = k0 + r < T ? load_elem(v + hoff + (k0 + r) * d + c) : 0.0f;
+      }
+      __syncthreads();
+    }
 #pragma unroll
-    for (int u = 0; u < kVMaxD / kVT; ++u) {
+    for (int u = 0; u < MAXD / kVT; ++u) {
       const int c = cl + kVT * u;
       if (c < d) {
         float a = 0.0f;
 #pragma unroll
-        for (int t = 0; t < kVT; ++t) a = fmaf(Ps[rl][t], Vs[t][c], a);
+        for (int t = 0; t < kVT; ++t) a = fmaf(Ps[rl][t], Vs(t, c), a);
         acc[u] += a;
       }
     }
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
     if (cl == 0) n_out[head * T + qi] = nn;
     if (cl == 0 && b_out) b_out[head * T + qi] = bsum;
 #pragma unroll
-    for (int u = 0; u < kVMaxD / kVT; ++u) {
+    for (int u = 0; u < MAXD / kVT; ++u) {
       const int c = cl + kVT * u;
       if (c < d) {
         const int64_t at = hoff + qi * d + c;
@@ -109,28 +118,32 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
   }
 }
 
+template <typename Tin, int MAXD>
+void launch_v(const void* q, const void* k, const void* v, const float* m, const Workspace& ws,
+              void* h_out, float* n_out, const Epilogue& ep, int64_t H, int64_t T, int64_t d,
+              hipStream_t stream) {
+  const int64_t row_tiles = (T + kVT - 1) / kVT;
+  hipLaunchKernelGGL((tiles_vector_kernel<Tin, MAXD>), dim3(unsigned(row_tiles * H)), dim3(256),
+                     0, stream, static_cast<const Tin*>(q), static_cast<const Tin*>(k),
+                     static_cast<const Tin*>(v), m, ws.anchor, ws.rowt, ws.colt,
+                     static_cast<Tin*>(h_out), n_out, static_cast<const Tin*>(ep.ogate),
+                     static_cast<Tin*>(ep.htilde), ep.b, T, int(d), ws.Tp, ws.nblk, row_tiles);
+}
+
 }  // namespace
 
 hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, const float* m,
                                const Workspace& ws, void* h_out, float* n_out,
                                const Epilogue& ep, int64_t H, int64_t T, int64_t d,
                                bool is_bf16, hipStream_t stream) {
-  const int64_t row_tiles = (T + kVT - 1) / kVT;
-  const dim3 grid(unsigned(row_tiles * H));
+  if (d % 16 != 0 || d < 16 || d > 1024) return hipErrorInvalidValue;
+  using B16 = __hip_bfloat16;
   if (is_bf16) {
-    using B16 = __hip_bfloat16;
-    hipLaunchKernelGGL(tiles_vector_kernel<B16>, grid, dim3(256), 0, stream,
-                       static_cast<const B16*>(q), static_cast<const B16*>(k),
-                       static_cast<const B16*>(v), m, ws.anchor, ws.rowt, ws.colt,
-                       static_cast<B16*>(h_out), n_out, static_cast<const B16*>(ep.ogate),
-                       static_cast<B16*>(ep.htilde), ep.b, T, int(d), ws.Tp, ws.nblk, row_tiles);
+    if (d <= 512) launch_v<B16, 512>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    else launch_v<B16, 1024>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
   } else {
-    hipLaunchKernelGGL(tiles_vector_kernel<float>, grid, dim3(256), 0, stream,
-                       static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), m, ws.anchor, ws.rowt, ws.colt,
-                       static_cast<float*>(h_out), n_out, static_cast<const float*>(ep.ogate),
-                       static_cast<float*>(ep.htilde), ep.b, T, int(d), ws.Tp, ws.nblk,
-                       row_tiles);
+    if (d <= 512) launch_v<float, 512>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
+    else launch_v<float, 1024>(q, k, v, m, ws, h_out, n_out, ep, H, T, d, stream);
   }
   return hipGetLastError();
 }

@@ -23,7 +23,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmlstm.so")
 
 MLSTM_FP32, MLSTM_BF16 = 0, 1
-KERNELS = {"auto": 0, "mfma": 1, "vector": 2, "mfma_all_tiles": 3, "mfma_single": 4}
+KERNELS = {"auto": 0, "mfma": 1, "vector": 2, "mfma_all_tiles": 3, "mfma_single": 4,
+           "mfma_wide": 5}
 FORGET_ACTIVATIONS = {"sigmoid": 0, "exp": 1}
 
 _lib = None

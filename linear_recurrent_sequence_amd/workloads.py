@@ -37,6 +37,9 @@ WORKLOADS = {
     # 8 independent sub-heads of 512, context 2048, batch 4
     "xlstm1p3b_layer": dict(B=4, NH=8, T=2048, d=512, dtype="bf16",
                             igate=("normal", 0.0, 1.0), fgate=("normal", 3.0, 1.0)),
+    # the same layer with true heads of 1024 (4 heads, one normalizer each)
+    "xlstm1p3b_layer_d1024": dict(B=4, NH=4, T=2048, d=1024, dtype="bf16",
+                                  igate=("normal", 0.0, 1.0), fgate=("normal", 3.0, 1.0)),
     # long-context stabilization stress: input gates across the exp overflow
     # range, fast and occasionally near-total forgetting
     "long_context_16k": dict(B=1, NH=8, T=16384, d=256, dtype="bf16",

@@ -64,7 +64,7 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced
     (dict(q=0), -1), (dict(igate=0), -1), (dict(n_out=0), -1),
     (dict(B=0), -2), (dict(T=0), -2), (dict(NH=-3), -2), (dict(d=0), -2),
     (dict(dtype=2), -3), (dict(dtype=-1), -3),
-    (dict(d=8), -4), (dict(d=24), -4), (dict(d=528), -4),
+    (dict(d=8), -4), (dict(d=24), -4), (dict(d=1040), -4), (dict(d=2048), -4),
     (dict(q=FAKE + 8), -5), (dict(m_out=FAKE + 4), -5),
 ])
 def test_parallel_fwd_rejects_before_device_work(case, status):
@@ -121,7 +121,7 @@ def test_gated_forward_rejects_before_device_work(case, status):
 @needs_lib
 @pytest.mark.parametrize("case,status", [
     (dict(q=0), -1), (dict(C_in=0), -1), (dict(h_out=0), -1),
-    (dict(d=24), -4), (dict(d=528), -4), (dict(B=0), -2), (dict(dtype=5), -3),
+    (dict(d=24), -4), (dict(d=1040), -4), (dict(B=0), -2), (dict(dtype=5), -3),
     (dict(C_in=FAKE + 8), -5), (dict(igate=FAKE + 2), -5),
     (dict(n_out=FAKE), -9),                       # n_out is n_in
     (dict(m_out=FAKE + (1 << 16)), -9),           # m_out is m_in
@@ -151,3 +151,16 @@ def test_training_entry_points_reject_unknown_forget_activation():
     assert lib.mlstm_parallel_fwd_train(*[FAKE] * 8, None, 1, 1, 64, 16, 1, 0, None) == -1
     with pytest.raises(ValueError):
         mlstm._forget_code("tanh")
+
+
+@needs_lib
+def test_backward_rejects_head_dims_above_its_limit():
+    lib = mlstm.load_library()
+    # d = 1024 is a valid forward head dimension, but beyond the backward's
+    # float32 LDS tiles; d = 1040 is beyond every entry point
+    assert lib.mlstm_parallel_bwd(*[FAKE] * 15, 1, 1, 64, 1024, 1, 0, None) == -4
+    assert lib.mlstm_parallel_bwd(*[FAKE] * 15, 1, 1, 64, 528, 0, 0, None) == -4
+    assert lib.mlstm_parallel_bwd(*[FAKE] * 15, 1, 1, 64, 1040, 1, 0, None) == -4
+    # the one-wave MFMA kernel stops at 512; the selector is checked first
+    assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, FAKE,
+                                  1, 1, 64, 1024, 0, 5, None) == -8

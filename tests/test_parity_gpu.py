@@ -570,3 +570,126 @@ def test_exp_forget_backward_matches_oracle(s):
     print(errs)
     for name, e in errs.items():
         assert e <= (tol if name in ("dq", "dk", "dv") else 10 * tol), (name, errs)
+
+
+# ---------------------------------------------------------------------------
+# wide heads (d up to 1024): the four-member MFMA kernel, the float32 vector
+# kernel's shared K/V buffer and the wider recurrent step
+# ---------------------------------------------------------------------------
+
+WIDE_CASES = [
+    spec(1, 1, 1, 1024), spec(1, 1, 33, 1024), spec(1, 2, 161, 1024),
+    spec(2, 1, 100, 544), spec(1, 1, 130, 640), spec(1, 1, 97, 768), spec(1, 1, 70, 896),
+    spec(1, 1, 300, 1024, ig=("uniform", -20, 20), fg=("normal", 0, 4),
+         fgate_floor=(0.01, -30.0)),
+    spec(8, 1, 65, 1024),  # head count divisible by 8 (XCD-grouped schedule)
+]
+
+
+@pytest.mark.parametrize("s", WIDE_CASES, ids=_id)
+def test_wide_heads_full(s):
+    x = W.make(s, seed=21)
+    h, m, n = run_gpu(x)
+    hr, mr, nr, _, rho = oracle_full(x)
+    print(check(h, m, n, hr, mr, nr, TOL_H["bf16"], kappa=rho / nr, kappa_max=1e3))
+
+
+@pytest.mark.parametrize("s", [spec(1, 1, 40, 16), spec(1, 2, 150, 64), spec(1, 1, 200, 384),
+                               spec(2, 1, 129, 512), spec(1, 1, 90, 1008)], ids=_id)
+def test_wide_kernel_forced_any_head_dim(s):
+    """The wide kernel pads d up to a multiple of 128 (at least 512); zero
+    columns add nothing, so it is correct for every head dimension."""
+    x = W.make(s, seed=22)
+    h, m, n = run_gpu(x, kernel="mfma_wide")
+    hr, mr, nr = oracle_full(x)[:3]
+    print(check(h, m, n, hr, mr, nr, TOL_H["bf16"]))
+
+
+@pytest.mark.parametrize("s", [spec(1, 1, 70, 1024, "fp32"), spec(1, 2, 45, 640, "fp32")],
+                         ids=_id)
+def test_wide_heads_fp32(s):
+    x = W.make(s, seed=23)
+    h, m, n = run_gpu(x)
+    hr, mr, nr = oracle_full(x)[:3]
+    print(check(h, m, n, hr, mr, nr, TOL_H["fp32"]))
+
+
+def test_wide_heads_vector_kernel_bf16_inputs():
+    x = W.make(spec(1, 1, 120, 1024), seed=24)
+    h, m, n = run_gpu(x, kernel="vector")
+    hr, mr, nr = oracle_full(x)[:3]
+    print(check(h, m, n, hr, mr, nr, 4e-3))
+
+
+def test_wide_heads_skipping_matches_all_tiles():
+    x = W.make(spec(1, 2, 700, 1024, ig=("uniform", -40, 40), fg=("normal", -2, 3)), seed=25)
+    a = _staged(x, "mfma")
+    b = _staged(x, "mfma_all_tiles")
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta, tb)
+    hr, mr, nr, _, rho = oracle_full(x)
+    print(check(_host(a[0]), _host(a[1]), _host(a[2]), hr, mr, nr, TOL_H["bf16"],
+                kappa=rho / nr, kappa_max=1e3))
+
+
+def test_wide_heads_deterministic_and_causal_bitwise():
+    x = W.make(spec(1, 2, 300, 1024), seed=26)
+    a = run_gpu(x)
+    b = run_gpu(x)
+    for ta, tb in zip(a, b):
+        assert np.array_equal(ta, tb)
+    t0 = 150
+    y = {k_: (v_.copy() if isinstance(v_, np.ndarray) else v_) for k_, v_ in x.items()}
+    rng = np.random.default_rng(27)
+    for key in ("q", "k", "v"):
+        y[key][:, :, t0 + 1:] = W.round_bf16(rng.standard_normal(y[key][:, :, t0 + 1:].shape)
+                                             .astype(np.float32))
+    c = run_gpu(y)
+    for ta, tc in zip(a, c):
+        assert np.array_equal(ta[:, :, :t0 + 1], tc[:, :, :t0 + 1])
+
+
+def test_wide_heads_output_gate_and_b():
+    x = W.make(spec(1, 2, 140, 1024, ig=("normal", 0, 2)), seed=28)
+    og_np = W.make_ogate(x["spec"], seed=28)
+    q, k, v, ig, fg = _dev(x)
+    og = torch.from_numpy(og_np).to("cuda").to(torch.bfloat16).contiguous()
+    h, ht, m, n = mlstm.parallel_fwd_gated(q, k, v, ig, fg, og, htilde=True)
+    h0, m0, n0 = mlstm.parallel_fwd(q, k, v, ig, fg)
+    _, _, _, b = mlstm.parallel_fwd_train(q, k, v, ig, fg)
+    torch.cuda.synchronize()
+    assert torch.equal(ht, h0) and torch.equal(m, m0) and torch.equal(n, n0)
+    hr, mr, nr, br, _ = oracle_full(x)
+    gated = oracle.output_gate(hr, og_np)
+    assert head_normwise(_host(h), gated) <= TOL_H["bf16"]
+    assert head_normwise(_host(b), br) <= 1e-5
+
+
+def test_wide_heads_recurrent_steps_match_oracle():
+    x = W.make(spec(1, 2, 12, 1024), seed=29)
+    h, m, den, (C, n, mT) = _run_steps(x)
+    hr, mr, denr, CT, nT = oracle.forward_recurrent_stabilized(
+        x["q"], x["k"], x["v"], x["igate"], x["fgate"])
+    print(check(h, m, den, hr, mr, denr, TOL_H["bf16"]))
+    assert head_normwise(C.reshape(C.shape[0], C.shape[1], -1),
+                         CT.reshape(CT.shape[0], CT.shape[1], -1)) <= 1e-4
+    assert head_normwise(n, nT) <= 1e-4
+
+
+def test_wide_heads_backward_rejected():
+    x = W.make(spec(1, 1, 64, 1024), seed=30)
+    q, k, v, ig, fg = _dev(x)
+    h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg)
+    with pytest.raises(mlstm.MlstmError) as e:
+        mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, torch.zeros_like(q))
+    assert e.value.status == -4
+
+
+def test_wide_heads_workload_sampled():
+    """The 1.3B-shaped layer with true heads of 1024 (B=4, NH=4, T=2048)."""
+    x = W.make("xlstm1p3b_layer_d1024", seed=0)
+    h, m, n = run_gpu(x)
+    rows = _sample_rows(x["spec"]["T"], np.random.default_rng(31), count=24)
+    hr, mr, nr, _ = _sampled_reference(x, rows)
+    print(check(h[:, :, rows], m[:, :, rows], n[:, :, rows], hr, mr, nr, TOL_H["bf16"]))
+    assert np.isfinite(h).all() and np.isfinite(n).all()
