@@ -34,14 +34,19 @@ TILE_SRC = os.path.join(ROOT, "linear_recurrent_sequence_amd", "csrc", "tiles_pa
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--settle-s", type=float, default=1.0,
+                   help="seconds of untimed calls before the warmup steps: under sustained "
+                        "load the GPU clock takes a few hundred ms to settle")
     p.add_argument("--workload", default="xlstm125m_layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true",
                    help="skip timing the backward pass")
     p.add_argument("--no-long-context", action="store_true",
                    help="skip the tile-skipping comparison on the 16K stress workload")
+    p.add_argument("--no-wide", action="store_true",
+                   help="skip the 1.3B-shaped layers (sub-heads of 512, true heads of 1024)")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="approximate CPU seconds for the oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -134,6 +139,47 @@ def long_context_skipping(torch, mlstm, workloads, dev, reps):
             "speedup": round(out["mfma_all_tiles"] / out["mfma"], 2)}
 
 
+def layer_timing(torch, mlstm, workloads, dev, name, reps=50):
+    """Whole call and tile kernel alone on another layer shape (default kernels)."""
+    x = workloads.make(name, seed=0)
+    spec = x["spec"]
+    B, NH, T, d = spec["B"], spec["NH"], spec["T"], spec["d"]
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16).contiguous()
+               for n in ("q", "k", "v"))
+    ig = torch.from_numpy(x["igate"]).to(dev).contiguous()
+    fg = torch.from_numpy(x["fgate"]).to(dev).contiguous()
+    h = torch.empty_like(q)
+    m = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+    n = torch.empty_like(m)
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(5):
+        mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+    e0.record(stream)
+    for _ in range(reps):
+        mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / reps
+    ws = mlstm.alloc_workspace(B, NH, T, dev)
+    mlstm.gate_scan(ig, fg, d, ws, m=m)
+    e0.record(stream)
+    for _ in range(reps):
+        mlstm.causal_tiles(q, k, v, m, ws, out=(h, n))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    tile_ms = e0.elapsed_time(e1) / reps
+    flops = workloads.counted_flops(B, NH, T, d)
+    kernel = "tiles_wide" if d > 512 else ("tiles_pairs" if d <= 384 else "tiles_mfma")
+    return {"workload": name, "B": B, "NH": NH, "T": T, "d": d, "kernel": kernel,
+            "ms_per_call": round(call_ms, 4),
+            "TFLOP/s": round(flops / (call_ms * 1e-3) / 1e12, 1),
+            "tile_avg_launch_ms": round(tile_ms, 5),
+            "tile_TFLOP/s": round(flops / (tile_ms * 1e-3) / 1e12, 1),
+            "tile_frac": round(flops / (tile_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def recurrent_decode(torch, mlstm, dev, B, NH, d, reps=50):
     """Time mlstm_recurrent_step (bf16 q/k/v, float32 state updated in place)."""
     g = torch.Generator(device="cpu").manual_seed(0)
@@ -221,6 +267,11 @@ def main():
     flops = workloads.counted_flops(B, NH, T, d)
 
     # ---- whole-call throughput ----
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(20):
+            mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
     torch.cuda.synchronize()
@@ -263,6 +314,11 @@ def main():
     skip_rec = None
     if not args.no_long_context:
         skip_rec = long_context_skipping(torch, mlstm, workloads, dev, reps=10)
+
+    wide = None
+    if not args.no_wide:
+        wide = [layer_timing(torch, mlstm, workloads, dev, name)
+                for name in ("xlstm1p3b_layer", "xlstm1p3b_layer_d1024")]
 
     # recurrent (generation) step on the same layer shape: the 8 x 4 heads'
     # state (19 MB) stays in the 256 MB last-level cache between steps; a
@@ -307,6 +363,8 @@ def main():
     }
     if skip_rec is not None:
         line["tile_skipping"] = skip_rec
+    if wide is not None:
+        line["other_layers"] = wide
     line["recurrent_step"] = rec
     if bwd is not None:
         line["backward"] = bwd
