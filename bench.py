@@ -210,8 +210,9 @@ def recurrent_decode(torch, mlstm, dev, B, NH, d, reps=50):
             "state_MB": round(H * d * d * 4 / 1e6, 1)}
 
 
-def backward_timing(torch, mlstm, workloads, x, dev, reps=3):
-    """Time mlstm_parallel_bwd (float32 vector tiles) on the benchmarked layer."""
+def backward_timing(torch, mlstm, workloads, x, dev, reps=20):
+    """Time mlstm_parallel_bwd on the benchmarked layer (whole call: gate scan,
+    per-row scalars, the three tile passes, the gate-gradient scan)."""
     spec = x["spec"]
     B, NH, T, d = spec["B"], spec["NH"], spec["T"], spec["d"]
     dt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
@@ -220,7 +221,11 @@ def backward_timing(torch, mlstm, workloads, x, dev, reps=3):
     fg = torch.from_numpy(x["fgate"]).to(dev).contiguous()
     h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg)
     dh = torch.randn(q.shape, generator=torch.Generator().manual_seed(1)).to(dev).to(dt)
-    mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, dh)
+    mfma = spec["dtype"] == "bf16" and d <= 384
+    if not mfma:
+        reps = 3
+    for _ in range(2):
+        mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, dh)
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -230,13 +235,20 @@ def backward_timing(torch, mlstm, workloads, x, dev, reps=3):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    counted = 2.5 * workloads.counted_flops(B, NH, T, d)   # 5 causal contractions
-    executed = 3.5 * workloads.counted_flops(B, NH, T, d)  # 7: S and dh v^T recomputed twice
-    return {"ms_per_call": round(ms, 3), "counted_flops": counted,
+    cf = workloads.counted_flops(B, NH, T, d)  # two causal contractions
+    counted = 2.5 * cf  # five causal contractions: S, dh v^T, dQ, dK, dV
+    # executed: the matrix-core passes recompute S twice and dh v^T once (8
+    # contractions); the vector passes recompute S and dh v^T once (7)
+    executed = (4.0 if mfma else 3.5) * cf
+    peak = PEAK_BF16_TFLOPS if mfma else 157.3
+    return {"ms_per_call": round(ms, 4), "reps": reps,
+            "kernels": "bf16 matrix-core passes (dQ and r, dK and c, dV)" if mfma
+                       else "float32 vector passes",
+            "counted_flops": counted,
             "counted_TFLOP/s": round(counted / (ms * 1e-3) / 1e12, 2),
             "executed_TFLOP/s": round(executed / (ms * 1e-3) / 1e12, 2),
-            "bound": "alu", "peak_fp32_vector_TFLOP/s": 157.3,
-            "frac": round(executed / (ms * 1e-3) / 1e12 / 157.3, 4)}
+            "bound": "mfma" if mfma else "alu", "peak": peak,
+            "frac": round(counted / (ms * 1e-3) / 1e12 / peak, 4)}
 
 
 def main():

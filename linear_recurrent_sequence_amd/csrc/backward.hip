@@ -25,7 +25,10 @@
 // Four kernels: per-row scalars (1/n and db), a row pass (dQ and r, one
 // workgroup per 16 query rows), a column pass (dK, dV and c, one workgroup
 // per 16 keys), and a per-head reverse scan for the gate gradients.  Every
-// reduction has a fixed order: results are bitwise reproducible.
+// reduction has a fixed order: results are bitwise reproducible.  For bf16
+// inputs with d <= 384 the row and column passes run on the matrix cores
+// instead (backward_mfma.hip); the per-row scalars and the gate scan are
+// shared.
 #include "mlstm_internal.h"
 
 #include <hip/hip_bf16.h>
@@ -314,17 +317,24 @@ hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* f
                         const Tin* h, const float* m, const float* n, const float* b,
                         const Tin* dh, const Workspace& ws, float* inv_n, float* db, float* rsum,
                         float* csum, Tin* dq, Tin* dk, Tin* dv, float* digate, float* dfgate,
-                        int64_t H, int64_t T, int64_t d, bool exp_forget, hipStream_t stream) {
+                        int64_t H, int64_t T, int64_t d, bool exp_forget, bool mfma,
+                        hipStream_t stream) {
   const int64_t rows = H * T;
   hipLaunchKernelGGL(bwd_rows_prep_kernel<Tin>, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
                      stream, h, dh, m, n, b, inv_n, db, rows, int(d));
-  const int64_t tiles = (T + kBT - 1) / kBT;
-  hipLaunchKernelGGL(bwd_rows_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream, q,
-                     k, v, dh, inv_n, db, ws.anchor, ws.rowt, ws.colt, dq, rsum, T, int(d),
-                     ws.Tp, ws.nblk, tiles);
-  hipLaunchKernelGGL(bwd_cols_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream, q,
-                     k, v, dh, inv_n, db, ws.anchor, ws.rowt, ws.colt, dk, dv, csum, T, int(d),
-                     ws.Tp, ws.nblk, tiles);
+  if (mfma) {
+    const hipError_t e = launch_backward_mfma_tiles(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum,
+                                                    csum, H, T, d, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    const int64_t tiles = (T + kBT - 1) / kBT;
+    hipLaunchKernelGGL(bwd_rows_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream, q,
+                       k, v, dh, inv_n, db, ws.anchor, ws.rowt, ws.colt, dq, rsum, T, int(d),
+                       ws.Tp, ws.nblk, tiles);
+    hipLaunchKernelGGL(bwd_cols_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream, q,
+                       k, v, dh, inv_n, db, ws.anchor, ws.rowt, ws.colt, dk, dv, csum, T, int(d),
+                       ws.Tp, ws.nblk, tiles);
+  }
   hipLaunchKernelGGL(bwd_gates_kernel, dim3(unsigned(H)), dim3(kGThreads), 0, stream, fgate,
                      rsum, csum, digate, dfgate, T, int(exp_forget));
   return hipGetLastError();
@@ -354,13 +364,14 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                              static_cast<const B16*>(v), fgate, static_cast<const B16*>(h), m, n,
                              b, static_cast<const B16*>(dh), ws, inv_n, db, rsum, csum,
                              static_cast<B16*>(dq), static_cast<B16*>(dk), static_cast<B16*>(dv),
-                             digate, dfgate, H, T, d, exp_forget, stream);
+                             digate, dfgate, H, T, d, exp_forget, backward_mfma_supports(d),
+                             stream);
   }
   return launch_typed<float>(static_cast<const float*>(q), static_cast<const float*>(k),
                              static_cast<const float*>(v), fgate, static_cast<const float*>(h), m,
                              n, b, static_cast<const float*>(dh), ws, inv_n, db, rsum, csum,
                              static_cast<float*>(dq), static_cast<float*>(dk),
-                             static_cast<float*>(dv), digate, dfgate, H, T, d, exp_forget,
+                             static_cast<float*>(dv), digate, dfgate, H, T, d, exp_forget, false,
                              stream);
 }
 

@@ -1,0 +1,374 @@
+// Backward pass of the stabilized parallel mLSTM (xLSTM appendix A.3,
+// "Parallel mLSTM Backward Pass", Eqs. 87-105) on gfx950 matrix cores, for
+// bf16 inputs: the three tile passes of the float32 backward (backward.hip)
+// with every contraction on v_mfma_f32_32x32x16_bf16 (float32 accumulation).
+//
+// Each pass is a variant of the one-wave forward tile kernel.  A workgroup of
+// 4 waves (one per SIMD) owns 128 consecutive "own" rows of one head, 32 per
+// wave, whose operands stay in registers as the B operand of the first
+// products; the other axis is walked in tiles of 32 rows copied into LDS
+// (double buffered, one barrier per tile).  A lane holds one own row and 16
+// rows of the other axis of each 32 x 32 block (the accumulator layout):
+//
+//   rows pass (own = queries i, tiles of keys j):
+//     S^T = K_J Q^T and G^T = V_J dH^T       (s_ij = q_i . k_j, g_ij = dh_i . v_j)
+//     P_ij = E_ij (g_ij / n_i + db_i)        (E dC~', Eqs. 91-93)
+//     r_i += sum_j s_ij P_ij                  (row sums of dD~ = C~' (.) dC~', Eq. 95)
+//     dQ^T += K_J^T bf16(P^T)                 (Eq. 98)
+//   keys pass (own = keys j, tiles of queries i):
+//     S = Q_I K^T and G = dH_I V^T;  P as above
+//     c_j += sum_i s_ij P_ij                  (column sums, Eqs. 97, 105)
+//     dK^T += Q_I^T bf16(P)                   (Eq. 99)
+//   values pass (own = keys j, tiles of queries i):
+//     S = Q_I K^T;  dV^T += dH_I^T bf16(s_ij E_ij / n_i)     (Eq. 100)
+//
+// E_ij = D'_ij / sqrt(d) = 2^((A_i - A_j) + r_i + c_j) from the gate scan's
+// terms, as in the forward pass (0 above the diagonal and past the sequence
+// end).  The accumulation reads its first operand transposed from LDS with
+// ds_read_b64_tr_b16, in the key order of the accumulator layout.  The sums
+// r and c add float32 products of float32 values (no bf16 rounding); dQ, dK
+// and dV carry the bf16 rounding of P, as the forward's h~ carries that of
+// C~'.  The rows and keys passes hold two sets of own fragments and d / 2
+// accumulator registers, which bounds them to d <= 384.
+#include "mlstm_internal.h"
+#include "tile_common.h"
+
+namespace mlstm {
+namespace {
+
+using namespace tilecommon;
+
+constexpr int kBThreads = 256;  // 4 waves, one per SIMD
+constexpr int kBWaves = kBThreads / 64;
+constexpr int kBPf = 2;         // LDS fragment prefetch distance (MFMA steps)
+
+enum { kRowsPass = 0, kKeysPass = 1, kValuesPass = 2 };
+
+// LDS layout of one buffer.  X1 is the tensor of the first product (K in the
+// rows pass, Q otherwise), X2 that of the second product (V, dH) or, in the
+// values pass, of the accumulation (dH).  A tensor read only by rows takes
+// the stride 2 DP + 16 (16 consecutive rows hit 16 distinct 16-byte slots),
+// one read only transposed 2 DP + 64 (the 4 rows of a quad hit 4 distinct
+// 64-byte groups); X1 of the rows and keys passes is read both ways and takes
+// 2 DP + 32, which costs at most a 2-way conflict for either read.
+template <int DP, int MODE>
+struct BCfg {
+  static_assert(DP % 64 == 0 && DP >= 64 && DP <= 384, "head dim of the matrix-core backward");
+  static constexpr int CH = DP / 8;  // 16-byte chunks per row
+  static constexpr int S1 = MODE == kValuesPass ? 2 * DP + 16 : 2 * DP + 32;
+  static constexpr int S2 = MODE == kValuesPass ? 2 * DP + 64 : 2 * DP + 16;
+  static constexpr int X1_OFF = 0;
+  static constexpr int X2_OFF = kBN * S1;
+  static constexpr int GT = X2_OFF + kBN * S2;  // c_j (rows pass) or r_i of the tile, float32
+  static constexpr int GN = GT + 128;           // 1 / n_i of the tile (keys, values passes)
+  static constexpr int GD = GT + 256;           // db_i of the tile (keys pass)
+  static constexpr int GA = GT + 384;           // float64 anchor of the tile
+  static constexpr int BUF = GA + 16;
+  static constexpr int SA = MODE == kValuesPass ? S2 : S1;          // transposed operand's stride
+  static constexpr int A_OFF = MODE == kValuesPass ? X2_OFF : X1_OFF;
+  static_assert(2 * BUF <= 160 * 1024, "LDS budget");
+};
+
+template <int DP, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
+                          amdgpu_waves_per_eu(1, 1))) void bwd_mfma_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    const u16* __restrict__ dh, const float* __restrict__ inv_n, const float* __restrict__ db,
+    const double* __restrict__ anchor, const float* __restrict__ rowt,
+    const float* __restrict__ colt, u16* __restrict__ out, float* __restrict__ sums, int T,
+    int d, int Tp, int nblk, int row_tiles, int H) {
+  using C = BCfg<DP, MODE>;
+  constexpr bool kTwo = MODE != kValuesPass;  // a second first-stage product (G)
+  constexpr int NS = DP / 16;                 // MFMA steps of a first-stage product
+  constexpr int NV = DP / 16;                 // MFMA steps of the accumulation
+  __shared__ __attribute__((aligned(1024))) char smem0[C::BUF];
+  __shared__ __attribute__((aligned(1024))) char smem1[C::BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int j16 = l32 & 15;
+  int64_t I64, head64;
+  map_tile(blockIdx.x, row_tiles, H, I64, head64);
+  // heaviest blocks first: the last query blocks for the rows pass, the first
+  // key blocks for the key passes
+  const int I = MODE == kRowsPass ? int(I64) : row_tiles - 1 - int(I64);
+  const int head = int(head64);
+  const int64_t hoff = int64_t(head) * T * d;
+  const int ow = I * kBM + 32 * w;  // first own row of this wave
+  const int oi = ow + l32;          // own row of this lane (< Tp)
+  const int dch = d / 8;
+  const int n_tiles = (T + kBN - 1) / kBN;
+
+  const u16* own1 = MODE == kRowsPass ? q : k;
+  const u16* own2 = MODE == kRowsPass ? dh : v;
+  const u16* x1 = MODE == kRowsPass ? k : q;
+  const u16* x2 = MODE == kRowsPass ? v : dh;
+
+  // own fragments (B operands): row oi, head dims 16 s + 8 g + 0..7; rows past
+  // the sequence end and padded columns are zeros
+  auto load_frags = [&](const u16* src, bf16x8* f) {
+    const int row = oi < T ? oi : T - 1;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int col = 16 * s + 8 * g;
+      const bool ok = oi < T && col < d;
+      const uint4 raw = *reinterpret_cast<const uint4*>(src + hoff + int64_t(row) * d + (ok ? col : 0));
+      const uint4 val = ok ? raw : make_uint4(0, 0, 0, 0);
+      f[s] = *reinterpret_cast<const bf16x8*>(&val);
+    }
+  };
+  bf16x8 f1[NS];
+  bf16x8 f2[kTwo ? NS : 1];
+  load_frags(own1, f1);
+  if (kTwo) load_frags(own2, f2);
+
+  // own gate terms: r_i, 1/n_i, db_i (rows pass) or c_j (key passes; -inf past
+  // the sequence end), and the anchor of the wave's 32 rows
+  const float own_t = MODE == kRowsPass ? rowt[int64_t(head) * Tp + oi] : colt[int64_t(head) * Tp + oi];
+  const double a_own = anchor[int64_t(head) * nblk + ow / kAnchorBlock];
+  float own_in = 0.0f, own_db = 0.0f;
+  if (MODE == kRowsPass && oi < T) {
+    own_in = inv_n[int64_t(head) * T + oi];
+    own_db = db[int64_t(head) * T + oi];
+  }
+
+  f32x16 acc[DP / 32];
+#pragma unroll
+  for (int b = 0; b < DP / 32; ++b) acc[b] = f32x16{};
+  float dsum = 0.0f;
+
+  // tiles of the other axis: keys 0 .. the diagonal (rows pass) or queries
+  // from the diagonal to the end (key passes); per wave, the tiles that hold
+  // some causal pair with its own rows
+  const int first = MODE == kRowsPass ? 0 : 4 * I;
+  const int last = MODE == kRowsPass ? (4 * I + 3 < n_tiles - 1 ? 4 * I + 3 : n_tiles - 1) : n_tiles - 1;
+  auto wave_needs = [&](int J) { return MODE == kRowsPass ? J <= 4 * I + w : J >= 4 * I + w; };
+
+  auto load_tile = [&](int J, char* buf) {
+    const int x0 = J * kBN;
+    const int rows = T - x0 < kBN ? T - x0 : kBN;
+    const int64_t nrec = int64_t(rows) * d * 2;
+    const auto r1 = make_rsrc(x1 + hoff + int64_t(x0) * d, nrec);
+    const auto r2 = make_rsrc(x2 + hoff + int64_t(x0) * d, nrec);
+#pragma unroll
+    for (int i = 0; i < kBN / kBWaves; ++i) {
+      const int r = w * (kBN / kBWaves) + i;
+      if (lane < C::CH) {
+        const unsigned off = lane < dch ? unsigned(r * d * 2 + 16 * lane) : kOutOfRange;
+        dma16(r1, off, buf + C::X1_OFF + r * C::S1);
+        dma16(r2, off, buf + C::X2_OFF + r * C::S2);
+      }
+    }
+    const float* tsrc = MODE == kRowsPass ? colt : rowt;
+    if (w == 0 && lane < kBN / 4)
+      dma16(make_rsrc(tsrc + int64_t(head) * Tp + x0, kBN * 4), unsigned(16 * lane), buf + C::GT);
+    if (MODE != kRowsPass) {
+      // per-row scalars of [H][T] arrays: 4 bytes per lane (rows need not be
+      // 16-byte aligned); rows past the sequence end read as zeros
+      if (w == 1 && lane < kBN)
+        dma4(make_rsrc(inv_n + int64_t(head) * T + x0, int64_t(rows) * 4), unsigned(4 * lane),
+             buf + C::GN);
+      if (MODE == kKeysPass && w == 2 && lane < kBN)
+        dma4(make_rsrc(db + int64_t(head) * T + x0, int64_t(rows) * 4), unsigned(4 * lane),
+             buf + C::GD);
+    }
+    if (w == 3 && lane < 2)
+      dma4(make_rsrc(anchor + int64_t(head) * nblk + x0 / kAnchorBlock, 8), unsigned(4 * lane),
+           buf + C::GA);
+  };
+
+  // per-lane LDS offsets: rows of X1 / X2 for the first products, the
+  // transposed gather of the accumulation operand
+  const int off1 = C::X1_OFF + l32 * C::S1 + 16 * g;
+  const int off2 = C::X2_OFF + l32 * C::S2 + 16 * g;
+  const int offt = C::A_OFF + (4 * g + (j16 >> 2)) * C::SA + 32 * (l32 >> 4) + 8 * (j16 & 3);
+
+  auto compute = [&](const char* buf, int J) {
+    // first products: Y1 = X1_J Own1^T (and Y2 = X2_J Own2^T)
+    f32x16 y1 = f32x16{}, y2 = f32x16{};
+    {
+      const char* p = buf + off1;
+      bf16x8 kf[kBPf + 1];
+#pragma unroll
+      for (int t = 0; t < kBPf; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(p + 32 * t);
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        if (t + kBPf < NS)
+          kf[(t + kBPf) % (kBPf + 1)] = *reinterpret_cast<const bf16x8*>(p + 32 * (t + kBPf));
+        y1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kBPf + 1)], f1[t], y1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (kTwo) {
+      const char* p = buf + off2;
+      bf16x8 kf[kBPf + 1];
+#pragma unroll
+      for (int t = 0; t < kBPf; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(p + 32 * t);
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        if (t + kBPf < NS)
+          kf[(t + kBPf) % (kBPf + 1)] = *reinterpret_cast<const bf16x8*>(p + 32 * (t + kBPf));
+        y2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kBPf + 1)], f2[t], y2, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // lane (g, l32), register r: own row l32, other row 8(r/4) + 4g + r%4 of the tile
+    const double a_x = *reinterpret_cast<const double*>(buf + C::GA);
+    const float d_anchor = MODE == kRowsPass ? float(a_own - a_x) : float(a_x - a_own);  // A_i - A_j
+    const bool diag = J * kBN == ow;
+    const float* gt = reinterpret_cast<const float*>(buf + C::GT);
+    const float* gn = reinterpret_cast<const float*>(buf + C::GN);
+    const float* gd = reinterpret_cast<const float*>(buf + C::GD);
+    float pv[16];
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const float4 t4 = *reinterpret_cast<const float4*>(gt + 8 * rq + 4 * g);
+      const float tt[4] = {t4.x, t4.y, t4.z, t4.w};
+      float nn[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (MODE != kRowsPass) {
+        const float4 n4 = *reinterpret_cast<const float4*>(gn + 8 * rq + 4 * g);
+        nn[0] = n4.x; nn[1] = n4.y; nn[2] = n4.z; nn[3] = n4.w;
+      }
+      if (MODE == kKeysPass) {
+        const float4 d4 = *reinterpret_cast<const float4*>(gd + 8 * rq + 4 * g);
+        dd[0] = d4.x; dd[1] = d4.y; dd[2] = d4.z; dd[3] = d4.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ol = 8 * rq + 4 * g + e;  // other row within the tile
+        // causal pairs j <= i only (Eq. 71), and real rows only
+        bool valid;
+        if (MODE == kRowsPass) valid = oi < T && !(diag && ol > l32);
+        else valid = J * kBN + ol < T && !(diag && l32 > ol);
+        const float E = valid ? __builtin_amdgcn_exp2f(d_anchor + own_t + tt[e]) : 0.0f;
+        const float s = y1[4 * rq + e];
+        if (MODE == kValuesPass) {
+          pv[4 * rq + e] = s * E * nn[e];
+        } else {
+          const float in_i = MODE == kRowsPass ? own_in : nn[e];
+          const float db_i = MODE == kRowsPass ? own_db : dd[e];
+          const float P = E * (y2[4 * rq + e] * in_i + db_i);
+          dsum += s * P;
+          pv[4 * rq + e] = P;
+        }
+      }
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pb[0][e] = (__bf16)pv[e];
+      pb[1][e] = (__bf16)pv[8 + e];
+    }
+    // accumulation: step t = (column block b, half c of the tile's rows); the
+    // A operand holds X[16c + 4g + 0..3][32b + l32] and X[16c + 8 + 4g + 0..3][32b + l32]
+    {
+      const char* p = buf + offt;
+      i16x4 lo[kBPf + 1], hi[kBPf + 1];
+      auto addr = [&](int t) { return p + 16 * (t & 1) * C::SA + 64 * (t >> 1); };
+#pragma unroll
+      for (int t = 0; t < kBPf; ++t) {
+        lo[t] = tr_read(addr(t));
+        hi[t] = tr_read(addr(t) + 8 * C::SA);
+      }
+#pragma unroll
+      for (int t = 0; t < NV; ++t) {
+        const int tn = t + kBPf;
+        if (tn < NV) {
+          lo[tn % (kBPf + 1)] = tr_read(addr(tn));
+          hi[tn % (kBPf + 1)] = tr_read(addr(tn) + 8 * C::SA);
+        }
+        const i16x8 a16 = __builtin_shufflevector(lo[t % (kBPf + 1)], hi[t % (kBPf + 1)], 0, 1, 2,
+                                                  3, 4, 5, 6, 7);
+        acc[t >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16),
+                                                              pb[t & 1], acc[t >> 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  load_tile(first, smem0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int J = first; J <= last; J += 2) {
+    if (J + 1 <= last) load_tile(J + 1, smem1);
+    if (wave_needs(J)) compute(smem0, J);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (J + 1 > last) break;
+    if (J + 2 <= last) load_tile(J + 2, smem0);
+    if (wave_needs(J + 1)) compute(smem1, J + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // ---- epilogue: the row or column sums of dD~, and dQ / dK / dV in bf16
+  if (MODE != kValuesPass) {
+    dsum += __shfl_xor(dsum, 32, 64);
+    if (oi < T && g == 0) sums[int64_t(head) * T + oi] = dsum;
+  }
+  if (oi < T) {
+    const int64_t row = hoff + int64_t(oi) * d;
+#pragma unroll
+    for (int b = 0; b < DP / 32; ++b) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int col = 32 * b + 8 * rq + 4 * g;
+        if (col < d) {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[b][4 * rq + e];
+          *reinterpret_cast<bf16x4*>(out + row + col) = o;
+        }
+      }
+    }
+  }
+}
+
+template <int DP, int MODE>
+void launch_pass(const void* q, const void* k, const void* v, const void* dh, const float* inv_n,
+                 const float* db, const Workspace& ws, void* out, float* sums, int64_t H,
+                 int64_t T, int64_t d, hipStream_t stream) {
+  const int64_t row_tiles = (T + kBM - 1) / kBM;
+  hipLaunchKernelGGL((bwd_mfma_kernel<DP, MODE>), dim3(unsigned(row_tiles * H)), dim3(kBThreads),
+                     0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                     static_cast<const u16*>(v), static_cast<const u16*>(dh), inv_n, db,
+                     ws.anchor, ws.rowt, ws.colt, static_cast<u16*>(out), sums, int(T), int(d),
+                     int(ws.Tp), int(ws.nblk), int(row_tiles), int(H));
+}
+
+template <int DP>
+void launch_all(const void* q, const void* k, const void* v, const void* dh, const float* inv_n,
+                const float* db, const Workspace& ws, void* dq, void* dk, void* dv, float* rsum,
+                float* csum, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+  launch_pass<DP, kRowsPass>(q, k, v, dh, inv_n, db, ws, dq, rsum, H, T, d, stream);
+  launch_pass<DP, kKeysPass>(q, k, v, dh, inv_n, db, ws, dk, csum, H, T, d, stream);
+  launch_pass<DP, kValuesPass>(q, k, v, dh, inv_n, db, ws, dv, nullptr, H, T, d, stream);
+}
+
+}  // namespace
+
+bool backward_mfma_supports(int64_t d) { return d % 16 == 0 && d >= 16 && d <= 384; }
+
+hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* v,
+                                      const void* dh, const float* inv_n, const float* db,
+                                      const Workspace& ws, void* dq, void* dk, void* dv,
+                                      float* rsum, float* csum, int64_t H, int64_t T, int64_t d,
+                                      hipStream_t stream) {
+  if (!backward_mfma_supports(d)) return hipErrorInvalidValue;
+  // head dims are padded up to a multiple of 64 (zero columns add nothing)
+  switch ((d + 63) / 64) {
+    case 1: launch_all<64>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 2: launch_all<128>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 3: launch_all<192>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 4: launch_all<256>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 5: launch_all<320>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 6: launch_all<384>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mlstm

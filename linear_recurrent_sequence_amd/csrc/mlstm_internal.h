@@ -147,6 +147,16 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                            void* dv, float* digate, float* dfgate, int64_t H, int64_t T,
                            int64_t d, bool is_bf16, bool exp_forget, hipStream_t stream);
 
+// The row and column passes of the backward on the matrix cores (bf16,
+// d <= 384): dQ and the row sums r of dD~, dK and the column sums c, dV, from
+// the per-row scalars 1/n and db of the float32 backward.
+bool backward_mfma_supports(int64_t d);
+hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* v,
+                                      const void* dh, const float* inv_n, const float* db,
+                                      const Workspace& ws, void* dq, void* dk, void* dv,
+                                      float* rsum, float* csum, int64_t H, int64_t T, int64_t d,
+                                      hipStream_t stream);
+
 // Recurrent step (generation), stabilized states in float32: C [H][d][d],
 // n [H][d], m [H].  C_out may equal C_in; n_out / m_out must not overlap
 // n_in / m_in.  den_out [H] is optional.  hipErrorInvalidValue for an
