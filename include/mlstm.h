@@ -232,8 +232,12 @@ int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v,
  * with forget_activation MLSTM_FORGET_EXP, d(log f)/df~ = 1.  The forward
  * outputs must come from the same forget_activation.
  * dL/dn uses sum_j C~'_ij v_j = n_i h~_i, so for bf16 it carries the
- * rounding of the stored h~.  Arithmetic is float32 on the vector ALUs
- * (tiles of 16 x 16); the library allocates a stream-ordered workspace.
+ * rounding of the stored h~.  For bf16 the contractions run on the matrix
+ * cores (bf16 operands, float32 accumulation; the operand E (.) dC~' of the
+ * dQ and dK products and C~'/n of the dV product are rounded to bf16, the
+ * row and column sums of dD~ behind the gate gradients are not); for float32
+ * everything is float32 on the vector ALUs.  Results are bitwise
+ * reproducible.  The library allocates a stream-ordered workspace.
  * Pointers 16-byte aligned; no output may alias an input.  d <= 512
  * (MLSTM_ERR_HEAD_DIM above).  Other errors as for mlstm_parallel_fwd.
  */

@@ -26,7 +26,7 @@
 // workgroup per 16 query rows), a column pass (dK, dV and c, one workgroup
 // per 16 keys), and a per-head reverse scan for the gate gradients.  Every
 // reduction has a fixed order: results are bitwise reproducible.  For bf16
-// inputs with d <= 384 the row and column passes run on the matrix cores
+// inputs the row and column passes run on the matrix cores
 // instead (backward_mfma.hip); the per-row scalars and the gate scan are
 // shared.
 #include "mlstm_internal.h"

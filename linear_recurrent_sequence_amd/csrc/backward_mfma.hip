@@ -29,7 +29,9 @@
 // r and c add float32 products of float32 values (no bf16 rounding); dQ, dK
 // and dV carry the bf16 rounding of P, as the forward's h~ carries that of
 // C~'.  The rows and keys passes hold two sets of own fragments and d / 2
-// accumulator registers, which bounds them to d <= 384.
+// accumulator registers; above d = 384 that exceeds a wave's 512 registers,
+// so there each of those passes is split over two workgroups per row block
+// that recompute S and G and accumulate one half of the output columns each.
 #include "mlstm_internal.h"
 #include "tile_common.h"
 
@@ -53,7 +55,10 @@ enum { kRowsPass = 0, kKeysPass = 1, kValuesPass = 2 };
 // 2 DP + 32, which costs at most a 2-way conflict for either read.
 template <int DP, int MODE>
 struct BCfg {
-  static_assert(DP % 64 == 0 && DP >= 64 && DP <= 384, "head dim of the matrix-core backward");
+  static_assert(DP % 64 == 0 && DP >= 64 && DP <= 512, "head dim of the matrix-core backward");
+  // output-column halves per row block (see the notes above)
+  static constexpr int SPLIT = (MODE != kValuesPass && DP > 384) ? 2 : 1;
+  static constexpr int NB = DP / 32 / SPLIT;  // 32-column accumulator blocks per wave
   static constexpr int CH = DP / 8;  // 16-byte chunks per row
   static constexpr int S1 = MODE == kValuesPass ? 2 * DP + 16 : 2 * DP + 32;
   static constexpr int S2 = MODE == kValuesPass ? 2 * DP + 64 : 2 * DP + 16;
@@ -80,7 +85,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   using C = BCfg<DP, MODE>;
   constexpr bool kTwo = MODE != kValuesPass;  // a second first-stage product (G)
   constexpr int NS = DP / 16;                 // MFMA steps of a first-stage product
-  constexpr int NV = DP / 16;                 // MFMA steps of the accumulation
+  constexpr int NV = 2 * C::NB;               // MFMA steps of the accumulation
+  const int cb0 = C::NB * int(blockIdx.y);    // first 32-column block of this workgroup
   __shared__ __attribute__((aligned(1024))) char smem0[C::BUF];
   __shared__ __attribute__((aligned(1024))) char smem1[C::BUF];
 
@@ -135,9 +141,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     own_db = db[int64_t(head) * T + oi];
   }
 
-  f32x16 acc[DP / 32];
+  f32x16 acc[C::NB];
 #pragma unroll
-  for (int b = 0; b < DP / 32; ++b) acc[b] = f32x16{};
+  for (int b = 0; b < C::NB; ++b) acc[b] = f32x16{};
   float dsum = 0.0f;
 
   // tiles of the other axis: keys 0 .. the diagonal (rows pass) or queries
@@ -267,7 +273,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     {
       const char* p = buf + offt;
       i16x4 lo[kBPf + 1], hi[kBPf + 1];
-      auto addr = [&](int t) { return p + 16 * (t & 1) * C::SA + 64 * (t >> 1); };
+      auto addr = [&](int t) { return p + 16 * (t & 1) * C::SA + 64 * (cb0 + (t >> 1)); };
 #pragma unroll
       for (int t = 0; t < kBPf; ++t) {
         lo[t] = tr_read(addr(t));
@@ -307,15 +313,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   // ---- epilogue: the row or column sums of dD~, and dQ / dK / dV in bf16
   if (MODE != kValuesPass) {
     dsum += __shfl_xor(dsum, 32, 64);
-    if (oi < T && g == 0) sums[int64_t(head) * T + oi] = dsum;
+    if (oi < T && g == 0 && blockIdx.y == 0) sums[int64_t(head) * T + oi] = dsum;
   }
   if (oi < T) {
     const int64_t row = hoff + int64_t(oi) * d;
 #pragma unroll
-    for (int b = 0; b < DP / 32; ++b) {
+    for (int b = 0; b < C::NB; ++b) {
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int col = 32 * b + 8 * rq + 4 * g;
+        const int col = 32 * (cb0 + b) + 8 * rq + 4 * g;
         if (col < d) {
           bf16x4 o;
 #pragma unroll
@@ -332,7 +338,8 @@ void launch_pass(const void* q, const void* k, const void* v, const void* dh, co
                  const float* db, const Workspace& ws, void* out, float* sums, int64_t H,
                  int64_t T, int64_t d, hipStream_t stream) {
   const int64_t row_tiles = (T + kBM - 1) / kBM;
-  hipLaunchKernelGGL((bwd_mfma_kernel<DP, MODE>), dim3(unsigned(row_tiles * H)), dim3(kBThreads),
+  hipLaunchKernelGGL((bwd_mfma_kernel<DP, MODE>),
+                     dim3(unsigned(row_tiles * H), unsigned(BCfg<DP, MODE>::SPLIT)), dim3(kBThreads),
                      0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), static_cast<const u16*>(dh), inv_n, db,
                      ws.anchor, ws.rowt, ws.colt, static_cast<u16*>(out), sums, int(T), int(d),
@@ -350,7 +357,7 @@ void launch_all(const void* q, const void* k, const void* v, const void* dh, con
 
 }  // namespace
 
-bool backward_mfma_supports(int64_t d) { return d % 16 == 0 && d >= 16 && d <= 384; }
+bool backward_mfma_supports(int64_t d) { return d % 16 == 0 && d >= 16 && d <= 512; }
 
 hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* v,
                                       const void* dh, const float* inv_n, const float* db,
@@ -366,6 +373,8 @@ hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* 
     case 4: launch_all<256>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
     case 5: launch_all<320>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
     case 6: launch_all<384>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 7: launch_all<448>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 8: launch_all<512>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -148,7 +148,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                            int64_t d, bool is_bf16, bool exp_forget, hipStream_t stream);
 
 // The row and column passes of the backward on the matrix cores (bf16,
-// d <= 384): dQ and the row sums r of dD~, dK and the column sums c, dV, from
+// d <= 512): dQ and the row sums r of dD~, dK and the column sums c, dV, from
 // the per-row scalars 1/n and db of the float32 backward.
 bool backward_mfma_supports(int64_t d);
 hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* v,

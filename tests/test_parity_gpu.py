@@ -705,6 +705,7 @@ BWD_MFMA_CASES = [
     spec(8, 1, 140, 64),  # head count divisible by 8 (XCD-grouped schedule)
     spec(1, 2, 333, 160, ig=("uniform", -20, 20), fg=("normal", 0, 4), fgate_floor=(0.01, -30.0)),
     spec(1, 1, 200, 64, ig=("normal", 0, 2), fg=("normal", 1, 2)),
+    spec(1, 1, 150, 448), spec(2, 1, 129, 512),  # output columns split over two workgroups
 ]
 
 
@@ -762,4 +763,13 @@ def test_backward_mfma_full_size_sampled_heads():
     dh_np = W.round_bf16(np.random.default_rng(34).standard_normal(x["q"].shape)
                          .astype(np.float32))
     got, ref, fwd = _backward_case(x, dh_np, heads=[(0, 0), (7, 3)])
+    _check_backward(got, ref, fwd)
+
+
+def test_backward_mfma_full_size_sub_heads_of_512():
+    """The 1.3B-shaped layer as sub-heads of 512 (B=4, NH=8, T=2048): two heads."""
+    x = W.make("xlstm1p3b_layer", seed=0)
+    dh_np = W.round_bf16(np.random.default_rng(35).standard_normal(x["q"].shape)
+                         .astype(np.float32))
+    got, ref, fwd = _backward_case(x, dh_np, heads=[(0, 1), (3, 7)])
     _check_backward(got, ref, fwd)
