@@ -16,17 +16,18 @@
 // terms each grow with the sequence length.
 //
 // One workgroup of 512 threads per head walks the sequence in chunks of
-// 4096 positions; each thread owns 8 consecutive positions (one eighth of a
-// 64-position anchor block).  Sums and the max-plus maps are carried in
-// float64; log sigmoid is evaluated in float32 (its relative error stays
-// local: only sums over the few positions where D' is not negligible matter).
+// 2048 positions; each thread owns 4 consecutive positions (one sixteenth of
+// a 64-position anchor block), loaded and stored as 16-byte vectors where the
+// row alignment allows.  Sums and the max-plus maps are carried in float64;
+// log sigmoid is evaluated in float32 (its relative error stays local: only
+// sums over the few positions where D' is not negligible matter).
 #include "mlstm_internal.h"
 
 namespace mlstm {
 namespace {
 
 constexpr int kScanThreads = 512;
-constexpr int kScanPer = 8;  // positions per thread per chunk
+constexpr int kScanPer = 4;  // positions per thread per chunk
 constexpr int kScanWaves = kScanThreads / 64;
 
 struct MaxPlus {  // the map x -> max(x + a, b)
@@ -64,6 +65,9 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
   float* cx = colx + head * Tp;
   float* rb = rowb + head * (Tp / kBoundTile);
   float* kb = keyb + head * (Tp / kBoundTile);
+  // the rows of the [H][T] arrays start 16-byte aligned when T % 4 == 0
+  // (their base pointers are 16-byte aligned)
+  const bool vec_rows = (T & 3) == 0;
 
   __shared__ double s_sum[kScanWaves];
   __shared__ double s_a[kScanWaves];
@@ -76,18 +80,25 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     const int64_t p0 = base + int64_t(tid) * kScanPer;
     float fb[kScanPer];
     float iv[kScanPer];
+    if (vec_rows && p0 + kScanPer <= T) {
+      const float4 f4 = *reinterpret_cast<const float4*>(f + p0);
+      const float4 i4 = *reinterpret_cast<const float4*>(ig + p0);
+      fb[0] = f4.x; fb[1] = f4.y; fb[2] = f4.z; fb[3] = f4.w;
+      iv[0] = i4.x; iv[1] = i4.y; iv[2] = i4.z; iv[3] = i4.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < kScanPer; ++e) {
+        const int64_t p = p0 + e;
+        fb[e] = p < T ? f[p] : 0.0f;
+        iv[e] = p < T ? ig[p] : -INFINITY;
+      }
+    }
     double tsum = 0.0;
     MaxPlus tmap = {0.0, -INFINITY};
 #pragma unroll
     for (int e = 0; e < kScanPer; ++e) {
-      const int64_t p = p0 + e;
-      if (p < T) {
-        fb[e] = exp_forget ? f[p] : log_sigmoid(f[p]);  // log f_t
-        iv[e] = ig[p];
-      } else {  // padding: no forgetting, no input; never reaches a real row
-        fb[e] = 0.0f;
-        iv[e] = -INFINITY;
-      }
+      // log f_t; padding has no forgetting and no input and never reaches a real row
+      fb[e] = p0 + e < T ? (exp_forget ? fb[e] : log_sigmoid(fb[e])) : 0.0f;
       tsum += double(fb[e]);
       tmap = compose(tmap, MaxPlus{double(fb[e]), double(iv[e])});
     }
@@ -135,47 +146,56 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     double cs = carry_cs + wsum + lsum;                 // sum of fbar before p0
     double m = apply(lmap, apply(wmap, carry_m));       // m at p0 - 1
     // anchor of this thread's 64-block: the prefix sum before the block start,
-    // held by the first of the 8 threads that share the block
-    const double blk_anchor = __shfl(cs, lane & ~7, 64);
+    // held by the first of the 16 threads that share the block
+    const double blk_anchor = __shfl(cs, lane & ~15, 64);
     if (p0 < Tp && (p0 & (kAnchorBlock - 1)) == 0) anc[p0 / kAnchorBlock] = blk_anchor * kLog2e;
     float rmax = -INFINITY, cmax = -INFINITY;  // of the values stored below
-    float cvals[kScanPer];
+    float mv[kScanPer], rv[kScanPer], cv[kScanPer];
 #pragma unroll
     for (int e = 0; e < kScanPer; ++e) {
-      cvals[e] = -INFINITY;
       const int64_t p = p0 + e;
       cs += double(fb[e]);
       m = fmax(m + double(fb[e]), double(iv[e]));
       const double loc = cs - blk_anchor;
       if (p < T) {
-        const float r = float((loc - m - half_ln_d) * kLog2e);
-        const float c = float((double(iv[e]) - loc) * kLog2e);
-        mo[p] = float(m);
-        rt[p] = r;
-        ct[p] = c;
-        cvals[e] = c;
-        rmax = fmaxf(rmax, r);
-        cmax = fmaxf(cmax, c);
-      } else if (p < Tp) {
-        rt[p] = 0.0f;
-        ct[p] = -INFINITY;
+        mv[e] = float(m);
+        rv[e] = float((loc - m - half_ln_d) * kLog2e);
+        cv[e] = float((double(iv[e]) - loc) * kLog2e);
+        rmax = fmaxf(rmax, rv[e]);
+        cmax = fmaxf(cmax, cv[e]);
+      } else {  // padding up to Tp
+        mv[e] = 0.0f;
+        rv[e] = 0.0f;
+        cv[e] = -INFINITY;
         rmax = fmaxf(rmax, 0.0f);
       }
     }
-    // tile bounds: the 4 threads of a 32-position tile are 4 consecutive lanes
+    // tile bounds: the 8 threads of a 32-position tile are 8 consecutive lanes
     rmax = fmaxf(rmax, __shfl_xor(rmax, 1, 64));
     rmax = fmaxf(rmax, __shfl_xor(rmax, 2, 64));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 4, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 1, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 2, 64));
-    if (p0 < Tp && (p0 & (kBoundTile - 1)) == 0) {
-      rb[p0 / kBoundTile] = rmax;
-      kb[p0 / kBoundTile] = cmax;
-    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 4, 64));
     // the key factor of the factored exponent, relative to its tile's maximum
+    float xv[kScanPer];
 #pragma unroll
-    for (int e = 0; e < kScanPer; ++e) {
-      const int64_t p = p0 + e;
-      if (p < Tp) cx[p] = p < T ? float(exp2(double(cvals[e]) - double(cmax))) : 0.0f;
+    for (int e = 0; e < kScanPer; ++e) xv[e] = p0 + e < T ? exp2f(cv[e] - cmax) : 0.0f;
+    if (p0 < Tp) {  // Tp is a multiple of 128: the 4 positions are all below it
+      *reinterpret_cast<float4*>(rt + p0) = make_float4(rv[0], rv[1], rv[2], rv[3]);
+      *reinterpret_cast<float4*>(ct + p0) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+      *reinterpret_cast<float4*>(cx + p0) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+      if ((p0 & (kBoundTile - 1)) == 0) {
+        rb[p0 / kBoundTile] = rmax;
+        kb[p0 / kBoundTile] = cmax;
+      }
+    }
+    if (vec_rows && p0 + kScanPer <= T) {
+      *reinterpret_cast<float4*>(mo + p0) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kScanPer; ++e)
+        if (p0 + e < T) mo[p0 + e] = mv[e];
     }
     carry_cs += tot_sum;
     carry_m = apply(tot_map, carry_m);
