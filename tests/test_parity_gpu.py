@@ -773,3 +773,24 @@ def test_backward_mfma_full_size_sub_heads_of_512():
                          .astype(np.float32))
     got, ref, fwd = _backward_case(x, dh_np, heads=[(0, 1), (3, 7)])
     _check_backward(got, ref, fwd)
+
+
+# ---------------------------------------------------------------------------
+# large shapes: a 65536-position head (512 row tiles, 2048 key tiles) and a
+# thousand small heads (grid and index arithmetic at size)
+# ---------------------------------------------------------------------------
+
+def test_long_sequence_sampled():
+    x = W.make(spec(1, 1, 65536, 64), seed=36)
+    h, m, n = run_gpu(x)
+    rows = _sample_rows(x["spec"]["T"], np.random.default_rng(37), count=24)
+    hr, mr, nr, _ = _sampled_reference(x, rows)
+    print(check(h[:, :, rows], m[:, :, rows], n[:, :, rows], hr, mr, nr, TOL_H["bf16"]))
+    assert np.isfinite(h).all() and np.isfinite(n).all()
+
+
+def test_many_small_heads():
+    x = W.make(spec(16, 64, 48, 16), seed=38)
+    h, m, n = run_gpu(x)
+    hr, mr, nr = oracle_full(x)[:3]
+    print(check(h, m, n, hr, mr, nr, TOL_H["bf16"]))
