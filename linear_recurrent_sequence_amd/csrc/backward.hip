@@ -26,9 +26,9 @@
 // workgroup per 16 query rows), a column pass (dK, dV and c, one workgroup
 // per 16 keys), and a per-head reverse scan for the gate gradients.  Every
 // reduction has a fixed order: results are bitwise reproducible.  For bf16
-// inputs the row and column passes run on the matrix cores
-// instead (backward_mfma.hip); the per-row scalars and the gate scan are
-// shared.
+// inputs the row and column passes run on the matrix cores instead
+// (backward_mfma.hip, whose rows pass also forms the per-row scalars); the
+// gate-gradient scan is shared.
 #include "mlstm_internal.h"
 
 #include <hip/hip_bf16.h>
@@ -319,14 +319,14 @@ hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* f
                         float* csum, Tin* dq, Tin* dk, Tin* dv, float* digate, float* dfgate,
                         int64_t H, int64_t T, int64_t d, bool exp_forget, bool mfma,
                         hipStream_t stream) {
-  const int64_t rows = H * T;
-  hipLaunchKernelGGL(bwd_rows_prep_kernel<Tin>, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
-                     stream, h, dh, m, n, b, inv_n, db, rows, int(d));
-  if (mfma) {
-    const hipError_t e = launch_backward_mfma_tiles(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum,
-                                                    csum, H, T, d, stream);
+  if (mfma) {  // the rows pass forms the per-row scalars itself
+    const hipError_t e = launch_backward_mfma_tiles(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq,
+                                                    dk, dv, rsum, csum, H, T, d, stream);
     if (e != hipSuccess) return e;
   } else {
+    const int64_t rows = H * T;
+    hipLaunchKernelGGL(bwd_rows_prep_kernel<Tin>, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
+                       stream, h, dh, m, n, b, inv_n, db, rows, int(d));
     const int64_t tiles = (T + kBT - 1) / kBT;
     hipLaunchKernelGGL(bwd_rows_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream, q,
                        k, v, dh, inv_n, db, ws.anchor, ws.rowt, ws.colt, dq, rsum, T, int(d),

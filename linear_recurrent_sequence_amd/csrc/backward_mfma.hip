@@ -28,7 +28,9 @@
 // ds_read_b64_tr_b16, in the key order of the accumulator layout.  The sums
 // r and c add float32 products of float32 values (no bf16 rounding); dQ, dK
 // and dV carry the bf16 rounding of P, as the forward's h~ carries that of
-// C~'.  The rows and keys passes hold two sets of own fragments and d / 2
+// C~'.  The rows pass also forms the per-row scalars 1/n_i and db_i
+// (Eqs. 88-90, from dh_i . h~_i) for its own rows and stores them for the two
+// key passes.  The rows and keys passes hold two sets of own fragments and d / 2
 // accumulator registers; above d = 384 that exceeds a wave's 512 registers,
 // so there each of those passes is split over two workgroups per row block
 // that recompute S and G and accumulate one half of the output columns each.
@@ -78,8 +80,9 @@ template <int DP, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
                           amdgpu_waves_per_eu(1, 1))) void bwd_mfma_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    const u16* __restrict__ dh, const float* __restrict__ inv_n, const float* __restrict__ db,
-    const double* __restrict__ anchor, const float* __restrict__ rowt,
+    const u16* __restrict__ dh, const u16* __restrict__ hsrc, const float* __restrict__ m_in,
+    const float* __restrict__ n_in, const float* __restrict__ b_in, float* __restrict__ inv_n,
+    float* __restrict__ db, const double* __restrict__ anchor, const float* __restrict__ rowt,
     const float* __restrict__ colt, u16* __restrict__ out, float* __restrict__ sums, int T,
     int d, int Tp, int nblk, int row_tiles, int H) {
   using C = BCfg<DP, MODE>;
@@ -128,7 +131,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   };
   bf16x8 f1[NS];
   bf16x8 f2[kTwo ? NS : 1];
-  load_frags(own1, f1);
   if (kTwo) load_frags(own2, f2);
 
   // own gate terms: r_i, 1/n_i, db_i (rows pass) or c_j (key passes; -inf past
@@ -136,10 +138,39 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   const float own_t = MODE == kRowsPass ? rowt[int64_t(head) * Tp + oi] : colt[int64_t(head) * Tp + oi];
   const double a_own = anchor[int64_t(head) * nblk + ow / kAnchorBlock];
   float own_in = 0.0f, own_db = 0.0f;
-  if (MODE == kRowsPass && oi < T) {
-    own_in = inv_n[int64_t(head) * T + oi];
-    own_db = db[int64_t(head) * T + oi];
+  if (MODE == kRowsPass) {
+    // dn_i = -(dh_i . h~_i) / n_i (Eqs. 88-89); db_i = sign(b_i) dn_i where
+    // |b_i| is above the floor exp(-m_i) (Eq. 90), else 0
+    float hd = 0.0f;
+    const int row = oi < T ? oi : T - 1;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int col = 16 * s + 8 * g;
+      const bool ok = oi < T && col < d;
+      const uint4 raw =
+          *reinterpret_cast<const uint4*>(hsrc + hoff + int64_t(row) * d + (ok ? col : 0));
+      const uint4 val = ok ? raw : make_uint4(0, 0, 0, 0);
+      const bf16x8 hv = *reinterpret_cast<const bf16x8*>(&val);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hd += float(f2[s][e]) * float(hv[e]);
+    }
+    hd += __shfl_xor(hd, 32, 64);
+    if (oi < T) {
+      const int64_t at = int64_t(head) * T + oi;
+      const float nn = n_in[at], bb = b_in[at];
+      const float dn = -hd / nn;
+      const bool above_floor = fabsf(bb) > expf(-m_in[at]);
+      own_in = 1.0f / nn;
+      own_db = above_floor ? (bb > 0.0f ? dn : (bb < 0.0f ? -dn : 0.0f)) : 0.0f;
+      if (g == 0 && blockIdx.y == 0) {  // for the key passes
+        inv_n[at] = own_in;
+        db[at] = own_db;
+      }
+    }
   }
+  // the h~ fragments are dead before the Q fragments are loaded
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags(own1, f1);
 
   f32x16 acc[C::NB];
 #pragma unroll
@@ -334,25 +365,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
 }
 
 template <int DP, int MODE>
-void launch_pass(const void* q, const void* k, const void* v, const void* dh, const float* inv_n,
-                 const float* db, const Workspace& ws, void* out, float* sums, int64_t H,
-                 int64_t T, int64_t d, hipStream_t stream) {
+void launch_pass(const void* q, const void* k, const void* v, const void* dh, const void* h,
+                 const float* m, const float* n, const float* b, float* inv_n, float* db,
+                 const Workspace& ws, void* out, float* sums, int64_t H, int64_t T, int64_t d,
+                 hipStream_t stream) {
   const int64_t row_tiles = (T + kBM - 1) / kBM;
   hipLaunchKernelGGL((bwd_mfma_kernel<DP, MODE>),
                      dim3(unsigned(row_tiles * H), unsigned(BCfg<DP, MODE>::SPLIT)), dim3(kBThreads),
                      0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), static_cast<const u16*>(dh), inv_n, db,
-                     ws.anchor, ws.rowt, ws.colt, static_cast<u16*>(out), sums, int(T), int(d),
+                     static_cast<const u16*>(v), static_cast<const u16*>(dh),
+                     static_cast<const u16*>(h), m, n, b, inv_n, db, ws.anchor, ws.rowt, ws.colt, static_cast<u16*>(out), sums, int(T), int(d),
                      int(ws.Tp), int(ws.nblk), int(row_tiles), int(H));
 }
 
 template <int DP>
-void launch_all(const void* q, const void* k, const void* v, const void* dh, const float* inv_n,
-                const float* db, const Workspace& ws, void* dq, void* dk, void* dv, float* rsum,
-                float* csum, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
-  launch_pass<DP, kRowsPass>(q, k, v, dh, inv_n, db, ws, dq, rsum, H, T, d, stream);
-  launch_pass<DP, kKeysPass>(q, k, v, dh, inv_n, db, ws, dk, csum, H, T, d, stream);
-  launch_pass<DP, kValuesPass>(q, k, v, dh, inv_n, db, ws, dv, nullptr, H, T, d, stream);
+void launch_all(const void* q, const void* k, const void* v, const void* dh, const void* h,
+                const float* m, const float* n, const float* b, float* inv_n, float* db,
+                const Workspace& ws, void* dq, void* dk, void* dv, float* rsum, float* csum,
+                int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+  launch_pass<DP, kRowsPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, rsum, H, T, d, stream);
+  launch_pass<DP, kKeysPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dk, csum, H, T, d, stream);
+  launch_pass<DP, kValuesPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dv, nullptr, H, T, d,
+                               stream);
 }
 
 }  // namespace
@@ -360,21 +394,22 @@ void launch_all(const void* q, const void* k, const void* v, const void* dh, con
 bool backward_mfma_supports(int64_t d) { return d % 16 == 0 && d >= 16 && d <= 512; }
 
 hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* v,
-                                      const void* dh, const float* inv_n, const float* db,
+                                      const void* dh, const void* h, const float* m,
+                                      const float* n, const float* b, float* inv_n, float* db,
                                       const Workspace& ws, void* dq, void* dk, void* dv,
                                       float* rsum, float* csum, int64_t H, int64_t T, int64_t d,
                                       hipStream_t stream) {
   if (!backward_mfma_supports(d)) return hipErrorInvalidValue;
   // head dims are padded up to a multiple of 64 (zero columns add nothing)
   switch ((d + 63) / 64) {
-    case 1: launch_all<64>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 2: launch_all<128>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 3: launch_all<192>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 4: launch_all<256>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 5: launch_all<320>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 6: launch_all<384>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 7: launch_all<448>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 8: launch_all<512>(q, k, v, dh, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 1: launch_all<64>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 2: launch_all<128>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 3: launch_all<192>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 4: launch_all<256>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 5: launch_all<320>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 6: launch_all<384>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 7: launch_all<448>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 8: launch_all<512>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -148,11 +148,12 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                            int64_t d, bool is_bf16, bool exp_forget, hipStream_t stream);
 
 // The row and column passes of the backward on the matrix cores (bf16,
-// d <= 512): dQ and the row sums r of dD~, dK and the column sums c, dV, from
-// the per-row scalars 1/n and db of the float32 backward.
+// d <= 512): dQ and the row sums r of dD~ (the rows pass also stores the
+// per-row scalars 1/n and db into inv_n, db), dK and the column sums c, dV.
 bool backward_mfma_supports(int64_t d);
 hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* v,
-                                      const void* dh, const float* inv_n, const float* db,
+                                      const void* dh, const void* h, const float* m,
+                                      const float* n, const float* b, float* inv_n, float* db,
                                       const Workspace& ws, void* dq, void* dk, void* dv,
                                       float* rsum, float* csum, int64_t H, int64_t T, int64_t d,
                                       hipStream_t stream);
