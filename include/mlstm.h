@@ -29,7 +29,9 @@
  * Ownership: every pointer is device memory owned by the caller, on the
  * device that is current when the call is made.  The library never frees or
  * retains a caller pointer beyond the work it enqueues.  Outputs are fully
- * overwritten.  Inputs and outputs must not alias.
+ * overwritten.  No output may overlap an input or another output (checked
+ * from the pointers and sizes: MLSTM_ERR_ALIAS, nothing launched); inputs
+ * may overlap each other.  The recurrent step alone may update C in place.
  *
  * Ordering: calls are asynchronous on the given HIP stream (NULL = the null
  * stream); results are valid once that stream has synchronized.  No host
@@ -104,7 +106,7 @@ enum {
   MLSTM_ERR_HIP = -6,         /* a HIP allocation or launch failed */
   MLSTM_ERR_WORKSPACE = -7,   /* caller workspace smaller than mlstm_workspace_bytes */
   MLSTM_ERR_KERNEL = -8,      /* unknown kernel selector, or an MFMA selector for fp32 */
-  MLSTM_ERR_ALIAS = -9,       /* an output overlaps an input it must not alias */
+  MLSTM_ERR_ALIAS = -9,       /* an output overlaps an input or another output */
   MLSTM_ERR_ACTIVATION = -10  /* unknown forget-gate activation */
 };
 

@@ -6,6 +6,8 @@
 
 #include <stdint.h>
 
+#include <initializer_list>
+
 namespace {
 
 using mlstm::Workspace;
@@ -36,6 +38,43 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MLSTM_OK : MLSTM_ERR_HIP; }
+
+// a caller buffer's byte range; a null pointer or an empty range is skipped
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// MLSTM_ERR_ALIAS if an output overlaps an input or another output (inputs
+// may overlap each other: they are only read).  Runs after every other
+// argument check, on shapes that check_shape has bounded.
+int check_alias(std::initializer_list<Span> ins, std::initializer_list<Span> outs) {
+  for (const Span* o = outs.begin(); o != outs.end(); ++o) {
+    if (!o->p || o->n == 0) continue;
+    for (const Span& i : ins)
+      if (i.p && i.n && overlaps(o->p, o->n, i.p, i.n)) return MLSTM_ERR_ALIAS;
+    for (const Span* o2 = outs.begin(); o2 != o; ++o2)
+      if (o2->p && o2->n && overlaps(o->p, o->n, o2->p, o2->n)) return MLSTM_ERR_ALIAS;
+  }
+  return MLSTM_OK;
+}
+
+// bytes of a [B][NH][T][d] tensor of `dtype` and of a [B][NH][T] float32 array
+size_t tensor_bytes(int64_t B, int64_t NH, int64_t T, int64_t d, int dtype) {
+  return size_t(B * NH) * size_t(T) * size_t(d) * (dtype == MLSTM_BF16 ? 2 : 4);
+}
+size_t rows_bytes(int64_t B, int64_t NH, int64_t T) { return size_t(B * NH) * size_t(T) * 4; }
+
+// the forward's inputs against its outputs (optional ones may be NULL)
+int check_forward_alias(const void* q, const void* k, const void* v, const float* igate,
+                        const float* fgate, const void* ogate, const void* h_out,
+                        const void* htilde_out, const float* m_out, const float* n_out,
+                        const float* b_out, int64_t B, int64_t NH, int64_t T, int64_t d,
+                        int dtype) {
+  const size_t tb = tensor_bytes(B, NH, T, d, dtype), rb = rows_bytes(B, NH, T);
+  return check_alias({{q, tb}, {k, tb}, {v, tb}, {igate, rb}, {fgate, rb}, {ogate, tb}},
+                     {{h_out, tb}, {htilde_out, tb}, {m_out, rb}, {n_out, rb}, {b_out, rb}});
+}
 
 int check_scan_args(const float* igate, const float* fgate, const float* m_out, const void* ws) {
   if (!igate || !fgate || !m_out || !ws) return MLSTM_ERR_NULL;
@@ -142,6 +181,10 @@ int mlstm_gate_scan(const float* igate, const float* fgate, float* m_out, void* 
   if ((st = check_shape(B, NH, T, d)) != MLSTM_OK) return st;
   const int64_t H = B * NH;
   if (workspace_bytes < mlstm::workspace_bytes(H, T)) return MLSTM_ERR_WORKSPACE;
+  const size_t rb = rows_bytes(B, NH, T);
+  if ((st = check_alias({{igate, rb}, {fgate, rb}},
+                        {{m_out, rb}, {workspace, mlstm::workspace_bytes(H, T)}})) != MLSTM_OK)
+    return st;
   const Workspace w = mlstm::carve(workspace, H, T);
   return hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d,
                                             forget_activation == MLSTM_FORGET_EXP,
@@ -157,6 +200,11 @@ int mlstm_causal_tiles(const void* q, const void* k, const void* v, const float*
   if ((st = check_shape(B, NH, T, d)) != MLSTM_OK) return st;
   const int64_t H = B * NH;
   if (workspace_bytes < mlstm::workspace_bytes(H, T)) return MLSTM_ERR_WORKSPACE;
+  const size_t tb = tensor_bytes(B, NH, T, d, dtype), rb = rows_bytes(B, NH, T);
+  if ((st = check_alias({{q, tb}, {k, tb}, {v, tb}, {m, rb},
+                         {workspace, mlstm::workspace_bytes(H, T)}},
+                        {{h_out, tb}, {n_out, rb}})) != MLSTM_OK)
+    return st;
   const Workspace w = mlstm::carve(const_cast<void*>(workspace), H, T);
   return run_tiles(q, k, v, m, w, h_out, n_out, mlstm::Epilogue{}, H, T, d, dtype, kernel,
                    static_cast<hipStream_t>(stream));
@@ -166,8 +214,10 @@ int mlstm_parallel_fwd_stream(const void* q, const void* k, const void* v, const
                               const float* fgate, void* h_out, float* m_out, float* n_out,
                               int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
                               void* stream) {
-  const int st = check_forward_args(q, k, v, igate, fgate, h_out, m_out, n_out, B, NH, T, d,
-                                    dtype);
+  int st = check_forward_args(q, k, v, igate, fgate, h_out, m_out, n_out, B, NH, T, d, dtype);
+  if (st != MLSTM_OK) return st;
+  st = check_forward_alias(q, k, v, igate, fgate, nullptr, h_out, nullptr, m_out, n_out, nullptr,
+                           B, NH, T, d, dtype);
   if (st != MLSTM_OK) return st;
   return forward(q, k, v, igate, fgate, mlstm::Epilogue{}, h_out, m_out, n_out, B, NH, T, d,
                  dtype, static_cast<hipStream_t>(stream));
@@ -181,6 +231,9 @@ int mlstm_parallel_fwd_gated(const void* q, const void* k, const void* v, const 
   if (st != MLSTM_OK) return st;
   if (!ogate) return MLSTM_ERR_NULL;
   if (!aligned16(ogate) || (htilde_out && !aligned16(htilde_out))) return MLSTM_ERR_ALIGN;
+  st = check_forward_alias(q, k, v, igate, fgate, ogate, h_out, htilde_out, m_out, n_out, nullptr,
+                           B, NH, T, d, dtype);
+  if (st != MLSTM_OK) return st;
   mlstm::Epilogue ep;
   ep.ogate = ogate;
   ep.htilde = htilde_out;
@@ -205,6 +258,9 @@ int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v, const 
     return MLSTM_ERR_ACTIVATION;
   if (!b_out) return MLSTM_ERR_NULL;
   if (!aligned16(b_out)) return MLSTM_ERR_ALIGN;
+  st = check_forward_alias(q, k, v, igate, fgate, nullptr, h_out, nullptr, m_out, n_out, b_out, B,
+                           NH, T, d, dtype);
+  if (st != MLSTM_OK) return st;
   mlstm::Epilogue ep;
   ep.b = b_out;
   return forward(q, k, v, igate, fgate, ep, h_out, m_out, n_out, B, NH, T, d, dtype,
@@ -233,6 +289,13 @@ int mlstm_parallel_bwd(const void* q, const void* k, const void* v, const float*
     if (!aligned16(p)) return MLSTM_ERR_ALIGN;
   for (const void* p : outs)
     if (!aligned16(p)) return MLSTM_ERR_ALIGN;
+  {
+    const size_t tb = tensor_bytes(B, NH, T, d, dtype), rb = rows_bytes(B, NH, T);
+    st = check_alias({{q, tb}, {k, tb}, {v, tb}, {h, tb}, {dh, tb}, {igate, rb}, {fgate, rb},
+                      {m, rb}, {n, rb}, {b, rb}},
+                     {{dq, tb}, {dk, tb}, {dv, tb}, {digate, rb}, {dfgate, rb}});
+    if (st != MLSTM_OK) return st;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t H = B * NH;
   const size_t wsb = mlstm::workspace_bytes(H, T);

@@ -164,3 +164,55 @@ def test_backward_rejects_head_dims_above_its_limit():
     # the one-wave MFMA kernel stops at 512; the selector is checked first
     assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, FAKE,
                                   1, 1, 64, 1024, 0, 5, None) == -8
+
+
+def _addrs(names):
+    """Distinct 16-byte-aligned fake addresses 16 MiB apart (never dereferenced)."""
+    return {n: FAKE + (i + 1) * (1 << 24) for i, n in enumerate(names)}
+
+
+@needs_lib
+@pytest.mark.parametrize("alias", [("h_out", "q"), ("h_out", "v", 1024), ("m_out", "n_out"),
+                                   ("n_out", "igate"), ("m_out", "fgate", 128)])
+def test_forward_rejects_outputs_that_alias(alias):
+    lib = mlstm.load_library()
+    names = ["q", "k", "v", "igate", "fgate", "h_out", "m_out", "n_out"]
+    a = _addrs(names)
+    a[alias[0]] = a[alias[1]] + (alias[2] if len(alias) > 2 else 0)
+    # B=1, NH=1, T=64, d=16, bf16: 2 KiB tensors, 256-byte gate rows
+    assert lib.mlstm_parallel_fwd(*[a[n] for n in names], 1, 1, 64, 16, 1) == -9
+
+
+@needs_lib
+def test_other_entry_points_reject_outputs_that_alias():
+    lib = mlstm.load_library()
+    # gated forward: h~ onto h, and h onto the output gate
+    names = ["q", "k", "v", "igate", "fgate", "ogate", "h_out", "htilde_out", "m_out", "n_out"]
+    a = _addrs(names)
+    b = dict(a, htilde_out=a["h_out"])
+    assert lib.mlstm_parallel_fwd_gated(*[b[n] for n in names], 1, 1, 64, 16, 1, None) == -9
+    b = dict(a, h_out=a["ogate"])
+    assert lib.mlstm_parallel_fwd_gated(*[b[n] for n in names], 1, 1, 64, 16, 1, None) == -9
+    # training forward: b onto n
+    names = ["q", "k", "v", "igate", "fgate", "h_out", "m_out", "n_out", "b_out"]
+    a = _addrs(names)
+    b = dict(a, b_out=a["n_out"])
+    assert lib.mlstm_parallel_fwd_train(*[b[n] for n in names], 1, 1, 64, 16, 1, 0, None) == -9
+    # backward: dq onto q, df~ onto f~
+    names = ["q", "k", "v", "igate", "fgate", "h", "m", "n", "b", "dh", "dq", "dk", "dv",
+             "digate", "dfgate"]
+    a = _addrs(names)
+    for out, inp in (("dq", "q"), ("dfgate", "fgate"), ("dk", "dv")):
+        b = dict(a, **{out: a[inp]})
+        assert lib.mlstm_parallel_bwd(*[b[n] for n in names], 1, 1, 64, 16, 1, 0, None) == -9
+    # staged: m onto i~, m inside the workspace, h onto q
+    ws = FAKE + (1 << 30)
+    wsb = lib.mlstm_workspace_bytes(1, 1, 64)
+    a = _addrs(["igate", "fgate", "m"])
+    assert lib.mlstm_gate_scan(a["igate"], a["fgate"], a["igate"], ws, wsb, 1, 1, 64, 16, 0,
+                               None) == -9
+    assert lib.mlstm_gate_scan(a["igate"], a["fgate"], ws + 256, ws, wsb, 1, 1, 64, 16, 0,
+                               None) == -9
+    a = _addrs(["q", "k", "v", "m", "h", "n"])
+    assert lib.mlstm_causal_tiles(a["q"], a["k"], a["v"], a["m"], ws, wsb, a["q"], a["n"],
+                                  1, 1, 64, 16, 1, 0, None) == -9

@@ -794,3 +794,22 @@ def test_many_small_heads():
     h, m, n = run_gpu(x)
     hr, mr, nr = oracle_full(x)[:3]
     print(check(h, m, n, hr, mr, nr, TOL_H["bf16"]))
+
+
+def test_aliased_outputs_rejected_on_gpu():
+    x = W.make(spec(1, 1, 64, 16), seed=39)
+    q, k, v, ig, fg = _dev(x)
+    m = torch.empty((1, 1, 64), dtype=torch.float32, device="cuda")
+    n = torch.empty_like(m)
+    with pytest.raises(mlstm.MlstmError) as e:
+        mlstm.parallel_fwd(q, k, v, ig, fg, out=(q, m, n))
+    assert e.value.status == -9
+    with pytest.raises(mlstm.MlstmError) as e:
+        mlstm.parallel_fwd(q, k, v, ig, fg, out=(torch.empty_like(q), m, m))
+    assert e.value.status == -9
+    # inputs may alias each other: q as its own key
+    h, m2, n2 = mlstm.parallel_fwd(q, q, v, ig, fg)
+    torch.cuda.synchronize()
+    y = dict(x, k=x["q"])
+    hr, mr, nr = oracle_full(y)[:3]
+    print(check(_host(h), _host(m2), _host(n2), hr, mr, nr, TOL_H["bf16"]))
