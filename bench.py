@@ -60,26 +60,36 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_counters(launch_bytes_key="bytes_per_launch"):
-    """HBM bytes per launch of the tile kernel from committed rocprofv3 counter
-    runs, or None if they are absent or were taken on a different kernel source."""
+def counters_record():
+    """The committed rocprofv3 counter record of the tile kernel, or None if
+    absent or taken on a different kernel source."""
     try:
         with open(COUNTERS) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha") != source_sha(TILE_SRC):
-        return None
-    return rec.get(launch_bytes_key)
+    return rec if rec.get("source_sha") == source_sha(TILE_SRC) else None
+
+
+def traffic_from_counters(launch_bytes_key="bytes_per_launch"):
+    """HBM bytes per launch of the tile kernel from committed rocprofv3 counter
+    runs, or None if they are absent or were taken on a different kernel source."""
+    rec = counters_record()
+    return rec.get(launch_bytes_key) if rec else None
 
 
 def cpu_baseline(x, budget_s):
     """Time the float64 oracle head by head until the budget is spent."""
     import numpy as np
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        info = threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in info
+                if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or blas
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     spec = x["spec"]
@@ -100,7 +110,7 @@ def cpu_baseline(x, budget_s):
     dt = time.perf_counter() - t0
     flops = 2.0 * T * T * d * done
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "host_cores": len(os.sched_getaffinity(0)), "blas": blas, "kind": "oracle",
             "sample": f"{done} of {B * NH} heads (full T={T}, d={d} each), float64 NumPy, "
                       f"{dt:.1f} s"}
 
@@ -137,6 +147,32 @@ def long_context_skipping(torch, mlstm, workloads, dev, reps):
             "counted_TFLOP/s_skipping": round(flops / (out["mfma"] * 1e-3) / 1e12, 1),
             "counted_TFLOP/s_all_tiles": round(flops / (out["mfma_all_tiles"] * 1e-3) / 1e12, 1),
             "speedup": round(out["mfma_all_tiles"] / out["mfma"], 2)}
+
+
+def scan_at_size(torch, mlstm, dev, reps=10):
+    """The gate scan alone at 2^26 positions (16384 heads of 4096), where it
+    moves enough bytes to show its bandwidth (supplementary)."""
+    B, NH, T, d = 1024, 16, 4096, 384
+    g = torch.Generator(device="cpu").manual_seed(0)
+    ig = torch.randn((B, NH, T), generator=g).to(dev)
+    fg = (3.0 + torch.randn((B, NH, T), generator=g)).to(dev)
+    ws = mlstm.alloc_workspace(B, NH, T, dev)
+    m = torch.empty_like(ig)
+    mlstm.gate_scan(ig, fg, d, ws, m=m)
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        mlstm.gate_scan(ig, fg, d, ws, m=m)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    H = B * NH
+    nbytes = H * T * (4 * 6) + H * (T // 64) * 8 + 2 * H * (T // 32) * 4
+    return {"B": B, "NH": NH, "T": T, "positions": H * T, "avg_launch_ms": round(ms, 4),
+            "algorithmic_bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def layer_timing(torch, mlstm, workloads, dev, name, reps=50):
@@ -297,10 +333,24 @@ def main():
     ms = (t1 - t0) * 1e3 / args.steps
     value = flops / (ms * 1e-3) / 1e12
 
+    # per-call durations: 100 calls, each between HIP events on the call's stream
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(100)]
+    for a, b in evs:
+        a.record(stream)
+        mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    per_call_rec = {"calls": len(per_call), "median_us": round(per_call[len(per_call) // 2], 2),
+                    "min_us": round(per_call[0], 2),
+                    "p90_us": round(per_call[int(0.9 * len(per_call))], 2),
+                    "median_TFLOP/s": round(flops / (per_call[len(per_call) // 2] * 1e-6) / 1e12, 1)}
+
     # ---- dominant kernel alone: HIP events on the launch stream ----
     ws = mlstm.alloc_workspace(B, NH, T, dev)
     mlstm.gate_scan(ig, fg, d, ws, m=m)
-    stream = torch.cuda.current_stream(dev)
     reps = max(args.steps, 20)
     for _ in range(3):
         mlstm.causal_tiles(q, k, v, m, ws, out=(h, n))
@@ -322,6 +372,7 @@ def main():
     torch.cuda.synchronize()
     scan_ms = e0.elapsed_time(e1) / reps
     scan_bytes = B * NH * T * (4 + 4 + 4 + 4 + 4 + 4) + B * NH * (T // 64 + 2) * 8
+    scan_large = scan_at_size(torch, mlstm, dev)
 
     # decay-aware tile skipping on the long-context stress workload: the same
     # call with skipping (default) and visiting every causal tile
@@ -372,7 +423,9 @@ def main():
         "gate_scan": {"avg_launch_ms": round(scan_ms, 5),
                       "algorithmic_bytes": scan_bytes,
                       "GB/s": round(scan_bytes / (scan_ms * 1e-3) / 1e9, 1),
-                      "frac_of_hbm": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                      "frac_of_hbm": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "at_2^26_positions": scan_large},
+        "per_call": per_call_rec,
         "output_finite": finite,
     }
     if skip_rec is not None:
