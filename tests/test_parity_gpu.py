@@ -813,3 +813,71 @@ def test_aliased_outputs_rejected_on_gpu():
     y = dict(x, k=x["q"])
     hr, mr, nr = oracle_full(y)[:3]
     print(check(_host(h), _host(m2), _host(n2), hr, mr, nr, TOL_H["bf16"]))
+
+
+# ---------------------------------------------------------------------------
+# HIP graphs and concurrent streams
+# ---------------------------------------------------------------------------
+
+def _inputs_into(bufs, x):
+    for name, t in zip(("q", "k", "v", "igate", "fgate"), bufs):
+        t.copy_(torch.from_numpy(x[name]).to(t.dtype))
+
+
+def test_graph_capture_replays_match_eager():
+    """mlstm_parallel_fwd (stream-ordered workspace) and the staged entry
+    points (caller workspace) captured into HIP graphs: every replay, with new
+    inputs copied in and eager work in between, equals the eager call bitwise."""
+    s = spec(2, 2, 300, 64)
+    xs = [W.make(s, seed=40 + i) for i in range(3)]
+    q, k, v, ig, fg = _dev(xs[0])
+    bufs = (q, k, v, ig, fg)
+    h = torch.empty_like(q)
+    m = torch.empty((2, 2, 300), dtype=torch.float32, device="cuda")
+    n = torch.empty_like(m)
+    ws = mlstm.alloc_workspace(2, 2, 300, q.device)
+    h2, n2, m2 = torch.empty_like(h), torch.empty_like(n), torch.empty_like(m)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on the capture stream
+        mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+        mlstm.gate_scan(ig, fg, 64, ws, m=m2)
+        mlstm.causal_tiles(q, k, v, m2, ws, out=(h2, n2))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+    with torch.cuda.graph(g2):
+        mlstm.gate_scan(ig, fg, 64, ws, m=m2)
+        mlstm.causal_tiles(q, k, v, m2, ws, out=(h2, n2))
+    for x in xs + xs[:1]:
+        _inputs_into(bufs, x)
+        g1.replay()
+        g2.replay()
+        torch.cuda.synchronize()
+        eh, em, en = mlstm.parallel_fwd(q, k, v, ig, fg)  # eager, between replays
+        torch.cuda.synchronize()
+        for a, b in ((h, eh), (m, em), (n, en), (h2, eh), (m2, em), (n2, en)):
+            assert torch.equal(a, b)
+
+
+def test_concurrent_streams_match_serial():
+    xa = W.make(spec(1, 4, 700, 128), seed=44)
+    xb = W.make(spec(2, 2, 513, 64), seed=45)
+    da, db = _dev(xa), _dev(xb)
+    ra = mlstm.parallel_fwd(*da)
+    rb = mlstm.parallel_fwd(*db)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            oa = mlstm.parallel_fwd(*da)
+        with torch.cuda.stream(sb):
+            ob = mlstm.parallel_fwd(*db)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for oa, ob in outs:
+        for t, r in zip(oa + ob, ra + rb):
+            assert torch.equal(t, r)
