@@ -1,6 +1,6 @@
 """Tolerance readings used by the GPU parity tests (test infrastructure).
 
-Spec bars: max relative error 1e-4 (float32 inputs) and 2e-2 (bf16 in,
+Required bars: max relative error 1e-4 (float32 inputs) and 2e-2 (bf16 in,
 float32 accumulate) for h~; 1e-5 relative for m and n.  "Relative" is read as
 follows, because m crosses zero and single rows of n and h~ can be
 cancellation-amplified (b_i is a signed sum, Eq. 83):
