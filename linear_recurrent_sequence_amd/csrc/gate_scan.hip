@@ -13,14 +13,20 @@
 // another, (a1, b1) then (a2, b2) = (a1 + a2, max(b1 + a2, b2)), so the
 // recurrence is an associative scan and runs in parallel.  This avoids the
 // cancellation of the closed form cs_i + max_j (i~_j - cs_j), whose two
-// terms each grow with the sequence length.
+// terms each grow with the sequence length.  The prefix sums of fbar ride
+// along as a second component of each scan element.
 //
-// One workgroup of 512 threads per head walks the sequence in chunks of
-// 2048 positions; each thread owns 4 consecutive positions (one sixteenth of
-// a 64-position anchor block), loaded and stored as 16-byte vectors where the
-// row alignment allows.  Sums and the max-plus maps are carried in float64;
-// log sigmoid is evaluated in float32 (its relative error stays local: only
-// sums over the few positions where D' is not negligible matter).
+// A workgroup of 512 threads scans a chunk of 2048 positions; each thread
+// owns 4 consecutive positions (one sixteenth of a 64-position anchor block),
+// loaded and stored as 16-byte vectors where the row alignment allows.  Short
+// sequences take one workgroup per head that walks its chunks in order.  Long
+// ones are scanned in two passes, so that every chunk has a workgroup of its
+// own: the first reduces each chunk to its element (sum, map), the second
+// gives each chunk the composition of all earlier chunks' elements (folded in
+// order across the workgroup's threads) as its carry and scans it.  Sums and
+// the max-plus maps are carried in float64; log sigmoid is evaluated in
+// float32 (its relative error stays local: only sums over the few positions
+// where D' is not negligible matter).
 #include "mlstm_internal.h"
 
 namespace mlstm {
@@ -29,6 +35,7 @@ namespace {
 constexpr int kScanThreads = 512;
 constexpr int kScanPer = 4;  // positions per thread per chunk
 constexpr int kScanWaves = kScanThreads / 64;
+static_assert(kScanThreads * kScanPer == kScanChunk, "chunk of the gate scan");
 
 struct MaxPlus {  // the map x -> max(x + a, b)
   double a, b;
@@ -40,22 +47,129 @@ __device__ inline MaxPlus compose(MaxPlus first, MaxPlus second) {
 
 __device__ inline double apply(MaxPlus f, double x) { return fmax(x + f.a, f.b); }
 
+// a scan element: a sum of fbar and the map of the same positions
+struct Elem {
+  double sum;
+  MaxPlus map;
+};
+
+__device__ inline Elem identity() { return {0.0, {0.0, -INFINITY}}; }
+
+__device__ inline Elem combine(Elem first, Elem second) {
+  return {first.sum + second.sum, compose(first.map, second.map)};
+}
+
 // log sigmoid(x) = min(x, 0) - log1p(exp(-|x|)): never forms exp(+|x|).
 __device__ inline float log_sigmoid(float x) {
   return fminf(x, 0.0f) - log1pf(expf(-fabsf(x)));
 }
 
+// Ordered scan of one element per thread over the workgroup (thread order):
+// returns the composition of the elements of all earlier threads and stores
+// that of all threads in `total`.
+__device__ Elem block_scan(Elem x, Elem& total) {
+  __shared__ double s_sum[kScanWaves];
+  __shared__ double s_a[kScanWaves];
+  __shared__ double s_b[kScanWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  Elem incl = x;  // inclusive scan across the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double os = __shfl_up(incl.sum, off, 64);
+    const double oa = __shfl_up(incl.map.a, off, 64);
+    const double ob = __shfl_up(incl.map.b, off, 64);
+    if (lane >= off) incl = combine(Elem{os, {oa, ob}}, incl);
+  }
+  if (lane == 63) {
+    s_sum[wave] = incl.sum;
+    s_a[wave] = incl.map.a;
+    s_b[wave] = incl.map.b;
+  }
+  __syncthreads();
+  Elem before = identity();  // the waves before this one
+  total = identity();
+  for (int w = 0; w < kScanWaves; ++w) {
+    const Elem e = {s_sum[w], {s_a[w], s_b[w]}};
+    if (w < wave) before = combine(before, e);
+    total = combine(total, e);
+  }
+  // lane-exclusive = inclusive of the previous lane
+  Elem lexcl = {__shfl_up(incl.sum, 1, 64),
+                {__shfl_up(incl.map.a, 1, 64), __shfl_up(incl.map.b, 1, 64)}};
+  if (lane == 0) lexcl = identity();
+  __syncthreads();  // the shared totals may be rewritten by the next call
+  return combine(before, lexcl);
+}
+
+// log f and i~ of positions p0 .. p0 + 3 (padding: no forgetting, no input;
+// it never reaches a real row)
+__device__ inline void load_gates(const float* f, const float* ig, int64_t p0, int64_t T,
+                                  bool vec_rows, int exp_forget, float fb[kScanPer],
+                                  float iv[kScanPer]) {
+  if (vec_rows && p0 + kScanPer <= T) {
+    const float4 f4 = *reinterpret_cast<const float4*>(f + p0);
+    const float4 i4 = *reinterpret_cast<const float4*>(ig + p0);
+    fb[0] = f4.x; fb[1] = f4.y; fb[2] = f4.z; fb[3] = f4.w;
+    iv[0] = i4.x; iv[1] = i4.y; iv[2] = i4.z; iv[3] = i4.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e) {
+      const int64_t p = p0 + e;
+      fb[e] = p < T ? f[p] : 0.0f;
+      iv[e] = p < T ? ig[p] : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kScanPer; ++e)
+    fb[e] = p0 + e < T ? (exp_forget ? fb[e] : log_sigmoid(fb[e])) : 0.0f;  // log f_t
+}
+
+// the element of one thread's positions
+__device__ inline Elem thread_elem(const float fb[kScanPer], const float iv[kScanPer]) {
+  Elem t = identity();
+#pragma unroll
+  for (int e = 0; e < kScanPer; ++e)
+    t = combine(t, Elem{double(fb[e]), {double(fb[e]), double(iv[e])}});
+  return t;
+}
+
+// First pass of the two-pass scan: the element of chunk c of head h
+// (workgroup h * nchunk + c), stored as (sum, a, b).
+__global__ __launch_bounds__(kScanThreads) void scan_totals_kernel(
+    const float* __restrict__ igate, const float* __restrict__ fgate, double* __restrict__ segs,
+    int64_t T, int64_t nchunk, int exp_forget) {
+  const int64_t head = int64_t(blockIdx.x) / nchunk;
+  const int64_t c = int64_t(blockIdx.x) % nchunk;
+  const int64_t p0 = c * kScanChunk + int64_t(threadIdx.x) * kScanPer;
+  float fb[kScanPer], iv[kScanPer];
+  load_gates(fgate + head * T, igate + head * T, p0, T, (T & 3) == 0, exp_forget, fb, iv);
+  Elem total;
+  block_scan(thread_elem(fb, iv), total);
+  if (threadIdx.x == 0) {
+    double* s = segs + (head * nchunk + c) * 3;
+    s[0] = total.sum;
+    s[1] = total.map.a;
+    s[2] = total.map.b;
+  }
+}
+
+// Scans chunks [c0, c0 + count) of one head: workgroup x covers head
+// x / groups and c0 = (x % groups) * count.  With segs != NULL the carry into
+// chunk c0 is the composition of the stored elements of chunks 0 .. c0 - 1
+// (each thread folds a contiguous run of them in order, then the runs are
+// composed in thread order).
 __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     const float* __restrict__ igate, const float* __restrict__ fgate, float* __restrict__ m_out,
     double* __restrict__ anchor, float* __restrict__ rowt, float* __restrict__ colt,
-    float* __restrict__ colx, float* __restrict__ rowb, float* __restrict__ keyb, int64_t T,
-    int64_t Tp, int64_t nblk,
-    double half_ln_d, int exp_forget) {
+    float* __restrict__ colx, float* __restrict__ rowb, float* __restrict__ keyb,
+    const double* __restrict__ segs, int64_t T, int64_t Tp, int64_t nblk, int64_t nchunk,
+    int64_t groups, int64_t count, double half_ln_d, int exp_forget) {
   const double kLog2e = 1.4426950408889634074;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int64_t head = blockIdx.x;
+  const int64_t head = int64_t(blockIdx.x) / groups;
+  const int64_t c0 = (int64_t(blockIdx.x) % groups) * count;
   const float* f = fgate + head * T;
   const float* ig = igate + head * T;
   float* mo = m_out + head * T;
@@ -69,82 +183,26 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
   // (their base pointers are 16-byte aligned)
   const bool vec_rows = (T & 3) == 0;
 
-  __shared__ double s_sum[kScanWaves];
-  __shared__ double s_a[kScanWaves];
-  __shared__ double s_b[kScanWaves];
+  Elem carry = identity();  // everything before the current chunk
+  if (segs != nullptr && c0 > 0) {
+    const int64_t per = (c0 + kScanThreads - 1) / kScanThreads;
+    Elem run = identity();
+    for (int64_t j = int64_t(tid) * per; j < c0 && j < int64_t(tid + 1) * per; ++j) {
+      const double* s = segs + (head * nchunk + j) * 3;
+      run = combine(run, Elem{s[0], {s[1], s[2]}});
+    }
+    block_scan(run, carry);
+  }
 
-  double carry_cs = 0.0;        // sum of fbar over all earlier chunks
-  double carry_m = -INFINITY;   // m at the last position of the previous chunk
+  for (int64_t chunk = c0; chunk < c0 + count && chunk * kScanChunk < Tp; ++chunk) {
+    const int64_t p0 = chunk * kScanChunk + int64_t(tid) * kScanPer;
+    float fb[kScanPer], iv[kScanPer];
+    load_gates(f, ig, p0, T, vec_rows, exp_forget, fb, iv);
+    Elem total;
+    const Elem before = block_scan(thread_elem(fb, iv), total);
 
-  for (int64_t base = 0; base < Tp; base += int64_t(kScanThreads) * kScanPer) {
-    const int64_t p0 = base + int64_t(tid) * kScanPer;
-    float fb[kScanPer];
-    float iv[kScanPer];
-    if (vec_rows && p0 + kScanPer <= T) {
-      const float4 f4 = *reinterpret_cast<const float4*>(f + p0);
-      const float4 i4 = *reinterpret_cast<const float4*>(ig + p0);
-      fb[0] = f4.x; fb[1] = f4.y; fb[2] = f4.z; fb[3] = f4.w;
-      iv[0] = i4.x; iv[1] = i4.y; iv[2] = i4.z; iv[3] = i4.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < kScanPer; ++e) {
-        const int64_t p = p0 + e;
-        fb[e] = p < T ? f[p] : 0.0f;
-        iv[e] = p < T ? ig[p] : -INFINITY;
-      }
-    }
-    double tsum = 0.0;
-    MaxPlus tmap = {0.0, -INFINITY};
-#pragma unroll
-    for (int e = 0; e < kScanPer; ++e) {
-      // log f_t; padding has no forgetting and no input and never reaches a real row
-      fb[e] = p0 + e < T ? (exp_forget ? fb[e] : log_sigmoid(fb[e])) : 0.0f;
-      tsum += double(fb[e]);
-      tmap = compose(tmap, MaxPlus{double(fb[e]), double(iv[e])});
-    }
-
-    // inclusive scan across the wave
-    double isum = tsum;
-    MaxPlus imap = tmap;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double os = __shfl_up(isum, off, 64);
-      const double oa = __shfl_up(imap.a, off, 64);
-      const double ob = __shfl_up(imap.b, off, 64);
-      if (lane >= off) {
-        isum = os + isum;
-        imap = compose(MaxPlus{oa, ob}, imap);
-      }
-    }
-    if (lane == 63) {
-      s_sum[wave] = isum;
-      s_a[wave] = imap.a;
-      s_b[wave] = imap.b;
-    }
-    __syncthreads();
-    // exclusive prefix of the wave totals (each thread recomputes it; 16 terms)
-    double wsum = 0.0;
-    MaxPlus wmap = {0.0, -INFINITY};
-    for (int w = 0; w < wave; ++w) {
-      wsum += s_sum[w];
-      wmap = compose(wmap, MaxPlus{s_a[w], s_b[w]});
-    }
-    double tot_sum = 0.0;
-    MaxPlus tot_map = {0.0, -INFINITY};
-    for (int w = 0; w < kScanWaves; ++w) {
-      tot_sum += s_sum[w];
-      tot_map = compose(tot_map, MaxPlus{s_a[w], s_b[w]});
-    }
-    // lane-exclusive = inclusive of the previous lane
-    double lsum = __shfl_up(isum, 1, 64);
-    MaxPlus lmap = {__shfl_up(imap.a, 1, 64), __shfl_up(imap.b, 1, 64)};
-    if (lane == 0) {
-      lsum = 0.0;
-      lmap = {0.0, -INFINITY};
-    }
-
-    double cs = carry_cs + wsum + lsum;                 // sum of fbar before p0
-    double m = apply(lmap, apply(wmap, carry_m));       // m at p0 - 1
+    double cs = carry.sum + before.sum;                         // sum of fbar before p0
+    double m = apply(before.map, apply(carry.map, -INFINITY));  // m at p0 - 1
     // anchor of this thread's 64-block: the prefix sum before the block start,
     // held by the first of the 16 threads that share the block
     const double blk_anchor = __shfl(cs, lane & ~15, 64);
@@ -197,9 +255,7 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
       for (int e = 0; e < kScanPer; ++e)
         if (p0 + e < T) mo[p0 + e] = mv[e];
     }
-    carry_cs += tot_sum;
-    carry_m = apply(tot_map, carry_m);
-    __syncthreads();  // s_* are rewritten by the next chunk
+    carry = combine(carry, total);
   }
 }
 
@@ -208,10 +264,22 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
 hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out,
                             const Workspace& ws, int64_t H, int64_t T, int64_t d,
                             bool exp_forget, hipStream_t stream) {
-  hipLaunchKernelGGL(gate_scan_kernel, dim3(unsigned(H)), dim3(kScanThreads), 0, stream, igate,
-                     fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb, ws.keyb, T, ws.Tp,
-                     ws.nblk,
-                     0.5 * log(double(d)), int(exp_forget));
+  const int64_t nchunk = scan_chunks(T);
+  const double half_ln_d = 0.5 * log(double(d));
+  if (nchunk < kScanTwoPassChunks) {  // one workgroup per head, chunks in order
+    hipLaunchKernelGGL(gate_scan_kernel, dim3(unsigned(H)), dim3(kScanThreads), 0, stream, igate,
+                       fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb, ws.keyb,
+                       static_cast<const double*>(nullptr), T, ws.Tp, ws.nblk, nchunk,
+                       int64_t(1), nchunk, half_ln_d, int(exp_forget));
+    return hipGetLastError();
+  }
+  const dim3 grid(unsigned(H * nchunk));
+  hipLaunchKernelGGL(scan_totals_kernel, grid, dim3(kScanThreads), 0, stream, igate, fgate,
+                     ws.segs, T, nchunk, int(exp_forget));
+  hipLaunchKernelGGL(gate_scan_kernel, grid, dim3(kScanThreads), 0, stream, igate, fgate, m_out,
+                     ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb, ws.keyb,
+                     static_cast<const double*>(ws.segs), T, ws.Tp, ws.nblk, nchunk, nchunk,
+                     int64_t(1), half_ln_d, int(exp_forget));
   return hipGetLastError();
 }
 

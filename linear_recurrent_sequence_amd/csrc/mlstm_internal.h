@@ -9,6 +9,8 @@
 //   colx   [H][Tp]     float32  e_j = 2^(c_j - keyb_{j/32})        (0 on padding)
 //   rowb   [H][Tp/32]  float32  max of r_i over each 32-row block
 //   keyb   [H][Tp/32]  float32  max of c_j over each 32-key tile (-inf if all padding)
+//   segs   [H][nchunk][3] float64  the scan element (sum of fbar, max-plus map a, b)
+//                                of each 2048-position chunk (long sequences)
 //
 // where fbar = log sigmoid(f~) and loc_i = (inclusive prefix sum of fbar up to
 // i) - (the same sum up to the start of i's 64-position block), so that, for
@@ -44,6 +46,8 @@ constexpr int kRowPad = 128;     // T is padded to a multiple of this
 constexpr int kAnchorBlock = 64; // positions per float64 anchor
 constexpr int kBoundTile = 32;   // rows / keys per entry of rowb and keyb
 constexpr float kSkipLog2 = -200.0f;
+constexpr int kScanChunk = 2048;        // positions per workgroup pass of the gate scan
+constexpr int kScanTwoPassChunks = 4;   // from this many chunks on, the scan runs in two passes
 
 struct Workspace {
   double* anchor;
@@ -52,6 +56,7 @@ struct Workspace {
   float* colx;
   float* rowb;
   float* keyb;
+  double* segs;
   int64_t Tp;
   int64_t nblk;
 };
@@ -60,11 +65,15 @@ inline int64_t padded_len(int64_t T) { return (T + kRowPad - 1) / kRowPad * kRow
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// chunks of the gate scan over a sequence of T positions
+inline int64_t scan_chunks(int64_t T) { return (padded_len(T) + kScanChunk - 1) / kScanChunk; }
+
 inline size_t workspace_bytes(int64_t H, int64_t T) {
   const int64_t Tp = padded_len(T);
   return align256(size_t(H) * size_t(Tp / kAnchorBlock) * sizeof(double)) +
          3 * align256(size_t(H) * size_t(Tp) * sizeof(float)) +
-         2 * align256(size_t(H) * size_t(Tp / kBoundTile) * sizeof(float));
+         2 * align256(size_t(H) * size_t(Tp / kBoundTile) * sizeof(float)) +
+         align256(size_t(H) * size_t(scan_chunks(T)) * 3 * sizeof(double));
 }
 
 inline Workspace carve(void* base, int64_t H, int64_t T) {
@@ -83,6 +92,8 @@ inline Workspace carve(void* base, int64_t H, int64_t T) {
   w.rowb = reinterpret_cast<float*>(p);
   p += align256(size_t(H) * size_t(w.Tp / kBoundTile) * sizeof(float));
   w.keyb = reinterpret_cast<float*>(p);
+  p += align256(size_t(H) * size_t(w.Tp / kBoundTile) * sizeof(float));
+  w.segs = reinterpret_cast<double*>(p);
   return w;
 }
 

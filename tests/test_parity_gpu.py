@@ -881,3 +881,43 @@ def test_concurrent_streams_match_serial():
     for oa, ob in outs:
         for t, r in zip(oa + ob, ra + rb):
             assert torch.equal(t, r)
+
+
+# ---------------------------------------------------------------------------
+# the gate scan over long sequences: two passes from four 2048-position
+# chunks on (chunk elements, then each chunk's carry folded from them)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [6144, 6145, 8192, 8193, 20000])
+def test_long_scan_m_matches_oracle(T):
+    """m on rows around every chunk boundary and a random sample, against the
+    oracle's row maximum of D~ (Eq. 80) taken row by row."""
+    x = W.make(spec(1, 3, T, 16, ig=("uniform", -20, 20), fg=("normal", 0, 4),
+                    fgate_floor=(0.01, -30.0)), seed=46)
+    q, k, v, ig, fg = _dev(x)
+    ws = mlstm.alloc_workspace(1, 3, T, "cuda")
+    m = _host(mlstm.gate_scan(ig, fg, 16, ws))
+    torch.cuda.synchronize()
+    edges = [c * 2048 + o for c in range(1, T // 2048 + 1) for o in (-2, -1, 0, 1)]
+    rows = np.array(sorted(set(r for r in edges if 0 <= r < T) |
+                           set(_sample_rows(T, np.random.default_rng(49), count=20))))
+    mr = np.stack([oracle.forward_rows(x["q"], x["k"], x["v"], x["igate"], x["fgate"], 0, hh,
+                                       rows)[1] for hh in range(3)])[None]
+    assert m_error(m[:, :, rows], mr) <= 1e-5
+
+
+@pytest.mark.parametrize("forget", ["sigmoid", "exp"])
+def test_long_scan_forward_sampled(forget):
+    fg = ("normal", 3, 1) if forget == "sigmoid" else ("uniform", -0.3, 0.0)
+    x = W.make(spec(1, 2, 12000, 64, fg=fg), seed=47)
+    q, k, v, ig, fgt = _dev(x)
+    h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fgt, forget=forget)
+    torch.cuda.synchronize()
+    rows = _sample_rows(12000, np.random.default_rng(48), count=24)
+    H = np.empty((1, 2, len(rows), 64)); M = np.empty((1, 2, len(rows))); N = np.empty_like(M)
+    for hh in range(2):
+        hr, mr, nr, _, _ = oracle.forward_rows(x["q"], x["k"], x["v"], x["igate"], x["fgate"],
+                                                0, hh, rows, forget=forget)
+        H[0, hh], M[0, hh], N[0, hh] = hr, mr, nr
+    print(check(_host(h)[:, :, rows], _host(m)[:, :, rows], _host(n)[:, :, rows], H, M, N,
+                TOL_H["bf16"]))
