@@ -13,8 +13,9 @@
 // another, (a1, b1) then (a2, b2) = (a1 + a2, max(b1 + a2, b2)), so the
 // recurrence is an associative scan and runs in parallel.  This avoids the
 // cancellation of the closed form cs_i + max_j (i~_j - cs_j), whose two
-// terms each grow with the sequence length.  The prefix sums of fbar ride
-// along as a second component of each scan element.
+// terms each grow with the sequence length.  The shift a of a composed map is
+// the sum of fbar over its positions, so the same scan also yields the prefix
+// sums of fbar.
 //
 // A workgroup of 512 threads scans a chunk of 2048 positions; each thread
 // owns 4 consecutive positions (one sixteenth of a 64-position anchor block),
@@ -47,17 +48,13 @@ __device__ inline MaxPlus compose(MaxPlus first, MaxPlus second) {
 
 __device__ inline double apply(MaxPlus f, double x) { return fmax(x + f.a, f.b); }
 
-// a scan element: a sum of fbar and the map of the same positions
-struct Elem {
-  double sum;
-  MaxPlus map;
-};
+// a scan element: the map of a run of positions; its shift a is the sum of
+// fbar over the run
+typedef MaxPlus Elem;
 
-__device__ inline Elem identity() { return {0.0, {0.0, -INFINITY}}; }
+__device__ inline Elem identity() { return {0.0, -INFINITY}; }
 
-__device__ inline Elem combine(Elem first, Elem second) {
-  return {first.sum + second.sum, compose(first.map, second.map)};
-}
+__device__ inline Elem combine(Elem first, Elem second) { return compose(first, second); }
 
 // log sigmoid(x) = min(x, 0) - log1p(exp(-|x|)): never forms exp(+|x|).
 __device__ inline float log_sigmoid(float x) {
@@ -68,7 +65,6 @@ __device__ inline float log_sigmoid(float x) {
 // returns the composition of the elements of all earlier threads and stores
 // that of all threads in `total`.
 __device__ Elem block_scan(Elem x, Elem& total) {
-  __shared__ double s_sum[kScanWaves];
   __shared__ double s_a[kScanWaves];
   __shared__ double s_b[kScanWaves];
   const int lane = threadIdx.x & 63;
@@ -76,27 +72,24 @@ __device__ Elem block_scan(Elem x, Elem& total) {
   Elem incl = x;  // inclusive scan across the wave
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const double os = __shfl_up(incl.sum, off, 64);
-    const double oa = __shfl_up(incl.map.a, off, 64);
-    const double ob = __shfl_up(incl.map.b, off, 64);
-    if (lane >= off) incl = combine(Elem{os, {oa, ob}}, incl);
+    const double oa = __shfl_up(incl.a, off, 64);
+    const double ob = __shfl_up(incl.b, off, 64);
+    if (lane >= off) incl = combine(Elem{oa, ob}, incl);
   }
   if (lane == 63) {
-    s_sum[wave] = incl.sum;
-    s_a[wave] = incl.map.a;
-    s_b[wave] = incl.map.b;
+    s_a[wave] = incl.a;
+    s_b[wave] = incl.b;
   }
   __syncthreads();
   Elem before = identity();  // the waves before this one
   total = identity();
   for (int w = 0; w < kScanWaves; ++w) {
-    const Elem e = {s_sum[w], {s_a[w], s_b[w]}};
+    const Elem e = {s_a[w], s_b[w]};
     if (w < wave) before = combine(before, e);
     total = combine(total, e);
   }
   // lane-exclusive = inclusive of the previous lane
-  Elem lexcl = {__shfl_up(incl.sum, 1, 64),
-                {__shfl_up(incl.map.a, 1, 64), __shfl_up(incl.map.b, 1, 64)}};
+  Elem lexcl = {__shfl_up(incl.a, 1, 64), __shfl_up(incl.b, 1, 64)};
   if (lane == 0) lexcl = identity();
   __syncthreads();  // the shared totals may be rewritten by the next call
   return combine(before, lexcl);
@@ -130,12 +123,12 @@ __device__ inline Elem thread_elem(const float fb[kScanPer], const float iv[kSca
   Elem t = identity();
 #pragma unroll
   for (int e = 0; e < kScanPer; ++e)
-    t = combine(t, Elem{double(fb[e]), {double(fb[e]), double(iv[e])}});
+    t = combine(t, Elem{double(fb[e]), double(iv[e])});
   return t;
 }
 
 // First pass of the two-pass scan: the element of chunk c of head h
-// (workgroup h * nchunk + c), stored as (sum, a, b).
+// (workgroup h * nchunk + c), stored as (a, b).
 __global__ __launch_bounds__(kScanThreads) void scan_totals_kernel(
     const float* __restrict__ igate, const float* __restrict__ fgate, double* __restrict__ segs,
     int64_t T, int64_t nchunk, int exp_forget) {
@@ -147,10 +140,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_totals_kernel(
   Elem total;
   block_scan(thread_elem(fb, iv), total);
   if (threadIdx.x == 0) {
-    double* s = segs + (head * nchunk + c) * 3;
-    s[0] = total.sum;
-    s[1] = total.map.a;
-    s[2] = total.map.b;
+    double* s = segs + (head * nchunk + c) * 2;
+    s[0] = total.a;
+    s[1] = total.b;
   }
 }
 
@@ -188,8 +180,8 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     const int64_t per = (c0 + kScanThreads - 1) / kScanThreads;
     Elem run = identity();
     for (int64_t j = int64_t(tid) * per; j < c0 && j < int64_t(tid + 1) * per; ++j) {
-      const double* s = segs + (head * nchunk + j) * 3;
-      run = combine(run, Elem{s[0], {s[1], s[2]}});
+      const double* s = segs + (head * nchunk + j) * 2;
+      run = combine(run, Elem{s[0], s[1]});
     }
     block_scan(run, carry);
   }
@@ -201,8 +193,8 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     Elem total;
     const Elem before = block_scan(thread_elem(fb, iv), total);
 
-    double cs = carry.sum + before.sum;                         // sum of fbar before p0
-    double m = apply(before.map, apply(carry.map, -INFINITY));  // m at p0 - 1
+    double cs = carry.a + before.a;                     // sum of fbar before p0
+    double m = apply(before, apply(carry, -INFINITY));  // m at p0 - 1
     // anchor of this thread's 64-block: the prefix sum before the block start,
     // held by the first of the 16 threads that share the block
     const double blk_anchor = __shfl(cs, lane & ~15, 64);

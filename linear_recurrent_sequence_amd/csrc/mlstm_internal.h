@@ -9,8 +9,9 @@
 //   colx   [H][Tp]     float32  e_j = 2^(c_j - keyb_{j/32})        (0 on padding)
 //   rowb   [H][Tp/32]  float32  max of r_i over each 32-row block
 //   keyb   [H][Tp/32]  float32  max of c_j over each 32-key tile (-inf if all padding)
-//   segs   [H][nchunk][3] float64  the scan element (sum of fbar, max-plus map a, b)
-//                                of each 2048-position chunk (long sequences)
+//   segs   [H][nchunk][2] float64  the scan element (max-plus map a, b; a is the
+//                                sum of fbar) of each 2048-position chunk
+//                                (long sequences)
 //
 // where fbar = log sigmoid(f~) and loc_i = (inclusive prefix sum of fbar up to
 // i) - (the same sum up to the start of i's 64-position block), so that, for
@@ -73,7 +74,7 @@ inline size_t workspace_bytes(int64_t H, int64_t T) {
   return align256(size_t(H) * size_t(Tp / kAnchorBlock) * sizeof(double)) +
          3 * align256(size_t(H) * size_t(Tp) * sizeof(float)) +
          2 * align256(size_t(H) * size_t(Tp / kBoundTile) * sizeof(float)) +
-         align256(size_t(H) * size_t(scan_chunks(T)) * 3 * sizeof(double));
+         align256(size_t(H) * size_t(scan_chunks(T)) * 2 * sizeof(double));
 }
 
 inline Workspace carve(void* base, int64_t H, int64_t T) {
