@@ -162,16 +162,18 @@ def long_context_skipping(torch, mlstm, workloads, dev, reps):
             "speedup": round(out["mfma_all_tiles"] / out["mfma"], 2)}
 
 
-def scan_at_size(torch, mlstm, dev, reps=10):
+def scan_at_size(torch, mlstm, dev, reps=20, warmup=5):
     """The gate scan alone at 2^26 positions (16384 heads of 4096), where it
-    moves enough bytes to show its bandwidth (supplementary)."""
+    moves enough bytes to show its bandwidth (supplementary).  The untimed
+    calls map the 1.6 GB of outputs and let the clock settle."""
     B, NH, T, d = 1024, 16, 4096, 384
     g = torch.Generator(device="cpu").manual_seed(0)
     ig = torch.randn((B, NH, T), generator=g).to(dev)
     fg = (3.0 + torch.randn((B, NH, T), generator=g)).to(dev)
     ws = mlstm.alloc_workspace(B, NH, T, dev)
     m = torch.empty_like(ig)
-    mlstm.gate_scan(ig, fg, d, ws, m=m)
+    for _ in range(warmup):
+        mlstm.gate_scan(ig, fg, d, ws, m=m)
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)

@@ -95,11 +95,9 @@ __device__ Elem block_scan(Elem x, Elem& total) {
   return combine(before, lexcl);
 }
 
-// log f and i~ of positions p0 .. p0 + 3 (padding: no forgetting, no input;
-// it never reaches a real row)
-__device__ inline void load_gates(const float* f, const float* ig, int64_t p0, int64_t T,
-                                  bool vec_rows, int exp_forget, float fb[kScanPer],
-                                  float iv[kScanPer]) {
+// f~ and i~ of positions p0 .. p0 + 3 as stored (padding: f~ = 0, i~ = -inf)
+__device__ inline void load_raw(const float* f, const float* ig, int64_t p0, int64_t T,
+                                bool vec_rows, float fb[kScanPer], float iv[kScanPer]) {
   if (vec_rows && p0 + kScanPer <= T) {
     const float4 f4 = *reinterpret_cast<const float4*>(f + p0);
     const float4 i4 = *reinterpret_cast<const float4*>(ig + p0);
@@ -113,9 +111,21 @@ __device__ inline void load_gates(const float* f, const float* ig, int64_t p0, i
       iv[e] = p < T ? ig[p] : -INFINITY;
     }
   }
+}
+
+// log f_t of the same positions (padding: no forgetting, no input; it never
+// reaches a real row)
+__device__ inline void to_log_forget(int64_t p0, int64_t T, int exp_forget, float fb[kScanPer]) {
 #pragma unroll
   for (int e = 0; e < kScanPer; ++e)
-    fb[e] = p0 + e < T ? (exp_forget ? fb[e] : log_sigmoid(fb[e])) : 0.0f;  // log f_t
+    fb[e] = p0 + e < T ? (exp_forget ? fb[e] : log_sigmoid(fb[e])) : 0.0f;
+}
+
+__device__ inline void load_gates(const float* f, const float* ig, int64_t p0, int64_t T,
+                                  bool vec_rows, int exp_forget, float fb[kScanPer],
+                                  float iv[kScanPer]) {
+  load_raw(f, ig, p0, T, vec_rows, fb, iv);
+  to_log_forget(p0, T, exp_forget, fb);
 }
 
 // the element of one thread's positions
@@ -186,10 +196,22 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     block_scan(run, carry);
   }
 
-  for (int64_t chunk = c0; chunk < c0 + count && chunk * kScanChunk < Tp; ++chunk) {
+  // the gates of the next chunk are loaded before the current one is scanned
+  const int64_t c_end = c0 + count < (Tp + kScanChunk - 1) / kScanChunk
+                            ? c0 + count
+                            : (Tp + kScanChunk - 1) / kScanChunk;
+  float fn[kScanPer], in[kScanPer];
+  if (c0 < c_end) load_raw(f, ig, c0 * kScanChunk + int64_t(tid) * kScanPer, T, vec_rows, fn, in);
+  for (int64_t chunk = c0; chunk < c_end; ++chunk) {
     const int64_t p0 = chunk * kScanChunk + int64_t(tid) * kScanPer;
     float fb[kScanPer], iv[kScanPer];
-    load_gates(f, ig, p0, T, vec_rows, exp_forget, fb, iv);
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e) {
+      fb[e] = fn[e];
+      iv[e] = in[e];
+    }
+    if (chunk + 1 < c_end) load_raw(f, ig, p0 + kScanChunk, T, vec_rows, fn, in);
+    to_log_forget(p0, T, exp_forget, fb);
     Elem total;
     const Elem before = block_scan(thread_elem(fb, iv), total);
 
