@@ -160,7 +160,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_totals_kernel(
 // x / groups and c0 = (x % groups) * count.  With segs != NULL the carry into
 // chunk c0 is the composition of the stored elements of chunks 0 .. c0 - 1
 // (each thread folds a contiguous run of them in order, then the runs are
-// composed in thread order).
+// composed in thread order).  kLoop = false handles count == 1 only: without
+// the chunk loop the kernel needs 63 registers instead of 108, so twice as
+// many workgroups fit on a CU.
+template <bool kLoop>
 __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     const float* __restrict__ igate, const float* __restrict__ fgate, float* __restrict__ m_out,
     double* __restrict__ anchor, float* __restrict__ rowt, float* __restrict__ colt,
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
                             : (Tp + kScanChunk - 1) / kScanChunk;
   float fn[kScanPer], in[kScanPer];
   if (c0 < c_end) load_raw(f, ig, c0 * kScanChunk + int64_t(tid) * kScanPer, T, vec_rows, fn, in);
-  for (int64_t chunk = c0; chunk < c_end; ++chunk) {
+  for (int64_t chunk = c0; chunk < (kLoop ? c_end : c0 + 1); ++chunk) {
     const int64_t p0 = chunk * kScanChunk + int64_t(tid) * kScanPer;
     float fb[kScanPer], iv[kScanPer];
 #pragma unroll
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
       fb[e] = fn[e];
       iv[e] = in[e];
     }
-    if (chunk + 1 < c_end) load_raw(f, ig, p0 + kScanChunk, T, vec_rows, fn, in);
+    if (kLoop && chunk + 1 < c_end) load_raw(f, ig, p0 + kScanChunk, T, vec_rows, fn, in);
     to_log_forget(p0, T, exp_forget, fb);
     Elem total;
     const Elem before = block_scan(thread_elem(fb, iv), total);
@@ -281,16 +284,22 @@ hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out
   const int64_t nchunk = scan_chunks(T);
   const double half_ln_d = 0.5 * log(double(d));
   if (nchunk < kScanTwoPassChunks) {  // one workgroup per head, chunks in order
-    hipLaunchKernelGGL(gate_scan_kernel, dim3(unsigned(H)), dim3(kScanThreads), 0, stream, igate,
-                       fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb, ws.keyb,
-                       static_cast<const double*>(nullptr), T, ws.Tp, ws.nblk, nchunk,
-                       int64_t(1), nchunk, half_ln_d, int(exp_forget));
+    if (nchunk == 1)
+      hipLaunchKernelGGL(gate_scan_kernel<false>, dim3(unsigned(H)), dim3(kScanThreads), 0, stream,
+                         igate, fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb,
+                         ws.keyb, static_cast<const double*>(nullptr), T, ws.Tp, ws.nblk, nchunk,
+                         int64_t(1), int64_t(1), half_ln_d, int(exp_forget));
+    else
+      hipLaunchKernelGGL(gate_scan_kernel<true>, dim3(unsigned(H)), dim3(kScanThreads), 0, stream,
+                         igate, fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb,
+                         ws.keyb, static_cast<const double*>(nullptr), T, ws.Tp, ws.nblk, nchunk,
+                         int64_t(1), nchunk, half_ln_d, int(exp_forget));
     return hipGetLastError();
   }
   const dim3 grid(unsigned(H * nchunk));
   hipLaunchKernelGGL(scan_totals_kernel, grid, dim3(kScanThreads), 0, stream, igate, fgate,
                      ws.segs, T, nchunk, int(exp_forget));
-  hipLaunchKernelGGL(gate_scan_kernel, grid, dim3(kScanThreads), 0, stream, igate, fgate, m_out,
+  hipLaunchKernelGGL(gate_scan_kernel<false>, grid, dim3(kScanThreads), 0, stream, igate, fgate, m_out,
                      ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb, ws.keyb,
                      static_cast<const double*>(ws.segs), T, ws.Tp, ws.nblk, nchunk, nchunk,
                      int64_t(1), half_ln_d, int(exp_forget));
