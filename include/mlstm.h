@@ -239,7 +239,13 @@ int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v,
  * dQ and dK products and C~'/n of the dV product are rounded to bf16, the
  * row and column sums of dD~ behind the gate gradients are not); for float32
  * everything is float32 on the vector ALUs.  Results are bitwise
- * reproducible.  The library allocates a stream-ordered workspace.
+ * reproducible.  The library allocates a stream-ordered workspace: per-row
+ * terms and, for bf16 on the matrix cores, the bf16 operand of the dV
+ * product, 8 KiB per head, 128-key block and 32-query tile of the causal
+ * triangle (142 MB for 32 heads of 2048), which the key pass stores so that
+ * the dV pass need not recompute S; above 2 GiB (or the byte count in the
+ * environment variable MLSTM_BWD_STORE_MAX, read at each call) the dV pass
+ * recomputes it instead (bitwise the same dV).
  * Pointers 16-byte aligned; no output may alias an input.  d <= 512
  * (MLSTM_ERR_HEAD_DIM above).  Other errors as for mlstm_parallel_fwd.
  */

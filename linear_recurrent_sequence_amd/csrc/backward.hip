@@ -29,6 +29,8 @@
 // inputs the row and column passes run on the matrix cores instead
 // (backward_mfma.hip, whose rows pass also forms the per-row scalars); the
 // gate-gradient scan is shared.
+#include <cstdlib>
+
 #include "mlstm_internal.h"
 
 #include <hip/hip_bf16.h>
@@ -316,12 +318,12 @@ template <typename Tin>
 hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* fgate,
                         const Tin* h, const float* m, const float* n, const float* b,
                         const Tin* dh, const Workspace& ws, float* inv_n, float* db, float* rsum,
-                        float* csum, Tin* dq, Tin* dk, Tin* dv, float* digate, float* dfgate,
-                        int64_t H, int64_t T, int64_t d, bool exp_forget, bool mfma,
+                        float* csum, void* vstore, Tin* dq, Tin* dk, Tin* dv, float* digate,
+                        float* dfgate, int64_t H, int64_t T, int64_t d, bool exp_forget, bool mfma,
                         hipStream_t stream) {
   if (mfma) {  // the rows pass forms the per-row scalars itself
     const hipError_t e = launch_backward_mfma_tiles(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq,
-                                                    dk, dv, rsum, csum, H, T, d, stream);
+                                                    dk, dv, rsum, csum, vstore, H, T, d, stream);
     if (e != hipSuccess) return e;
   } else {
     const int64_t rows = H * T;
@@ -342,8 +344,22 @@ hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* f
 
 }  // namespace
 
-size_t backward_scratch_bytes(int64_t H, int64_t T) {
-  return 4 * align256(size_t(H) * size_t(T) * sizeof(float));
+// The stored dV operand is used up to this size (the environment variable
+// MLSTM_BWD_STORE_MAX, in bytes, overrides it); above it the values pass
+// recomputes S (bitwise the same results, more time, no quadratic memory).
+constexpr size_t kBackwardStoreMax = size_t(2) << 30;
+
+size_t backward_store_bytes(int64_t H, int64_t T, int64_t d, bool is_bf16) {
+  if (!is_bf16 || !backward_mfma_supports(d)) return 0;
+  size_t cap = kBackwardStoreMax;
+  if (const char* e = std::getenv("MLSTM_BWD_STORE_MAX")) cap = size_t(std::strtoull(e, nullptr, 10));
+  const size_t b = backward_mfma_store_bytes(H, T);
+  return b <= cap ? b : 0;
+}
+
+size_t backward_scratch_bytes(int64_t H, int64_t T, int64_t d, bool is_bf16) {
+  return 4 * align256(size_t(H) * size_t(T) * sizeof(float)) +
+         align256(backward_store_bytes(H, T, d, is_bf16));
 }
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* fgate,
@@ -358,11 +374,12 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
   float* db = reinterpret_cast<float*>(p + one);
   float* rsum = reinterpret_cast<float*>(p + 2 * one);
   float* csum = reinterpret_cast<float*>(p + 3 * one);
+  void* vstore = backward_store_bytes(H, T, d, is_bf16) ? p + 4 * one : nullptr;
   if (is_bf16) {
     using B16 = __hip_bfloat16;
     return launch_typed<B16>(static_cast<const B16*>(q), static_cast<const B16*>(k),
                              static_cast<const B16*>(v), fgate, static_cast<const B16*>(h), m, n,
-                             b, static_cast<const B16*>(dh), ws, inv_n, db, rsum, csum,
+                             b, static_cast<const B16*>(dh), ws, inv_n, db, rsum, csum, vstore,
                              static_cast<B16*>(dq), static_cast<B16*>(dk), static_cast<B16*>(dv),
                              digate, dfgate, H, T, d, exp_forget, backward_mfma_supports(d),
                              stream);
@@ -370,7 +387,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
   return launch_typed<float>(static_cast<const float*>(q), static_cast<const float*>(k),
                              static_cast<const float*>(v), fgate, static_cast<const float*>(h), m,
                              n, b, static_cast<const float*>(dh), ws, inv_n, db, rsum, csum,
-                             static_cast<float*>(dq), static_cast<float*>(dk),
+                             nullptr, static_cast<float*>(dq), static_cast<float*>(dk),
                              static_cast<float*>(dv), digate, dfgate, H, T, d, exp_forget, false,
                              stream);
 }

@@ -46,7 +46,9 @@ constexpr int kBThreads = 256;  // 4 waves, one per SIMD
 constexpr int kBWaves = kBThreads / 64;
 constexpr int kBPf = 2;         // LDS fragment prefetch distance (MFMA steps)
 
-enum { kRowsPass = 0, kKeysPass = 1, kValuesPass = 2 };
+// kValuesStored: the values pass on the operand bf16(C~'/n) that the keys pass
+// stored (no first product)
+enum { kRowsPass = 0, kKeysPass = 1, kValuesPass = 2, kValuesStored = 3 };
 
 // LDS layout of one buffer.  X1 is the tensor of the first product (K in the
 // rows pass, Q otherwise), X2 that of the second product (V, dH) or, in the
@@ -58,25 +60,40 @@ enum { kRowsPass = 0, kKeysPass = 1, kValuesPass = 2 };
 template <int DP, int MODE>
 struct BCfg {
   static_assert(DP % 64 == 0 && DP >= 64 && DP <= 512, "head dim of the matrix-core backward");
+  static constexpr bool VAL = MODE == kValuesPass || MODE == kValuesStored;
   // output-column halves per row block (see the notes above)
-  static constexpr int SPLIT = (MODE != kValuesPass && DP > 384) ? 2 : 1;
+  static constexpr int SPLIT = (!VAL && DP > 384) ? 2 : 1;
   static constexpr int NB = DP / 32 / SPLIT;  // 32-column accumulator blocks per wave
   static constexpr int CH = DP / 8;  // 16-byte chunks per row
-  static constexpr int S1 = MODE == kValuesPass ? 2 * DP + 16 : 2 * DP + 32;
-  static constexpr int S2 = MODE == kValuesPass ? 2 * DP + 64 : 2 * DP + 16;
+  static constexpr int S1 = VAL ? 2 * DP + 16 : 2 * DP + 32;
+  static constexpr int S2 = VAL ? 2 * DP + 64 : 2 * DP + 16;
   static constexpr int X1_OFF = 0;
-  static constexpr int X2_OFF = kBN * S1;
+  static constexpr int X2_OFF = MODE == kValuesStored ? 0 : kBN * S1;  // only dH: no X1
   static constexpr int GT = X2_OFF + kBN * S2;  // c_j (rows pass) or r_i of the tile, float32
   static constexpr int GN = GT + 128;           // 1 / n_i of the tile (keys, values passes)
   static constexpr int GD = GT + 256;           // db_i of the tile (keys pass)
   static constexpr int GA = GT + 384;           // float64 anchor of the tile
-  static constexpr int BUF = GA + 16;
-  static constexpr int SA = MODE == kValuesPass ? S2 : S1;          // transposed operand's stride
-  static constexpr int A_OFF = MODE == kValuesPass ? X2_OFF : X1_OFF;
+  static constexpr int BUF = MODE == kValuesStored ? GT : GA + 16;
+  static constexpr int SA = VAL ? S2 : S1;          // transposed operand's stride
+  static constexpr int A_OFF = VAL ? X2_OFF : X1_OFF;
   static_assert(2 * BUF <= 160 * 1024, "LDS budget");
 };
 
-template <int DP, int MODE>
+// The stored operand of the dV product: for each head, key block I (128
+// keys) and 32-query tile J >= 4 I of the causal triangle, one 2 KiB slot per
+// wave holding its bf16(C~'/n) fragments (lane L's first 16 bytes at 16 L,
+// its second at 1024 + 16 L).  Slots of tiles J < 4 I + w, which wave w does
+// not need, are neither written nor read.
+__host__ __device__ inline int64_t store_tiles(int64_t T) {  // tiles of one head
+  const int64_t nt = (T + kBN - 1) / kBN, rt = (T + kBM - 1) / kBM;
+  return rt * nt - 2 * rt * (rt - 1);  // sum over I < rt of (nt - 4 I)
+}
+
+// STORE (keys pass only): also store the values pass's operand.  Above
+// d = 384 both workgroups of a row block store the same bytes (they compute
+// the same S and E); a branch on the workgroup would cost the keys pass
+// register spills.
+template <int DP, int MODE, bool STORE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
                           amdgpu_waves_per_eu(1, 1))) void bwd_mfma_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
@@ -84,9 +101,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     const float* __restrict__ n_in, const float* __restrict__ b_in, float* __restrict__ inv_n,
     float* __restrict__ db, const double* __restrict__ anchor, const float* __restrict__ rowt,
     const float* __restrict__ colt, u16* __restrict__ out, float* __restrict__ sums, int T,
-    int d, int Tp, int nblk, int row_tiles, int H) {
+    int d, int Tp, int nblk, int row_tiles, int H, u16* __restrict__ vstore, int64_t tri) {
   using C = BCfg<DP, MODE>;
-  constexpr bool kTwo = MODE != kValuesPass;  // a second first-stage product (G)
+  constexpr bool kTwo = MODE == kRowsPass || MODE == kKeysPass;  // a second first product (G)
+  constexpr bool kFirst = MODE != kValuesStored;                  // first products at all
   constexpr int NS = DP / 16;                 // MFMA steps of a first-stage product
   constexpr int NV = 2 * C::NB;               // MFMA steps of the accumulation
   const int cb0 = C::NB * int(blockIdx.y);    // first 32-column block of this workgroup
@@ -129,7 +147,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       f[s] = *reinterpret_cast<const bf16x8*>(&val);
     }
   };
-  bf16x8 f1[NS];
+  bf16x8 f1[kFirst ? NS : 1];
   bf16x8 f2[kTwo ? NS : 1];
   if (kTwo) load_frags(own2, f2);
 
@@ -170,7 +188,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   }
   // the h~ fragments are dead before the Q fragments are loaded
   __builtin_amdgcn_sched_barrier(0);
-  load_frags(own1, f1);
+  if (kFirst) load_frags(own1, f1);
 
   f32x16 acc[C::NB];
 #pragma unroll
@@ -195,10 +213,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       const int r = w * (kBN / kBWaves) + i;
       if (lane < C::CH) {
         const unsigned off = lane < dch ? unsigned(r * d * 2 + 16 * lane) : kOutOfRange;
-        dma16(r1, off, buf + C::X1_OFF + r * C::S1);
+        if (kFirst) dma16(r1, off, buf + C::X1_OFF + r * C::S1);
         dma16(r2, off, buf + C::X2_OFF + r * C::S2);
       }
     }
+    if (!kFirst) return;
     const float* tsrc = MODE == kRowsPass ? colt : rowt;
     if (w == 0 && lane < kBN / 4)
       dma16(make_rsrc(tsrc + int64_t(head) * Tp + x0, kBN * 4), unsigned(16 * lane), buf + C::GT);
@@ -223,7 +242,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   const int off2 = C::X2_OFF + l32 * C::S2 + 16 * g;
   const int offt = C::A_OFF + (4 * g + (j16 >> 2)) * C::SA + 32 * (l32 >> 4) + 8 * (j16 & 3);
 
-  auto compute = [&](const char* buf, int J) {
+  // byte offset of this wave's slot of the stored dV operand for tile J
+  auto slot = [&](int J) {
+    const int64_t t = int64_t(I) * n_tiles - 2 * int64_t(I) * (I - 1) + (J - 4 * I);
+    return ((int64_t(head) * tri + t) * kBWaves + w) * 2048;
+  };
+
+  auto compute = [&](const char* buf, int J, const bf16x8 (&pin)[2]) {
+    bf16x8 pb[2];
+    if constexpr (MODE == kValuesStored) {
+      pb[0] = pin[0];
+      pb[1] = pin[1];
+    } else {
     // first products: Y1 = X1_J Own1^T (and Y2 = X2_J Own2^T)
     f32x16 y1 = f32x16{}, y2 = f32x16{};
     {
@@ -260,6 +290,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     const float* gn = reinterpret_cast<const float*>(buf + C::GN);
     const float* gd = reinterpret_cast<const float*>(buf + C::GD);
     float pv[16];
+    // with STORE, vb receives the values pass's operand bf16(s E / n_i), in
+    // the layout of its B fragments and computed as there (so dV is bitwise
+    // that of the recomputing values pass)
+    bf16x8 vb[2];
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const float4 t4 = *reinterpret_cast<const float4*>(gt + 8 * rq + 4 * g);
@@ -290,14 +324,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
           const float P = E * (y2[4 * rq + e] * in_i + db_i);
           dsum += s * P;
           pv[4 * rq + e] = P;
+          if (STORE) vb[rq >> 1][4 * (rq & 1) + e] = (__bf16)(s * E * nn[e]);
         }
       }
     }
-    bf16x8 pb[2];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       pb[0][e] = (__bf16)pv[e];
       pb[1][e] = (__bf16)pv[8 + e];
+    }
+    if constexpr (STORE) {
+      char* dst = reinterpret_cast<char*>(vstore) + slot(J);
+      *reinterpret_cast<bf16x8*>(dst + 16 * lane) = vb[0];
+      *reinterpret_cast<bf16x8*>(dst + 1024 + 16 * lane) = vb[1];
+    }
     }
     // accumulation: step t = (column block b, half c of the tile's rows); the
     // A operand holds X[16c + 4g + 0..3][32b + l32] and X[16c + 8 + 4g + 0..3][32b + l32]
@@ -326,23 +366,47 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     }
   };
 
+  // the stored operand of the values pass: tile J + 1's is loaded while tile
+  // J is computed, and has landed by the closing wait of tile J
+  bf16x8 pin[2] = {bf16x8{}, bf16x8{}}, pnext[2] = {bf16x8{}, bf16x8{}};
+  auto load_pin = [&](int J, bf16x8 (&dst)[2]) {
+    if constexpr (MODE == kValuesStored) {
+      if (J <= last && wave_needs(J)) {
+        const char* src = reinterpret_cast<const char*>(vstore) + slot(J);
+        dst[0] = *reinterpret_cast<const bf16x8*>(src + 16 * lane);
+        dst[1] = *reinterpret_cast<const bf16x8*>(src + 1024 + 16 * lane);
+      }
+    }
+  };
+  auto next_pin = [&]() {
+    if constexpr (MODE == kValuesStored) {
+      pin[0] = pnext[0];
+      pin[1] = pnext[1];
+    }
+  };
+
   load_tile(first, smem0);
+  load_pin(first, pin);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int J = first; J <= last; J += 2) {
+    load_pin(J + 1, pnext);
     if (J + 1 <= last) load_tile(J + 1, smem1);
-    if (wave_needs(J)) compute(smem0, J);
+    if (wave_needs(J)) compute(smem0, J, pin);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (J + 1 > last) break;
+    next_pin();
+    load_pin(J + 2, pnext);
     if (J + 2 <= last) load_tile(J + 2, smem0);
-    if (wave_needs(J + 1)) compute(smem1, J + 1);
+    if (wave_needs(J + 1)) compute(smem1, J + 1, pin);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    next_pin();
   }
 
   // ---- epilogue: the row or column sums of dD~, and dQ / dK / dV in bf16
-  if (MODE != kValuesPass) {
+  if (MODE == kRowsPass || MODE == kKeysPass) {
     dsum += __shfl_xor(dsum, 32, 64);
     if (oi < T && g == 0 && blockIdx.y == 0) sums[int64_t(head) * T + oi] = dsum;
   }
@@ -364,52 +428,67 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   }
 }
 
-template <int DP, int MODE>
+template <int DP, int MODE, bool STORE = false>
 void launch_pass(const void* q, const void* k, const void* v, const void* dh, const void* h,
                  const float* m, const float* n, const float* b, float* inv_n, float* db,
-                 const Workspace& ws, void* out, float* sums, int64_t H, int64_t T, int64_t d,
-                 hipStream_t stream) {
+                 const Workspace& ws, void* out, float* sums, void* vstore, int64_t H, int64_t T,
+                 int64_t d, hipStream_t stream) {
   const int64_t row_tiles = (T + kBM - 1) / kBM;
-  hipLaunchKernelGGL((bwd_mfma_kernel<DP, MODE>),
+  static_assert(!STORE || MODE == kKeysPass, "only the keys pass stores the dV operand");
+  hipLaunchKernelGGL((bwd_mfma_kernel<DP, MODE, STORE>),
                      dim3(unsigned(row_tiles * H), unsigned(BCfg<DP, MODE>::SPLIT)), dim3(kBThreads),
                      0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), static_cast<const u16*>(dh),
-                     static_cast<const u16*>(h), m, n, b, inv_n, db, ws.anchor, ws.rowt, ws.colt, static_cast<u16*>(out), sums, int(T), int(d),
-                     int(ws.Tp), int(ws.nblk), int(row_tiles), int(H));
+                     static_cast<const u16*>(h), m, n, b, inv_n, db, ws.anchor, ws.rowt, ws.colt,
+                     static_cast<u16*>(out), sums, int(T), int(d), int(ws.Tp), int(ws.nblk),
+                     int(row_tiles), int(H), static_cast<u16*>(vstore), store_tiles(T));
 }
 
 template <int DP>
 void launch_all(const void* q, const void* k, const void* v, const void* dh, const void* h,
                 const float* m, const float* n, const float* b, float* inv_n, float* db,
                 const Workspace& ws, void* dq, void* dk, void* dv, float* rsum, float* csum,
-                int64_t H, int64_t T, int64_t d, hipStream_t stream) {
-  launch_pass<DP, kRowsPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, rsum, H, T, d, stream);
-  launch_pass<DP, kKeysPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dk, csum, H, T, d, stream);
-  launch_pass<DP, kValuesPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dv, nullptr, H, T, d,
+                void* vstore, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+  launch_pass<DP, kRowsPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, rsum, nullptr, H, T, d,
+                             stream);
+  if (vstore != nullptr) {
+    launch_pass<DP, kKeysPass, true>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dk, csum, vstore, H,
+                                     T, d, stream);
+    launch_pass<DP, kValuesStored>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dv, nullptr, vstore, H,
+                                   T, d, stream);
+  } else {
+    launch_pass<DP, kKeysPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dk, csum, nullptr, H, T, d,
                                stream);
+    launch_pass<DP, kValuesPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dv, nullptr, nullptr, H,
+                                 T, d, stream);
+  }
 }
 
 }  // namespace
 
 bool backward_mfma_supports(int64_t d) { return d % 16 == 0 && d >= 16 && d <= 512; }
 
+size_t backward_mfma_store_bytes(int64_t H, int64_t T) {
+  return size_t(H) * size_t(store_tiles(T)) * kBWaves * 2048;
+}
+
 hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* v,
                                       const void* dh, const void* h, const float* m,
                                       const float* n, const float* b, float* inv_n, float* db,
                                       const Workspace& ws, void* dq, void* dk, void* dv,
-                                      float* rsum, float* csum, int64_t H, int64_t T, int64_t d,
-                                      hipStream_t stream) {
+                                      float* rsum, float* csum, void* vstore, int64_t H,
+                                      int64_t T, int64_t d, hipStream_t stream) {
   if (!backward_mfma_supports(d)) return hipErrorInvalidValue;
   // head dims are padded up to a multiple of 64 (zero columns add nothing)
   switch ((d + 63) / 64) {
-    case 1: launch_all<64>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 2: launch_all<128>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 3: launch_all<192>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 4: launch_all<256>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 5: launch_all<320>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 6: launch_all<384>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 7: launch_all<448>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
-    case 8: launch_all<512>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, H, T, d, stream); break;
+    case 1: launch_all<64>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, vstore, H, T, d, stream); break;
+    case 2: launch_all<128>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, vstore, H, T, d, stream); break;
+    case 3: launch_all<192>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, vstore, H, T, d, stream); break;
+    case 4: launch_all<256>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, vstore, H, T, d, stream); break;
+    case 5: launch_all<320>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, vstore, H, T, d, stream); break;
+    case 6: launch_all<384>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, vstore, H, T, d, stream); break;
+    case 7: launch_all<448>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, vstore, H, T, d, stream); break;
+    case 8: launch_all<512>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, dk, dv, rsum, csum, vstore, H, T, d, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

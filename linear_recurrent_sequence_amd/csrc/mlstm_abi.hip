@@ -300,7 +300,7 @@ int mlstm_parallel_bwd(const void* q, const void* k, const void* v, const float*
   const int64_t H = B * NH;
   const size_t wsb = mlstm::workspace_bytes(H, T);
   const size_t mb = mlstm::align256(size_t(H) * size_t(T) * sizeof(float));
-  const size_t scb = mlstm::backward_scratch_bytes(H, T);
+  const size_t scb = mlstm::backward_scratch_bytes(H, T, d, dtype == MLSTM_BF16);
   void* ws = nullptr;
   if (hipMallocAsync(&ws, wsb + mb + scb, s) != hipSuccess) {
     (void)hipGetLastError();

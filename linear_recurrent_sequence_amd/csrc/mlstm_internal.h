@@ -149,10 +149,12 @@ hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, cons
 
 // Backward pass (Eqs. 87-105), float32 vector tiles, d <= kBackwardMaxHeadDim
 // (four 16-row float32 tiles of the head dimension share the LDS).  `ws` holds
-// the gate scan's terms for the same inputs; `scratch` holds backward_scratch_bytes(H,
-// T) bytes (256-byte aligned) of per-row temporaries.
+// the gate scan's terms for the same inputs; `scratch` holds
+// backward_scratch_bytes(H, T, d, is_bf16) bytes (256-byte aligned): per-row
+// temporaries and, on the matrix-core path, the stored operand of the dV
+// product.
 constexpr int kBackwardMaxHeadDim = 512;
-size_t backward_scratch_bytes(int64_t H, int64_t T);
+size_t backward_scratch_bytes(int64_t H, int64_t T, int64_t d, bool is_bf16);
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* fgate,
                            const void* h, const float* m, const float* n, const float* b,
                            const void* dh, const Workspace& ws, void* scratch, void* dq, void* dk,
@@ -162,13 +164,17 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
 // The row and column passes of the backward on the matrix cores (bf16,
 // d <= 512): dQ and the row sums r of dD~ (the rows pass also stores the
 // per-row scalars 1/n and db into inv_n, db), dK and the column sums c, dV.
+// With vstore != NULL (backward_mfma_store_bytes(H, T) bytes) the keys pass
+// also stores bf16(C~'/n), the operand of the dV product, and the values
+// pass reads it instead of recomputing S; dV is bitwise the same either way.
 bool backward_mfma_supports(int64_t d);
+size_t backward_mfma_store_bytes(int64_t H, int64_t T);
 hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* v,
                                       const void* dh, const void* h, const float* m,
                                       const float* n, const float* b, float* inv_n, float* db,
                                       const Workspace& ws, void* dq, void* dk, void* dv,
-                                      float* rsum, float* csum, int64_t H, int64_t T, int64_t d,
-                                      hipStream_t stream);
+                                      float* rsum, float* csum, void* vstore, int64_t H,
+                                      int64_t T, int64_t d, hipStream_t stream);
 
 // Recurrent step (generation), stabilized states in float32: C [H][d][d],
 // n [H][d], m [H].  C_out may equal C_in; n_out / m_out must not overlap

@@ -775,6 +775,26 @@ def test_backward_mfma_full_size_sub_heads_of_512():
     _check_backward(got, ref, fwd)
 
 
+@pytest.mark.parametrize("shape", [(2, 2, 600, 384), (1, 2, 300, 512), (1, 1, 129, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_backward_stored_dv_operand_is_bitwise_the_recomputed_one(shape, monkeypatch):
+    """The dV pass on the operand that the dK pass stored gives bitwise the
+    gradients of the dV pass that recomputes S (MLSTM_BWD_STORE_MAX=0)."""
+    B, NH, T, d = shape
+    x = W.make(spec(B, NH, T, d), seed=40)
+    q, k, v, ig, fg = _dev(x)
+    h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg)
+    dh = torch.from_numpy(W.round_bf16(np.random.default_rng(41).standard_normal(
+        x["q"].shape).astype(np.float32))).to("cuda").to(torch.bfloat16)
+    monkeypatch.delenv("MLSTM_BWD_STORE_MAX", raising=False)
+    stored = mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, dh)
+    monkeypatch.setenv("MLSTM_BWD_STORE_MAX", "0")
+    recomputed = mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, dh)
+    torch.cuda.synchronize()
+    for name, a, c in zip(("dq", "dk", "dv", "digate", "dfgate"), stored, recomputed):
+        assert torch.equal(a, c), name
+
+
 # ---------------------------------------------------------------------------
 # large shapes: a 65536-position head (512 row tiles, 2048 key tiles) and a
 # thousand small heads (grid and index arithmetic at size)
