@@ -305,7 +305,9 @@ __global__ __launch_bounds__(kGThreads) void bwd_gates_kernel(
         const float f = fgate[head * T + p];
         // d(log f)/d f~: sigma(-f~) (Eq. 104), or 1 for the exponential gate
         const double dlogf = exp_forget ? 1.0 : 1.0 / (1.0 + exp(double(f)));
-        dfgate[head * T + p] = float(dlogf * run);
+        // f_0 never enters F (Eq. 101): its sum is empty, exactly 0, where the
+        // suffix form would leave the rounding of sum r - sum c
+        dfgate[head * T + p] = p == 0 ? 0.0f : float(dlogf * run);
         digate[head * T + p] = c[p];
       }
     }

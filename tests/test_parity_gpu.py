@@ -775,6 +775,22 @@ def test_backward_mfma_full_size_sub_heads_of_512():
     _check_backward(got, ref, fwd)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_first_forget_gate_gradient_is_exactly_zero(dtype):
+    """f_0 enters no product F_ij (Eq. 101): its gradient is exactly 0, as in
+    the oracle's double sum over j < 0 (the suffix-sum form would leave the
+    rounding of sum r - sum c there)."""
+    for T in (1, 2, 77):
+        x = W.make(spec(2, 2, T, 32, dtype), seed=42)
+        q, k, v, ig, fg = _dev(x)
+        h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg)
+        dh = torch.ones_like(q)
+        dfg = mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, dh)[4]
+        torch.cuda.synchronize()
+        assert bool((dfg[..., 0] == 0).all()), (T, dfg[..., 0])
+        assert torch.isfinite(dfg).all()
+
+
 @pytest.mark.parametrize("shape", [(2, 2, 600, 384), (1, 2, 300, 512), (1, 1, 129, 64)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_backward_stored_dv_operand_is_bitwise_the_recomputed_one(shape, monkeypatch):
