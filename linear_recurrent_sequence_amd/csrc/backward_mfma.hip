@@ -108,8 +108,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   constexpr int NS = DP / 16;                 // MFMA steps of a first-stage product
   constexpr int NV = 2 * C::NB;               // MFMA steps of the accumulation
   const int cb0 = C::NB * int(blockIdx.y);    // first 32-column block of this workgroup
-  __shared__ __attribute__((aligned(1024))) char smem0[C::BUF];
-  __shared__ __attribute__((aligned(1024))) char smem1[C::BUF];
+  // two tile buffers; before the tile loop the same space stages the own rows
+  constexpr int RSQ = 2 * DP + 16;  // staging row stride: 16 consecutive rows hit
+                                    // 16 distinct 16-byte slots
+  constexpr int kStage = kFirst ? kBM * RSQ : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF > kStage ? 2 * C::BUF : kStage];
+  char* const smem0 = smem;
+  char* const smem1 = smem + C::BUF;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -135,21 +140,35 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   const u16* x2 = MODE == kRowsPass ? v : dh;
 
   // own fragments (B operands): row oi, head dims 16 s + 8 g + 0..7; rows past
-  // the sequence end and padded columns are zeros
-  auto load_frags = [&](const u16* src, bf16x8* f) {
-    const int row = oi < T ? oi : T - 1;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int col = 16 * s + 8 * g;
-      const bool ok = oi < T && col < d;
-      const uint4 raw = *reinterpret_cast<const uint4*>(src + hoff + int64_t(row) * d + (ok ? col : 0));
-      const uint4 val = ok ? raw : make_uint4(0, 0, 0, 0);
-      f[s] = *reinterpret_cast<const bf16x8*>(&val);
+  // the sequence end and padded columns are zeros.  The workgroup's 128 own
+  // rows of a tensor are staged in LDS with one copy per row (lanes fetch
+  // consecutive 16-byte chunks), then each wave reads its 32 rows' fragments:
+  // loading them straight from memory, 32 rows per instruction, was slower.
+  const unsigned vchunk = lane < dch ? unsigned(16 * lane) : kOutOfRange;
+  auto stage = [&](const u16* src) {
+#pragma unroll 4
+    for (int i = 0; i < kBM / kBWaves; ++i) {
+      const int r = (kBM / kBWaves) * w + i;
+      const int row = I * kBM + r;
+      if (lane < C::CH)
+        dma16(make_rsrc(src + hoff + int64_t(row) * d, row < T ? 2 * d : 0), vchunk,
+              smem + r * RSQ);
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  const char* const frow = smem + (32 * w + l32) * RSQ + 16 * g;
+  auto read_frags = [&](bf16x8* f) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) f[s] = *reinterpret_cast<const bf16x8*>(frow + 32 * s);
   };
   bf16x8 f1[kFirst ? NS : 1];
   bf16x8 f2[kTwo ? NS : 1];
-  if (kTwo) load_frags(own2, f2);
+  if (kTwo) {
+    stage(own2);
+    read_frags(f2);
+    __syncthreads();  // the staging space is refilled below
+  }
 
   // own gate terms: r_i, 1/n_i, db_i (rows pass) or c_j (key passes; -inf past
   // the sequence end), and the anchor of the wave's 32 rows
@@ -160,18 +179,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     // dn_i = -(dh_i . h~_i) / n_i (Eqs. 88-89); db_i = sign(b_i) dn_i where
     // |b_i| is above the floor exp(-m_i) (Eq. 90), else 0
     float hd = 0.0f;
-    const int row = oi < T ? oi : T - 1;
+    stage(hsrc);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int col = 16 * s + 8 * g;
-      const bool ok = oi < T && col < d;
-      const uint4 raw =
-          *reinterpret_cast<const uint4*>(hsrc + hoff + int64_t(row) * d + (ok ? col : 0));
-      const uint4 val = ok ? raw : make_uint4(0, 0, 0, 0);
-      const bf16x8 hv = *reinterpret_cast<const bf16x8*>(&val);
+      const bf16x8 hv = *reinterpret_cast<const bf16x8*>(frow + 32 * s);
 #pragma unroll
       for (int e = 0; e < 8; ++e) hd += float(f2[s][e]) * float(hv[e]);
     }
+    __syncthreads();  // the staging space is refilled below
     hd += __shfl_xor(hd, 32, 64);
     if (oi < T) {
       const int64_t at = int64_t(head) * T + oi;
@@ -188,7 +203,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   }
   // the h~ fragments are dead before the Q fragments are loaded
   __builtin_amdgcn_sched_barrier(0);
-  if (kFirst) load_frags(own1, f1);
+  if (kFirst) {
+    stage(own1);
+    read_frags(f1);
+    __syncthreads();  // the tile buffers are filled below
+  }
 
   f32x16 acc[C::NB];
 #pragma unroll
