@@ -108,13 +108,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   constexpr int NS = DP / 16;                 // MFMA steps of a first-stage product
   constexpr int NV = 2 * C::NB;               // MFMA steps of the accumulation
   const int cb0 = C::NB * int(blockIdx.y);    // first 32-column block of this workgroup
-  // two tile buffers; before the tile loop the same space stages the own rows
+  // two distinct tile buffers, so that the copies into one never alias reads
+  // of the other (one array would make the compiler wait for the copies
+  // before reading); before the tile loop they stage the own rows, 64 each
+  __shared__ __attribute__((aligned(1024))) char smem0[C::BUF];
+  __shared__ __attribute__((aligned(1024))) char smem1[C::BUF];
   constexpr int RSQ = 2 * DP + 16;  // staging row stride: 16 consecutive rows hit
                                     // 16 distinct 16-byte slots
-  constexpr int kStage = kFirst ? kBM * RSQ : 0;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF > kStage ? 2 * C::BUF : kStage];
-  char* const smem0 = smem;
-  char* const smem1 = smem + C::BUF;
+  static_assert(!kFirst || (kBM / 2) * RSQ <= C::BUF, "64 staged rows fit in a tile buffer");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,12 +153,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       const int row = I * kBM + r;
       if (lane < C::CH)
         dma16(make_rsrc(src + hoff + int64_t(row) * d, row < T ? 2 * d : 0), vchunk,
-              smem + r * RSQ);
+              (r < kBM / 2 ? smem0 : smem1) + (r % (kBM / 2)) * RSQ);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  const char* const frow = smem + (32 * w + l32) * RSQ + 16 * g;
+  const char* const frow = (w < 2 ? smem0 : smem1) + (32 * (w & 1) + l32) * RSQ + 16 * g;
   auto read_frags = [&](bf16x8* f) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) f[s] = *reinterpret_cast<const bf16x8*>(frow + 32 * s);

@@ -85,19 +85,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int64_t qi = qw + l32;     // query row of this lane
   const int dch = d / 8;           // real 16-byte chunks per row
 
-  // Q^T fragments: B operand of S^T = K Q^T, reduction index = head dim.
-  // Branch-free: out-of-range rows and padded columns read a valid address
-  // and are replaced by zeros.
+  // Q^T fragments: B operand of S^T = K Q^T, reduction index = head dim.  The
+  // workgroup's 128 query rows are staged in the two tile buffers (64 rows
+  // each, one copy per row, overlapping the first-tile search); rows past the
+  // sequence end and padded columns arrive as zeros.  Each wave then reads
+  // its 32 rows' fragments (loading them straight from memory, where each
+  // instruction touches 32 rows, was slower).
+  static_assert((kBM / 2) * C::RSK <= C::BUF, "64 staged rows fit in a tile buffer");
   bf16x8 qf[DP / 16];
   {
-    const int64_t qrow = qi < T ? qi : T - 1;
-#pragma unroll
-    for (int s = 0; s < DP / 16; ++s) {
-      const int col = 16 * s + 8 * g;
-      const bool ok = qi < T && col < d;
-      const uint4 raw = *reinterpret_cast<const uint4*>(q + hoff + qrow * d + (ok ? col : 0));
-      const uint4 val = ok ? raw : make_uint4(0, 0, 0, 0);
-      qf[s] = *reinterpret_cast<const bf16x8*>(&val);
+    const unsigned vchunk = lane < dch ? unsigned(16 * lane) : kOutOfRange;
+#pragma unroll 4
+    for (int i = 0; i < kBM / kWaves; ++i) {
+      const int r = (kBM / kWaves) * w + i;
+      const int64_t row = q0 + r;
+      if (lane < C::CH)
+        dma16(make_rsrc(q + hoff + row * d, row < T ? 2 * d : 0), vchunk,
+              (r < kBM / 2 ? smem0 : smem1) + (r % (kBM / 2)) * C::RSK);
     }
   }
   const float r_i = rowt[head * Tp + qi];
@@ -272,6 +276,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     }
   };
 
+  {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const char* qrow = (w < 2 ? smem0 : smem1) + (32 * (w & 1) + l32) * C::RSK + 16 * g;
+#pragma unroll
+    for (int s = 0; s < DP / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+    __syncthreads();  // the buffers are refilled below
+  }
   load_tile(first_tile, smem0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
