@@ -22,6 +22,13 @@
 //   values pass (own = keys j, tiles of queries i):
 //     S = Q_I K^T;  dV^T += dH_I^T bf16(s_ij E_ij / n_i)     (Eq. 100)
 //
+// The values pass needs the S and E of the keys pass, on the same (key block,
+// query tile) pairs, so by default the keys pass stores the operand
+// bf16(s_ij E_ij / n_i) in the layout of the values pass's B fragments and
+// the values pass (kValuesStored) only reads it: dV is bitwise the same.  The
+// own rows' fragments are staged through LDS (one copy per row) before the
+// tile loop.
+//
 // E_ij = D'_ij / sqrt(d) = 2^((A_i - A_j) + r_i + c_j) from the gate scan's
 // terms, as in the forward pass (0 above the diagonal and past the sequence
 // end).  The accumulation reads its first operand transposed from LDS with
