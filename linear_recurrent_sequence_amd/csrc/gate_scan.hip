@@ -61,21 +61,45 @@ __device__ inline float log_sigmoid(float x) {
   return fminf(x, 0.0f) - log1pf(expf(-fabsf(x)));
 }
 
+// A float64 value from another lane by a DPP pattern (two 32-bit moves);
+// lanes without a source in the pattern, and rows outside ROW_MASK, get `old`.
+template <int CTRL, int ROW_MASK>
+__device__ inline double dpp64(double x, double old) {
+  const uint64_t xb = __builtin_bit_cast(uint64_t, x), ob = __builtin_bit_cast(uint64_t, old);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(int(uint32_t(ob)), int(uint32_t(xb)),
+                                                            CTRL, ROW_MASK, 0xF, false));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(int(uint32_t(ob >> 32)),
+                                                            int(uint32_t(xb >> 32)), CTRL, ROW_MASK,
+                                                            0xF, false));
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+// the element of an earlier lane by the pattern, the identity where there is none
+template <int CTRL, int ROW_MASK>
+__device__ inline Elem dpp_elem(Elem x) {
+  const Elem id = identity();
+  return {dpp64<CTRL, ROW_MASK>(x.a, id.a), dpp64<CTRL, ROW_MASK>(x.b, id.b)};
+}
+// DPP controls (gfx9): shift right within rows of 16 lanes, broadcast lane 15
+// of a row to the next row, lane 31 to rows 2 and 3, shift the wave right by 1
+constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
+
 // Ordered scan of one element per thread over the workgroup (thread order):
 // returns the composition of the elements of all earlier threads and stores
-// that of all threads in `total`.
+// that of all threads in `total`.  Within a wave: an inclusive scan by row
+// shifts of 1, 2, 4, 8 lanes, then the row totals by the two row broadcasts
+// (DPP moves, no LDS); across the waves, in order through LDS.
 __device__ Elem block_scan(Elem x, Elem& total) {
   __shared__ double s_a[kScanWaves];
   __shared__ double s_b[kScanWaves];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   Elem incl = x;  // inclusive scan across the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double oa = __shfl_up(incl.a, off, 64);
-    const double ob = __shfl_up(incl.b, off, 64);
-    if (lane >= off) incl = combine(Elem{oa, ob}, incl);
-  }
+  incl = combine(dpp_elem<kRowShr + 1, 0xF>(incl), incl);
+  incl = combine(dpp_elem<kRowShr + 2, 0xF>(incl), incl);
+  incl = combine(dpp_elem<kRowShr + 4, 0xF>(incl), incl);
+  incl = combine(dpp_elem<kRowShr + 8, 0xF>(incl), incl);
+  incl = combine(dpp_elem<kRowBcast15, 0xA>(incl), incl);
+  incl = combine(dpp_elem<kRowBcast31, 0xC>(incl), incl);
   if (lane == 63) {
     s_a[wave] = incl.a;
     s_b[wave] = incl.b;
@@ -88,9 +112,8 @@ __device__ Elem block_scan(Elem x, Elem& total) {
     if (w < wave) before = combine(before, e);
     total = combine(total, e);
   }
-  // lane-exclusive = inclusive of the previous lane
-  Elem lexcl = {__shfl_up(incl.a, 1, 64), __shfl_up(incl.b, 1, 64)};
-  if (lane == 0) lexcl = identity();
+  // lane-exclusive = inclusive of the previous lane (the identity on lane 0)
+  const Elem lexcl = dpp_elem<kWaveShr1, 0xF>(incl);
   __syncthreads();  // the shared totals may be rewritten by the next call
   return combine(before, lexcl);
 }
