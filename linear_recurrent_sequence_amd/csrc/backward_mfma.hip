@@ -80,7 +80,11 @@ struct BCfg {
   static constexpr int GN = GT + 128;           // 1 / n_i of the tile (keys, values passes)
   static constexpr int GD = GT + 256;           // db_i of the tile (keys pass)
   static constexpr int GA = GT + 384;           // float64 anchor of the tile
-  static constexpr int BUF = MODE == kValuesStored ? GT : GA + 16;
+  // the stored-operand values pass holds two consecutive dH tiles per buffer
+  // (tile J at 0, tile J + 1 at GT), so it waits and synchronises once per
+  // 64 queries: its 24 matrix instructions per tile do not cover a load's
+  // latency
+  static constexpr int BUF = MODE == kValuesStored ? 2 * GT : GA + 16;
   static constexpr int SA = VAL ? S2 : S1;          // transposed operand's stride
   static constexpr int A_OFF = VAL ? X2_OFF : X1_OFF;
   static_assert(2 * BUF <= 160 * 1024, "LDS budget");
@@ -412,6 +416,50 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     }
   };
 
+  if constexpr (MODE == kValuesStored) {
+    // pairs of tiles: (J, J + 1) from one buffer while (J + 2, J + 3) land in
+    // the other
+    bf16x8 pin1[2] = {bf16x8{}, bf16x8{}}, pnext1[2] = {bf16x8{}, bf16x8{}};
+    auto load_pair = [&](int J, char* buf) {
+      load_tile(J, buf);
+      if (J + 1 <= last) load_tile(J + 1, buf + C::GT);
+    };
+    auto compute_pair = [&](const char* buf, int J) {
+      if (wave_needs(J)) compute(buf, J, pin);
+      if (J + 1 <= last && wave_needs(J + 1)) compute(buf + C::GT, J + 1, pin1);
+    };
+    auto next_pins = [&](int J) {
+      pin[0] = pnext[0];
+      pin[1] = pnext[1];
+      pin1[0] = pnext1[0];
+      pin1[1] = pnext1[1];
+      load_pin(J, pnext);
+      load_pin(J + 1, pnext1);
+    };
+    load_pair(first, smem0);
+    load_pin(first, pin);
+    load_pin(first + 1, pin1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int J = first; J <= last; J += 4) {
+      load_pin(J + 2, pnext);
+      load_pin(J + 3, pnext1);
+      if (J + 2 <= last) load_pair(J + 2, smem1);
+      compute_pair(smem0, J);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (J + 2 > last) break;
+      next_pins(J + 4);
+      if (J + 4 <= last) load_pair(J + 4, smem0);
+      compute_pair(smem1, J + 2);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      pin[0] = pnext[0];
+      pin[1] = pnext[1];
+      pin1[0] = pnext1[0];
+      pin1[1] = pnext1[1];
+    }
+  } else {
   load_tile(first, smem0);
   load_pin(first, pin);
   __builtin_amdgcn_s_waitcnt(0);
@@ -430,6 +478,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     next_pin();
+  }
   }
 
   // ---- epilogue: the row or column sums of dD~, and dQ / dK / dV in bf16
