@@ -349,6 +349,8 @@ hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* f
 // The stored dV operand is used up to this size (the environment variable
 // MLSTM_BWD_STORE_MAX, in bytes, overrides it); above it the values pass
 // recomputes S (bitwise the same results, more time, no quadratic memory).
+// The entry point calls this once per call and hands the result to both the
+// scratch sizing and the launch, so the two can never disagree.
 constexpr size_t kBackwardStoreMax = size_t(2) << 30;
 
 size_t backward_store_bytes(int64_t H, int64_t T, int64_t d, bool is_bf16) {
@@ -359,24 +361,28 @@ size_t backward_store_bytes(int64_t H, int64_t T, int64_t d, bool is_bf16) {
   return b <= cap ? b : 0;
 }
 
-size_t backward_scratch_bytes(int64_t H, int64_t T, int64_t d, bool is_bf16) {
-  return 4 * align256(size_t(H) * size_t(T) * sizeof(float)) +
-         align256(backward_store_bytes(H, T, d, is_bf16));
+size_t backward_scratch_bytes(int64_t H, int64_t T, size_t store_bytes) {
+  return 4 * align256(size_t(H) * size_t(T) * sizeof(float)) + align256(store_bytes);
 }
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* fgate,
                            const void* h, const float* m, const float* n, const float* b,
-                           const void* dh, const Workspace& ws, void* scratch, void* dq, void* dk,
-                           void* dv, float* digate, float* dfgate, int64_t H, int64_t T,
-                           int64_t d, bool is_bf16, bool exp_forget, hipStream_t stream) {
+                           const void* dh, const Workspace& ws, void* scratch,
+                           size_t store_bytes, void* dq, void* dk, void* dv, float* digate,
+                           float* dfgate, int64_t H, int64_t T, int64_t d, bool is_bf16,
+                           bool exp_forget, hipStream_t stream) {
   if (d % 16 != 0 || d < 16 || d > kBMaxD) return hipErrorInvalidValue;
+  // the stored operand is all or nothing: a partial size would be overrun
+  if (store_bytes != 0 &&
+      (!is_bf16 || !backward_mfma_supports(d) || store_bytes != backward_mfma_store_bytes(H, T)))
+    return hipErrorInvalidValue;
   char* p = static_cast<char*>(scratch);
   const size_t one = align256(size_t(H) * size_t(T) * sizeof(float));
   float* inv_n = reinterpret_cast<float*>(p);
   float* db = reinterpret_cast<float*>(p + one);
   float* rsum = reinterpret_cast<float*>(p + 2 * one);
   float* csum = reinterpret_cast<float*>(p + 3 * one);
-  void* vstore = backward_store_bytes(H, T, d, is_bf16) ? p + 4 * one : nullptr;
+  void* vstore = store_bytes ? p + 4 * one : nullptr;
   if (is_bf16) {
     using B16 = __hip_bfloat16;
     return launch_typed<B16>(static_cast<const B16*>(q), static_cast<const B16*>(k),

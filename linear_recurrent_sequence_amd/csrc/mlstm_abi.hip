@@ -300,7 +300,9 @@ int mlstm_parallel_bwd(const void* q, const void* k, const void* v, const float*
   const int64_t H = B * NH;
   const size_t wsb = mlstm::workspace_bytes(H, T);
   const size_t mb = mlstm::align256(size_t(H) * size_t(T) * sizeof(float));
-  const size_t scb = mlstm::backward_scratch_bytes(H, T, d, dtype == MLSTM_BF16);
+  // read once: the scratch size and the launch must see the same store size
+  const size_t store = mlstm::backward_store_bytes(H, T, d, dtype == MLSTM_BF16);
+  const size_t scb = mlstm::backward_scratch_bytes(H, T, store);
   void* ws = nullptr;
   if (hipMallocAsync(&ws, wsb + mb + scb, s) != hipSuccess) {
     (void)hipGetLastError();
@@ -313,8 +315,8 @@ int mlstm_parallel_bwd(const void* q, const void* k, const void* v, const float*
   // bitwise the forward's)
   st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_scan, w, H, T, d, exp_forget, s));
   if (st == MLSTM_OK)
-    st = hip_status(mlstm::launch_backward(q, k, v, fgate, h, m, n, b, dh, w, scratch, dq, dk,
-                                           dv, digate, dfgate, H, T, d, dtype == MLSTM_BF16,
+    st = hip_status(mlstm::launch_backward(q, k, v, fgate, h, m, n, b, dh, w, scratch, store, dq,
+                                           dk, dv, digate, dfgate, H, T, d, dtype == MLSTM_BF16,
                                            exp_forget, s));
   if (hipFreeAsync(ws, s) != hipSuccess && st == MLSTM_OK) st = MLSTM_ERR_HIP;
   return st;

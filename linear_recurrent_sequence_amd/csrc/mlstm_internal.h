@@ -149,17 +149,21 @@ hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, cons
 
 // Backward pass (Eqs. 87-105), float32 vector tiles, d <= kBackwardMaxHeadDim
 // (four 16-row float32 tiles of the head dimension share the LDS).  `ws` holds
-// the gate scan's terms for the same inputs; `scratch` holds
-// backward_scratch_bytes(H, T, d, is_bf16) bytes (256-byte aligned): per-row
-// temporaries and, on the matrix-core path, the stored operand of the dV
-// product.
+// the gate scan's terms for the same inputs.  backward_store_bytes gives the
+// size of the stored operand of the dV product (0: the values pass recomputes
+// it); it reads the environment, so a caller evaluates it once and passes the
+// same value to backward_scratch_bytes and launch_backward.  `scratch` holds
+// backward_scratch_bytes(H, T, store_bytes) bytes (256-byte aligned): per-row
+// temporaries, then the stored operand.
 constexpr int kBackwardMaxHeadDim = 512;
-size_t backward_scratch_bytes(int64_t H, int64_t T, int64_t d, bool is_bf16);
+size_t backward_store_bytes(int64_t H, int64_t T, int64_t d, bool is_bf16);
+size_t backward_scratch_bytes(int64_t H, int64_t T, size_t store_bytes);
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* fgate,
                            const void* h, const float* m, const float* n, const float* b,
-                           const void* dh, const Workspace& ws, void* scratch, void* dq, void* dk,
-                           void* dv, float* digate, float* dfgate, int64_t H, int64_t T,
-                           int64_t d, bool is_bf16, bool exp_forget, hipStream_t stream);
+                           const void* dh, const Workspace& ws, void* scratch,
+                           size_t store_bytes, void* dq, void* dk, void* dv, float* digate,
+                           float* dfgate, int64_t H, int64_t T, int64_t d, bool is_bf16,
+                           bool exp_forget, hipStream_t stream);
 
 // The row and column passes of the backward on the matrix cores (bf16,
 // d <= 512): dQ and the row sums r of dD~ (the rows pass also stores the
@@ -179,7 +183,7 @@ hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* 
 // Recurrent step (generation), stabilized states in float32: C [H][d][d],
 // n [H][d], m [H].  C_out may equal C_in; n_out / m_out must not overlap
 // n_in / m_in.  den_out [H] is optional.  hipErrorInvalidValue for an
-// unsupported d (a multiple of 16 in [16, 512] is supported).
+// unsupported d (a multiple of 16 in [16, 1024] is supported).
 hipError_t launch_recurrent_step(const void* q, const void* k, const void* v, const float* igate,
                                  const float* fgate, const float* C_in, const float* n_in,
                                  const float* m_in, float* C_out, float* n_out, float* m_out,

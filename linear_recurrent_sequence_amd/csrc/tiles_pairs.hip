@@ -413,10 +413,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
   }
   if (ogate == nullptr && htilde == nullptr) {
     // bf16(h~) goes through LDS (the tile regions are free now): row
-    // 32 pq + l32 of the block, logical 16-byte chunk c at slot c ^ sw(row);
-    // then the block's rows, contiguous in memory, are stored 1 KiB per
-    // instruction.  Rows past the sequence end fall outside the buffer range
-    // and are not written.
+    // 32 pq + l32 of the block at the K rows' padded stride, columns in
+    // order; then the block's rows, contiguous in memory, are stored 1 KiB
+    // per instruction.  Rows past the sequence end fall outside the buffer
+    // range and are not written.
     const int orow = C::K_OFF + (32 * pq + l32) * C::RSK;
 #pragma unroll
     for (int b = 0; b < C::NB; ++b) {
