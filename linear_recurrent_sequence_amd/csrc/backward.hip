@@ -47,10 +47,11 @@ __device__ inline float load_elem(const __hip_bfloat16* p) { return __bfloat162f
 __device__ inline void store_elem(float* p, float x) { *p = x; }
 __device__ inline void store_elem(__hip_bfloat16* p, float x) { *p = __float2bfloat16(x); }
 
-// E_ij = D'_ij / sqrt(d) from the gate-scan terms (0 above the diagonal or
-// past the sequence end)
-__device__ inline float gate_factor(double a_i, double a_j, float r_i, float c_j, bool valid) {
-  return valid ? exp2f(float(a_i - a_j) + r_i + c_j) : 0.0f;
+// E_ij = D'_ij / sqrt(d) = 2^(R_i + C_j) from the gate-scan terms, the
+// exponent summed in float64 and rounded once (0 above the diagonal or past
+// the sequence end)
+__device__ inline float gate_factor(double r_i, double c_j, bool valid) {
+  return valid ? exp2f(float(r_i + c_j)) : 0.0f;
 }
 
 // 1/n_i and db_i, one wave per row
@@ -82,9 +83,8 @@ template <typename Tin>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dh, const float* __restrict__ inv_n, const float* __restrict__ db,
-    const double* __restrict__ anchor, const float* __restrict__ rowt,
-    const float* __restrict__ colt, Tin* __restrict__ dq, float* __restrict__ rsum, int64_t T,
-    int d, int64_t Tp, int64_t nblk, int64_t row_tiles) {
+    const double* __restrict__ rowt, const double* __restrict__ colt, Tin* __restrict__ dq,
+    float* __restrict__ rsum, int64_t T, int d, int64_t Tp, int64_t row_tiles) {
   __shared__ float Qs[kBT][kBPad];
   __shared__ float Gs[kBT][kBPad];  // dh rows
   __shared__ float Ks[kBT][kBPad];
@@ -104,8 +104,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
     Gs[r][c] = in ? load_elem(dh + hoff + (q0 + r) * d + c) : 0.0f;
   }
   const bool row_in = qi < T;
-  const float r_i = rowt[head * Tp + qi];
-  const double a_i = anchor[head * nblk + q0 / kAnchorBlock];
+  const double r_i = rowt[head * Tp + qi];
   const float in_i = row_in ? inv_n[head * T + qi] : 0.0f;
   const float db_i = row_in ? db[head * T + qi] : 0.0f;
 
@@ -131,8 +130,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
       gg = fmaf(Gs[rl][c], Vs[cl][c], gg);
     }
     const bool valid = row_in && kj <= qi && kj < T;
-    const float e = gate_factor(a_i, anchor[head * nblk + k0 / kAnchorBlock], r_i,
-                                colt[head * Tp + kj], valid);
+    const float e = gate_factor(r_i, colt[head * Tp + kj], valid);
     const float dct = gg * in_i + db_i;  // dC~' (Eqs. 91-93)
     rs += (s * e) * dct;                 // dD~ = C~' dC~' (Eq. 95)
     Ps[rl][cl] = e * dct;
@@ -168,9 +166,9 @@ template <typename Tin>
 __global__ __launch_bounds__(256) void bwd_cols_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ dh, const float* __restrict__ inv_n, const float* __restrict__ db,
-    const double* __restrict__ anchor, const float* __restrict__ rowt,
-    const float* __restrict__ colt, Tin* __restrict__ dk, Tin* __restrict__ dv,
-    float* __restrict__ csum, int64_t T, int d, int64_t Tp, int64_t nblk, int64_t key_tiles) {
+    const double* __restrict__ rowt, const double* __restrict__ colt, Tin* __restrict__ dk,
+    Tin* __restrict__ dv, float* __restrict__ csum, int64_t T, int d, int64_t Tp,
+    int64_t key_tiles) {
   __shared__ float Ks[kBT][kBPad];
   __shared__ float Vs[kBT][kBPad];
   __shared__ float Qs[kBT][kBPad];
@@ -191,8 +189,7 @@ __global__ __launch_bounds__(256) void bwd_cols_kernel(
     Vs[r][c] = in ? load_elem(v + hoff + (k0 + r) * d + c) : 0.0f;
   }
   const bool key_in = kj < T;
-  const float c_j = colt[head * Tp + kj];  // kj < Tp
-  const double a_j = anchor[head * nblk + k0 / kAnchorBlock];
+  const double c_j = colt[head * Tp + kj];  // kj < Tp
 
   float acck[kBMaxD / kBT], accv[kBMaxD / kBT];
 #pragma unroll
@@ -216,8 +213,8 @@ __global__ __launch_bounds__(256) void bwd_cols_kernel(
       gg = fmaf(Gs[cl][c], Vs[kl][c], gg);
     }
     const bool valid = key_in && row_in && kj <= qi;
-    const float r_i = rowt[head * Tp + (row_in ? qi : 0)];
-    const float e = gate_factor(anchor[head * nblk + q0 / kAnchorBlock], a_j, r_i, c_j, valid);
+    const double r_i = rowt[head * Tp + (row_in ? qi : 0)];
+    const float e = gate_factor(r_i, c_j, valid);
     const float in_i = row_in ? inv_n[head * T + qi] : 0.0f;
     const float db_i = row_in ? db[head * T + qi] : 0.0f;
     const float dct = gg * in_i + db_i;
@@ -333,11 +330,11 @@ hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* f
                        stream, h, dh, m, n, b, inv_n, db, rows, int(d));
     const int64_t tiles = (T + kBT - 1) / kBT;
     hipLaunchKernelGGL(bwd_rows_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream, q,
-                       k, v, dh, inv_n, db, ws.anchor, ws.rowt, ws.colt, dq, rsum, T, int(d),
-                       ws.Tp, ws.nblk, tiles);
+                       k, v, dh, inv_n, db, ws.rowt, ws.colt, dq, rsum, T, int(d), ws.Tp,
+                       tiles);
     hipLaunchKernelGGL(bwd_cols_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream, q,
-                       k, v, dh, inv_n, db, ws.anchor, ws.rowt, ws.colt, dk, dv, csum, T, int(d),
-                       ws.Tp, ws.nblk, tiles);
+                       k, v, dh, inv_n, db, ws.rowt, ws.colt, dk, dv, csum, T, int(d), ws.Tp,
+                       tiles);
   }
   hipLaunchKernelGGL(bwd_gates_kernel, dim3(unsigned(H)), dim3(kGThreads), 0, stream, fgate,
                      rsum, csum, digate, dfgate, T, int(exp_forget));

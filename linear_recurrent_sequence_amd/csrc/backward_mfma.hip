@@ -76,15 +76,15 @@ struct BCfg {
   static constexpr int S2 = VAL ? 2 * DP + 64 : 2 * DP + 16;
   static constexpr int X1_OFF = 0;
   static constexpr int X2_OFF = MODE == kValuesStored ? 0 : kBN * S1;  // only dH: no X1
-  static constexpr int GT = X2_OFF + kBN * S2;  // c_j (rows pass) or r_i of the tile, float32
-  static constexpr int GN = GT + 128;           // 1 / n_i of the tile (keys, values passes)
-  static constexpr int GD = GT + 256;           // db_i of the tile (keys pass)
-  static constexpr int GA = GT + 384;           // float64 anchor of the tile
+  static constexpr int GT = X2_OFF + kBN * S2;  // C_j (rows pass) or R_i of the tile, float64
+  static constexpr int GN = GT + 256;           // 1 / n_i of the tile (keys, values passes)
+  static constexpr int GD = GT + 384;           // db_i of the tile (keys pass)
+  static constexpr int GEND = GT + 512;
   // the stored-operand values pass holds two consecutive dH tiles per buffer
   // (tile J at 0, tile J + 1 at GT), so it waits and synchronises once per
   // 64 queries: its 24 matrix instructions per tile do not cover a load's
   // latency
-  static constexpr int BUF = MODE == kValuesStored ? 2 * GT : GA + 16;
+  static constexpr int BUF = MODE == kValuesStored ? 2 * GT : GEND;
   static constexpr int SA = VAL ? S2 : S1;          // transposed operand's stride
   static constexpr int A_OFF = VAL ? X2_OFF : X1_OFF;
   static_assert(2 * BUF <= 160 * 1024, "LDS budget");
@@ -110,9 +110,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const u16* __restrict__ dh, const u16* __restrict__ hsrc, const float* __restrict__ m_in,
     const float* __restrict__ n_in, const float* __restrict__ b_in, float* __restrict__ inv_n,
-    float* __restrict__ db, const double* __restrict__ anchor, const float* __restrict__ rowt,
-    const float* __restrict__ colt, u16* __restrict__ out, float* __restrict__ sums, int T,
-    int d, int Tp, int nblk, int row_tiles, int H, u16* __restrict__ vstore, int64_t tri) {
+    float* __restrict__ db, const double* __restrict__ rowt, const double* __restrict__ colt,
+    u16* __restrict__ out, float* __restrict__ sums, int T, int d, int Tp, int row_tiles, int H,
+    u16* __restrict__ vstore, int64_t tri) {
   using C = BCfg<DP, MODE>;
   constexpr bool kTwo = MODE == kRowsPass || MODE == kKeysPass;  // a second first product (G)
   constexpr bool kFirst = MODE != kValuesStored;                  // first products at all
@@ -182,10 +182,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     __syncthreads();  // the staging space is refilled below
   }
 
-  // own gate terms: r_i, 1/n_i, db_i (rows pass) or c_j (key passes; -inf past
-  // the sequence end), and the anchor of the wave's 32 rows
-  const float own_t = MODE == kRowsPass ? rowt[int64_t(head) * Tp + oi] : colt[int64_t(head) * Tp + oi];
-  const double a_own = anchor[int64_t(head) * nblk + ow / kAnchorBlock];
+  // own gate terms: R_i, 1/n_i, db_i (rows pass) or C_j (key passes; -inf past
+  // the sequence end)
+  const double own_t =
+      MODE == kRowsPass ? rowt[int64_t(head) * Tp + oi] : colt[int64_t(head) * Tp + oi];
   float own_in = 0.0f, own_db = 0.0f;
   if (MODE == kRowsPass) {
     // dn_i = -(dh_i . h~_i) / n_i (Eqs. 88-89); db_i = sign(b_i) dn_i where
@@ -249,9 +249,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       }
     }
     if (!kFirst) return;
-    const float* tsrc = MODE == kRowsPass ? colt : rowt;
-    if (w == 0 && lane < kBN / 4)
-      dma16(make_rsrc(tsrc + int64_t(head) * Tp + x0, kBN * 4), unsigned(16 * lane), buf + C::GT);
+    const double* tsrc = MODE == kRowsPass ? colt : rowt;
+    if (w == 0 && lane < kBN / 2)
+      dma16(make_rsrc(tsrc + int64_t(head) * Tp + x0, kBN * 8), unsigned(16 * lane), buf + C::GT);
     if (MODE != kRowsPass) {
       // per-row scalars of [H][T] arrays: 4 bytes per lane (rows need not be
       // 16-byte aligned); rows past the sequence end read as zeros
@@ -262,9 +262,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
         dma4(make_rsrc(db + int64_t(head) * T + x0, int64_t(rows) * 4), unsigned(4 * lane),
              buf + C::GD);
     }
-    if (w == 3 && lane < 2)
-      dma4(make_rsrc(anchor + int64_t(head) * nblk + x0 / kAnchorBlock, 8), unsigned(4 * lane),
-           buf + C::GA);
   };
 
   // per-lane LDS offsets: rows of X1 / X2 for the first products, the
@@ -314,10 +311,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       }
     }
     // lane (g, l32), register r: own row l32, other row 8(r/4) + 4g + r%4 of the tile
-    const double a_x = *reinterpret_cast<const double*>(buf + C::GA);
-    const float d_anchor = MODE == kRowsPass ? float(a_own - a_x) : float(a_x - a_own);  // A_i - A_j
     const bool diag = J * kBN == ow;
-    const float* gt = reinterpret_cast<const float*>(buf + C::GT);
+    const double* gt = reinterpret_cast<const double*>(buf + C::GT);
     const float* gn = reinterpret_cast<const float*>(buf + C::GN);
     const float* gd = reinterpret_cast<const float*>(buf + C::GD);
     float pv[16];
@@ -327,8 +322,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     bf16x8 vb[2];
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const float4 t4 = *reinterpret_cast<const float4*>(gt + 8 * rq + 4 * g);
-      const float tt[4] = {t4.x, t4.y, t4.z, t4.w};
+      const double2 t01 = *reinterpret_cast<const double2*>(gt + 8 * rq + 4 * g);
+      const double2 t23 = *reinterpret_cast<const double2*>(gt + 8 * rq + 4 * g + 2);
+      const double tt[4] = {t01.x, t01.y, t23.x, t23.y};
       float nn[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (MODE != kRowsPass) {
         const float4 n4 = *reinterpret_cast<const float4*>(gn + 8 * rq + 4 * g);
@@ -345,7 +341,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
         bool valid;
         if (MODE == kRowsPass) valid = oi < T && !(diag && ol > l32);
         else valid = J * kBN + ol < T && !(diag && l32 > ol);
-        const float E = valid ? __builtin_amdgcn_exp2f(d_anchor + own_t + tt[e]) : 0.0f;
+        // E = 2^(R_i + C_j), summed in float64 and rounded once
+        const float E = valid ? __builtin_amdgcn_exp2f(float(own_t + tt[e])) : 0.0f;
         const float s = y1[4 * rq + e];
         if (MODE == kValuesPass) {
           pv[4 * rq + e] = s * E * nn[e];
@@ -515,9 +512,9 @@ void launch_pass(const void* q, const void* k, const void* v, const void* dh, co
                      dim3(unsigned(row_tiles * H), unsigned(BCfg<DP, MODE>::SPLIT)), dim3(kBThreads),
                      0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), static_cast<const u16*>(dh),
-                     static_cast<const u16*>(h), m, n, b, inv_n, db, ws.anchor, ws.rowt, ws.colt,
-                     static_cast<u16*>(out), sums, int(T), int(d), int(ws.Tp), int(ws.nblk),
-                     int(row_tiles), int(H), static_cast<u16*>(vstore), store_tiles(T));
+                     static_cast<const u16*>(h), m, n, b, inv_n, db, ws.rowt, ws.colt,
+                     static_cast<u16*>(out), sums, int(T), int(d), int(ws.Tp), int(row_tiles),
+                     int(H), static_cast<u16*>(vstore), store_tiles(T));
 }
 
 template <int DP>

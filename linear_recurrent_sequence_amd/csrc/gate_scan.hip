@@ -18,16 +18,17 @@
 // sums of fbar.
 //
 // A workgroup of 512 threads scans a chunk of 2048 positions; each thread
-// owns 4 consecutive positions (one sixteenth of a 64-position anchor block),
+// owns 4 consecutive positions (an eighth of a 32-position tile),
 // loaded and stored as 16-byte vectors where the row alignment allows.  Short
 // sequences take one workgroup per head that walks its chunks in order.  Long
 // ones are scanned in two passes, so that every chunk has a workgroup of its
 // own: the first reduces each chunk to its element (sum, map), the second
 // gives each chunk the composition of all earlier chunks' elements (folded in
 // order across the workgroup's threads) as its carry and scans it.  Sums and
-// the max-plus maps are carried in float64; log sigmoid is evaluated in
-// float32 (its relative error stays local: only sums over the few positions
-// where D' is not negligible matter).
+// the max-plus maps are carried in float64.  log sigmoid(x) is the exact
+// min(x, 0) minus log1p(exp(-|x|)), a value in (0, ln 2] whose float32
+// evaluation is off by about 1e-7 at most: the sum is taken in float64, so
+// the error of fbar does not grow with |x|.
 #include "mlstm_internal.h"
 
 namespace mlstm {
@@ -56,9 +57,11 @@ __device__ inline Elem identity() { return {0.0, -INFINITY}; }
 
 __device__ inline Elem combine(Elem first, Elem second) { return compose(first, second); }
 
-// log sigmoid(x) = min(x, 0) - log1p(exp(-|x|)): never forms exp(+|x|).
-__device__ inline float log_sigmoid(float x) {
-  return fminf(x, 0.0f) - log1pf(expf(-fabsf(x)));
+// log sigmoid(x) = min(x, 0) - log1p(exp(-|x|)): never forms exp(+|x|).  The
+// first term is exact; the second, in (0, ln 2], is evaluated in float32 and
+// subtracted in float64.
+__device__ inline double log_sigmoid(float x) {
+  return double(fminf(x, 0.0f)) - double(log1pf(expf(-fabsf(x))));
 }
 
 // A float64 value from another lane by a DPP pattern (two 32-bit moves);
@@ -138,25 +141,27 @@ __device__ inline void load_raw(const float* f, const float* ig, int64_t p0, int
 
 // log f_t of the same positions (padding: no forgetting, no input; it never
 // reaches a real row)
-__device__ inline void to_log_forget(int64_t p0, int64_t T, int exp_forget, float fb[kScanPer]) {
+__device__ inline void to_log_forget(int64_t p0, int64_t T, int exp_forget,
+                                     const float fr[kScanPer], double fb[kScanPer]) {
 #pragma unroll
   for (int e = 0; e < kScanPer; ++e)
-    fb[e] = p0 + e < T ? (exp_forget ? fb[e] : log_sigmoid(fb[e])) : 0.0f;
+    fb[e] = p0 + e < T ? (exp_forget ? double(fr[e]) : log_sigmoid(fr[e])) : 0.0;
 }
 
 __device__ inline void load_gates(const float* f, const float* ig, int64_t p0, int64_t T,
-                                  bool vec_rows, int exp_forget, float fb[kScanPer],
+                                  bool vec_rows, int exp_forget, double fb[kScanPer],
                                   float iv[kScanPer]) {
-  load_raw(f, ig, p0, T, vec_rows, fb, iv);
-  to_log_forget(p0, T, exp_forget, fb);
+  float fr[kScanPer];
+  load_raw(f, ig, p0, T, vec_rows, fr, iv);
+  to_log_forget(p0, T, exp_forget, fr, fb);
 }
 
 // the element of one thread's positions
-__device__ inline Elem thread_elem(const float fb[kScanPer], const float iv[kScanPer]) {
+__device__ inline Elem thread_elem(const double fb[kScanPer], const float iv[kScanPer]) {
   Elem t = identity();
 #pragma unroll
   for (int e = 0; e < kScanPer; ++e)
-    t = combine(t, Elem{double(fb[e]), double(iv[e])});
+    t = combine(t, Elem{fb[e], double(iv[e])});
   return t;
 }
 
@@ -168,7 +173,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_totals_kernel(
   const int64_t head = int64_t(blockIdx.x) / nchunk;
   const int64_t c = int64_t(blockIdx.x) % nchunk;
   const int64_t p0 = c * kScanChunk + int64_t(threadIdx.x) * kScanPer;
-  float fb[kScanPer], iv[kScanPer];
+  double fb[kScanPer];
+  float iv[kScanPer];
   load_gates(fgate + head * T, igate + head * T, p0, T, (T & 3) == 0, exp_forget, fb, iv);
   Elem total;
   block_scan(thread_elem(fb, iv), total);
@@ -189,10 +195,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_totals_kernel(
 template <bool kLoop>
 __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
     const float* __restrict__ igate, const float* __restrict__ fgate, float* __restrict__ m_out,
-    double* __restrict__ anchor, float* __restrict__ rowt, float* __restrict__ colt,
-    float* __restrict__ colx, float* __restrict__ rowb, float* __restrict__ keyb,
-    const double* __restrict__ segs, int64_t T, int64_t Tp, int64_t nblk, int64_t nchunk,
-    int64_t groups, int64_t count, double half_ln_d, int exp_forget) {
+    double* __restrict__ rowt, double* __restrict__ colt, float* __restrict__ colx,
+    double* __restrict__ rowb, double* __restrict__ keyb, const double* __restrict__ segs,
+    int64_t T, int64_t Tp, int64_t nchunk, int64_t groups, int64_t count, double half_ln_d,
+    int exp_forget) {
   const double kLog2e = 1.4426950408889634074;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -201,12 +207,11 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
   const float* f = fgate + head * T;
   const float* ig = igate + head * T;
   float* mo = m_out + head * T;
-  double* anc = anchor + head * nblk;
-  float* rt = rowt + head * Tp;
-  float* ct = colt + head * Tp;
+  double* rt = rowt + head * Tp;
+  double* ct = colt + head * Tp;
   float* cx = colx + head * Tp;
-  float* rb = rowb + head * (Tp / kBoundTile);
-  float* kb = keyb + head * (Tp / kBoundTile);
+  double* rb = rowb + head * (Tp / kBoundTile);
+  double* kb = keyb + head * (Tp / kBoundTile);
   // the rows of the [H][T] arrays start 16-byte aligned when T % 4 == 0
   // (their base pointers are 16-byte aligned)
   const bool vec_rows = (T & 3) == 0;
@@ -230,58 +235,58 @@ __global__ __launch_bounds__(kScanThreads) void gate_scan_kernel(
   if (c0 < c_end) load_raw(f, ig, c0 * kScanChunk + int64_t(tid) * kScanPer, T, vec_rows, fn, in);
   for (int64_t chunk = c0; chunk < (kLoop ? c_end : c0 + 1); ++chunk) {
     const int64_t p0 = chunk * kScanChunk + int64_t(tid) * kScanPer;
-    float fb[kScanPer], iv[kScanPer];
+    float fr[kScanPer], iv[kScanPer];
 #pragma unroll
     for (int e = 0; e < kScanPer; ++e) {
-      fb[e] = fn[e];
+      fr[e] = fn[e];
       iv[e] = in[e];
     }
     if (kLoop && chunk + 1 < c_end) load_raw(f, ig, p0 + kScanChunk, T, vec_rows, fn, in);
-    to_log_forget(p0, T, exp_forget, fb);
+    double fb[kScanPer];
+    to_log_forget(p0, T, exp_forget, fr, fb);
     Elem total;
     const Elem before = block_scan(thread_elem(fb, iv), total);
 
     double cs = carry.a + before.a;                     // sum of fbar before p0
     double m = apply(before, apply(carry, -INFINITY));  // m at p0 - 1
-    // anchor of this thread's 64-block: the prefix sum before the block start,
-    // held by the first of the 16 threads that share the block
-    const double blk_anchor = __shfl(cs, lane & ~15, 64);
-    if (p0 < Tp && (p0 & (kAnchorBlock - 1)) == 0) anc[p0 / kAnchorBlock] = blk_anchor * kLog2e;
-    float rmax = -INFINITY, cmax = -INFINITY;  // of the values stored below
-    float mv[kScanPer], rv[kScanPer], cv[kScanPer];
+    double rmax = -INFINITY, cmax = -INFINITY;  // of the values stored below
+    float mv[kScanPer];
+    double rv[kScanPer], cv[kScanPer];
 #pragma unroll
     for (int e = 0; e < kScanPer; ++e) {
       const int64_t p = p0 + e;
-      cs += double(fb[e]);
-      m = fmax(m + double(fb[e]), double(iv[e]));
-      const double loc = cs - blk_anchor;
+      cs += fb[e];
+      m = fmax(m + fb[e], double(iv[e]));
       if (p < T) {
         mv[e] = float(m);
-        rv[e] = float((loc - m - half_ln_d) * kLog2e);
-        cv[e] = float((double(iv[e]) - loc) * kLog2e);
-        rmax = fmaxf(rmax, rv[e]);
-        cmax = fmaxf(cmax, cv[e]);
+        rv[e] = (cs - m - half_ln_d) * kLog2e;
+        cv[e] = (double(iv[e]) - cs) * kLog2e;
+        rmax = fmax(rmax, rv[e]);
+        cmax = fmax(cmax, cv[e]);
       } else {  // padding up to Tp
         mv[e] = 0.0f;
-        rv[e] = 0.0f;
+        rv[e] = 0.0;
         cv[e] = -INFINITY;
-        rmax = fmaxf(rmax, 0.0f);
+        rmax = fmax(rmax, 0.0);
       }
     }
     // tile bounds: the 8 threads of a 32-position tile are 8 consecutive lanes
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 1, 64));
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 2, 64));
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 4, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 1, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 2, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 4, 64));
-    // the key factor of the factored exponent, relative to its tile's maximum
+    rmax = fmax(rmax, __shfl_xor(rmax, 1, 64));
+    rmax = fmax(rmax, __shfl_xor(rmax, 2, 64));
+    rmax = fmax(rmax, __shfl_xor(rmax, 4, 64));
+    cmax = fmax(cmax, __shfl_xor(cmax, 1, 64));
+    cmax = fmax(cmax, __shfl_xor(cmax, 2, 64));
+    cmax = fmax(cmax, __shfl_xor(cmax, 4, 64));
+    // the key factor of the factored exponent, relative to its tile's maximum:
+    // the difference is formed in float64 and rounded once
     float xv[kScanPer];
 #pragma unroll
-    for (int e = 0; e < kScanPer; ++e) xv[e] = p0 + e < T ? exp2f(cv[e] - cmax) : 0.0f;
+    for (int e = 0; e < kScanPer; ++e) xv[e] = p0 + e < T ? exp2f(float(cv[e] - cmax)) : 0.0f;
     if (p0 < Tp) {  // Tp is a multiple of 128: the 4 positions are all below it
-      *reinterpret_cast<float4*>(rt + p0) = make_float4(rv[0], rv[1], rv[2], rv[3]);
-      *reinterpret_cast<float4*>(ct + p0) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+      *reinterpret_cast<double2*>(rt + p0) = make_double2(rv[0], rv[1]);
+      *reinterpret_cast<double2*>(rt + p0 + 2) = make_double2(rv[2], rv[3]);
+      *reinterpret_cast<double2*>(ct + p0) = make_double2(cv[0], cv[1]);
+      *reinterpret_cast<double2*>(ct + p0 + 2) = make_double2(cv[2], cv[3]);
       *reinterpret_cast<float4*>(cx + p0) = make_float4(xv[0], xv[1], xv[2], xv[3]);
       if ((p0 & (kBoundTile - 1)) == 0) {
         rb[p0 / kBoundTile] = rmax;
@@ -309,23 +314,23 @@ hipError_t launch_gate_scan(const float* igate, const float* fgate, float* m_out
   if (nchunk < kScanTwoPassChunks) {  // one workgroup per head, chunks in order
     if (nchunk == 1)
       hipLaunchKernelGGL(gate_scan_kernel<false>, dim3(unsigned(H)), dim3(kScanThreads), 0, stream,
-                         igate, fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb,
-                         ws.keyb, static_cast<const double*>(nullptr), T, ws.Tp, ws.nblk, nchunk,
-                         int64_t(1), int64_t(1), half_ln_d, int(exp_forget));
+                         igate, fgate, m_out, ws.rowt, ws.colt, ws.colx, ws.rowb, ws.keyb,
+                         static_cast<const double*>(nullptr), T, ws.Tp, nchunk, int64_t(1),
+                         int64_t(1), half_ln_d, int(exp_forget));
     else
       hipLaunchKernelGGL(gate_scan_kernel<true>, dim3(unsigned(H)), dim3(kScanThreads), 0, stream,
-                         igate, fgate, m_out, ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb,
-                         ws.keyb, static_cast<const double*>(nullptr), T, ws.Tp, ws.nblk, nchunk,
-                         int64_t(1), nchunk, half_ln_d, int(exp_forget));
+                         igate, fgate, m_out, ws.rowt, ws.colt, ws.colx, ws.rowb, ws.keyb,
+                         static_cast<const double*>(nullptr), T, ws.Tp, nchunk, int64_t(1),
+                         nchunk, half_ln_d, int(exp_forget));
     return hipGetLastError();
   }
   const dim3 grid(unsigned(H * nchunk));
   hipLaunchKernelGGL(scan_totals_kernel, grid, dim3(kScanThreads), 0, stream, igate, fgate,
                      ws.segs, T, nchunk, int(exp_forget));
   hipLaunchKernelGGL(gate_scan_kernel<false>, grid, dim3(kScanThreads), 0, stream, igate, fgate, m_out,
-                     ws.anchor, ws.rowt, ws.colt, ws.colx, ws.rowb, ws.keyb,
-                     static_cast<const double*>(ws.segs), T, ws.Tp, ws.nblk, nchunk, nchunk,
-                     int64_t(1), half_ln_d, int(exp_forget));
+                     ws.rowt, ws.colt, ws.colx, ws.rowb, ws.keyb,
+                     static_cast<const double*>(ws.segs), T, ws.Tp, nchunk, nchunk, int64_t(1),
+                     half_ln_d, int(exp_forget));
   return hipGetLastError();
 }
 

@@ -3,39 +3,40 @@
 // Workspace written by the gate scan and read by the tile kernels, for H
 // heads of length T, padded to Tp = ceil(T / 128) * 128 positions:
 //
-//   anchor [H][Tp/64]  float64  A_b = (sum of fbar over positions < 64 b) * log2(e)
-//   rowt   [H][Tp]     float32  r_i = (loc_i - m_i - ln(d)/2) * log2(e)
-//   colt   [H][Tp]     float32  c_j = (i~_j - loc_j) * log2(e)    (-inf on padding)
-//   colx   [H][Tp]     float32  e_j = 2^(c_j - keyb_{j/32})        (0 on padding)
-//   rowb   [H][Tp/32]  float32  max of r_i over each 32-row block
-//   keyb   [H][Tp/32]  float32  max of c_j over each 32-key tile (-inf if all padding)
+//   rowt   [H][Tp]     float64  R_i = (cs_i - m_i - ln(d)/2) * log2(e)      (0 on padding)
+//   colt   [H][Tp]     float64  C_j = (i~_j - cs_j) * log2(e)               (-inf on padding)
+//   colx   [H][Tp]     float32  e_j = 2^fl32(C_j - keyb_{j/32})             (0 on padding)
+//   rowb   [H][Tp/32]  float64  max of R_i over each 32-row block
+//   keyb   [H][Tp/32]  float64  max of C_j over each 32-key tile (-inf if all padding)
 //   segs   [H][nchunk][2] float64  the scan element (max-plus map a, b; a is the
 //                                sum of fbar) of each 2048-position chunk
 //                                (long sequences)
 //
-// where fbar = log sigmoid(f~) and loc_i = (inclusive prefix sum of fbar up to
-// i) - (the same sum up to the start of i's 64-position block), so that, for
-// j <= i (Eqs. 79-82 and 101 of the xLSTM appendix),
+// where fbar = log sigmoid(f~) (or f~ for an exponential forget gate) and cs
+// is its inclusive prefix sum, so that, for j <= i (Eqs. 79-82 and 101 of the
+// xLSTM appendix),
 //
-//   log2( D'_ij / sqrt(d) ) = (A_{i/64} - A_{j/64}) + r_i + c_j.
+//   log2( D'_ij / sqrt(d) ) = R_i + C_j.
 //
-// The block anchors keep the difference of two long prefix sums out of
-// float32: the anchor difference is taken in float64 and rounded once, and
-// every other term is bounded by one block's worth of forget gates.
+// Every term is float64, and a kernel forms each exponent in float64 and
+// rounds it to float32 once, right before the exp2: the rounding error of an
+// exponent is then 2^-24 of its own magnitude, whatever the sizes of R_i and
+// C_j (both grow with the prefix sums).  The float64 prefix sums resolve
+// differences cs_i - cs_j to about 2^-53 |cs| per position between j and i.
 //
 // Factored exponent: below the diagonal (every key of a 32-key tile J before
-// every query of a 32-row block), 2^((A_i - A_J) + r_i + c_j) equals
-// 2^((A_i - A_J) + r_i + keyb_J) * e_j, and neither factor can overflow:
-// the first is at most 1 (D' <= 1 and keyb_J is attained by a key of the
-// tile), the second lies in (0, 1].
+// every query of a 32-row block), 2^(R_i + C_j) equals 2^(R_i + keyb_J) * e_j,
+// with both exponents formed in float64 and rounded once; neither factor can
+// overflow: the first is at most 1 (D' <= 1 and keyb_J is attained by a key of
+// the tile), the second lies in (0, 1].  Each rounding is bounded by its own
+// exponent, and the two exponents have the sign and sum of R_i + C_j.
 //
-// Tile bound: the tile kernels form each exponent as
-// fl(fl(float(A_{i/64} - A_{j/64}) + r_i) + c_j).  Rounding is monotone, so
-// fl(fl(float(A_W - A_J) + rowb_W) + keyb_J), with the anchors of a 32-row
-// block W and a 32-key tile J, is at least every computed exponent of the
-// 32 x 32 tile.  Where it is below kSkipLog2 every exponential of the tile is
-// exactly 0 in float32, every C~' entry is 0, and the tile contributes
-// nothing: the tile kernels skip it without changing any result.
+// Tile bound: every exponent a tile kernel forms for the 32 x 32 block of a
+// 32-row block W and a 32-key tile J is fl32 of a float64 value at most
+// rowb_W + keyb_J (float64 addition and rounding are monotone).  Where that
+// sum is below kSkipLog2 every exponential of the tile is exactly 0 in
+// float32, every C~' entry is 0, and the tile contributes nothing: the tile
+// kernels skip it without changing any result.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -44,22 +45,19 @@
 namespace mlstm {
 
 constexpr int kRowPad = 128;     // T is padded to a multiple of this
-constexpr int kAnchorBlock = 64; // positions per float64 anchor
 constexpr int kBoundTile = 32;   // rows / keys per entry of rowb and keyb
-constexpr float kSkipLog2 = -200.0f;
+constexpr double kSkipLog2 = -200.0;
 constexpr int kScanChunk = 2048;        // positions per workgroup pass of the gate scan
 constexpr int kScanTwoPassChunks = 4;   // from this many chunks on, the scan runs in two passes
 
 struct Workspace {
-  double* anchor;
-  float* rowt;
-  float* colt;
+  double* rowt;
+  double* colt;
   float* colx;
-  float* rowb;
-  float* keyb;
+  double* rowb;
+  double* keyb;
   double* segs;
   int64_t Tp;
-  int64_t nblk;
 };
 
 inline int64_t padded_len(int64_t T) { return (T + kRowPad - 1) / kRowPad * kRowPad; }
@@ -71,29 +69,26 @@ inline int64_t scan_chunks(int64_t T) { return (padded_len(T) + kScanChunk - 1) 
 
 inline size_t workspace_bytes(int64_t H, int64_t T) {
   const int64_t Tp = padded_len(T);
-  return align256(size_t(H) * size_t(Tp / kAnchorBlock) * sizeof(double)) +
-         3 * align256(size_t(H) * size_t(Tp) * sizeof(float)) +
-         2 * align256(size_t(H) * size_t(Tp / kBoundTile) * sizeof(float)) +
+  return 2 * align256(size_t(H) * size_t(Tp) * sizeof(double)) +
+         align256(size_t(H) * size_t(Tp) * sizeof(float)) +
+         2 * align256(size_t(H) * size_t(Tp / kBoundTile) * sizeof(double)) +
          align256(size_t(H) * size_t(scan_chunks(T)) * 2 * sizeof(double));
 }
 
 inline Workspace carve(void* base, int64_t H, int64_t T) {
   Workspace w;
   w.Tp = padded_len(T);
-  w.nblk = w.Tp / kAnchorBlock;
   char* p = static_cast<char*>(base);
-  w.anchor = reinterpret_cast<double*>(p);
-  p += align256(size_t(H) * size_t(w.nblk) * sizeof(double));
-  w.rowt = reinterpret_cast<float*>(p);
-  p += align256(size_t(H) * size_t(w.Tp) * sizeof(float));
-  w.colt = reinterpret_cast<float*>(p);
-  p += align256(size_t(H) * size_t(w.Tp) * sizeof(float));
+  w.rowt = reinterpret_cast<double*>(p);
+  p += align256(size_t(H) * size_t(w.Tp) * sizeof(double));
+  w.colt = reinterpret_cast<double*>(p);
+  p += align256(size_t(H) * size_t(w.Tp) * sizeof(double));
   w.colx = reinterpret_cast<float*>(p);
   p += align256(size_t(H) * size_t(w.Tp) * sizeof(float));
-  w.rowb = reinterpret_cast<float*>(p);
-  p += align256(size_t(H) * size_t(w.Tp / kBoundTile) * sizeof(float));
-  w.keyb = reinterpret_cast<float*>(p);
-  p += align256(size_t(H) * size_t(w.Tp / kBoundTile) * sizeof(float));
+  w.rowb = reinterpret_cast<double*>(p);
+  p += align256(size_t(H) * size_t(w.Tp / kBoundTile) * sizeof(double));
+  w.keyb = reinterpret_cast<double*>(p);
+  p += align256(size_t(H) * size_t(w.Tp / kBoundTile) * sizeof(double));
   w.segs = reinterpret_cast<double*>(p);
   return w;
 }

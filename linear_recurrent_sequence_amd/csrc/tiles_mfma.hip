@@ -28,9 +28,9 @@
 // buffer resources whose range ends at the sequence end, so rows past it and
 // head-dimension padding arrive as zeros.
 //
-// Exponents: log2(D'_ij / sqrt(d)) = (A_{i/64} - A_{j/64}) + r_i + c_j with the
-// terms of the gate scan; the anchor difference is formed in float64 once per
-// (wave, tile), the key-tile anchor travelling with the tile into LDS.
+// Exponents: log2(D'_ij / sqrt(d)) = R_i + C_j with the float64 terms of the
+// gate scan, summed in float64 and rounded to float32 once per entry; C_j of
+// the tile's keys travels with the tile into LDS.
 #include "mlstm_internal.h"
 #include "tile_common.h"
 
@@ -51,22 +51,20 @@ struct Cfg {
   static constexpr int RSV = DP * 2 + 64;         // V row stride: transpose reads 2-way at most
   static constexpr int K_BYTES = kBN * RSK;
   static constexpr int V_BYTES = kBN * RSV;
-  static constexpr int C_OFF = K_BYTES + V_BYTES;
-  static constexpr int A_OFF = C_OFF + kBN * 4;  // float64 anchor of the key tile
-  static constexpr int KB_OFF = A_OFF + 8;       // max of c_j over the key tile
-  static constexpr int BUF = (KB_OFF + 4 + 15) / 16 * 16;
+  static constexpr int C_OFF = K_BYTES + V_BYTES;  // C_j of the tile's keys (float64)
+  static constexpr int KB_OFF = C_OFF + kBN * 8;   // max of C_j over the key tile (float64)
+  static constexpr int BUF = (KB_OFF + 8 + 15) / 16 * 16;
 };
 
 template <int DP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void tiles_mfma_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    const float* __restrict__ m_in, const double* __restrict__ anchor,
-    const float* __restrict__ rowt, const float* __restrict__ colt, u16* __restrict__ h_out,
-    const float* __restrict__ rowb, const float* __restrict__ keyb, float* __restrict__ n_out,
-    const u16* __restrict__ ogate, u16* __restrict__ htilde, float* __restrict__ b_out,
-    int64_t T, int d, int64_t Tp,
-    int64_t nblk, int64_t row_tiles, int64_t H, int skip) {
+    const float* __restrict__ m_in, const double* __restrict__ rowt,
+    const double* __restrict__ colt, u16* __restrict__ h_out, const double* __restrict__ rowb,
+    const double* __restrict__ keyb, float* __restrict__ n_out, const u16* __restrict__ ogate,
+    u16* __restrict__ htilde, float* __restrict__ b_out, int64_t T, int d, int64_t Tp,
+    int64_t row_tiles, int64_t H, int skip) {
   using C = Cfg<DP>;
   // two distinct buffers, so the loads into one never alias reads of the other
   __shared__ __attribute__((aligned(1024))) char smem0[C::BUF];
@@ -104,8 +102,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
               (r < kBM / 2 ? smem0 : smem1) + (r % (kBM / 2)) * C::RSK);
     }
   }
-  const float r_i = rowt[head * Tp + qi];
-  const double a_i = anchor[head * nblk + qw / kAnchorBlock];
+  const double r_i = rowt[head * Tp + qi];  // R_i, qi < Tp
 
   f32x16 acc[DP / 32];
 #pragma unroll
@@ -122,31 +119,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   // tile some wave needs, and inside the loop each wave skips the products
   // of tiles it does not need.
   const int64_t nb32 = Tp / kBoundTile;
-  const float rb_w = rowb[head * nb32 + qw / kBoundTile];
-  auto tile_needed = [&](double a_row, float rb, double a_key, float kb) {
-    return float(a_row - a_key) + rb + kb >= kSkipLog2;
-  };
+  const double rb_w = rowb[head * nb32 + qw / kBoundTile];
+  auto tile_needed = [&](double rb, double kb) { return rb + kb >= kSkipLog2; };
   int64_t first_tile = 0;
   if (skip) {
     __shared__ int64_t s_first[kWaves];
-    double a_rows[kWaves];
-    float rb_rows[kWaves];
+    double rb_rows[kWaves];
     int64_t last_w[kWaves];
 #pragma unroll
     for (int u = 0; u < kWaves; ++u) {
       const int64_t qu = q0 + 32 * u;
-      a_rows[u] = anchor[head * nblk + qu / kAnchorBlock];
       rb_rows[u] = rowb[head * nb32 + qu / kBoundTile];
       last_w[u] = (4 * I + u < n_key_tiles - 1) ? 4 * I + u : n_key_tiles - 1;
     }
     int64_t mine = last_tile;  // the diagonal tile of wave 0 bounds the answer
     for (int64_t J = tid; J < last_tile; J += kThreads) {
-      const double a_key = anchor[head * nblk + (J * kBN) / kAnchorBlock];
-      const float kb = keyb[head * nb32 + J];
+      const double kb = keyb[head * nb32 + J];
       bool need = false;
 #pragma unroll
       for (int u = 0; u < kWaves; ++u)
-        need = need || (J <= last_w[u] && tile_needed(a_rows[u], rb_rows[u], a_key, kb));
+        need = need || (J <= last_w[u] && tile_needed(rb_rows[u], kb));
       if (need) {
         mine = J;
         break;  // J grows with each iteration: the first hit is this thread's least
@@ -181,20 +173,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         dma16(rv, off, buf + C::K_BYTES + r * C::RSV);
       }
     }
-    if (w == 0 && lane < kBN / 4)
-      dma16(make_rsrc(colt + head * Tp + k0, kBN * 4), unsigned(16 * lane), buf + C::C_OFF);
-    if (w == 1 && lane < 2)
-      dma4(make_rsrc(anchor + head * nblk + k0 / kAnchorBlock, 8), unsigned(4 * lane),
-           buf + C::A_OFF);
-    if (w == 2 && lane < 1) dma4(make_rsrc(keyb + head * nb32 + J, 4), 0u, buf + C::KB_OFF);
+    if (w == 0 && lane < kBN / 2)
+      dma16(make_rsrc(colt + head * Tp + k0, kBN * 8), unsigned(16 * lane), buf + C::C_OFF);
+    if (w == 2 && lane < 2)
+      dma4(make_rsrc(keyb + head * nb32 + J, 8), unsigned(4 * lane), buf + C::KB_OFF);
   };
   // whether this wave's rows need tile J (copied into `buf`)
   auto wave_needs = [&](const char* buf, int64_t J) {
     if (J > wave_last) return false;
     if (!skip) return true;
-    const double a_key = *reinterpret_cast<const double*>(buf + C::A_OFF);
-    const float kb = *reinterpret_cast<const float*>(buf + C::KB_OFF);
-    return tile_needed(a_i, rb_w, a_key, kb);
+    const double kb = *reinterpret_cast<const double*>(buf + C::KB_OFF);
+    return tile_needed(rb_w, kb);
   };
 
   // per-lane LDS offsets of the operand reads
@@ -222,19 +211,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       }
     }
     // lane (g, l32), register r holds S^T[key 8(r/4) + 4g + r%4][query l32]
-    const double a_j = *reinterpret_cast<const double*>(buf + C::A_OFF);
-    const float base = float(a_i - a_j) + r_i;
     const bool diag = (J * kBN == qw);
-    const float* cb = reinterpret_cast<const float*>(buf + C::C_OFF);
+    const double* cb = reinterpret_cast<const double*>(buf + C::C_OFF);
     float cv[16];
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const float4 c4 = *reinterpret_cast<const float4*>(cb + 8 * rq + 4 * g);
-      const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+      const double2 c01 = *reinterpret_cast<const double2*>(cb + 8 * rq + 4 * g);
+      const double2 c23 = *reinterpret_cast<const double2*>(cb + 8 * rq + 4 * g + 2);
+      const double cc[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = 8 * rq + 4 * g + e;
-        float ex = base + cc[e];
+        float ex = float(r_i + cc[e]);
         if (diag && key > l32) ex = -INFINITY;  // above the diagonal (Eq. 71)
         const float c = st[4 * rq + e] * __builtin_amdgcn_exp2f(ex);  // C~' (Eq. 82)
         bsum += c;                                                 // b (Eq. 83)
@@ -289,7 +277,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   __syncthreads();
 
   // No plain global load is issued inside the loop: everything a tile needs
-  // (K, V, c and the key-tile anchor) arrives by the copies into LDS, so the
+  // (K, V, C and the key tile's bound) arrives by the copies into LDS, so the
   // waits on those copies stay exact.
   for (int64_t J = first_tile; J <= last_tile; J += 2) {
     // even tile from smem0, prefetch into smem1
@@ -350,10 +338,10 @@ hipError_t launch_dp(const void* q, const void* k, const void* v, const float* m
   const int64_t row_tiles = (T + kBM - 1) / kBM;
   hipLaunchKernelGGL(tiles_mfma_kernel<DP>, dim3(unsigned(row_tiles * H)), dim3(kThreads), 0,
                      stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), m, ws.anchor, ws.rowt, ws.colt,
+                     static_cast<const u16*>(v), m, ws.rowt, ws.colt,
                      static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
                      static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), ep.b, T,
-                     int(d), ws.Tp, ws.nblk, row_tiles, H, int(skip));
+                     int(d), ws.Tp, row_tiles, H, int(skip));
   return hipGetLastError();
 }
 

@@ -34,9 +34,10 @@
 // waits for its own copies (vmcnt) before each barrier.
 //
 // Exponents.  On a tile below the diagonal the exponent factors as
-// 2^(base_i + keyb_J) * e_j with e_j from the gate scan (one exponential per
+// 2^(R_i + keyb_J) * e_j with e_j from the gate scan (one exponential per
 // query row and tile); on a diagonal tile every entry takes its own
-// exponential under the causal mask (Eq. 71).
+// exponential 2^(R_i + C_j) under the causal mask (Eq. 71).  Each exponent is
+// summed in float64 and rounded to float32 once.
 #include "mlstm_internal.h"
 #include "tile_common.h"
 
@@ -73,11 +74,10 @@ struct WCfg {
   static constexpr int RPW = kSK / kWWaves;  // rows of a 64-key tile copied per wave
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = kSK * RSK;
-  static constexpr int GC = V_OFF + kSK * RSV;  // c_j of the K tile's 64 keys (float32)
-  static constexpr int GE = GC + 256;        // e_j (float32)
-  static constexpr int GA = GC + 512;        // float64 anchor of the 64 keys
-  static constexpr int GB = GC + 528;        // keyb of the two 32-key tiles
-  static constexpr int X_OFF = GC + 544;     // bf16(C~'^T) exchange, 2 KiB per wave
+  static constexpr int GC = V_OFF + kSK * RSV;  // C_j of the K tile's 64 keys (float64)
+  static constexpr int GE = GC + 512;        // e_j (float32)
+  static constexpr int GB = GC + 768;        // keyb of the two 32-key tiles (float64)
+  static constexpr int X_OFF = GC + 784;     // bf16(C~'^T) exchange, 2 KiB per wave
   static constexpr int BYTES = X_OFF + kWWaves * 2048;
   static_assert(2 * kSK * RSK <= GC, "the staged Q block fits in the K and V regions");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
@@ -87,12 +87,11 @@ template <int DP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
                           amdgpu_waves_per_eu(2, 2))) void tiles_pairs_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    const float* __restrict__ m_in, const double* __restrict__ anchor,
-    const float* __restrict__ rowt, const float* __restrict__ colt,
-    const float* __restrict__ colx, u16* __restrict__ h_out, const float* __restrict__ rowb,
-    const float* __restrict__ keyb, float* __restrict__ n_out, const u16* __restrict__ ogate,
-    u16* __restrict__ htilde, float* __restrict__ b_out, int T, int d, int Tp, int nblk,
-    int row_tiles, int H, int skip) {
+    const float* __restrict__ m_in, const double* __restrict__ rowt,
+    const double* __restrict__ colt, const float* __restrict__ colx, u16* __restrict__ h_out,
+    const double* __restrict__ rowb, const double* __restrict__ keyb, float* __restrict__ n_out,
+    const u16* __restrict__ ogate, u16* __restrict__ htilde, float* __restrict__ b_out, int T,
+    int d, int Tp, int row_tiles, int H, int skip) {
   using C = WCfg<DP>;
   __shared__ __attribute__((aligned(1024))) char lds[C::BYTES];
 
@@ -116,15 +115,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
   // Q^T fragments (full head dim): B operand of S^T = K Q^T, read from the
   // workgroup's Q block staged in LDS by the prologue
   bf16x8 qf[C::NS];
-  const float r_i = rowt[int64_t(head) * Tp + qi];
-  // the pair's anchor (uniform across the wave)
-  double a_i = anchor[int64_t(head) * nblk + qw / kAnchorBlock];
-  {
-    const uint64_t bits = __builtin_bit_cast(uint64_t, a_i);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(bits));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(bits >> 32));
-    a_i = __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
-  }
+  const double r_i = rowt[int64_t(head) * Tp + qi];  // R_i, qi < Tp
 
   f32x16 acc[C::NB];
 #pragma unroll
@@ -156,21 +147,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
     const int r = w + kWWaves * i;
     copy_row(v, s * kSK + r, lds_addr(lds + C::V_OFF + r * C::RSV));
   };
-  // gate terms of super-step s: one small copy each for waves 0..3
+  // gate terms of super-step s: one small copy each for waves 0..2
   auto copy_gates = [&](int s) {
     const int k0 = s * kSK;
-    if (w == 0 && lane < 16)
-      copy16(rsrc_words(colt + int64_t(head) * Tp + k0, kSK * 4), unsigned(16 * lane),
+    if (w == 0 && lane < 32)
+      copy16(rsrc_words(colt + int64_t(head) * Tp + k0, kSK * 8), unsigned(16 * lane),
              lds_addr(lds + C::GC));
     if (w == 1 && lane < 16)
       copy16(rsrc_words(colx + int64_t(head) * Tp + k0, kSK * 4), unsigned(16 * lane),
              lds_addr(lds + C::GE));
-    if (w == 2 && lane < 2)
-      copy4(rsrc_words(anchor + int64_t(head) * nblk + k0 / kAnchorBlock, 8), unsigned(4 * lane),
-            lds_addr(lds + C::GA));
-    if (w == 3 && lane < 2)
-      copy4(rsrc_words(keyb + int64_t(head) * nb32 + k0 / kBoundTile, 8), unsigned(4 * lane),
-            lds_addr(lds + C::GB));
+    if (w == 2 && lane < 1)
+      copy16(rsrc_words(keyb + int64_t(head) * nb32 + k0 / kBoundTile, 16), 0u,
+             lds_addr(lds + C::GB));
   };
 
   // ---- the workgroup's Q block (128 rows, contiguous in memory) is copied
@@ -185,32 +173,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
   // ---- decay-aware start of the key loop: the first 32-key tile some pair
   // needs (the bound of mlstm_internal.h); inside the loop each member skips
   // the products of tiles its rows do not need.
-  const float rb_w = __builtin_bit_cast(
-      float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, rowb[int64_t(head) * nb32 + qw / kBoundTile])));
-  auto tile_needed = [&](double a_row, float rb, double a_key, float kb) {
-    return float(a_row - a_key) + rb + kb >= kSkipLog2;
-  };
+  const double rb_w = rowb[int64_t(head) * nb32 + qw / kBoundTile];  // uniform across the wave
+  auto tile_needed = [&](double rb, double kb) { return rb + kb >= kSkipLog2; };
   int first_tile = 0;
   if (skip) {
     __shared__ int s_first[kWWaves];
-    double a_rows[4];
-    float rb_rows[4];
+    double rb_rows[4];
     int last_p[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int qu = q0 + 32 * u;
-      a_rows[u] = anchor[int64_t(head) * nblk + qu / kAnchorBlock];
       rb_rows[u] = rowb[int64_t(head) * nb32 + qu / kBoundTile];
       last_p[u] = (4 * It + u < n_key_tiles - 1) ? 4 * It + u : n_key_tiles - 1;
     }
     int mine = last_tile;
     for (int J = tid; J < last_tile; J += kWThreads) {
-      const double a_key = anchor[int64_t(head) * nblk + (J * kBN) / kAnchorBlock];
-      const float kb = keyb[int64_t(head) * nb32 + J];
+      const double kb = keyb[int64_t(head) * nb32 + J];
       bool need = false;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        need = need || (J <= last_p[u] && tile_needed(a_rows[u], rb_rows[u], a_key, kb));
+        need = need || (J <= last_p[u] && tile_needed(rb_rows[u], kb));
       if (need) {
         mine = J;
         break;  // J grows with each iteration: the first hit is this thread's least
@@ -266,12 +248,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
 
   for (int s = s_first_step; s <= s_last_step; ++s) {
     // ===== phase 1: K_s and its gate terms are resident; copies bring V_s =====
-    const double a_key = *reinterpret_cast<const double*>(lds + C::GA);
     // whether this member's and the partner's key tiles reach the pair's rows
     auto member_needs = [&](int hk) {
       const int J = 2 * s + hk;
-      const float kb = *reinterpret_cast<const float*>(lds + C::GB + 4 * hk);
-      const bool nd = J <= pair_last && (!skip || tile_needed(a_i, rb_w, a_key, kb));
+      const double kb = *reinterpret_cast<const double*>(lds + C::GB + 8 * hk);
+      const bool nd = J <= pair_last && (!skip || tile_needed(rb_w, kb));
       return __builtin_amdgcn_readfirstlane(int(nd)) != 0;
     };
     const bool need_own = member_needs(hh);
@@ -298,27 +279,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
         __builtin_amdgcn_sched_barrier(0);
       }
       // lane (g, l32), register r holds S^T[key 8(r/4) + 4g + r%4][query l32]
-      const float base = float(a_i - a_key) + r_i;
       const bool diag = (2 * s + hh) * kBN == qw;
-      const float* gc = reinterpret_cast<const float*>(lds + C::GC) + 32 * hh;
+      const double* gc = reinterpret_cast<const double*>(lds + C::GC) + 32 * hh;
       const float* ge = reinterpret_cast<const float*>(lds + C::GE) + 32 * hh;
       // C~' = S (.) D' in place of S (Eq. 82), b += C~' (Eq. 83)
       if (diag) {
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          const float4 c4 = *reinterpret_cast<const float4*>(gc + 8 * rq + 4 * g);
-          const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+          const double2 c01 = *reinterpret_cast<const double2*>(gc + 8 * rq + 4 * g);
+          const double2 c23 = *reinterpret_cast<const double2*>(gc + 8 * rq + 4 * g + 2);
+          const double cc[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int key = 8 * rq + 4 * g + e;
-            const float ex = key > l32 ? -INFINITY : base + cc[e];  // causal mask (Eq. 71)
+            // causal mask (Eq. 71)
+            const float ex = key > l32 ? -INFINITY : float(r_i + cc[e]);
             st[4 * rq + e] *= __builtin_amdgcn_exp2f(ex);
             bsum += st[4 * rq + e];
           }
         }
       } else {
-        const float kb = *reinterpret_cast<const float*>(lds + C::GB + 4 * hh);
-        const float ei = __builtin_amdgcn_exp2f(base + kb);
+        const double kb = *reinterpret_cast<const double*>(lds + C::GB + 8 * hh);
+        const float ei = __builtin_amdgcn_exp2f(float(r_i + kb));
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const float4 e4 = *reinterpret_cast<const float4*>(ge + 8 * rq + 4 * g);
@@ -485,10 +467,10 @@ hipError_t launch_w(const void* q, const void* k, const void* v, const float* m,
   const int64_t row_tiles = (T + kBM - 1) / kBM;
   hipLaunchKernelGGL(tiles_pairs_kernel<DP>, dim3(unsigned(row_tiles * H)), dim3(kWThreads), 0,
                      stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), m, ws.anchor, ws.rowt, ws.colt, ws.colx,
+                     static_cast<const u16*>(v), m, ws.rowt, ws.colt, ws.colx,
                      static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
                      static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), ep.b, T,
-                     int(d), int(ws.Tp), int(ws.nblk), int(row_tiles), int(H), int(skip));
+                     int(d), int(ws.Tp), int(row_tiles), int(H), int(skip));
   return hipGetLastError();
 }
 

@@ -27,10 +27,10 @@ __device__ inline void store_elem(__hip_bfloat16* p, float x) { *p = __float2bfl
 template <typename Tin, int MAXD>
 __global__ __launch_bounds__(256) void tiles_vector_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-    const float* __restrict__ m_in, const double* __restrict__ anchor,
-    const float* __restrict__ rowt, const float* __restrict__ colt, Tin* __restrict__ h_out,
-    float* __restrict__ n_out, const Tin* __restrict__ ogate, Tin* __restrict__ htilde,
-    float* __restrict__ b_out, int64_t T, int d, int64_t Tp, int64_t nblk, int64_t row_tiles) {
+    const float* __restrict__ m_in, const double* __restrict__ rowt,
+    const double* __restrict__ colt, Tin* __restrict__ h_out, float* __restrict__ n_out,
+    const Tin* __restrict__ ogate, Tin* __restrict__ htilde, float* __restrict__ b_out,
+    int64_t T, int d, int64_t Tp, int64_t row_tiles) {
   constexpr bool kShared = MAXD > 512;  // K and V tiles share one buffer
   __shared__ float Qs[kVT][MAXD + 1];
   __shared__ float Ks[kVT][MAXD + 1];
@@ -50,8 +50,7 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
     const int r = idx / d, c = idx % d;
     Qs[r][c] = (q0 + r < T) ? load_elem(q + hoff + (q0 + r) * d + c) : 0.0f;
   }
-  const float r_i = rowt[head * Tp + qi];  // qi < Tp: Tp is T rounded up to 128
-  const double a_i = anchor[head * nblk + q0 / kAnchorBlock];
+  const double r_i = rowt[head * Tp + qi];  // R_i; qi < Tp: Tp is T rounded up to 128
 
   float acc[MAXD / kVT];
 #pragma unroll
@@ -71,9 +70,8 @@ __global__ __launch_bounds__(256) void tiles_vector_kernel(
     const int64_t kj = k0 + cl;
     float s = 0.0f;
     for (int c = 0; c < d; ++c) s = fmaf(Qs[rl][c], Ks[cl][c], s);
-    // log2(D'_ij / sqrt(d)) = (A_{i/64} - A_{j/64}) + r_i + c_j   (Eqs. 79, 81, 82)
-    const float delta = float(a_i - anchor[head * nblk + k0 / kAnchorBlock]);
-    const float ex = delta + r_i + colt[head * Tp + kj];
+    // log2(D'_ij / sqrt(d)) = R_i + C_j, rounded once   (Eqs. 79, 81, 82)
+    const float ex = float(r_i + colt[head * Tp + kj]);
     const bool valid = (kj <= qi) && (kj < T) && (qi < T);
     const float cv = valid ? s * exp2f(ex) : 0.0f;  // C~'_ij (Eq. 82)
     bsum += cv;                                     // b_i (Eq. 83), float32
@@ -125,9 +123,9 @@ void launch_v(const void* q, const void* k, const void* v, const float* m, const
   const int64_t row_tiles = (T + kVT - 1) / kVT;
   hipLaunchKernelGGL((tiles_vector_kernel<Tin, MAXD>), dim3(unsigned(row_tiles * H)), dim3(256),
                      0, stream, static_cast<const Tin*>(q), static_cast<const Tin*>(k),
-                     static_cast<const Tin*>(v), m, ws.anchor, ws.rowt, ws.colt,
+                     static_cast<const Tin*>(v), m, ws.rowt, ws.colt,
                      static_cast<Tin*>(h_out), n_out, static_cast<const Tin*>(ep.ogate),
-                     static_cast<Tin*>(ep.htilde), ep.b, T, int(d), ws.Tp, ws.nblk, row_tiles);
+                     static_cast<Tin*>(ep.htilde), ep.b, T, int(d), ws.Tp, row_tiles);
 }
 
 }  // namespace

@@ -61,11 +61,10 @@ struct XCfg {
   static constexpr int RPW = kBN / kXWaves;   // rows of a 32-key tile copied per wave
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = kBN * RSK;
-  static constexpr int GC = V_OFF + kBN * RSV;  // c_j of the K tile's 32 keys (float32)
-  static constexpr int GE = GC + 128;           // e_j (float32)
-  static constexpr int GA = GC + 256;           // float64 anchor of the tile
-  static constexpr int GB = GC + 264;           // keyb of the tile
-  static constexpr int X_OFF = GC + 272;        // partial sums, 12 KiB per query block
+  static constexpr int GC = V_OFF + kBN * RSV;  // C_j of the K tile's 32 keys (float64)
+  static constexpr int GE = GC + 256;           // e_j (float32)
+  static constexpr int GB = GC + 384;           // keyb of the tile (float64)
+  static constexpr int X_OFF = GC + 400;        // partial sums, 12 KiB per query block
   static constexpr int P_OFF = X_OFF + 2 * 12 * 1024;  // bf16 C~'^T, 2 KiB per query block
   static constexpr int BYTES = P_OFF + 2 * 2048;
   static_assert(kXM * RSK <= GC, "the staged Q and output blocks fit in the K and V regions");
@@ -77,12 +76,11 @@ template <int DP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kXThreads, kXThreads),
                           amdgpu_waves_per_eu(2, 2))) void tiles_wide_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    const float* __restrict__ m_in, const double* __restrict__ anchor,
-    const float* __restrict__ rowt, const float* __restrict__ colt,
-    const float* __restrict__ colx, u16* __restrict__ h_out, const float* __restrict__ rowb,
-    const float* __restrict__ keyb, float* __restrict__ n_out, const u16* __restrict__ ogate,
-    u16* __restrict__ htilde, float* __restrict__ b_out, int T, int d, int Tp, int nblk,
-    int row_tiles, int H, int skip) {
+    const float* __restrict__ m_in, const double* __restrict__ rowt,
+    const double* __restrict__ colt, const float* __restrict__ colx, u16* __restrict__ h_out,
+    const double* __restrict__ rowb, const double* __restrict__ keyb, float* __restrict__ n_out,
+    const u16* __restrict__ ogate, u16* __restrict__ htilde, float* __restrict__ b_out, int T,
+    int d, int Tp, int row_tiles, int H, int skip) {
   using C = XCfg<DP>;
   __shared__ __attribute__((aligned(1024))) char lds[C::BYTES];
 
@@ -104,14 +102,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kXThreads, kXThreads),
   const int dch = d / 8;        // real 16-byte chunks per row
 
   bf16x8 qf[C::NS];  // Q^T over this member's quarter: B operand of the partial S^T
-  const float r_i = rowt[int64_t(head) * Tp + qi];
-  double a_i = anchor[int64_t(head) * nblk + qw / kAnchorBlock];  // uniform across the wave
-  {
-    const uint64_t bits = __builtin_bit_cast(uint64_t, a_i);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(bits));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(bits >> 32));
-    a_i = __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
-  }
+  const double r_i = rowt[int64_t(head) * Tp + qi];  // R_i
 
   f32x16 acc[C::NB];
 #pragma unroll
@@ -146,17 +137,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kXThreads, kXThreads),
   };
   auto copy_gates = [&](int J) {
     const int k0 = J * kBN;
-    if (w == 0 && lane < 8)
-      copy16(rsrc_words(colt + int64_t(head) * Tp + k0, kBN * 4), unsigned(16 * lane),
+    if (w == 0 && lane < 16)
+      copy16(rsrc_words(colt + int64_t(head) * Tp + k0, kBN * 8), unsigned(16 * lane),
              lds_addr(lds + C::GC));
     if (w == 1 && lane < 8)
       copy16(rsrc_words(colx + int64_t(head) * Tp + k0, kBN * 4), unsigned(16 * lane),
              lds_addr(lds + C::GE));
     if (w == 2 && lane < 2)
-      copy4(rsrc_words(anchor + int64_t(head) * nblk + k0 / kAnchorBlock, 8), unsigned(4 * lane),
-            lds_addr(lds + C::GA));
-    if (w == 3 && lane < 1)
-      copy4(rsrc_words(keyb + int64_t(head) * nb32 + J, 4), unsigned(4 * lane),
+      copy4(rsrc_words(keyb + int64_t(head) * nb32 + J, 8), unsigned(4 * lane),
             lds_addr(lds + C::GB));
   };
   constexpr int kUnits = C::RPW * C::NCP;
@@ -173,33 +161,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kXThreads, kXThreads),
   // ---- decay-aware start of the key loop: the first 32-key tile either
   // block needs (the bound of mlstm_internal.h); inside the loop each block
   // skips the products of tiles its rows do not need.
-  const float rb_w = __builtin_bit_cast(
-      float, __builtin_amdgcn_readfirstlane(
-                 __builtin_bit_cast(int, rowb[int64_t(head) * nb32 + qw / kBoundTile])));
-  auto tile_needed = [&](double a_row, float rb, double a_key, float kb) {
-    return float(a_row - a_key) + rb + kb >= kSkipLog2;
-  };
+  const double rb_w = rowb[int64_t(head) * nb32 + qw / kBoundTile];  // uniform across the wave
+  auto tile_needed = [&](double rb, double kb) { return rb + kb >= kSkipLog2; };
   int first_tile = 0;
   if (skip) {
     __shared__ int s_first[kXWaves];
-    double a_rows[2];
-    float rb_rows[2];
+    double rb_rows[2];
     int last_b[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int qu = q0 + 32 * u;
-      a_rows[u] = anchor[int64_t(head) * nblk + qu / kAnchorBlock];
       rb_rows[u] = rowb[int64_t(head) * nb32 + qu / kBoundTile];
       last_b[u] = (2 * I + u < n_key_tiles - 1) ? 2 * I + u : n_key_tiles - 1;
     }
     int mine = last_tile;
     for (int J = tid; J < last_tile; J += kXThreads) {
-      const double a_key = anchor[int64_t(head) * nblk + (J * kBN) / kAnchorBlock];
-      const float kb = keyb[int64_t(head) * nb32 + J];
+      const double kb = keyb[int64_t(head) * nb32 + J];
       bool need = false;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        need = need || (J <= last_b[u] && tile_needed(a_rows[u], rb_rows[u], a_key, kb));
+        need = need || (J <= last_b[u] && tile_needed(rb_rows[u], kb));
       if (need) {
         mine = J;
         break;  // J grows with each iteration: the first hit is this thread's least
@@ -256,10 +237,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kXThreads, kXThreads),
 
   for (int J = first_tile; J <= last_tile; ++J) {
     // ===== phase 1: K_J and its gate terms are resident; copies bring V_J =====
-    const double a_key = *reinterpret_cast<const double*>(lds + C::GA);
-    const float kb = *reinterpret_cast<const float*>(lds + C::GB);
+    const double kb = *reinterpret_cast<const double*>(lds + C::GB);
     const bool need = __builtin_amdgcn_readfirstlane(
-                          int(J <= block_last && (!skip || tile_needed(a_i, rb_w, a_key, kb)))) != 0;
+                          int(J <= block_last && (!skip || tile_needed(rb_w, kb)))) != 0;
     f32x16 st = f32x16{};
     if (need) {
       bf16x8 kf[kXPf + 1];
@@ -308,19 +288,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kXThreads, kXThreads),
       tot += hh == 2 ? own : hh < 2 ? pr[1] : pr[2];
       tot += hh == 3 ? own : pr[2];
       float p[4] = {tot.x, tot.y, tot.z, tot.w};
-      const float base = float(a_i - a_key) + r_i;
       if (J * kBN == qw) {  // diagonal tile: causal mask (Eq. 71)
-        const float4 c4 = *reinterpret_cast<const float4*>(lds + C::GC + 4 * (8 * hh + 4 * g));
-        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+        const double* gc = reinterpret_cast<const double*>(lds + C::GC) + 8 * hh + 4 * g;
+        const double2 c01 = *reinterpret_cast<const double2*>(gc);
+        const double2 c23 = *reinterpret_cast<const double2*>(gc + 2);
+        const double cc[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = 8 * hh + 4 * g + e;
-          const float ex = key > l32 ? -INFINITY : base + cc[e];
+          const float ex = key > l32 ? -INFINITY : float(r_i + cc[e]);
           p[e] *= __builtin_amdgcn_exp2f(ex);
           bsum += p[e];
         }
       } else {
-        const float ei = __builtin_amdgcn_exp2f(base + kb);
+        const float ei = __builtin_amdgcn_exp2f(float(r_i + kb));
         const float4 e4 = *reinterpret_cast<const float4*>(lds + C::GE + 4 * (8 * hh + 4 * g));
         const float ee[4] = {e4.x, e4.y, e4.z, e4.w};
 #pragma unroll
@@ -471,10 +452,10 @@ hipError_t launch_x(const void* q, const void* k, const void* v, const float* m,
   const int64_t row_tiles = (T + kXM - 1) / kXM;
   hipLaunchKernelGGL(tiles_wide_kernel<DP>, dim3(unsigned(row_tiles * H)), dim3(kXThreads), 0,
                      stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), m, ws.anchor, ws.rowt, ws.colt, ws.colx,
+                     static_cast<const u16*>(v), m, ws.rowt, ws.colt, ws.colx,
                      static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
                      static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), ep.b, T,
-                     int(d), int(ws.Tp), int(ws.nblk), int(row_tiles), int(H), int(skip));
+                     int(d), int(ws.Tp), int(row_tiles), int(H), int(skip));
   return hipGetLastError();
 }
 

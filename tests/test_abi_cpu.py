@@ -46,15 +46,15 @@ def test_strerror_and_workspace_size():
         assert msg and msg != "unknown status"
     assert mlstm.strerror(-99) == "unknown status"
     lib = mlstm.load_library()
-    # float64 anchors (one per 64 positions), three float32 terms per position,
-    # two float32 tile bounds per 32 positions and two float64 scan-chunk
-    # terms per 2048 positions, T padded to 128, each region 256-byte aligned
-    assert lib.mlstm_workspace_bytes(1, 1, 64) == 256 + 3 * 512 + 2 * 256 + 256
-    assert lib.mlstm_workspace_bytes(8, 4, 2048) == (32 * 32 * 8 + 3 * 32 * 2048 * 4
-                                                     + 2 * 32 * 64 * 4 + 512)
+    # two float64 terms and one float32 term per position, two float64 tile
+    # bounds per 32 positions and two float64 scan-chunk terms per 2048
+    # positions, T padded to 128, each region 256-byte aligned
+    assert lib.mlstm_workspace_bytes(1, 1, 64) == 2 * 1024 + 512 + 2 * 256 + 256
+    assert lib.mlstm_workspace_bytes(8, 4, 2048) == (2 * 32 * 2048 * 8 + 32 * 2048 * 4
+                                                     + 2 * 32 * 64 * 8 + 512)
     # 8 heads of 16384: 8 scan chunks each
-    assert lib.mlstm_workspace_bytes(1, 8, 16384) == (8 * 256 * 8 + 3 * 8 * 16384 * 4
-                                                      + 2 * 8 * 512 * 4 + 8 * 8 * 16)
+    assert lib.mlstm_workspace_bytes(1, 8, 16384) == (2 * 8 * 16384 * 8 + 8 * 16384 * 4
+                                                      + 2 * 8 * 512 * 8 + 8 * 8 * 16)
     assert lib.mlstm_workspace_bytes(0, 4, 2048) == 0
     assert lib.mlstm_workspace_bytes(1, 1, 0) == 0
 
