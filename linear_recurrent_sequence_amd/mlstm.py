@@ -89,23 +89,53 @@ def _forget_code(forget):
     return FORGET_ACTIVATIONS[forget]
 
 
+def _require(name, t, shape, dtype, device=None):
+    """Raise unless ``t`` is a contiguous tensor of exactly ``shape`` and
+    ``dtype`` (and, if ``device`` is given, on that GPU).  Every tensor handed
+    to the C ABI goes through here first: a host pointer, a wrong element type
+    or a short buffer would otherwise reach the kernels."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None:
+        _require_device(name, t, device)
+
+
+def _require_device(name, t, device):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (there is no CPU path), got {t.device}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+
+
+def _require_workspace(ws, device):
+    """A workspace: a contiguous 1-D uint8 GPU tensor on ``device`` (its size
+    is checked by the library against mlstm_workspace_bytes)."""
+    if not isinstance(ws, torch.Tensor) or ws.dim() != 1:
+        raise ValueError("workspace must be a 1-D tensor (see alloc_workspace)")
+    _require("workspace", ws, ws.shape, torch.uint8, device)
+
+
 def _check_inputs(q, k, v, igate, fgate):
+    if not isinstance(q, torch.Tensor):
+        raise TypeError(f"q must be a torch.Tensor, got {type(q).__name__}")
     if q.dim() != 4:
         raise ValueError(f"q must be [B, NH, T, d], got shape {tuple(q.shape)}")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"q/k/v must be float32 or bfloat16, got {q.dtype}")
     B, NH, T, d = q.shape
-    for name, t in (("k", k), ("v", v)):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must match q in shape and dtype")
-    for name, t in (("igate", igate), ("fgate", fgate)):
-        if tuple(t.shape) != (B, NH, T) or t.dtype != torch.float32:
-            raise ValueError(f"{name} must be float32 [B, NH, T] = {(B, NH, T)}")
-    for name, t in (("q", q), ("k", k), ("v", v), ("igate", igate), ("fgate", fgate)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-        if t.device != q.device:
-            raise ValueError("all tensors must be on the same device")
+    named = (("q", q), ("k", k), ("v", v), ("igate", igate), ("fgate", fgate))
+    for name, t in named[:3]:
+        _require(name, t, q.shape, q.dtype)
+    for name, t in named[3:]:
+        _require(name, t, (B, NH, T), torch.float32)
+    for name, t in named:  # devices last: a malformed tensor is named first
+        _require_device(name, t, q.device)
     return B, NH, T, d
 
 
@@ -126,6 +156,9 @@ def parallel_fwd(q, k, v, igate, fgate, out=None):
         n = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
     else:
         h, m, n = out
+        _require("h", h, q.shape, q.dtype, q.device)
+        _require("m", m, (B, NH, T), torch.float32, q.device)
+        _require("n", n, (B, NH, T), torch.float32, q.device)
     with torch.cuda.device(q.device):
         st = lib.mlstm_parallel_fwd_stream(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
@@ -144,10 +177,7 @@ def parallel_fwd_gated(q, k, v, igate, fgate, ogate, htilde=False):
     """
     lib = load_library()
     B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
-    if ogate.shape != q.shape or ogate.dtype != q.dtype or ogate.device != q.device:
-        raise ValueError("ogate must match q in shape, dtype and device")
-    if not ogate.is_contiguous():
-        raise ValueError("ogate must be contiguous")
+    _require("ogate", ogate, q.shape, q.dtype, q.device)
     h = torch.empty_like(q)
     ht = torch.empty_like(q) if htilde else None
     m = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
@@ -177,14 +207,16 @@ def alloc_workspace(B, NH, T, device):
 def gate_scan(igate, fgate, d, workspace, m=None, forget="sigmoid"):
     """Stage 1: m (Eq. 80) and the exponent terms, written into ``workspace``."""
     lib = load_library()
-    if igate.dim() != 3 or igate.shape != fgate.shape:
-        raise ValueError("igate and fgate must both be [B, NH, T]")
+    if not isinstance(igate, torch.Tensor) or igate.dim() != 3:
+        raise ValueError("igate must be a [B, NH, T] tensor")
     B, NH, T = igate.shape
-    for t in (igate, fgate):
-        if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32):
-            raise ValueError("gates must be contiguous float32 GPU tensors")
+    _require("igate", igate, (B, NH, T), torch.float32, igate.device)
+    _require("fgate", fgate, (B, NH, T), torch.float32, igate.device)
+    _require_workspace(workspace, igate.device)
     if m is None:
         m = torch.empty((B, NH, T), dtype=torch.float32, device=igate.device)
+    else:
+        _require("m", m, (B, NH, T), torch.float32, igate.device)
     with torch.cuda.device(igate.device):
         st = lib.mlstm_gate_scan(igate.data_ptr(), fgate.data_ptr(), m.data_ptr(),
                                  workspace.data_ptr(), workspace.numel(), B, NH, T, d,
@@ -198,11 +230,16 @@ def causal_tiles(q, k, v, m, workspace, kernel="auto", out=None):
     """Stage 2: h~ and n from q, k, v and the stage-1 results -> (h, n)."""
     lib = load_library()
     B, NH, T, d = _check_inputs(q, k, v, m, m)
+    _require_workspace(workspace, q.device)
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {tuple(KERNELS)}, got {kernel!r}")
     if out is None:
         h = torch.empty_like(q)
         n = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
     else:
         h, n = out
+        _require("h", h, q.shape, q.dtype, q.device)
+        _require("n", n, (B, NH, T), torch.float32, q.device)
     with torch.cuda.device(q.device):
         st = lib.mlstm_causal_tiles(q.data_ptr(), k.data_ptr(), v.data_ptr(), m.data_ptr(),
                                     workspace.data_ptr(), workspace.numel(), h.data_ptr(),
@@ -239,23 +276,23 @@ def recurrent_step(q, k, v, igate, fgate, state, out_state=None, den=False, forg
     default C is updated in place and new n, m are allocated.
     """
     lib = load_library()
-    if q.dim() != 3:
-        raise ValueError(f"q must be [B, NH, d], got {tuple(q.shape)}")
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a [B, NH, d] tensor")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"q/k/v must be float32 or bfloat16, got {q.dtype}")
     B, NH, d = q.shape
     C, n, m = state
-    for name, t in (("k", k), ("v", v)):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must match q in shape and dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(name, t, q.shape, q.dtype, q.device)
     for name, t, shp in (("igate", igate, (B, NH)), ("fgate", fgate, (B, NH)),
                          ("C", C, (B, NH, d, d)), ("n", n, (B, NH, d)), ("m", m, (B, NH))):
-        if tuple(t.shape) != shp or t.dtype != torch.float32:
-            raise ValueError(f"{name} must be float32 {shp}")
-    for t in (q, k, v, igate, fgate, C, n, m):
-        if not (t.is_cuda and t.is_contiguous() and t.device == q.device):
-            raise ValueError("all tensors must be contiguous on the same GPU")
+        _require(name, t, shp, torch.float32, q.device)
     if out_state is None:
         out_state = (C, torch.empty_like(n), torch.empty_like(m))
     Co, no, mo = out_state
+    for name, t, shp in (("C_out", Co, (B, NH, d, d)), ("n_out", no, (B, NH, d)),
+                         ("m_out", mo, (B, NH))):
+        _require(name, t, shp, torch.float32, q.device)
     h = torch.empty_like(q)
     dn = torch.empty((B, NH), dtype=torch.float32, device=q.device) if den else None
     with torch.cuda.device(q.device):
@@ -290,11 +327,9 @@ def parallel_bwd(q, k, v, igate, fgate, h, m, n, b, dh, forget="sigmoid"):
     lib = load_library()
     B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
     for name, t in (("h", h), ("dh", dh)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must match q in shape and dtype, contiguous on the GPU")
+        _require(name, t, q.shape, q.dtype, q.device)
     for name, t in (("m", m), ("n", n), ("b", b)):
-        if tuple(t.shape) != (B, NH, T) or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous float32 [B, NH, T]")
+        _require(name, t, (B, NH, T), torch.float32, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dig, dfg = torch.empty_like(igate), torch.empty_like(fgate)
     with torch.cuda.device(q.device):

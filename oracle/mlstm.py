@@ -139,7 +139,15 @@ def _rows_one_head(q, k, v, ig, fg, rows, dtype, forget="sigmoid"):
     n = np.maximum(np.abs(b), np.exp(-m))  # Eq. 84
     C = Ct / n[:, None]  # Eq. 85
     h = C @ v[:ncol].astype(dtype)  # Eq. 86
-    return h, m, n, b, np.abs(Ct).sum(axis=1)
+    # diagnostics, not part of the method: b_i is a sum over j and c of the
+    # products D'_ij q_ic k_jc / sqrt(d); rho_i sums their magnitudes.  Each
+    # numerator n_i h~_ic = sum_j C~'_ij v_jc is a sum over j and c' of
+    # D'_ij q_ic' k_jc' v_jc / sqrt(d); rho_num_i is the largest over c of the
+    # sums of their magnitudes.
+    Sabs = (np.abs(q[rows]).astype(dtype) @ np.abs(k[:ncol]).astype(dtype).T) / dtype(math.sqrt(d))
+    rho = (Sabs * Dp).sum(axis=1)
+    rho_num = ((Sabs * Dp) @ np.abs(v[:ncol]).astype(dtype)).max(axis=1)
+    return h, m, n, b, rho, rho_num
 
 
 def forward_stabilized(q, k, v, igate, fgate, block_rows=256, dtype=np.float64,
@@ -149,8 +157,14 @@ def forward_stabilized(q, k, v, igate, fgate, block_rows=256, dtype=np.float64,
     Rows are processed in blocks of ``block_rows`` only to bound memory; each
     row's arithmetic is independent of every other row's.
     Returns (h [B,NH,T,d], m [B,NH,T], n [B,NH,T]); with ``return_diag`` also
-    (b, rho) where b is the signed row sum (Eq. 83) and rho_i = sum_j |C~'_ij|,
-    so that rho / n is the cancellation factor of row i.
+    (b, rho) where b is the signed row sum (Eq. 83) and
+    rho_i = sum_j D'_ij sum_c |q_ic k_jc| / sqrt(d), the sum of the magnitudes
+    of all the products whose signed sum is b_i, so that rho / n is the
+    condition number of n_i: a relative error eps in every product moves n_i
+    by at most eps * rho_i / n_i relative to n_i.  Last, rho_num
+    [B,NH,T]: max over c of sum_j D'_ij (sum_c' |q_ic' k_jc'|) |v_jc| / sqrt(d),
+    the same for the numerators n_i h~_ic (its ratio to max_c |n_i h~_ic| is
+    the condition number of the row's numerator).
     """
     q = np.asarray(q)
     B, NH, T, d = q.shape
@@ -159,6 +173,7 @@ def forward_stabilized(q, k, v, igate, fgate, block_rows=256, dtype=np.float64,
     n = np.empty((B, NH, T), dtype=dtype)
     bsum = np.empty((B, NH, T), dtype=dtype)
     rho = np.empty((B, NH, T), dtype=dtype)
+    rho_num = np.empty((B, NH, T), dtype=dtype)
     for bi in range(B):
         for hi in range(NH):
             qh, kh, vh = (np.asarray(a[bi, hi], dtype=np.float64) for a in (q, k, v))
@@ -166,14 +181,15 @@ def forward_stabilized(q, k, v, igate, fgate, block_rows=256, dtype=np.float64,
             fg = np.asarray(fgate[bi, hi], dtype=np.float64)
             for r0 in range(0, T, block_rows):
                 rows = np.arange(r0, min(T, r0 + block_rows))
-                hh, mm, nn, bb, rr = _rows_one_head(qh, kh, vh, ig, fg, rows, dtype, forget)
+                hh, mm, nn, bb, rr, rn = _rows_one_head(qh, kh, vh, ig, fg, rows, dtype, forget)
                 h[bi, hi, rows] = hh
                 m[bi, hi, rows] = mm
                 n[bi, hi, rows] = nn
                 bsum[bi, hi, rows] = bb
                 rho[bi, hi, rows] = rr
+                rho_num[bi, hi, rows] = rn
     if return_diag:
-        return h, m, n, bsum, rho
+        return h, m, n, bsum, rho, rho_num
     return h, m, n
 
 
@@ -181,7 +197,8 @@ def forward_rows(q, k, v, igate, fgate, bi, hi, rows, dtype=np.float64, forget="
     """Eqs. 79-86 for selected rows ``rows`` of head (bi, hi) only.
 
     Costs O(len(rows) * max(rows) * d): used to check single outputs of very
-    long sequences one by one.  Returns (h [R, d], m [R], n [R], b [R], rho [R]).
+    long sequences one by one.  Returns (h [R, d], m [R], n [R], b [R], rho [R],
+    rho_num [R]) (the diagnostics of ``forward_stabilized``).
     """
     qh, kh, vh = (np.asarray(a[bi, hi], dtype=np.float64) for a in (q, k, v))
     ig = np.asarray(igate[bi, hi], dtype=np.float64)

@@ -125,7 +125,7 @@ def test_exact_rational_example_rows(ex):
     q, k, v, ig, fg = _example_inputs(ex)
     H, maxD, N = _exact(ex)
     rows = [4, 0, 2]
-    h, m, n, _, _ = oracle.forward_rows(q, k, v, ig, fg, 0, 0, rows)
+    h, m, n = oracle.forward_rows(q, k, v, ig, fg, 0, 0, rows)[:3]
     for t, i in enumerate(rows):
         assert np.allclose(h[t], [float(x) for x in H[i]], rtol=1e-12, atol=1e-12)
         assert abs(m[t] - math.log(float(maxD[i]))) < 1e-12
@@ -209,12 +209,25 @@ def test_stabilizer_properties():
     x = W.make(dict(B=2, NH=2, T=50, d=8, dtype="fp32", igate=("uniform", -20, 20),
                     fgate=("normal", 0.0, 4.0), fgate_floor=(0.05, -30.0)), seed=3)
     args = (x["q"], x["k"], x["v"], x["igate"], x["fgate"])
-    h, m, n, b, rho = oracle.forward_stabilized(*args, return_diag=True)
+    h, m, n, b, rho, rho_num = oracle.forward_stabilized(*args, return_diag=True)
     # P9: n >= exp(-m), n >= |b|, and n equals one of them (Eq. 84)
     floor = np.exp(-m)
     assert np.all(n >= floor) and np.all(n >= np.abs(b))
     assert np.all((n == floor) | (n == np.abs(b)))
     assert np.all(rho >= np.abs(b) * (1 - 1e-12))
+    # rho sums the magnitudes of the products behind b: it bounds sum_j |C~'_ij|
+    # too, and with nonnegative q and k nothing cancels, so rho equals b
+    Dt0 = oracle.log_gate_matrix(x["fgate"][0, 0], x["igate"][0, 0])
+    Ct0 = (x["q"][0, 0].astype(np.float64) @ x["k"][0, 0].astype(np.float64).T
+           / math.sqrt(8) * np.exp(Dt0 - m[0, 0][:, None]))
+    assert np.all(rho[0, 0] >= np.abs(Ct0).sum(axis=1) * (1 - 1e-12))
+    hp, _, np_, bp, rhop, rnp = oracle.forward_stabilized(
+        np.abs(x["q"]), np.abs(x["k"]), np.abs(x["v"]), x["igate"], x["fgate"], return_diag=True)
+    assert np.allclose(rhop, bp, rtol=1e-13, atol=0)
+    # the numerators' magnitude sums bound the numerators, with equality when
+    # nothing cancels
+    assert np.all(rho_num >= np.abs(h * n[..., None]).max(axis=-1) * (1 - 1e-12))
+    assert np.allclose(rnp, (hp * np_[..., None]).max(axis=-1), rtol=1e-12, atol=0)
     for bi in range(2):
         for hi in range(2):
             fg, ig = x["fgate"][bi, hi], x["igate"][bi, hi]
@@ -250,9 +263,9 @@ def test_input_gate_shift():
                     fgate=("normal", 3, 1)), seed=7)
     args = (x["q"], x["k"], x["v"])
     c = 5.25
-    h0, m0, n0, b0, _ = oracle.forward_stabilized(*args, x["igate"], x["fgate"], return_diag=True)
+    h0, m0, n0, b0 = oracle.forward_stabilized(*args, x["igate"], x["fgate"], return_diag=True)[:4]
     ig1 = x["igate"].astype(np.float64) + c
-    h1, m1, n1, b1, _ = oracle.forward_stabilized(*args, ig1, x["fgate"], return_diag=True)
+    h1, m1, n1, b1 = oracle.forward_stabilized(*args, ig1, x["fgate"], return_diag=True)[:4]
     assert np.allclose(m1, m0 + c, rtol=0, atol=1e-12)
     assert np.allclose(b1, b0, rtol=1e-11, atol=1e-14)
     ok = (np.abs(b0) >= np.exp(-m0)) & (np.abs(b1) >= np.exp(-m1))
@@ -335,7 +348,7 @@ def test_row_blocking_and_rows_api_consistent():
     h2, m2, n2 = oracle.forward_stabilized(*args, block_rows=17)
     assert _rel(h2, h1) < 1e-14 and _rel(m2, m1) < 1e-14 and _rel(n2, n1) < 1e-14
     rows = [0, 64, 129, 7]
-    h3, m3, n3, _, _ = oracle.forward_rows(*args, 0, 1, rows)
+    h3, m3, n3 = oracle.forward_rows(*args, 0, 1, rows)[:3]
     assert _rel(h3, h1[0, 1, rows]) < 1e-14
     assert _rel(m3, m1[0, 1, rows]) < 1e-14 and _rel(n3, n1[0, 1, rows]) < 1e-14
 
@@ -402,7 +415,8 @@ def _mutant_rows(kind):
         floor = np.exp(m) if kind == "floor_sign" else np.exp(-m)
         n = np.maximum(np.abs(b), floor)
         h = (Ct / n[:, None]) @ v[:ncol]
-        return h, m, n, b, np.abs(Ct).sum(axis=1)
+        # the diagnostics are not under test here
+        return h, m, n, b, np.abs(Ct).sum(axis=1), np.abs(Ct).sum(axis=1)
     return rows
 
 
@@ -528,7 +542,7 @@ def test_backward_matches_finite_differences(seed, ig_scale, fg_mu):
     fg = fg_mu + 2.0 * rng.standard_normal((B, NH, T))
     dh = rng.standard_normal((B, NH, T, d))
     # rows on both sides of the floor exp(-m) (Eq. 84)
-    _, m, n, b, _ = om.forward_stabilized(q, k, v, ig, fg, return_diag=True)
+    _, m, n, b = om.forward_stabilized(q, k, v, ig, fg, return_diag=True)[:4]
     dq, dk, dv, di, df = om.backward_stabilized(q, k, v, ig, fg, dh)
     L = lambda **kw: _loss(kw.get("q", q), kw.get("k", k), kw.get("v", v), kw.get("ig", ig),
                            kw.get("fg", fg), dh)
@@ -546,7 +560,7 @@ def test_backward_floor_rows_and_sign_of_b():
     q, k, v = (rng.standard_normal((B, NH, T, d)) for _ in range(3))
     ig = 2.0 * rng.standard_normal((B, NH, T))
     fg = 1.0 + rng.standard_normal((B, NH, T))
-    _, m, n, b, _ = om.forward_stabilized(q, k, v, ig, fg, return_diag=True)
+    _, m, n, b = om.forward_stabilized(q, k, v, ig, fg, return_diag=True)[:4]
     assert (b < -np.exp(-m)).any() and (np.abs(b) < np.exp(-m)).any()
     dh = rng.standard_normal((B, NH, T, d))
     _, _, _, di, _ = om.backward_stabilized(q, k, v, ig, fg, dh)

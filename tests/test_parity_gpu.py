@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from linear_recurrent_sequence_amd import workloads as W
-from parity import check, head_normwise, m_error
+from parity import K_H, K_NUM, b_over_bar, check, conditions, head_normwise, m_error, row_relative
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -45,9 +45,36 @@ def run_gpu(x, kernel="auto"):
     return _host(h), _host(m), _host(n)
 
 
-def oracle_full(x):
+def oracle_full(x, forget="sigmoid"):
+    """(h, m, n, b, rho, rho_num) of the oracle on every row; rho and rho_num
+    give each row's condition numbers (tests/parity.py)."""
     return oracle.forward_stabilized(x["q"], x["k"], x["v"], x["igate"], x["fgate"],
-                                     return_diag=True)
+                                     return_diag=True, forget=forget)
+
+
+def check_full(h, m, n, x, dtype, tol_h=None, forget="sigmoid", h_ref=None):
+    """The readings of tests/parity.py on every row against the oracle
+    (h_ref replaces the oracle's h~, e.g. by its output-gated value)."""
+    hr, mr, nr, _, rho, rho_num = oracle_full(x, forget)
+    kap, kapn = conditions(nr, hr, rho, rho_num)
+    out = check(h, m, n, hr if h_ref is None else h_ref, mr, nr, kap, kapn,
+                TOL_H[dtype] if tol_h is None else tol_h, K_H[dtype], K_NUM[dtype])
+    print(out)
+    return out
+
+
+def m_every_position(x, forget="sigmoid"):
+    """m_i = max_j D~_ij (Eq. 80) at every position, from the oracle's D~
+    taken in blocks of rows."""
+    B, NH, T = x["igate"].shape
+    M = np.empty((B, NH, T))
+    for b in range(B):
+        for hh in range(NH):
+            for r0 in range(0, T, 1024):
+                rows = np.arange(r0, min(T, r0 + 1024))
+                M[b, hh, rows] = oracle.log_gate_matrix(x["fgate"][b, hh], x["igate"][b, hh],
+                                                        rows=rows, forget=forget).max(axis=1)
+    return M
 
 
 def spec(B, NH, T, d, dtype="bf16", ig=("normal", 0.0, 1.0), fg=("normal", 3.0, 1.0), **kw):
@@ -78,8 +105,7 @@ def _id(s):
 def test_bf16_ragged_full(s):
     x = W.make(s, seed=1)
     h, m, n = run_gpu(x)
-    hr, mr, nr, _, rho = oracle_full(x)
-    print(check(h, m, n, hr, mr, nr, TOL_H["bf16"]))
+    check_full(h, m, n, x, "bf16")
 
 
 @pytest.mark.parametrize("s", [spec(1, 2, 100, 32, "fp32"), spec(2, 1, 77, 512, "fp32"),
@@ -87,25 +113,48 @@ def test_bf16_ragged_full(s):
 def test_fp32_ragged_full(s):
     x = W.make(s, seed=2)
     h, m, n = run_gpu(x)
-    hr, mr, nr = oracle_full(x)[:3]
-    print(check(h, m, n, hr, mr, nr, TOL_H["fp32"]))
+    check_full(h, m, n, x, "fp32")
 
 
 def test_tiny_fp32_workload():
     x = W.make("tiny_fp32", seed=0)
     h, m, n = run_gpu(x)
-    hr, mr, nr = oracle_full(x)[:3]
-    print(check(h, m, n, hr, mr, nr, TOL_H["fp32"]))
-    # the recurrent form agrees too (the oracle is pinned to it)
+    check_full(h, m, n, x, "fp32")
+    # the recurrent form agrees too (the oracle is pinned to it), row by row
     hrec, _ = oracle.forward_recurrent(x["q"], x["k"], x["v"], x["igate"], x["fgate"])
-    assert head_normwise(h, hrec) <= TOL_H["fp32"]
+    hr, _, nr, _, rho, rho_num = oracle_full(x)
+    kap, kapn = conditions(nr, hr, rho, rho_num)
+    keep = (kap <= K_H["fp32"]) & (kapn <= K_NUM["fp32"])
+    assert row_relative(h, hrec)[keep].max() <= TOL_H["fp32"]
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "small_bf16"])
+def test_plain_entry_point_on_the_null_stream(name):
+    """mlstm_parallel_fwd itself (no stream argument: the null stream) through
+    the C ABI: against the oracle, and bitwise equal to the stream variant."""
+    x = W.make(name, seed=0)
+    q, k, v, ig, fg = _dev(x)
+    B, NH, T, d = q.shape
+    h = torch.empty_like(q)
+    m = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
+    n = torch.empty_like(m)
+    lib = mlstm.load_library()
+    torch.cuda.synchronize()  # the inputs are in place before the null-stream call
+    st = lib.mlstm_parallel_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), ig.data_ptr(),
+                                fg.data_ptr(), h.data_ptr(), m.data_ptr(), n.data_ptr(),
+                                B, NH, T, d, mlstm._dtype_code(q))
+    assert st == 0, mlstm.strerror(st)
+    torch.cuda.synchronize()
+    h2, m2, n2 = mlstm.parallel_fwd(q, k, v, ig, fg)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h2) and torch.equal(m, m2) and torch.equal(n, n2)
+    check_full(_host(h), _host(m), _host(n), x, x["spec"]["dtype"])
 
 
 def test_small_bf16_workload():
     x = W.make("small_bf16", seed=0)
     h, m, n = run_gpu(x)
-    hr, mr, nr = oracle_full(x)[:3]
-    print(check(h, m, n, hr, mr, nr, TOL_H["bf16"]))
+    check_full(h, m, n, x, "bf16")
 
 
 @pytest.mark.parametrize("s", [spec(1, 2, 257, 128), spec(1, 1, 150, 384),
@@ -118,8 +167,7 @@ def test_vector_kernel_bf16_inputs(s):
     independent GPU evaluation of the same pass."""
     x = W.make(s, seed=3)
     h, m, n = run_gpu(x, kernel="vector")
-    hr, mr, nr = oracle_full(x)[:3]
-    print(check(h, m, n, hr, mr, nr, 4e-3))
+    check_full(h, m, n, x, "bf16", tol_h=4e-3)
 
 
 def test_gate_scan_m_matches_oracle():
@@ -128,8 +176,7 @@ def test_gate_scan_m_matches_oracle():
     q, k, v, ig, fg = _dev(x)
     ws = mlstm.alloc_workspace(2, 3, 1000, "cuda")
     m = _host(mlstm.gate_scan(ig, fg, 64, ws))
-    mr = oracle_full(x)[1]
-    assert m_error(m, mr) <= 1e-5
+    assert m_error(m, m_every_position(x)) <= 1e-5
 
 
 # ---------------------------------------------------------------------------
@@ -151,37 +198,40 @@ def _sampled_reference(x, rows):
     M = np.empty((B, NH, len(rows)))
     N = np.empty((B, NH, len(rows)))
     R = np.empty((B, NH, len(rows)))
+    RN = np.empty((B, NH, len(rows)))
     for b in range(B):
         for hh in range(NH):
-            h, m, n, bb, rho = oracle.forward_rows(x["q"], x["k"], x["v"], x["igate"], x["fgate"],
-                                                   b, hh, rows)
-            H[b, hh], M[b, hh], N[b, hh], R[b, hh] = h, m, n, rho
-    return H, M, N, R
+            h, m, n, bb, rho, rho_num = oracle.forward_rows(x["q"], x["k"], x["v"], x["igate"],
+                                                            x["fgate"], b, hh, rows)
+            H[b, hh], M[b, hh], N[b, hh], R[b, hh], RN[b, hh] = h, m, n, rho, rho_num
+    return H, M, N, R, RN
+
+
+def _check_sampled(h, m, n, x, rows, seed_label, h_ref=None):
+    """h~ and n on the sampled rows, m at every position."""
+    hr, mr, nr, rho, rho_num = _sampled_reference(x, rows)
+    assert m_error(m, m_every_position(x)) <= 1e-5
+    kap, kapn = conditions(nr, hr, rho, rho_num)
+    out = check(h[:, :, rows], m[:, :, rows], n[:, :, rows], hr if h_ref is None else h_ref, mr,
+                nr, kap, kapn, TOL_H["bf16"], K_H["bf16"], K_NUM["bf16"])
+    print(seed_label, out)
+    assert np.isfinite(h).all() and np.isfinite(n).all() and np.isfinite(m).all()
+    return out
 
 
 @pytest.mark.parametrize("name", ["xlstm125m_layer", "xlstm1p3b_layer"])
 def test_language_model_workloads_sampled(name):
     x = W.make(name, seed=0)
     h, m, n = run_gpu(x)
-    T = x["spec"]["T"]
-    # m is cheap: compare every position against the oracle's rows below
-    rows = _sample_rows(T, np.random.default_rng(5))
-    hr, mr, nr, _ = _sampled_reference(x, rows)
-    print(check(h[:, :, rows], m[:, :, rows], n[:, :, rows], hr, mr, nr, TOL_H["bf16"]))
-    assert np.isfinite(h).all() and np.isfinite(n).all()
+    rows = _sample_rows(x["spec"]["T"], np.random.default_rng(5))
+    _check_sampled(h, m, n, x, rows, name)
 
 
 def test_long_context_workload_sampled():
     x = W.make("long_context_16k", seed=0)
     h, m, n = run_gpu(x)
-    T = x["spec"]["T"]
-    rows = _sample_rows(T, np.random.default_rng(6), count=30)
-    hr, mr, nr, rho = _sampled_reference(x, rows)
-    kappa = rho / nr
-    res = check(h[:, :, rows], m[:, :, rows], n[:, :, rows], hr, mr, nr, TOL_H["bf16"],
-                kappa=kappa, kappa_max=1e3)
-    print(res)
-    assert np.isfinite(h).all() and np.isfinite(n).all() and np.isfinite(m).all()
+    rows = _sample_rows(x["spec"]["T"], np.random.default_rng(6), count=30)
+    _check_sampled(h, m, n, x, rows, "long_context_16k")
 
 
 # ---------------------------------------------------------------------------
@@ -267,10 +317,8 @@ def test_output_gate_fused(s):
     torch.cuda.synchronize()
     assert torch.equal(ht, h0) and torch.equal(m, m0) and torch.equal(n, n0)
     assert torch.equal(h, h2) and torch.equal(m2, m0) and torch.equal(n2, n0)
-    hr, mr, nr = oracle_full(x)[:3]
-    gated_ref = oracle.output_gate(hr, og)
-    tol = TOL_H["bf16"] if s["dtype"] == "bf16" else TOL_H["fp32"]
-    print(check(_host(h), _host(m), _host(n), gated_ref, mr, nr, tol))
+    hr = oracle_full(x)[0]
+    check_full(_host(h), _host(m), _host(n), x, s["dtype"], h_ref=oracle.output_gate(hr, og))
 
 
 def test_output_gate_language_model_sampled():
@@ -282,9 +330,8 @@ def test_output_gate_language_model_sampled():
     torch.cuda.synchronize()
     h, m, n = _host(h), _host(m), _host(n)
     rows = _sample_rows(x["spec"]["T"], np.random.default_rng(13), count=20)
-    hr, mr, nr, _ = _sampled_reference(x, rows)
-    gated_ref = oracle.output_gate(hr, og[:, :, rows])
-    print(check(h[:, :, rows], m[:, :, rows], n[:, :, rows], gated_ref, mr, nr, TOL_H["bf16"]))
+    hr = _sampled_reference(x, rows)[0]
+    _check_sampled(h, m, n, x, rows, "gated", h_ref=oracle.output_gate(hr, og[:, :, rows]))
 
 
 # ---------------------------------------------------------------------------
@@ -310,9 +357,7 @@ def test_tile_skipping_matches_all_tiles_and_oracle(s):
     b = _staged(x, "mfma_all_tiles")
     for ta, tb in zip(a, b):
         assert torch.equal(ta, tb)  # equal values (an exact zero may differ in sign)
-    hr, mr, nr, _, rho = oracle_full(x)
-    print(check(_host(a[0]), _host(a[1]), _host(a[2]), hr, mr, nr, TOL_H["bf16"],
-                kappa=rho / nr, kappa_max=1e3))
+    check_full(_host(a[0]), _host(a[1]), _host(a[2]), x, "bf16")
 
 
 def test_tile_skipping_long_context_full_size():
@@ -360,15 +405,17 @@ def test_recurrent_steps_match_oracle(s):
     h, m, den, (C, n, mT) = _run_steps(x)
     hr, mr, denr, CT, nT = oracle.forward_recurrent_stabilized(
         x["q"], x["k"], x["v"], x["igate"], x["fgate"])
-    tol = TOL_H["bf16"] if s["dtype"] == "bf16" else TOL_H["fp32"]
-    print(check(h, m, den, hr, mr, denr, tol))
+    dt = s["dtype"]
+    # the denominator is row t's n (Eq. 84): the parallel form gives its condition number
+    hp, mp, npar, _, rho, rho_num = oracle_full(x)
+    kap, kapn = conditions(npar, hp, rho, rho_num)
+    print(check(h, m, den, hr, mr, denr, kap, kapn, TOL_H[dt], K_H[dt], K_NUM[dt]))
     # final states (float32 recurrences; states are not rounded to bf16)
     assert head_normwise(C.reshape(C.shape[0], C.shape[1], -1),
                          CT.reshape(CT.shape[0], CT.shape[1], -1)) <= 1e-4
     assert head_normwise(n, nT) <= 1e-4
     # the recurrent step and the parallel pass agree on h~, m and n
-    hp, mp, npar = oracle.forward_stabilized(x["q"], x["k"], x["v"], x["igate"], x["fgate"])
-    print(check(h, m, den, hp, mp, npar, tol))
+    print(check(h, m, den, hp, mp, npar, kap, kapn, TOL_H[dt], K_H[dt], K_NUM[dt]))
 
 
 def test_recurrent_step_in_place_equals_out_of_place_bitwise():
@@ -430,9 +477,9 @@ def test_training_forward_returns_b():
     h0, m0, n0 = mlstm.parallel_fwd(q, k, v, ig, fg)
     torch.cuda.synchronize()
     assert torch.equal(h, h0) and torch.equal(m, m0) and torch.equal(n, n0)
-    _, _, nr, br, _ = oracle_full(x)
+    _, _, nr, br, rho, _ = oracle_full(x)
     bb = _host(b)
-    assert head_normwise(bb, br) <= 1e-5
+    assert b_over_bar(bb, br, nr, rho / nr) <= 1.0
     # n = max(|b|, exp(-m)) (Eq. 84): exactly |b| above the floor
     nn, floor = _host(n), np.exp(-_host(m))
     above = np.abs(bb) > floor * (1 + 1e-6)
@@ -464,21 +511,8 @@ def test_backward_matches_oracle(s):
     torch.cuda.synchronize()
     got = [_host(t) for t in grads]
     ref = oracle.backward_stabilized(x["q"], x["k"], x["v"], x["igate"], x["fgate"], dh_np)
-    tol = 2e-2 if s["dtype"] == "bf16" else 1e-4
-    # The backward reuses the forward's h~ (dL/dn_i = -(dh_i . h~_i) / n_i) and
-    # recomputes D' with the same float32 exponent terms, so it cannot be more
-    # accurate than the forward on the same inputs: with input gates spread
-    # over U(-20, 20) the float32 forward itself is near 1.4e-4.  The bar is
-    # the nominal one or three times the forward's own h~ error, whichever is
-    # larger.
     hr = oracle_full(x)[0]
-    fwd_err = head_normwise(_host(h), hr)
-    tol = max(tol, 3.0 * fwd_err)
-    errs = {name: head_normwise(g, r) for name, g, r in
-            zip(("dq", "dk", "dv", "digate", "dfgate"), got, ref)}
-    print(errs, "forward h error", fwd_err)
-    for name, e in errs.items():
-        assert e <= (tol if name in ("dq", "dk", "dv") else 10 * tol), (name, errs)
+    _check_backward(got, ref, head_normwise(_host(h), hr), s["dtype"])
 
 
 def test_backward_deterministic_bitwise():
@@ -515,11 +549,9 @@ def test_exp_forget_forward_matches_oracle(s):
     torch.cuda.synchronize()
     assert torch.equal(h, ht) and torch.equal(m, mt) and torch.equal(n, nt)
     assert not torch.equal(m, ms)
-    hr, mr, nr, br, rho = oracle.forward_stabilized(x["q"], x["k"], x["v"], x["igate"],
-                                                    x["fgate"], return_diag=True, forget="exp")
-    print(check(_host(h), _host(m), _host(n), hr, mr, nr, TOL_H[s["dtype"]],
-                kappa=rho / nr, kappa_max=1e3))
-    assert head_normwise(_host(b), br) <= 1e-5
+    check_full(_host(h), _host(m), _host(n), x, s["dtype"], forget="exp")
+    _, _, nr, br, rho, _ = oracle_full(x, forget="exp")
+    assert b_over_bar(_host(b), br, nr, rho / nr) <= 1.0
 
 
 @pytest.mark.parametrize("s", [spec(1, 2, 40, 64, "fp32", fg=("normal", -0.05, 0.03)),
@@ -541,7 +573,10 @@ def test_exp_forget_recurrent_steps_match_oracle(s):
     h, m, den = (_host(torch.stack(a, dim=2)) for a in (hs, ms, dens))
     hr, mr, denr, CT, nT = oracle.forward_recurrent_stabilized(
         x["q"], x["k"], x["v"], x["igate"], x["fgate"], forget="exp")
-    print(check(h, m, den, hr, mr, denr, TOL_H[s["dtype"]]))
+    hp, _, npar, _, rho, rho_num = oracle_full(x, forget="exp")
+    kap, kapn = conditions(npar, hp, rho, rho_num)
+    dt = s["dtype"]
+    print(check(h, m, den, hr, mr, denr, kap, kapn, TOL_H[dt], K_H[dt], K_NUM[dt]))
     C = _host(state[0])
     assert head_normwise(C.reshape(B, NH, -1), CT.reshape(B, NH, -1)) <= 1e-4
     assert head_normwise(_host(state[1]), nT) <= 1e-4
@@ -564,12 +599,7 @@ def test_exp_forget_backward_matches_oracle(s):
                                      forget="exp")
     hr = oracle.forward_stabilized(x["q"], x["k"], x["v"], x["igate"], x["fgate"],
                                    forget="exp")[0]
-    tol = max(2e-2 if s["dtype"] == "bf16" else 1e-4, 3.0 * head_normwise(_host(h), hr))
-    errs = {name: head_normwise(_host(g), r) for name, g, r in
-            zip(("dq", "dk", "dv", "digate", "dfgate"), grads, ref)}
-    print(errs)
-    for name, e in errs.items():
-        assert e <= (tol if name in ("dq", "dk", "dv") else 10 * tol), (name, errs)
+    _check_backward([_host(g) for g in grads], ref, head_normwise(_host(h), hr), s["dtype"])
 
 
 # ---------------------------------------------------------------------------
@@ -590,8 +620,7 @@ WIDE_CASES = [
 def test_wide_heads_full(s):
     x = W.make(s, seed=21)
     h, m, n = run_gpu(x)
-    hr, mr, nr, _, rho = oracle_full(x)
-    print(check(h, m, n, hr, mr, nr, TOL_H["bf16"], kappa=rho / nr, kappa_max=1e3))
+    check_full(h, m, n, x, "bf16")
 
 
 @pytest.mark.parametrize("s", [spec(1, 1, 40, 16), spec(1, 2, 150, 64), spec(1, 1, 200, 384),
@@ -601,8 +630,7 @@ def test_wide_kernel_forced_any_head_dim(s):
     columns add nothing, so it is correct for every head dimension."""
     x = W.make(s, seed=22)
     h, m, n = run_gpu(x, kernel="mfma_wide")
-    hr, mr, nr = oracle_full(x)[:3]
-    print(check(h, m, n, hr, mr, nr, TOL_H["bf16"]))
+    check_full(h, m, n, x, "bf16")
 
 
 @pytest.mark.parametrize("s", [spec(1, 1, 70, 1024, "fp32"), spec(1, 2, 45, 640, "fp32")],
@@ -610,15 +638,13 @@ def test_wide_kernel_forced_any_head_dim(s):
 def test_wide_heads_fp32(s):
     x = W.make(s, seed=23)
     h, m, n = run_gpu(x)
-    hr, mr, nr = oracle_full(x)[:3]
-    print(check(h, m, n, hr, mr, nr, TOL_H["fp32"]))
+    check_full(h, m, n, x, "fp32")
 
 
 def test_wide_heads_vector_kernel_bf16_inputs():
     x = W.make(spec(1, 1, 120, 1024), seed=24)
     h, m, n = run_gpu(x, kernel="vector")
-    hr, mr, nr = oracle_full(x)[:3]
-    print(check(h, m, n, hr, mr, nr, 4e-3))
+    check_full(h, m, n, x, "bf16", tol_h=4e-3)
 
 
 def test_wide_heads_skipping_matches_all_tiles():
@@ -627,9 +653,7 @@ def test_wide_heads_skipping_matches_all_tiles():
     b = _staged(x, "mfma_all_tiles")
     for ta, tb in zip(a, b):
         assert torch.equal(ta, tb)
-    hr, mr, nr, _, rho = oracle_full(x)
-    print(check(_host(a[0]), _host(a[1]), _host(a[2]), hr, mr, nr, TOL_H["bf16"],
-                kappa=rho / nr, kappa_max=1e3))
+    check_full(_host(a[0]), _host(a[1]), _host(a[2]), x, "bf16")
 
 
 def test_wide_heads_deterministic_and_causal_bitwise():
@@ -659,10 +683,9 @@ def test_wide_heads_output_gate_and_b():
     _, _, _, b = mlstm.parallel_fwd_train(q, k, v, ig, fg)
     torch.cuda.synchronize()
     assert torch.equal(ht, h0) and torch.equal(m, m0) and torch.equal(n, n0)
-    hr, mr, nr, br, _ = oracle_full(x)
-    gated = oracle.output_gate(hr, og_np)
-    assert head_normwise(_host(h), gated) <= TOL_H["bf16"]
-    assert head_normwise(_host(b), br) <= 1e-5
+    hr, mr, nr, br, rho, _ = oracle_full(x)
+    check_full(_host(h), _host(m), _host(n), x, "bf16", h_ref=oracle.output_gate(hr, og_np))
+    assert b_over_bar(_host(b), br, nr, rho / nr) <= 1.0
 
 
 def test_wide_heads_recurrent_steps_match_oracle():
@@ -670,7 +693,9 @@ def test_wide_heads_recurrent_steps_match_oracle():
     h, m, den, (C, n, mT) = _run_steps(x)
     hr, mr, denr, CT, nT = oracle.forward_recurrent_stabilized(
         x["q"], x["k"], x["v"], x["igate"], x["fgate"])
-    print(check(h, m, den, hr, mr, denr, TOL_H["bf16"]))
+    hp, _, npar, _, rho, rho_num = oracle_full(x)
+    kap, kapn = conditions(npar, hp, rho, rho_num)
+    print(check(h, m, den, hr, mr, denr, kap, kapn, TOL_H["bf16"], K_H["bf16"], K_NUM["bf16"]))
     assert head_normwise(C.reshape(C.shape[0], C.shape[1], -1),
                          CT.reshape(CT.shape[0], CT.shape[1], -1)) <= 1e-4
     assert head_normwise(n, nT) <= 1e-4
@@ -690,9 +715,7 @@ def test_wide_heads_workload_sampled():
     x = W.make("xlstm1p3b_layer_d1024", seed=0)
     h, m, n = run_gpu(x)
     rows = _sample_rows(x["spec"]["T"], np.random.default_rng(31), count=24)
-    hr, mr, nr, _ = _sampled_reference(x, rows)
-    print(check(h[:, :, rows], m[:, :, rows], n[:, :, rows], hr, mr, nr, TOL_H["bf16"]))
-    assert np.isfinite(h).all() and np.isfinite(n).all()
+    _check_sampled(h, m, n, x, rows, "xlstm1p3b_layer_d1024")
 
 
 # ---------------------------------------------------------------------------
@@ -734,13 +757,18 @@ def _backward_case(x, dh_np, heads=None):
     return ([cat(out_got, i) for i in range(5)], [cat(out_ref, i) for i in range(5)], fwd)
 
 
-def _check_backward(got, ref, fwd_err, nominal=2e-2):
-    tol = max(nominal, 3.0 * fwd_err)
+def _check_backward(got, ref, fwd_err, dtype="bf16"):
+    """Gradients per head, normwise, against the oracle's Eqs. 87-105.  bf16:
+    2e-2 for all five (the products' operands are rounded to bf16 like the
+    forward's C~').  float32: 1e-4, or three times the forward's own h~ error
+    on the same inputs if that is larger: dL/dn_i = -(dh_i . h~_i) / n_i uses
+    the forward's h~, so the backward cannot be more accurate than it."""
+    tol = 2e-2 if dtype == "bf16" else max(1e-4, 3.0 * fwd_err)
     errs = {name: head_normwise(g, r) for name, g, r in
             zip(("dq", "dk", "dv", "digate", "dfgate"), got, ref)}
     print(errs, "forward h error", fwd_err)
     for name, e in errs.items():
-        assert e <= (tol if name in ("dq", "dk", "dv") else 10 * tol), (name, errs)
+        assert e <= tol, (name, errs)
     return errs
 
 
@@ -750,11 +778,7 @@ def test_backward_mfma_matches_oracle(s):
     dh_np = W.round_bf16(np.random.default_rng(33).standard_normal(x["q"].shape)
                          .astype(np.float32))
     got, ref, fwd = _backward_case(x, dh_np)
-    errs = _check_backward(got, ref, fwd)
-    # the gate gradients come from float32 sums of float32 products: on
-    # ordinary gates they are far inside the bar
-    if s["igate"] == ("normal", 0.0, 1.0):
-        assert errs["digate"] <= 2e-2 and errs["dfgate"] <= 2e-2, errs
+    _check_backward(got, ref, fwd)
 
 
 def test_backward_mfma_full_size_sampled_heads():
@@ -820,16 +844,19 @@ def test_long_sequence_sampled():
     x = W.make(spec(1, 1, 65536, 64), seed=36)
     h, m, n = run_gpu(x)
     rows = _sample_rows(x["spec"]["T"], np.random.default_rng(37), count=24)
-    hr, mr, nr, _ = _sampled_reference(x, rows)
-    print(check(h[:, :, rows], m[:, :, rows], n[:, :, rows], hr, mr, nr, TOL_H["bf16"]))
+    # m on the sampled rows only here: its row maxima at every position would
+    # take the oracle 65536^2 entries
+    hr, mr, nr, rho, rho_num = _sampled_reference(x, rows)
+    kap, kapn = conditions(nr, hr, rho, rho_num)
+    print(check(h[:, :, rows], m[:, :, rows], n[:, :, rows], hr, mr, nr, kap, kapn,
+                TOL_H["bf16"], K_H["bf16"], K_NUM["bf16"]))
     assert np.isfinite(h).all() and np.isfinite(n).all()
 
 
 def test_many_small_heads():
     x = W.make(spec(16, 64, 48, 16), seed=38)
     h, m, n = run_gpu(x)
-    hr, mr, nr = oracle_full(x)[:3]
-    print(check(h, m, n, hr, mr, nr, TOL_H["bf16"]))
+    check_full(h, m, n, x, "bf16")
 
 
 def test_aliased_outputs_rejected_on_gpu():
@@ -847,8 +874,7 @@ def test_aliased_outputs_rejected_on_gpu():
     h, m2, n2 = mlstm.parallel_fwd(q, q, v, ig, fg)
     torch.cuda.synchronize()
     y = dict(x, k=x["q"])
-    hr, mr, nr = oracle_full(y)[:3]
-    print(check(_host(h), _host(m2), _host(n2), hr, mr, nr, TOL_H["bf16"]))
+    check_full(_host(h), _host(m2), _host(n2), y, "bf16")
 
 
 # ---------------------------------------------------------------------------
@@ -951,12 +977,16 @@ def test_long_scan_forward_sampled(forget):
     torch.cuda.synchronize()
     rows = _sample_rows(12000, np.random.default_rng(48), count=24)
     H = np.empty((1, 2, len(rows), 64)); M = np.empty((1, 2, len(rows))); N = np.empty_like(M)
+    R = np.empty_like(M)
+    RN = np.empty_like(M)
     for hh in range(2):
-        hr, mr, nr, _, _ = oracle.forward_rows(x["q"], x["k"], x["v"], x["igate"], x["fgate"],
-                                                0, hh, rows, forget=forget)
-        H[0, hh], M[0, hh], N[0, hh] = hr, mr, nr
-    print(check(_host(h)[:, :, rows], _host(m)[:, :, rows], _host(n)[:, :, rows], H, M, N,
-                TOL_H["bf16"]))
+        hr, mr, nr, _, rho, rho_num = oracle.forward_rows(x["q"], x["k"], x["v"], x["igate"],
+                                                          x["fgate"], 0, hh, rows, forget=forget)
+        H[0, hh], M[0, hh], N[0, hh], R[0, hh], RN[0, hh] = hr, mr, nr, rho, rho_num
+    assert m_error(_host(m), m_every_position(x, forget)) <= 1e-5
+    kap, kapn = conditions(N, H, R, RN)
+    print(check(_host(h)[:, :, rows], _host(m)[:, :, rows], _host(n)[:, :, rows], H, M, N, kap,
+                kapn, TOL_H["bf16"], K_H["bf16"], K_NUM["bf16"]))
 
 
 # ---------------------------------------------------------------------------
@@ -989,10 +1019,4 @@ def _random_specs(count=24, seed=50):
 def test_random_shapes_match_oracle(s):
     x = W.make(s, seed=51)
     h, m, n = run_gpu(x)
-    hr, mr, nr, _, rho = oracle_full(x)
-    # fp32 inputs are held to 1e-4, so rows whose cancellation factor exceeds 10
-    # are left to the numerator check: under the stress gate law (i~ uniform in
-    # [-20, 20], f~ ~ N(0, 4) with floors) a plain all-float32 evaluation of the
-    # stabilized formula misses 1e-4 by two orders of magnitude on such rows.
-    kappa_max = 1e3 if s["dtype"] == "bf16" else 10.0
-    print(check(h, m, n, hr, mr, nr, TOL_H[s["dtype"]], kappa=rho / nr, kappa_max=kappa_max))
+    check_full(h, m, n, x, s["dtype"])
