@@ -107,7 +107,8 @@ enum {
   MLSTM_ERR_WORKSPACE = -7,   /* caller workspace smaller than mlstm_workspace_bytes */
   MLSTM_ERR_KERNEL = -8,      /* unknown kernel selector, or an MFMA selector for fp32 */
   MLSTM_ERR_ALIAS = -9,       /* an output overlaps an input or another output */
-  MLSTM_ERR_ACTIVATION = -10  /* unknown forget-gate activation */
+  MLSTM_ERR_ACTIVATION = -10, /* unknown forget-gate activation */
+  MLSTM_ERR_SCRATCH = -11     /* beyond the allocation-free entry point's fixed workspace */
 };
 
 /*
@@ -147,6 +148,29 @@ int mlstm_parallel_fwd_stream(const void* q, const void* k, const void* v,
                               void* h_out, float* m_out, float* n_out,
                               int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
                               void* stream);
+
+/*
+ * mlstm_parallel_fwd_noalloc -- mlstm_parallel_fwd_stream for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It calls no allocating routine.
+ * Its workspace is a fixed array of MLSTM_NOALLOC_SCRATCH_BYTES in the
+ * library's device code, one per GPU, held until the process ends; a call
+ * needs mlstm_workspace_bytes(B, NH, T) of it (about 20.5 bytes per position
+ * of B * NH * T, T padded to a multiple of 128: up to ~800 K positions) and
+ * returns MLSTM_ERR_SCRATCH, before any device work, for a problem that needs
+ * more.  All calls on one GPU share that GPU's array: calls that overlap in
+ * time on one GPU (different streams, host threads) race and must be
+ * serialized by the caller.  Nothing needs to be cleared between calls: each
+ * call writes every workspace byte it reads.  Arguments, results and other
+ * errors as for mlstm_parallel_fwd_stream; the first call on a device also
+ * looks up the array's address on that device (MLSTM_ERR_HIP if that fails).
+ */
+enum { MLSTM_NOALLOC_SCRATCH_BYTES = 16 << 20 };
+int mlstm_parallel_fwd_noalloc(const void* q, const void* k, const void* v,
+                               const float* igate, const float* fgate,
+                               void* h_out, float* m_out, float* n_out,
+                               int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
+                               void* stream);
 
 /*
  * mlstm_parallel_fwd_gated -- the forward pass followed by the output gate of

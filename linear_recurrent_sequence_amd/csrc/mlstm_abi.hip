@@ -7,6 +7,17 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
+
+namespace mlstm {
+
+// Workspace of mlstm_parallel_fwd_noalloc: one fixed array per GPU, which
+// holds it until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address on each GPU comes from
+// hipGetSymbolAddress, and only that address is ever handed to a kernel.
+__device__ __attribute__((aligned(256))) char scratch[MLSTM_NOALLOC_SCRATCH_BYTES];
+
+}  // namespace mlstm
 
 namespace {
 
@@ -127,25 +138,62 @@ int run_tiles(const void* q, const void* k, const void* v, const float* m, const
                                              stream));
 }
 
+// Both stages on a given workspace (mlstm::workspace_bytes(B * NH, T) bytes,
+// 256-byte aligned).  Arguments are checked by the caller.
+int forward_on(void* ws, const void* q, const void* k, const void* v, const float* igate,
+               const float* fgate, const mlstm::Epilogue& ep, void* h_out, float* m_out,
+               float* n_out, int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
+               hipStream_t s, bool exp_forget) {
+  const int64_t H = B * NH;
+  const Workspace w = mlstm::carve(ws, H, T);
+  int st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d, exp_forget, s));
+  if (st == MLSTM_OK)
+    st = run_tiles(q, k, v, m_out, w, h_out, n_out, ep, H, T, d, dtype, MLSTM_KERNEL_AUTO, s);
+  return st;
+}
+
 // Both stages with a stream-ordered workspace (safe under concurrent calls on
 // different streams).  Arguments are checked by the caller.
 int forward(const void* q, const void* k, const void* v, const float* igate, const float* fgate,
             const mlstm::Epilogue& ep, void* h_out, float* m_out, float* n_out, int64_t B,
             int64_t NH, int64_t T, int64_t d, int dtype, hipStream_t s,
             bool exp_forget = false) {
-  const int64_t H = B * NH;
-  const size_t bytes = mlstm::workspace_bytes(H, T);
+  const size_t bytes = mlstm::workspace_bytes(B * NH, T);
   void* ws = nullptr;
   if (hipMallocAsync(&ws, bytes, s) != hipSuccess) {
     (void)hipGetLastError();
     return MLSTM_ERR_HIP;
   }
-  const Workspace w = mlstm::carve(ws, H, T);
-  int st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d, exp_forget, s));
-  if (st == MLSTM_OK)
-    st = run_tiles(q, k, v, m_out, w, h_out, n_out, ep, H, T, d, dtype, MLSTM_KERNEL_AUTO, s);
+  int st = forward_on(ws, q, k, v, igate, fgate, ep, h_out, m_out, n_out, B, NH, T, d, dtype, s,
+                      exp_forget);
   if (hipFreeAsync(ws, s) != hipSuccess && st == MLSTM_OK) st = MLSTM_ERR_HIP;
   return st;
+}
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MLSTM_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MLSTM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(mlstm::scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return MLSTM_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLSTM_OK;
 }
 
 int check_forward_args(const void* q, const void* k, const void* v, const float* igate,
@@ -239,6 +287,26 @@ int mlstm_parallel_fwd_gated(const void* q, const void* k, const void* v, const 
   ep.htilde = htilde_out;
   return forward(q, k, v, igate, fgate, ep, h_out, m_out, n_out, B, NH, T, d, dtype,
                  static_cast<hipStream_t>(stream));
+}
+
+int mlstm_parallel_fwd_noalloc(const void* q, const void* k, const void* v, const float* igate,
+                               const float* fgate, void* h_out, float* m_out, float* n_out,
+                               int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
+                               void* stream) {
+  int st = check_forward_args(q, k, v, igate, fgate, h_out, m_out, n_out, B, NH, T, d, dtype);
+  if (st != MLSTM_OK) return st;
+  if (mlstm::workspace_bytes(B * NH, T) > size_t(MLSTM_NOALLOC_SCRATCH_BYTES))
+    return MLSTM_ERR_SCRATCH;
+  st = check_forward_alias(q, k, v, igate, fgate, nullptr, h_out, nullptr, m_out, n_out, nullptr,
+                           B, NH, T, d, dtype);
+  if (st != MLSTM_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws)) != MLSTM_OK) return st;
+  // every byte of the workspace that a kernel reads is written earlier in the
+  // same call (the scan writes all its terms up to the padded length), so
+  // nothing left by an earlier call needs clearing
+  return forward_on(ws, q, k, v, igate, fgate, mlstm::Epilogue{}, h_out, m_out, n_out, B, NH, T,
+                    d, dtype, static_cast<hipStream_t>(stream), false);
 }
 
 int mlstm_parallel_fwd(const void* q, const void* k, const void* v, const float* igate,
@@ -370,6 +438,7 @@ const char* mlstm_strerror(int status) {
     case MLSTM_ERR_KERNEL: return "unknown kernel selector, or the MFMA kernel asked for float32";
     case MLSTM_ERR_ALIAS: return "an output overlaps an input it must not alias";
     case MLSTM_ERR_ACTIVATION: return "unknown forget-gate activation";
+    case MLSTM_ERR_SCRATCH: return "the problem needs more workspace than the allocation-free entry point's fixed buffer holds (MLSTM_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

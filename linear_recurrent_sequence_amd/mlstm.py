@@ -50,6 +50,8 @@ def load_library():
     lib.mlstm_parallel_fwd.restype = i32
     lib.mlstm_parallel_fwd_stream.argtypes = [vp] * 8 + [i64] * 4 + [i32, vp]
     lib.mlstm_parallel_fwd_stream.restype = i32
+    lib.mlstm_parallel_fwd_noalloc.argtypes = [vp] * 8 + [i64] * 4 + [i32, vp]
+    lib.mlstm_parallel_fwd_noalloc.restype = i32
     lib.mlstm_parallel_fwd_gated.argtypes = [vp] * 10 + [i64] * 4 + [i32, vp]
     lib.mlstm_parallel_fwd_gated.restype = i32
     lib.mlstm_recurrent_step.argtypes = [vp] * 13 + [i64] * 3 + [i32, i32, vp]
@@ -166,6 +168,27 @@ def parallel_fwd(q, k, v, igate, fgate, out=None):
             _stream_ptr(q.device))
     if st != 0:
         raise MlstmError(st, "mlstm_parallel_fwd")
+    return h, m, n
+
+
+def parallel_fwd_noalloc(q, k, v, igate, fgate, out):
+    """parallel_fwd through mlstm_parallel_fwd_noalloc: the library allocates
+    nothing (its workspace is a fixed per-GPU array, shared by every call on
+    that GPU, so calls must not overlap).  ``out`` = (h, m, n) is required:
+    this path allocates no outputs either."""
+    lib = load_library()
+    B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
+    h, m, n = out
+    _require("h", h, q.shape, q.dtype, q.device)
+    _require("m", m, (B, NH, T), torch.float32, q.device)
+    _require("n", n, (B, NH, T), torch.float32, q.device)
+    with torch.cuda.device(q.device):
+        st = lib.mlstm_parallel_fwd_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
+            h.data_ptr(), m.data_ptr(), n.data_ptr(), B, NH, T, d, _dtype_code(q),
+            _stream_ptr(q.device))
+    if st != 0:
+        raise MlstmError(st, "mlstm_parallel_fwd_noalloc")
     return h, m, n
 
 

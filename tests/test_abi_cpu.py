@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_strerror_and_workspace_size():
-    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11):
         msg = mlstm.strerror(st)
         assert msg and msg != "unknown status"
     assert mlstm.strerror(-99) == "unknown status"
@@ -219,3 +219,24 @@ def test_other_entry_points_reject_outputs_that_alias():
     a = _addrs(["q", "k", "v", "m", "h", "n"])
     assert lib.mlstm_causal_tiles(a["q"], a["k"], a["v"], a["m"], ws, wsb, a["q"], a["n"],
                                   1, 1, 64, 16, 1, 0, None) == -9
+
+
+@needs_lib
+def test_noalloc_entry_point_rejects_before_device_work():
+    lib = mlstm.load_library()
+    lib.mlstm_parallel_fwd_noalloc.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int64] * 4 + [
+        ctypes.c_int, ctypes.c_void_p]
+    names = ["q", "k", "v", "igate", "fgate", "h_out", "m_out", "n_out"]
+    a = {n: FAKE + (i + 1) * (1 << 40) for i, n in enumerate(names)}
+    call = lambda B, NH, T, d, **kw: lib.mlstm_parallel_fwd_noalloc(
+        *[kw.get(n, a[n]) for n in names], B, NH, T, d, 1, None)
+    limit = 16 << 20
+    # the fixed workspace: 32 heads of 2048 fit; 128 heads of 8192 do not
+    assert lib.mlstm_workspace_bytes(8, 4, 2048) <= limit
+    assert lib.mlstm_workspace_bytes(16, 8, 8192) > limit
+    assert call(16, 8, 8192, 64) == -11
+    assert call(1, 1, 1 << 20, 64) == -11
+    # the ordinary checks come first
+    assert call(16, 8, 8192, 24) == -4
+    assert call(1, 1, 64, 16, q=None) == -1
+    assert call(1, 1, 64, 16, h_out=a["q"]) == -9
