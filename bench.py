@@ -2,17 +2,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one full call of mlstm_parallel_fwd (gate scan + causal tile
-kernel, workspace allocation included) on one batch of synthetic inputs that
-are resident in HBM before timing starts.  The default workload is the
-~125M-parameter xLSTM mLSTM layer (B=8, NH=4, T=2048, d=384, bf16 q/k/v).
-Prints ONE JSON line.
+A step is one full call of mlstm_parallel_fwd on one batch of synthetic
+inputs that are resident in HBM before timing starts.  The default workload
+is the ~125M-parameter xLSTM mLSTM layer (B=8, NH=4, T=2048, d=384, bf16
+q/k/v), where the call is a single launch of the causal tile kernel that
+scans its head's gates in its prologue (no workspace); longer sequences run
+the gate scan and the tile kernel as two launches on a stream-ordered
+workspace.  Prints ONE JSON line.
 
 Metric: TFLOP/s with the causal work counted as 2 * T^2 * d per head.
-The "roofline" object times the dominant kernel (the causal tile kernel)
-alone, with HIP events on the stream it is launched on, against the bf16
-dense MFMA peak.  The "cpu_baseline" object times the CPU oracle (float64
-NumPy) on a bounded sample of the same workload on this host.
+The "roofline" object times the dominant kernel alone (on the default
+workload the call's only kernel), with HIP events on the stream it is
+launched on, against the bf16 dense MFMA peak; "staged" times the two-launch
+form of the same pass.  The "cpu_baseline" object times the CPU oracle
+(float64 NumPy) on a bounded sample of the same workload on this host.
 """
 import argparse
 import hashlib
@@ -26,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU ("2.5 PFLOP/s")
 PEAK_HBM_GBS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "tiles_pairs_xlstm125m_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "tiles_pairs_fused_xlstm125m_counters.json")
 COPY_BYTES = 512 << 20
 TILE_SRC = os.path.join(ROOT, "linear_recurrent_sequence_amd", "csrc", "tiles_pairs.hip")
 
@@ -49,6 +52,10 @@ def parse():
                    help="skip the 1.3B-shaped layers (sub-heads of 512, true heads of 1024)")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="approximate CPU seconds for the oracle sample")
+    p.add_argument("--oracle-budget-s", type=float, default=6.0,
+                   help="approximate CPU seconds of oracle per named workload")
+    p.add_argument("--no-per-config", action="store_true",
+                   help="skip the whole-call timing and oracle timing of every named workload")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 512 MiB float32 device copy (a torch neg kernel) "
                         "three times, the reference for rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -113,6 +120,100 @@ def cpu_baseline(x, budget_s):
             "host_cores": len(os.sched_getaffinity(0)), "blas": blas, "kind": "oracle",
             "sample": f"{done} of {B * NH} heads (full T={T}, d={d} each), float64 NumPy, "
                       f"{dt:.1f} s"}
+
+
+def single_launch(spec):
+    """Whether mlstm_parallel_fwd runs this workload as one kernel launch (the
+    library's condition: bf16, d <= 384, T <= 2048 and divisible by 4)."""
+    return (spec["dtype"] == "bf16" and spec["d"] <= 384 and spec["T"] <= 2048
+            and spec["T"] % 4 == 0)
+
+
+SCAN_MIN_BYTES_PER_POSITION = 16  # least traffic of the scan: f~, i~ in; m and one prefix term out
+
+
+def scan_kernel_bytes(H, T):
+    """The gate scan's own algorithmic bytes: f~, i~ in (8 B/position); m,
+    R, C (float64), e out (24 B/position); two float64 bounds per 32 positions."""
+    return H * T * (4 + 4 + 4 + 8 + 8 + 4) + 2 * H * (T // 32) * 8
+
+
+NAMED = ("tiny_fp32", "small_bf16", "xlstm125m_layer", "xlstm1p3b_layer", "long_context_16k")
+
+
+def per_config(torch, mlstm, workloads, dev, oracle_budget_s, with_oracle, calls=100,
+               settle_s=0.5):
+    """Every named workload: the whole mlstm_parallel_fwd call (median of
+    ``calls`` calls, each between HIP events on its stream) and the CPU oracle
+    (float64 NumPy) on the host, the full workload where it takes seconds,
+    else a stated sample of heads."""
+    import numpy as np
+    out = []
+    for name in NAMED:
+        x = workloads.make(name, seed=0)
+        spec = x["spec"]
+        B, NH, T, d = spec["B"], spec["NH"], spec["T"], spec["d"]
+        dt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
+        q, k, v = (torch.from_numpy(x[n]).to(dev).to(dt).contiguous() for n in ("q", "k", "v"))
+        ig = torch.from_numpy(x["igate"]).to(dev).contiguous()
+        fg = torch.from_numpy(x["fgate"]).to(dev).contiguous()
+        h = torch.empty_like(q)
+        m = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+        n = torch.empty_like(m)
+        # untimed calls until the clock has settled (the oracle timing of the
+        # previous workload left the GPU idle), then 10 warm-up calls
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < settle_s:
+            for _ in range(10):
+                mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+            torch.cuda.synchronize()
+        for _ in range(10):
+            mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+        stream = torch.cuda.current_stream(dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(calls)]
+        for a, b in evs:
+            a.record(stream)
+            mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        med = us[len(us) // 2]
+        flops = workloads.counted_flops(B, NH, T, d)
+        rec = {"workload": name, "B": B, "NH": NH, "T": T, "d": d, "dtype": spec["dtype"],
+               "call_median_us": round(med, 2), "call_min_us": round(us[0], 2),
+               "counted_TFLOP/s": round(flops / (med * 1e-6) / 1e12, 3)}
+        if with_oracle:
+            rec["oracle"] = oracle_timing(x, oracle_budget_s)
+            rec["oracle_over_gpu"] = round(rec["oracle"]["seconds_full"] / (med * 1e-6), 0)
+        out.append(rec)
+    return out
+
+
+def oracle_timing(x, budget_s):
+    """Seconds of the float64 oracle on this workload: heads one at a time
+    until the whole workload is done or ``budget_s`` is spent; the full-time
+    figure scales the measured heads to all of them (heads are equal work)."""
+    import oracle
+    spec = x["spec"]
+    B, NH = spec["B"], spec["NH"]
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(B):
+        for h in range(NH):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            oracle.forward_stabilized(x["q"][sl], x["k"][sl], x["v"][sl],
+                                      x["igate"][sl], x["fgate"][sl])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            continue
+        break
+    dt = time.perf_counter() - t0
+    return {"heads_timed": done, "heads": B * NH, "seconds": round(dt, 3),
+            "seconds_full": round(dt * B * NH / done, 3),
+            "sample": "all heads" if done == B * NH else f"{done} of {B * NH} heads, scaled"}
 
 
 def long_context_skipping(torch, mlstm, workloads, dev, reps):
@@ -184,10 +285,14 @@ def scan_at_size(torch, mlstm, dev, reps=20, warmup=5):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     H = B * NH
-    nbytes = H * T * (4 * 6) + H * (T // 64) * 8 + 2 * H * (T // 32) * 4
+    nbytes = scan_kernel_bytes(H, T)
+    sbytes = H * T * SCAN_MIN_BYTES_PER_POSITION
     return {"B": B, "NH": NH, "T": T, "positions": H * T, "avg_launch_ms": round(ms, 4),
-            "algorithmic_bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "kernel_bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_16_per_position": sbytes,
+            "GB/s_16_per_position": round(sbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_16_per_position": round(sbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def layer_timing(torch, mlstm, workloads, dev, name, reps=50):
@@ -364,30 +469,46 @@ def main():
                     "p90_us": round(per_call[int(0.9 * len(per_call))], 2),
                     "median_TFLOP/s": round(flops / (per_call[len(per_call) // 2] * 1e-6) / 1e12, 1)}
 
-    # ---- dominant kernel alone: HIP events on the launch stream ----
-    ws = mlstm.alloc_workspace(B, NH, T, dev)
-    mlstm.gate_scan(ig, fg, d, ws, m=m)
+    # ---- dominant kernel alone: HIP events on the launch stream.  On a
+    # single-launch workload the call is that kernel: back-to-back calls keep
+    # the GPU busy, so the average over them is the kernel's duration.
+    single = single_launch(spec)
     reps = max(args.steps, 20)
-    for _ in range(3):
-        mlstm.causal_tiles(q, k, v, m, ws, out=(h, n))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    ws = mlstm.alloc_workspace(B, NH, T, dev)
+    m_ws = torch.empty_like(m)
+    mlstm.gate_scan(ig, fg, d, ws, m=m_ws)
+    for _ in range(3):
+        mlstm.causal_tiles(q, k, v, m_ws, ws, out=(h, n))
     e0.record(stream)
     for _ in range(reps):
-        mlstm.causal_tiles(q, k, v, m, ws, out=(h, n))
+        mlstm.causal_tiles(q, k, v, m_ws, ws, out=(h, n))
     e1.record(stream)
     torch.cuda.synchronize()
-    tile_ms = e0.elapsed_time(e1) / reps
+    staged_tile_ms = e0.elapsed_time(e1) / reps
+    if single:
+        e0.record(stream)
+        for _ in range(reps):
+            mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tile_ms = e0.elapsed_time(e1) / reps
+        kernel_name = f"tiles_pairs_kernel<{(d + 63) // 64 * 64}, gate scan fused>"
+    else:
+        tile_ms = staged_tile_ms
+        kernel_name = "causal tile kernel of the two-launch form"
     achieved = flops / (tile_ms * 1e-3) / 1e12
 
     # gate scan alone (HBM-bound in principle, latency-bound at these sizes)
     e0.record(stream)
     for _ in range(reps):
-        mlstm.gate_scan(ig, fg, d, ws, m=m)
+        mlstm.gate_scan(ig, fg, d, ws, m=m_ws)
     e1.record(stream)
     torch.cuda.synchronize()
     scan_ms = e0.elapsed_time(e1) / reps
-    scan_bytes = B * NH * T * (4 + 4 + 4 + 4 + 4 + 4) + B * NH * (T // 64 + 2) * 8
+    scan_bytes = scan_kernel_bytes(B * NH, T)
+    scan_bytes16 = B * NH * T * SCAN_MIN_BYTES_PER_POSITION
     scan_large = scan_at_size(torch, mlstm, dev)
 
     # decay-aware tile skipping on the long-context stress workload: the same
@@ -408,6 +529,11 @@ def main():
            recurrent_decode(torch, mlstm, dev, 256, NH, d, reps=20)]
 
     bwd = None if args.no_backward else backward_timing(torch, mlstm, workloads, x, dev)
+
+    configs = None
+    if not args.no_per_config:
+        configs = per_config(torch, mlstm, workloads, dev, args.oracle_budget_s,
+                             with_oracle=not args.no_cpu_baseline)
 
     # correctness spot check of the timed output (not part of the timing)
     mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
@@ -431,17 +557,24 @@ def main():
                    "heads": B * NH, "counted_flops": flops,
                    "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {
-            "bound": "mfma", "kernel": "tiles_pairs", "achieved": round(achieved, 2),
+            "bound": "mfma", "kernel": kernel_name, "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_from_counters(), "avg_launch_ms": round(tile_ms, 5),
+            "traffic": traffic_from_counters() if single else None,
+            "avg_launch_ms": round(tile_ms, 5),
         },
+        "staged": {"gate_scan_avg_launch_ms": round(scan_ms, 5),
+                   "tile_avg_launch_ms": round(staged_tile_ms, 5),
+                   "tile_TFLOP/s": round(flops / (staged_tile_ms * 1e-3) / 1e12, 2)},
         "gate_scan": {"avg_launch_ms": round(scan_ms, 5),
-                      "algorithmic_bytes": scan_bytes,
+                      "kernel_bytes": scan_bytes,
                       "GB/s": round(scan_bytes / (scan_ms * 1e-3) / 1e9, 1),
                       "frac_of_hbm": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                      "bytes_16_per_position": scan_bytes16,
+                      "GB/s_16_per_position": round(scan_bytes16 / (scan_ms * 1e-3) / 1e9, 1),
                       "at_2^26_positions": scan_large},
-        "per_call": per_call_rec,
+        "per_call": dict(per_call_rec, median_minus_kernel_us=round(
+            per_call_rec["median_us"] - tile_ms * 1e3, 2)),
         "output_finite": finite,
     }
     if skip_rec is not None:
@@ -451,6 +584,8 @@ def main():
     line["recurrent_step"] = rec
     if bwd is not None:
         line["backward"] = bwd
+    if configs is not None:
+        line["per_config"] = configs
     if args.copy_calibration:
         # reads and writes exactly COPY_BYTES each per launch
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)

@@ -134,7 +134,12 @@ enum { MLSTM_FORGET_SIGMOID = 0, MLSTM_FORGET_EXP = 1 };
  *   n_out     out  [B][NH][T] float32: the normalizer n (Eq. 84)
  *   B, NH, T  >= 1;  d a multiple of 16 in [16, 1024]
  *   dtype     MLSTM_FP32 or MLSTM_BF16
- * Runs on the null stream with a library-allocated, stream-ordered workspace.
+ * Runs on the null stream.  For bf16 with d <= 384 and T <= 2048, T a
+ * multiple of 4, the pass is one kernel launch that needs no workspace: each
+ * workgroup scans its head's gates itself (the gate-scan arithmetic in the
+ * same order, so every output is bitwise that of the two stages).  Otherwise
+ * the gate scan and the tile kernel run as two launches on a
+ * library-allocated, stream-ordered workspace.
  * Returns MLSTM_OK or a negative status.
  */
 int mlstm_parallel_fwd(const void* q, const void* k, const void* v,
@@ -158,9 +163,10 @@ int mlstm_parallel_fwd_stream(const void* q, const void* k, const void* v,
  * needs mlstm_workspace_bytes(B, NH, T) of it (about 20.5 bytes per position
  * of B * NH * T, T padded to a multiple of 128: up to ~800 K positions) and
  * returns MLSTM_ERR_SCRATCH, before any device work, for a problem that needs
- * more.  All calls on one GPU share that GPU's array: calls that overlap in
- * time on one GPU (different streams, host threads) race and must be
- * serialized by the caller.  Nothing needs to be cleared between calls: each
+ * more (also where the single-launch path of mlstm_parallel_fwd, which uses
+ * no workspace, would run).  All calls on one GPU share that GPU's array:
+ * calls that overlap in time on one GPU (different streams, host threads)
+ * race and must be serialized by the caller.  Nothing needs to be cleared between calls: each
  * call writes every workspace byte it reads.  Arguments, results and other
  * errors as for mlstm_parallel_fwd_stream; the first call on a device also
  * looks up the array's address on that device (MLSTM_ERR_HIP if that fails).

@@ -138,13 +138,23 @@ int run_tiles(const void* q, const void* k, const void* v, const float* m, const
                                              stream));
 }
 
+// Whether the whole pass runs as one launch of the tile kernel that scans its
+// gates itself (no workspace).
+bool fused_path(int64_t T, int64_t d, int dtype) {
+  return dtype == MLSTM_BF16 && mlstm::tiles_pairs_fused_supports(T, d);
+}
+
 // Both stages on a given workspace (mlstm::workspace_bytes(B * NH, T) bytes,
-// 256-byte aligned).  Arguments are checked by the caller.
+// 256-byte aligned; unused on the fused path).  Arguments are checked by the
+// caller.
 int forward_on(void* ws, const void* q, const void* k, const void* v, const float* igate,
                const float* fgate, const mlstm::Epilogue& ep, void* h_out, float* m_out,
                float* n_out, int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
                hipStream_t s, bool exp_forget) {
   const int64_t H = B * NH;
+  if (fused_path(T, d, dtype))
+    return hip_status(mlstm::launch_tiles_pairs_fused(q, k, v, igate, fgate, h_out, m_out, n_out,
+                                                      ep, exp_forget, H, T, d, s));
   const Workspace w = mlstm::carve(ws, H, T);
   int st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d, exp_forget, s));
   if (st == MLSTM_OK)
@@ -158,6 +168,9 @@ int forward(const void* q, const void* k, const void* v, const float* igate, con
             const mlstm::Epilogue& ep, void* h_out, float* m_out, float* n_out, int64_t B,
             int64_t NH, int64_t T, int64_t d, int dtype, hipStream_t s,
             bool exp_forget = false) {
+  if (fused_path(T, d, dtype))
+    return forward_on(nullptr, q, k, v, igate, fgate, ep, h_out, m_out, n_out, B, NH, T, d,
+                      dtype, s, exp_forget);
   const size_t bytes = mlstm::workspace_bytes(B * NH, T);
   void* ws = nullptr;
   if (hipMallocAsync(&ws, bytes, s) != hipSuccess) {
@@ -301,7 +314,7 @@ int mlstm_parallel_fwd_noalloc(const void* q, const void* k, const void* v, cons
                            B, NH, T, d, dtype);
   if (st != MLSTM_OK) return st;
   void* ws = nullptr;
-  if ((st = scratch_on_current_device(&ws)) != MLSTM_OK) return st;
+  if (!fused_path(T, d, dtype) && (st = scratch_on_current_device(&ws)) != MLSTM_OK) return st;
   // every byte of the workspace that a kernel reads is written earlier in the
   // same call (the scan writes all its terms up to the padded length), so
   // nothing left by an earlier call needs clearing

@@ -128,6 +128,17 @@ hipError_t launch_tiles_pairs(const void* q, const void* k, const void* v, const
                               const Epilogue& ep, bool skip, int64_t H, int64_t T, int64_t d,
                               hipStream_t stream);
 
+// Both stages in one launch (d <= 384, T <= 2048, T divisible by 4): the
+// same kernel, which scans its head's gates in its prologue and keeps the
+// terms in LDS, with no workspace; m, n, h (and the epilogue's outputs)
+// bitwise those of the two stages.  Decay-aware skipping is on.
+bool tiles_pairs_fused_supports(int64_t T, int64_t d);
+hipError_t launch_tiles_pairs_fused(const void* q, const void* k, const void* v,
+                                    const float* igate, const float* fgate, void* h_out,
+                                    float* m_out, float* n_out, const Epilogue& ep,
+                                    bool exp_forget, int64_t H, int64_t T, int64_t d,
+                                    hipStream_t stream);
+
 // Stage 2, bf16 matrix-core tiles for wide heads (d <= 1024): four waves
 // share 32 query rows and split the head dimension in quarters.
 bool tiles_wide_supports(int64_t d);

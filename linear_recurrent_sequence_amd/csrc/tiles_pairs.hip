@@ -38,7 +38,17 @@
 // query row and tile); on a diagonal tile every entry takes its own
 // exponential 2^(R_i + C_j) under the causal mask (Eq. 71).  Each exponent is
 // summed in float64 and rounded to float32 once.
+//
+// Fused gate scan (FUSED: at most 2048 positions, a multiple of 4).  Instead
+// of reading the gate scan's terms from a workspace, each workgroup scans its
+// head's gates from position 0 to its last row in its prologue, with the
+// scan code of the gate-scan kernel (the same block structure, so the terms
+// are bitwise the same), and keeps C_j, e_j and the tile bounds of all its
+// keys in LDS; it writes m of its own rows.  The gate rows are copied into
+// LDS ahead of the Q block, so the scan overlaps the Q copies.  The whole
+// forward pass is then one launch with no workspace.
 #include "mlstm_internal.h"
+#include "scan_common.h"
 #include "tile_common.h"
 
 namespace mlstm {
@@ -50,6 +60,13 @@ constexpr int kWThreads = 512;  // 8 waves: two per SIMD
 constexpr int kWWaves = kWThreads / 64;
 constexpr int kSK = 64;   // keys per super-step (two 32-key tiles)
 constexpr int kWPf = 3;   // LDS fragment prefetch distance (MFMA steps)
+constexpr int kFusedMaxT = 2048;  // longest sequence of the fused gate scan (one scan chunk)
+constexpr int kQCopies = 16;      // row copies per wave of the workgroup's Q block
+// s_waitcnt operand: vmcnt(kQCopies) (bits 3:0 and 15:14), no wait on expcnt
+// (bits 6:4) or lgkmcnt (bits 11:8)
+constexpr int kWaitAllButQCopies =
+    (kQCopies & 15) | ((kQCopies >> 4) << 14) | (7 << 4) | (15 << 8);
+static_assert(kFusedMaxT == scan::kScanThreads * scan::kScanPer, "one block scan");
 
 // LDS layout: rows are padded so that the fragment reads are free of bank
 // conflicts (LDS serves 256 bytes per clock in 64 banks; a 16-byte read of
@@ -63,7 +80,7 @@ constexpr int kWPf = 3;   // LDS fragment prefetch distance (MFMA steps)
 //   DP / 32 + 1 odd: 4 distinct groups.
 // Each row is copied by one instruction whose lanes fetch consecutive 16-byte
 // chunks, so a copy needs no per-lane address arithmetic.
-template <int DP>
+template <int DP, bool FUSED>
 struct WCfg {
   static_assert(DP % 64 == 0 && DP >= 64 && DP <= 384, "head dim of the two-wave kernel");
   static constexpr int CH = DP / 8;          // 16-byte chunks per row
@@ -78,12 +95,29 @@ struct WCfg {
   static constexpr int GE = GC + 512;        // e_j (float32)
   static constexpr int GB = GC + 768;        // keyb of the two 32-key tiles (float64)
   static constexpr int X_OFF = GC + 784;     // bf16(C~'^T) exchange, 2 KiB per wave
-  static constexpr int BYTES = X_OFF + kWWaves * 2048;
+  // fused gate scan: the terms of every key and the workgroup's rows
+  static constexpr int F_C = X_OFF + kWWaves * 2048;  // C_j of keys [0, 2048) (float64)
+  static constexpr int F_E = F_C + kFusedMaxT * 8;    // e_j (float32)
+  static constexpr int F_KB = F_E + kFusedMaxT * 4;   // keyb of each 32-key tile (float64)
+  static constexpr int F_RB = F_KB + kFusedMaxT / 4;  // rowb of each 32-row block (float64)
+  static constexpr int F_R = F_RB + kFusedMaxT / 4;   // R_i of the workgroup's 128 rows (float64)
+  static constexpr int F_M = F_R + kBM * 8;           // m of those rows (float32)
+  static constexpr int BYTES = FUSED ? F_M + kBM * 4 : X_OFF + kWWaves * 2048;
   static_assert(2 * kSK * RSK <= GC, "the staged Q block fits in the K and V regions");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DP>
+// Gate inputs of the fused variant (FUSED): the pre-activations, the forget
+// activation, ln(d)/2, and the m output of the workgroup's rows.
+struct FusedGates {
+  const float* igate;
+  const float* fgate;
+  float* m_out;
+  double half_ln_d;
+  int exp_forget;
+};
+
+template <int DP, bool FUSED>
 __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
                           amdgpu_waves_per_eu(2, 2))) void tiles_pairs_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
@@ -91,8 +125,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
     const double* __restrict__ colt, const float* __restrict__ colx, u16* __restrict__ h_out,
     const double* __restrict__ rowb, const double* __restrict__ keyb, float* __restrict__ n_out,
     const u16* __restrict__ ogate, u16* __restrict__ htilde, float* __restrict__ b_out, int T,
-    int d, int Tp, int row_tiles, int H, int skip) {
-  using C = WCfg<DP>;
+    int d, int Tp, int row_tiles, int H, int skip, FusedGates fg) {
+  using C = WCfg<DP, FUSED>;
   __shared__ __attribute__((aligned(1024))) char lds[C::BYTES];
 
   const int tid = threadIdx.x;
@@ -115,7 +149,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
   // Q^T fragments (full head dim): B operand of S^T = K Q^T, read from the
   // workgroup's Q block staged in LDS by the prologue
   bf16x8 qf[C::NS];
-  const double r_i = rowt[int64_t(head) * Tp + qi];  // R_i, qi < Tp
 
   f32x16 acc[C::NB];
 #pragma unroll
@@ -147,8 +180,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
     const int r = w + kWWaves * i;
     copy_row(v, s * kSK + r, lds_addr(lds + C::V_OFF + r * C::RSV));
   };
-  // gate terms of super-step s: one small copy each for waves 0..2
+  // gate terms of super-step s: one small copy each for waves 0..2 (the
+  // fused variant holds every key's terms in LDS from its prologue)
   auto copy_gates = [&](int s) {
+    if (FUSED) return;
     const int k0 = s * kSK;
     if (w == 0 && lane < 32)
       copy16(rsrc_words(colt + int64_t(head) * Tp + k0, kSK * 8), unsigned(16 * lane),
@@ -161,19 +196,95 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
              lds_addr(lds + C::GB));
   };
 
+  // ---- fused: the gate pre-activations of positions [0, t_eff) are copied
+  // into LDS (the C_j region, which the scan rewrites only after reading
+  // them) ahead of the Q block.  A wave's loads complete in order: a load
+  // issued after the Q copies would wait for all of them, while these are
+  // waited for alone (all but the wave's last kQCopies copies).  The fused
+  // variant takes lengths divisible by 4 only, so that every head's gate row
+  // starts 16-byte aligned.
+  const int t_eff = T < q0 + kBM ? T : q0 + kBM;
+  if constexpr (FUSED) {
+    const unsigned off = unsigned(1024 * w + 16 * lane);
+    copy16(rsrc_words(fg.fgate + int64_t(head) * T, int64_t(t_eff) * 4), off,
+           lds_addr(lds + C::F_C + 1024 * w));
+    copy16(rsrc_words(fg.igate + int64_t(head) * T, int64_t(t_eff) * 4), off,
+           lds_addr(lds + C::F_C + 4 * kFusedMaxT + 1024 * w));
+  }
+
   // ---- the workgroup's Q block (128 rows, contiguous in memory) is copied
   // into the K and V regions with the tiles' chunk permutation, overlapping
-  // the first-tile search; the prologue reads the Q^T fragments from there.
+  // the gate scan and the first-tile search; the prologue reads the Q^T
+  // fragments from there.
 #pragma unroll
   for (int i = 0; i < kBM / kWWaves; ++i) {
     const int r = w + kWWaves * i;
     copy_row(q, q0 + r, lds_addr(lds + C::K_OFF + r * C::RSK));
   }
 
+  // ---- fused gate scan of positions [0, q0 + 128) of the head while the Q
+  // copies are in flight: thread tid owns positions 4 tid .. 4 tid + 3
+  if constexpr (FUSED) {
+    using namespace scan;
+    const int64_t p0 = int64_t(kScanPer) * tid;
+    static_assert(kBM / kWWaves == kQCopies, "Q copies per wave");
+    __builtin_amdgcn_s_waitcnt(kWaitAllButQCopies);
+    __syncthreads();
+    const float4 f4 = reinterpret_cast<const float4*>(lds + C::F_C)[tid];
+    const float4 i4 = reinterpret_cast<const float4*>(lds + C::F_C + 4 * kFusedMaxT)[tid];
+    const float fa[kScanPer] = {f4.x, f4.y, f4.z, f4.w};
+    const float ia[kScanPer] = {i4.x, i4.y, i4.z, i4.w};
+    float fr[kScanPer], iv[kScanPer];
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e) {  // padding: no forgetting, no input
+      fr[e] = p0 + e < t_eff ? fa[e] : 0.0f;
+      iv[e] = p0 + e < t_eff ? ia[e] : -INFINITY;
+    }
+    double fb[kScanPer];
+    to_log_forget(p0, t_eff, fg.exp_forget, fr, fb);
+    Elem total;
+    const Elem before = block_scan(thread_elem(fb, iv), total);
+    Terms tm;
+    position_terms(identity(), before, fb, iv, p0, t_eff, fg.half_ln_d, tm);
+    if (p0 < q0 + kBM) {
+      double* fc = reinterpret_cast<double*>(lds + C::F_C) + p0;
+      *reinterpret_cast<double2*>(fc) = make_double2(tm.c[0], tm.c[1]);
+      *reinterpret_cast<double2*>(fc + 2) = make_double2(tm.c[2], tm.c[3]);
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(lds + C::F_E) + p0) =
+          make_float4(tm.e[0], tm.e[1], tm.e[2], tm.e[3]);
+      if ((p0 & (kBoundTile - 1)) == 0) {
+        reinterpret_cast<double*>(lds + C::F_KB)[p0 / kBoundTile] = tm.cmax;
+        reinterpret_cast<double*>(lds + C::F_RB)[p0 / kBoundTile] = tm.rmax;
+      }
+      if (p0 >= q0) {
+        const int o = int(p0) - q0;
+        double* fr2 = reinterpret_cast<double*>(lds + C::F_R) + o;
+        *reinterpret_cast<double2*>(fr2) = make_double2(tm.r[0], tm.r[1]);
+        *reinterpret_cast<double2*>(fr2 + 2) = make_double2(tm.r[2], tm.r[3]);
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(lds + C::F_M) + o) =
+            make_float4(tm.m[0], tm.m[1], tm.m[2], tm.m[3]);
+#pragma unroll
+        for (int e = 0; e < kScanPer; ++e)
+          if (p0 + e < T) fg.m_out[int64_t(head) * T + p0 + e] = tm.m[e];
+      }
+    }
+    __syncthreads();
+  }
+  const double r_i = FUSED ? reinterpret_cast<const double*>(lds + C::F_R)[qi - q0]
+                           : rowt[int64_t(head) * Tp + qi];  // R_i, qi < Tp
+  auto row_bound = [&](int r) {  // rowb of the 32-row block of row r
+    return FUSED ? reinterpret_cast<const double*>(lds + C::F_RB)[r / kBoundTile]
+                 : rowb[int64_t(head) * nb32 + r / kBoundTile];
+  };
+  auto key_bound = [&](int J) {  // keyb of 32-key tile J
+    return FUSED ? reinterpret_cast<const double*>(lds + C::F_KB)[J]
+                 : keyb[int64_t(head) * nb32 + J];
+  };
+
   // ---- decay-aware start of the key loop: the first 32-key tile some pair
   // needs (the bound of mlstm_internal.h); inside the loop each member skips
   // the products of tiles its rows do not need.
-  const double rb_w = rowb[int64_t(head) * nb32 + qw / kBoundTile];  // uniform across the wave
+  const double rb_w = row_bound(qw);  // uniform across the wave
   auto tile_needed = [&](double rb, double kb) { return rb + kb >= kSkipLog2; };
   int first_tile = 0;
   if (skip) {
@@ -183,12 +294,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int qu = q0 + 32 * u;
-      rb_rows[u] = rowb[int64_t(head) * nb32 + qu / kBoundTile];
+      rb_rows[u] = row_bound(qu);
       last_p[u] = (4 * It + u < n_key_tiles - 1) ? 4 * It + u : n_key_tiles - 1;
     }
     int mine = last_tile;
     for (int J = tid; J < last_tile; J += kWThreads) {
-      const double kb = keyb[int64_t(head) * nb32 + J];
+      const double kb = key_bound(J);
       bool need = false;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -248,10 +359,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
 
   for (int s = s_first_step; s <= s_last_step; ++s) {
     // ===== phase 1: K_s and its gate terms are resident; copies bring V_s =====
+    // the gate terms of the super-step's 64 keys (C_j, e_j, keyb of its tiles)
+    const char* const g_c = FUSED ? lds + C::F_C + 8 * kSK * s : lds + C::GC;
+    const char* const g_e = FUSED ? lds + C::F_E + 4 * kSK * s : lds + C::GE;
+    const char* const g_b = FUSED ? lds + C::F_KB + 16 * s : lds + C::GB;
     // whether this member's and the partner's key tiles reach the pair's rows
     auto member_needs = [&](int hk) {
       const int J = 2 * s + hk;
-      const double kb = *reinterpret_cast<const double*>(lds + C::GB + 8 * hk);
+      const double kb = *reinterpret_cast<const double*>(g_b + 8 * hk);
       const bool nd = J <= pair_last && (!skip || tile_needed(rb_w, kb));
       return __builtin_amdgcn_readfirstlane(int(nd)) != 0;
     };
@@ -280,8 +395,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
       }
       // lane (g, l32), register r holds S^T[key 8(r/4) + 4g + r%4][query l32]
       const bool diag = (2 * s + hh) * kBN == qw;
-      const double* gc = reinterpret_cast<const double*>(lds + C::GC) + 32 * hh;
-      const float* ge = reinterpret_cast<const float*>(lds + C::GE) + 32 * hh;
+      const double* gc = reinterpret_cast<const double*>(g_c) + 32 * hh;
+      const float* ge = reinterpret_cast<const float*>(g_e) + 32 * hh;
       // C~' = S (.) D' in place of S (Eq. 82), b += C~' (Eq. 83)
       if (diag) {
 #pragma unroll
@@ -299,7 +414,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
           }
         }
       } else {
-        const double kb = *reinterpret_cast<const double*>(lds + C::GB + 8 * hh);
+        const double kb = *reinterpret_cast<const double*>(g_b + 8 * hh);
         const float ei = __builtin_amdgcn_exp2f(float(r_i + kb));
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
@@ -382,7 +497,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
   // ---- epilogue: b of the pair (member 0's keys first), n (Eq. 84),
   // h~ = acc / n (Eqs. 85, 86), output gate (Eq. 78) on this member's columns
   bsum += __shfl_xor(bsum, 32, 64);
-  const float m_q = qi < T ? m_in[int64_t(head) * T + qi] : 0.0f;
+  const float m_q = FUSED ? reinterpret_cast<const float*>(lds + C::F_M)[qi - q0]
+                          : (qi < T ? m_in[int64_t(head) * T + qi] : 0.0f);
   reinterpret_cast<float*>(xmine)[lane] = bsum;
   __syncthreads();
   const float bpart = reinterpret_cast<const float*>(xpart)[lane];
@@ -460,38 +576,67 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
   }
 }
 
-template <int DP>
+template <int DP, bool FUSED>
 hipError_t launch_w(const void* q, const void* k, const void* v, const float* m,
                     const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep, bool skip,
-                    int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+                    int64_t H, int64_t T, int64_t d, const FusedGates& fg, hipStream_t stream) {
   const int64_t row_tiles = (T + kBM - 1) / kBM;
-  hipLaunchKernelGGL(tiles_pairs_kernel<DP>, dim3(unsigned(row_tiles * H)), dim3(kWThreads), 0,
-                     stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), m, ws.rowt, ws.colt, ws.colx,
-                     static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
-                     static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), ep.b, T,
-                     int(d), int(ws.Tp), int(row_tiles), int(H), int(skip));
+  hipLaunchKernelGGL((tiles_pairs_kernel<DP, FUSED>), dim3(unsigned(row_tiles * H)),
+                     dim3(kWThreads), 0, stream, static_cast<const u16*>(q),
+                     static_cast<const u16*>(k), static_cast<const u16*>(v), m, ws.rowt, ws.colt,
+                     ws.colx, static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
+                     static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), ep.b,
+                     int(T), int(d), int(ws.Tp), int(row_tiles), int(H), int(skip), fg);
   return hipGetLastError();
+}
+
+template <bool FUSED>
+hipError_t launch_any(const void* q, const void* k, const void* v, const float* m,
+                      const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,
+                      bool skip, int64_t H, int64_t T, int64_t d, const FusedGates& fg,
+                      hipStream_t stream) {
+  // head dims are padded up to a multiple of 64 (zero columns add nothing)
+  switch ((d + 63) / 64) {
+    case 1: return launch_w<64, FUSED>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, fg, stream);
+    case 2: return launch_w<128, FUSED>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, fg, stream);
+    case 3: return launch_w<192, FUSED>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, fg, stream);
+    case 4: return launch_w<256, FUSED>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, fg, stream);
+    case 5: return launch_w<320, FUSED>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, fg, stream);
+    case 6: return launch_w<384, FUSED>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, fg, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 bool tiles_pairs_supports(int64_t d) { return d % 16 == 0 && d >= 16 && d <= 384; }
 
+bool tiles_pairs_fused_supports(int64_t T, int64_t d) {
+  return tiles_pairs_supports(d) && T >= 1 && T <= kFusedMaxT && T % 4 == 0;
+}
+
 hipError_t launch_tiles_pairs(const void* q, const void* k, const void* v, const float* m,
                               const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,
                               bool skip, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
   if (!tiles_pairs_supports(d)) return hipErrorInvalidValue;
-  // head dims are padded up to a multiple of 64 (zero columns add nothing)
-  switch ((d + 63) / 64) {
-    case 1: return launch_w<64>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 2: return launch_w<128>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 3: return launch_w<192>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 4: return launch_w<256>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 5: return launch_w<320>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 6: return launch_w<384>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_any<false>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, FusedGates{}, stream);
+}
+
+hipError_t launch_tiles_pairs_fused(const void* q, const void* k, const void* v,
+                                    const float* igate, const float* fgate, void* h_out,
+                                    float* m_out, float* n_out, const Epilogue& ep,
+                                    bool exp_forget, int64_t H, int64_t T, int64_t d,
+                                    hipStream_t stream) {
+  if (!tiles_pairs_fused_supports(T, d)) return hipErrorInvalidValue;
+  Workspace none{};
+  none.Tp = padded_len(T);
+  FusedGates fg;
+  fg.igate = igate;
+  fg.fgate = fgate;
+  fg.m_out = m_out;
+  fg.half_ln_d = 0.5 * log(double(d));
+  fg.exp_forget = int(exp_forget);
+  return launch_any<true>(q, k, v, nullptr, none, h_out, n_out, ep, true, H, T, d, fg, stream);
 }
 
 }  // namespace mlstm

@@ -360,6 +360,41 @@ def test_tile_skipping_matches_all_tiles_and_oracle(s):
     check_full(_host(a[0]), _host(a[1]), _host(a[2]), x, "bf16")
 
 
+FUSED_CASES = [
+    spec(1, 1, 4, 16), spec(1, 2, 64, 48), spec(1, 1, 68, 80), spec(2, 1, 132, 96),
+    spec(2, 3, 300, 64, ig=("normal", 0, 2), fg=("normal", 3, 1.5)), spec(1, 2, 260, 128),
+    spec(1, 1, 2044, 192), spec(1, 2, 2048, 256), spec(1, 1, 1000, 320), spec(2, 2, 2048, 384),
+    spec(1, 1, 1, 16), spec(1, 2, 63, 48),  # lengths not divisible by 4: the two stages
+    spec(1, 2, 2048, 64, ig=("uniform", -20, 20), fg=("normal", 0, 4), fgate_floor=(0.01, -30.0)),
+    spec(1, 2, 1500, 128, ig=("uniform", -40, 40), fg=("normal", -2, 3)),
+]
+
+
+@pytest.mark.parametrize("forget", ["sigmoid", "exp"])
+@pytest.mark.parametrize("s", FUSED_CASES, ids=_id)
+def test_fused_scan_equals_the_two_stage_pass_bitwise(s, forget):
+    """Up to 2048 positions (bf16, head dim up to 384, length divisible by 4)
+    the one-shot entry points run a single tile kernel that scans the gates in
+    its prologue; the
+    scan there has the gate-scan kernel's block structure, so h, m and n must
+    be the bits of the two-stage pass (gate scan, then the same tile kernel
+    on the workspace)."""
+    x = W.make(s, seed=71)
+    if forget == "exp":  # log f = f~, small and negative
+        x["fgate"] = (-0.02 * np.abs(x["fgate"])).astype(np.float32)
+    q, k, v, ig, fg = _dev(x)
+    if forget == "sigmoid":
+        a = mlstm.parallel_fwd(q, k, v, ig, fg)
+    else:
+        a = mlstm.parallel_fwd_train(q, k, v, ig, fg, forget="exp")[:3]
+    b = mlstm.parallel_fwd_staged(q, k, v, ig, fg, kernel="mfma", forget=forget)
+    torch.cuda.synchronize()
+    for name, ta, tb in zip("hmn", a, b):
+        assert torch.equal(ta, tb), name
+    if s["T"] <= 300:
+        check_full(_host(a[0]), _host(a[1]), _host(a[2]), x, "bf16", forget=forget)
+
+
 def test_tile_skipping_long_context_full_size():
     x = W.make("long_context_16k", seed=0)
     a = _staged(x, "auto")
