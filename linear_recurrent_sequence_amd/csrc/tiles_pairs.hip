@@ -222,6 +222,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
     copy_row(q, q0 + r, lds_addr(lds + C::K_OFF + r * C::RSK));
   }
 
+  // each wave's Q^T fragments (like K fragments) from the staged Q block
+  auto read_q_fragments = [&]() {
+    const int qrow = C::K_OFF + (32 * pq + l32) * C::RSK + 16 * g;
+#pragma unroll
+    for (int t = 0; t < C::NS; ++t) qf[t] = *reinterpret_cast<const bf16x8*>(lds + qrow + 32 * t);
+  };
+
   // ---- fused gate scan of positions [0, q0 + 128) of the head while the Q
   // copies are in flight: thread tid owns positions 4 tid .. 4 tid + 3
   if constexpr (FUSED) {
@@ -240,13 +247,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
       fr[e] = p0 + e < t_eff ? fa[e] : 0.0f;
       iv[e] = p0 + e < t_eff ? ia[e] : -INFINITY;
     }
-    double fb[kScanPer];
-    to_log_forget(p0, t_eff, fg.exp_forget, fr, fb);
+    // a wave whose positions all lie at or past the workgroup's last row
+    // holds padding only (log f = 0, i~ = -inf): it skips the logarithms and
+    // the per-position terms, which nothing reads
+    const bool active = kScanPer * 64 * w < q0 + kBM;  // uniform across the wave
+    double fb[kScanPer] = {0.0, 0.0, 0.0, 0.0};
+    if (active) to_log_forget(p0, t_eff, fg.exp_forget, fr, fb);
+    const Elem mine = thread_elem(fb, iv);
+    // the Q block has landed meanwhile: its Q^T fragments are read, and the
+    // first K tile is copied before the rest of the scan runs (the first
+    // super-step is taken to be 0 until the decay bounds say otherwise)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    read_q_fragments();
+    __syncthreads();  // the region is refilled below
+#pragma unroll
+    for (int i = 0; i < C::RPW; ++i) copy_k(0, i);
     Elem total;
-    const Elem before = block_scan(thread_elem(fb, iv), total);
+    const Elem before = block_scan(mine, total);
     Terms tm;
-    position_terms(identity(), before, fb, iv, p0, t_eff, fg.half_ln_d, tm);
-    if (p0 < q0 + kBM) {
+    if (active) position_terms(identity(), before, fb, iv, p0, t_eff, fg.half_ln_d, tm);
+    if (active && p0 < q0 + kBM) {
       double* fc = reinterpret_cast<double*>(lds + C::F_C) + p0;
       *reinterpret_cast<double2*>(fc) = make_double2(tm.c[0], tm.c[1]);
       *reinterpret_cast<double2*>(fc + 2) = make_double2(tm.c[2], tm.c[3]);
@@ -297,22 +318,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
       rb_rows[u] = row_bound(qu);
       last_p[u] = (4 * It + u < n_key_tiles - 1) ? 4 * It + u : n_key_tiles - 1;
     }
+    // the wave's least needed tile: lanes test J0 + tid in blocks of the
+    // workgroup's threads; the first block with a hit in the wave holds it,
+    // at its lowest hitting lane (a ballot, no lane-to-lane moves)
     int mine = last_tile;
-    for (int J = tid; J < last_tile; J += kWThreads) {
-      const double kb = key_bound(J);
+    for (int J0 = 0; J0 < last_tile; J0 += kWThreads) {
+      const int J = J0 + tid;
       bool need = false;
+      if (J < last_tile) {
+        const double kb = key_bound(J);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        need = need || (J <= last_p[u] && tile_needed(rb_rows[u], kb));
-      if (need) {
-        mine = J;
-        break;  // J grows with each iteration: the first hit is this thread's least
+        for (int u = 0; u < 4; ++u)
+          need = need || (J <= last_p[u] && tile_needed(rb_rows[u], kb));
       }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const int o = __shfl_xor(mine, off, 64);
-      mine = o < mine ? o : mine;
+      const uint64_t hits = __builtin_amdgcn_ballot_w64(need);
+      if (hits != 0) {
+        mine = J0 + 64 * w + int(__builtin_ctzll(hits));
+        break;
+      }
     }
     if (lane == 0) s_first[w] = mine;
     __syncthreads();
@@ -340,19 +363,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
 
   // ---- prologue: each wave reads its Q^T fragments (like K fragments) from
   // the staged Q block; then K and the gate terms of the first super-step are
-  // copied into the K region.
-  {
+  // copied into the K region.  The fused variant read its fragments and
+  // copied K_0 during the scan: it copies again only when the first
+  // super-step is not 0 (a wave's copies land in order, so the later copy of
+  // the same rows is the one that stays).
+  if constexpr (!FUSED) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int qrow = C::K_OFF + (32 * pq + l32) * C::RSK + 16 * g;
-#pragma unroll
-    for (int t = 0; t < C::NS; ++t) qf[t] = *reinterpret_cast<const bf16x8*>(lds + qrow + 32 * t);
+    read_q_fragments();
     __syncthreads();  // the region is refilled below
   }
   {
+    if (!FUSED || s_first_step != 0) {
 #pragma unroll
-    for (int i = 0; i < C::RPW; ++i) copy_k(s_first_step, i);
-    copy_gates(s_first_step);
+      for (int i = 0; i < C::RPW; ++i) copy_k(s_first_step, i);
+      copy_gates(s_first_step);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
