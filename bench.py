@@ -11,10 +11,11 @@ the gate scan and the tile kernel as two launches on a stream-ordered
 workspace.  Prints ONE JSON line.
 
 Metric: TFLOP/s with the causal work counted as 2 * T^2 * d per head.
-The "roofline" object times the dominant kernel alone (on the default
-workload the call's only kernel), with HIP events on the stream it is
-launched on, against the bf16 dense MFMA peak; "staged" times the two-launch
-form of the same pass.  The "cpu_baseline" object times the CPU oracle
+The "roofline" object gives the dominant kernel's average duration from
+HIP events on the stream it is launched on (on the default workload the
+call's only kernel, so the events bracket the timed steps themselves),
+against the bf16 dense MFMA peak; "staged" times the two-launch form of the
+same pass.  The "cpu_baseline" object times the CPU oracle
 (float64 NumPy) on a bounded sample of the same workload on this host.
 """
 import argparse
@@ -446,16 +447,24 @@ def main():
     for _ in range(args.warmup):
         mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
     torch.cuda.synchronize()
+    # HIP events on the launch stream bracket the same timed steps: on a
+    # single-launch workload their average is the dominant kernel's duration
+    # over the timed region itself
+    stream = torch.cuda.current_stream(dev)
+    ev_t0 = torch.cuda.Event(enable_timing=True)
+    ev_t1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev_t0.record(stream)
     for _ in range(args.steps):
         mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+    ev_t1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     value = flops / (ms * 1e-3) / 1e12
+    timed_kernel_ms = ev_t0.elapsed_time(ev_t1) / args.steps
 
     # per-call durations: 100 calls, each between HIP events on the call's stream
-    stream = torch.cuda.current_stream(dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(100)]
     for a, b in evs:
@@ -470,8 +479,8 @@ def main():
                     "median_TFLOP/s": round(flops / (per_call[len(per_call) // 2] * 1e-6) / 1e12, 1)}
 
     # ---- dominant kernel alone: HIP events on the launch stream.  On a
-    # single-launch workload the call is that kernel: back-to-back calls keep
-    # the GPU busy, so the average over them is the kernel's duration.
+    # single-launch workload the call is that kernel, and the timed steps
+    # above are its launches, back to back.
     single = single_launch(spec)
     reps = max(args.steps, 20)
     e0 = torch.cuda.Event(enable_timing=True)
@@ -488,12 +497,7 @@ def main():
     torch.cuda.synchronize()
     staged_tile_ms = e0.elapsed_time(e1) / reps
     if single:
-        e0.record(stream)
-        for _ in range(reps):
-            mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
-        e1.record(stream)
-        torch.cuda.synchronize()
-        tile_ms = e0.elapsed_time(e1) / reps
+        tile_ms = timed_kernel_ms
         kernel_name = f"tiles_pairs_kernel<{(d + 63) // 64 * 64}, gate scan fused>"
     else:
         tile_ms = staged_tile_ms
