@@ -525,6 +525,11 @@ def main():
     if not args.no_wide:
         wide = [layer_timing(torch, mlstm, workloads, dev, name)
                 for name in ("xlstm1p3b_layer", "xlstm1p3b_layer_d1024")]
+        if not args.no_backward:
+            # above d = 512 the backward runs the float32 vector passes in
+            # head-dimension chunks (a correctness path): two calls
+            xw = workloads.make("xlstm1p3b_layer_d1024", seed=0)
+            wide[1]["backward"] = backward_timing(torch, mlstm, workloads, xw, dev, reps=2)
 
     # recurrent (generation) step on the same layer shape: the 8 x 4 heads'
     # state (19 MB) stays in the 256 MB last-level cache between steps; a

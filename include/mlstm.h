@@ -264,11 +264,13 @@ int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v,
  * with forget_activation MLSTM_FORGET_EXP, d(log f)/df~ = 1.  The forward
  * outputs must come from the same forget_activation.
  * dL/dn uses sum_j C~'_ij v_j = n_i h~_i, so for bf16 it carries the
- * rounding of the stored h~.  For bf16 the contractions run on the matrix
- * cores (bf16 operands, float32 accumulation; the operand E (.) dC~' of the
- * dQ and dK products and C~'/n of the dV product are rounded to bf16, the
- * row and column sums of dD~ behind the gate gradients are not); for float32
- * everything is float32 on the vector ALUs.  Results are bitwise
+ * rounding of the stored h~.  For bf16 with d <= 512 the contractions run
+ * on the matrix cores (bf16 operands, float32 accumulation; the operand
+ * E (.) dC~' of the dQ and dK products and C~'/n of the dV product are
+ * rounded to bf16, the row and column sums of dD~ behind the gate gradients
+ * are not); for float32, and for bf16 above d = 512, everything is float32
+ * on the vector ALUs (above d = 512 in head-dimension chunks, a correctness
+ * path far slower than the matrix cores).  Results are bitwise
  * reproducible.  The library allocates a stream-ordered workspace: per-row
  * terms and, for bf16 on the matrix cores, the bf16 operand of the dV
  * product, 8 KiB per head, 128-key block and 32-query tile of the causal
@@ -276,8 +278,9 @@ int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v,
  * the dV pass need not recompute S; above 2 GiB (or the byte count in the
  * environment variable MLSTM_BWD_STORE_MAX, read at each call) the dV pass
  * recomputes it instead (bitwise the same dV).
- * Pointers 16-byte aligned; no output may alias an input.  d <= 512
- * (MLSTM_ERR_HEAD_DIM above).  Other errors as for mlstm_parallel_fwd.
+ * Pointers 16-byte aligned; no output may alias an input.  Any d of the
+ * forward pass (a multiple of 16 up to 1024).  Errors as for
+ * mlstm_parallel_fwd.
  */
 int mlstm_parallel_bwd(const void* q, const void* k, const void* v,
                        const float* igate, const float* fgate,

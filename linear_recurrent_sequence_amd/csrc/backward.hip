@@ -38,9 +38,14 @@
 namespace mlstm {
 namespace {
 
-constexpr int kBT = 16;  // rows and keys per tile
-constexpr int kBMaxD = kBackwardMaxHeadDim;
+constexpr int kBT = 16;    // rows and keys per tile
+constexpr int kBMaxD = 512;  // the row and column passes hold whole rows in LDS up to here
 constexpr int kBPad = kBMaxD + 1;
+// above kBMaxD (up to kBackwardMaxHeadDim) the wide passes take the head
+// dimension in LDS chunks of kWC columns
+constexpr int kWC = 256;
+constexpr int kWChunks = kBackwardMaxHeadDim / kWC;
+constexpr int kWPer = kWC / kBT;  // accumulator columns per thread and chunk
 
 __device__ inline float load_elem(const float* p) { return *p; }
 __device__ inline float load_elem(const __hip_bfloat16* p) { return __bfloat162float(*p); }
@@ -253,6 +258,221 @@ __global__ __launch_bounds__(256) void bwd_cols_kernel(
   }
 }
 
+// The row pass for kBMaxD < d <= kBackwardMaxHeadDim: the same entries and
+// sums in the same order, with the head dimension in LDS chunks of kWC
+// columns.  The dot products s_ij and g_ij run over the chunks in turn (each
+// chunk of the tile's Q, dH, K and V rows staged once per key tile); the dQ
+// columns of each chunk accumulate from that chunk of K, staged again.
+template <typename Tin>
+__global__ __launch_bounds__(256) void bwd_rows_wide_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const Tin* __restrict__ dh, const float* __restrict__ inv_n, const float* __restrict__ db,
+    const double* __restrict__ rowt, const double* __restrict__ colt, Tin* __restrict__ dq,
+    float* __restrict__ rsum, int64_t T, int d, int64_t Tp, int64_t row_tiles) {
+  __shared__ float Qs[kBT][kWC + 1];
+  __shared__ float Gs[kBT][kWC + 1];  // dh rows
+  __shared__ float Ks[kBT][kWC + 1];
+  __shared__ float Vs[kBT][kWC + 1];
+  __shared__ float Ps[kBT][kBT + 1];  // E dC~'
+
+  const int tid = threadIdx.x;
+  const int rl = tid / kBT, cl = tid % kBT;
+  const int64_t head = blockIdx.x / row_tiles;
+  const int64_t q0 = (blockIdx.x % row_tiles) * kBT;
+  const int64_t qi = q0 + rl;
+  const int64_t hoff = head * T * int64_t(d);
+  const bool row_in = qi < T;
+  const double r_i = rowt[head * Tp + qi];  // qi < Tp
+  const float in_i = row_in ? inv_n[head * T + qi] : 0.0f;
+  const float db_i = row_in ? db[head * T + qi] : 0.0f;
+
+  float acc[kWChunks * kWPer];
+#pragma unroll
+  for (int u = 0; u < kWChunks * kWPer; ++u) acc[u] = 0.0f;
+  float rs = 0.0f;
+
+  const int64_t last_key = (q0 + kBT - 1 < T ? q0 + kBT - 1 : T - 1);
+  for (int64_t k0 = 0; k0 <= last_key; k0 += kBT) {
+    float s = 0.0f, gg = 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < kWChunks; ++ch) {
+      const int c0 = ch * kWC;
+      if (c0 < d) {
+        const int wc = d - c0 < kWC ? d - c0 : kWC;
+        __syncthreads();
+        for (int idx = tid; idx < kBT * wc; idx += 256) {
+          const int r = idx / wc, c = idx % wc;
+          const bool qin = q0 + r < T, kin = k0 + r < T;
+          Qs[r][c] = qin ? load_elem(q + hoff + (q0 + r) * d + c0 + c) : 0.0f;
+          Gs[r][c] = qin ? load_elem(dh + hoff + (q0 + r) * d + c0 + c) : 0.0f;
+          Ks[r][c] = kin ? load_elem(k + hoff + (k0 + r) * d + c0 + c) : 0.0f;
+          Vs[r][c] = kin ? load_elem(v + hoff + (k0 + r) * d + c0 + c) : 0.0f;
+        }
+        __syncthreads();
+        for (int c = 0; c < wc; ++c) {
+          s = fmaf(Qs[rl][c], Ks[cl][c], s);
+          gg = fmaf(Gs[rl][c], Vs[cl][c], gg);
+        }
+      }
+    }
+    const int64_t kj = k0 + cl;
+    const bool valid = row_in && kj <= qi && kj < T;
+    const float e = gate_factor(r_i, colt[head * Tp + kj], valid);
+    const float dct = gg * in_i + db_i;  // dC~' (Eqs. 91-93)
+    rs += (s * e) * dct;                 // dD~ = C~' dC~' (Eq. 95)
+    Ps[rl][cl] = e * dct;
+#pragma unroll
+    for (int ch = 0; ch < kWChunks; ++ch) {
+      const int c0 = ch * kWC;
+      if (c0 < d) {
+        const int wc = d - c0 < kWC ? d - c0 : kWC;
+        __syncthreads();  // P is complete; every read of the previous chunk is done
+        for (int idx = tid; idx < kBT * wc; idx += 256) {
+          const int r = idx / wc, c = idx % wc;
+          Ks[r][c] = k0 + r < T ? load_elem(k + hoff + (k0 + r) * d + c0 + c) : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kWPer; ++u) {
+          const int c = cl + kBT * u;
+          if (c < wc) {
+            float a = 0.0f;
+#pragma unroll
+            for (int t = 0; t < kBT; ++t) a = fmaf(Ps[rl][t], Ks[t][c], a);
+            acc[ch * kWPer + u] += a;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = kBT / 2; off > 0; off >>= 1) rs += __shfl_xor(rs, off, 64);
+  if (row_in) {
+    if (cl == 0) rsum[head * T + qi] = rs;
+#pragma unroll
+    for (int ch = 0; ch < kWChunks; ++ch) {
+#pragma unroll
+      for (int u = 0; u < kWPer; ++u) {
+        const int c = ch * kWC + cl + kBT * u;
+        if (c < d) store_elem(dq + hoff + qi * d + c, acc[ch * kWPer + u]);  // Eq. 98
+      }
+    }
+  }
+}
+
+// The column pass for kBMaxD < d <= kBackwardMaxHeadDim, in head-dimension
+// chunks as the wide row pass.
+template <typename Tin>
+__global__ __launch_bounds__(256) void bwd_cols_wide_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const Tin* __restrict__ dh, const float* __restrict__ inv_n, const float* __restrict__ db,
+    const double* __restrict__ rowt, const double* __restrict__ colt, Tin* __restrict__ dk,
+    Tin* __restrict__ dv, float* __restrict__ csum, int64_t T, int d, int64_t Tp,
+    int64_t key_tiles) {
+  __shared__ float Ks[kBT][kWC + 1];
+  __shared__ float Vs[kBT][kWC + 1];
+  __shared__ float Qs[kBT][kWC + 1];
+  __shared__ float Gs[kBT][kWC + 1];
+  __shared__ float Ps[kBT][kBT + 1];  // E dC~' (key-major)
+  __shared__ float Ns[kBT][kBT + 1];  // C~' / n (key-major)
+
+  const int tid = threadIdx.x;
+  const int kl = tid / kBT, cl = tid % kBT;
+  const int64_t head = blockIdx.x / key_tiles;
+  const int64_t k0 = (blockIdx.x % key_tiles) * kBT;
+  const int64_t kj = k0 + kl;
+  const int64_t hoff = head * T * int64_t(d);
+  const bool key_in = kj < T;
+  const double c_j = colt[head * Tp + kj];  // kj < Tp
+
+  float acck[kWChunks * kWPer], accv[kWChunks * kWPer];
+#pragma unroll
+  for (int u = 0; u < kWChunks * kWPer; ++u) acck[u] = accv[u] = 0.0f;
+  float cs = 0.0f;
+
+  for (int64_t q0 = k0; q0 < T; q0 += kBT) {
+    float s = 0.0f, gg = 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < kWChunks; ++ch) {
+      const int c0 = ch * kWC;
+      if (c0 < d) {
+        const int wc = d - c0 < kWC ? d - c0 : kWC;
+        __syncthreads();
+        for (int idx = tid; idx < kBT * wc; idx += 256) {
+          const int r = idx / wc, c = idx % wc;
+          const bool kin = k0 + r < T, qin = q0 + r < T;
+          Ks[r][c] = kin ? load_elem(k + hoff + (k0 + r) * d + c0 + c) : 0.0f;
+          Vs[r][c] = kin ? load_elem(v + hoff + (k0 + r) * d + c0 + c) : 0.0f;
+          Qs[r][c] = qin ? load_elem(q + hoff + (q0 + r) * d + c0 + c) : 0.0f;
+          Gs[r][c] = qin ? load_elem(dh + hoff + (q0 + r) * d + c0 + c) : 0.0f;
+        }
+        __syncthreads();
+        for (int c = 0; c < wc; ++c) {
+          s = fmaf(Qs[cl][c], Ks[kl][c], s);
+          gg = fmaf(Gs[cl][c], Vs[kl][c], gg);
+        }
+      }
+    }
+    const int64_t qi = q0 + cl;
+    const bool row_in = qi < T;
+    const bool valid = key_in && row_in && kj <= qi;
+    const double r_i = rowt[head * Tp + (row_in ? qi : 0)];
+    const float e = gate_factor(r_i, c_j, valid);
+    const float in_i = row_in ? inv_n[head * T + qi] : 0.0f;
+    const float db_i = row_in ? db[head * T + qi] : 0.0f;
+    const float dct = gg * in_i + db_i;
+    const float ct = s * e;
+    cs += ct * dct;
+    Ps[kl][cl] = e * dct;
+    Ns[kl][cl] = ct * in_i;
+#pragma unroll
+    for (int ch = 0; ch < kWChunks; ++ch) {
+      const int c0 = ch * kWC;
+      if (c0 < d) {
+        const int wc = d - c0 < kWC ? d - c0 : kWC;
+        __syncthreads();  // P and N are complete; every read of the previous chunk is done
+        for (int idx = tid; idx < kBT * wc; idx += 256) {
+          const int r = idx / wc, c = idx % wc;
+          const bool qin = q0 + r < T;
+          Qs[r][c] = qin ? load_elem(q + hoff + (q0 + r) * d + c0 + c) : 0.0f;
+          Gs[r][c] = qin ? load_elem(dh + hoff + (q0 + r) * d + c0 + c) : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kWPer; ++u) {
+          const int c = cl + kBT * u;
+          if (c < wc) {
+            float a = 0.0f, bsum = 0.0f;
+#pragma unroll
+            for (int t = 0; t < kBT; ++t) {
+              a = fmaf(Ps[kl][t], Qs[t][c], a);
+              bsum = fmaf(Ns[kl][t], Gs[t][c], bsum);
+            }
+            acck[ch * kWPer + u] += a;
+            accv[ch * kWPer + u] += bsum;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = kBT / 2; off > 0; off >>= 1) cs += __shfl_xor(cs, off, 64);
+  if (key_in) {
+    if (cl == 0) csum[head * T + kj] = cs;
+#pragma unroll
+    for (int ch = 0; ch < kWChunks; ++ch) {
+#pragma unroll
+      for (int u = 0; u < kWPer; ++u) {
+        const int c = ch * kWC + cl + kBT * u;
+        if (c < d) {
+          store_elem(dk + hoff + kj * d + c, acck[ch * kWPer + u]);  // Eq. 99
+          store_elem(dv + hoff + kj * d + c, accv[ch * kWPer + u]);  // Eq. 100
+        }
+      }
+    }
+  }
+}
+
 // Gate gradients for one head per workgroup: di~ = c (Eq. 105) and
 // df~_k = sigma(-f~_k) sum_{i>=k} (r_i - c_i) (Eqs. 102-104), the suffix
 // sums accumulated in float64 from the end of the sequence, one chunk of
@@ -329,12 +549,21 @@ hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* f
     hipLaunchKernelGGL(bwd_rows_prep_kernel<Tin>, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
                        stream, h, dh, m, n, b, inv_n, db, rows, int(d));
     const int64_t tiles = (T + kBT - 1) / kBT;
-    hipLaunchKernelGGL(bwd_rows_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream, q,
-                       k, v, dh, inv_n, db, ws.rowt, ws.colt, dq, rsum, T, int(d), ws.Tp,
-                       tiles);
-    hipLaunchKernelGGL(bwd_cols_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream, q,
-                       k, v, dh, inv_n, db, ws.rowt, ws.colt, dk, dv, csum, T, int(d), ws.Tp,
-                       tiles);
+    if (d <= kBMaxD) {
+      hipLaunchKernelGGL(bwd_rows_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream,
+                         q, k, v, dh, inv_n, db, ws.rowt, ws.colt, dq, rsum, T, int(d), ws.Tp,
+                         tiles);
+      hipLaunchKernelGGL(bwd_cols_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream,
+                         q, k, v, dh, inv_n, db, ws.rowt, ws.colt, dk, dv, csum, T, int(d),
+                         ws.Tp, tiles);
+    } else {
+      hipLaunchKernelGGL(bwd_rows_wide_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0,
+                         stream, q, k, v, dh, inv_n, db, ws.rowt, ws.colt, dq, rsum, T, int(d),
+                         ws.Tp, tiles);
+      hipLaunchKernelGGL(bwd_cols_wide_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0,
+                         stream, q, k, v, dh, inv_n, db, ws.rowt, ws.colt, dk, dv, csum, T,
+                         int(d), ws.Tp, tiles);
+    }
   }
   hipLaunchKernelGGL(bwd_gates_kernel, dim3(unsigned(H)), dim3(kGThreads), 0, stream, fgate,
                      rsum, csum, digate, dfgate, T, int(exp_forget));
@@ -368,7 +597,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                            size_t store_bytes, void* dq, void* dk, void* dv, float* digate,
                            float* dfgate, int64_t H, int64_t T, int64_t d, bool is_bf16,
                            bool exp_forget, hipStream_t stream) {
-  if (d % 16 != 0 || d < 16 || d > kBMaxD) return hipErrorInvalidValue;
+  if (d % 16 != 0 || d < 16 || d > kBackwardMaxHeadDim) return hipErrorInvalidValue;
   // the stored operand is all or nothing: a partial size would be overrun
   if (store_bytes != 0 &&
       (!is_bf16 || !backward_mfma_supports(d) || store_bytes != backward_mfma_store_bytes(H, T)))

@@ -153,15 +153,16 @@ hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, cons
                                const Epilogue& ep, int64_t H, int64_t T, int64_t d,
                                bool is_bf16, hipStream_t stream);
 
-// Backward pass (Eqs. 87-105), float32 vector tiles, d <= kBackwardMaxHeadDim
-// (four 16-row float32 tiles of the head dimension share the LDS).  `ws` holds
+// Backward pass (Eqs. 87-105), d <= kBackwardMaxHeadDim: bf16 inputs with
+// d <= 512 on the matrix cores, everything else on float32 vector tiles (whole
+// 16-row tiles in LDS up to d = 512, head-dimension chunks of 256 above).  `ws` holds
 // the gate scan's terms for the same inputs.  backward_store_bytes gives the
 // size of the stored operand of the dV product (0: the values pass recomputes
 // it); it reads the environment, so a caller evaluates it once and passes the
 // same value to backward_scratch_bytes and launch_backward.  `scratch` holds
 // backward_scratch_bytes(H, T, store_bytes) bytes (256-byte aligned): per-row
 // temporaries, then the stored operand.
-constexpr int kBackwardMaxHeadDim = 512;
+constexpr int kBackwardMaxHeadDim = 1024;
 size_t backward_store_bytes(int64_t H, int64_t T, int64_t d, bool is_bf16);
 size_t backward_scratch_bytes(int64_t H, int64_t T, size_t store_bytes);
 hipError_t launch_backward(const void* q, const void* k, const void* v, const float* fgate,

@@ -159,11 +159,11 @@ def test_training_entry_points_reject_unknown_forget_activation():
 @needs_lib
 def test_backward_rejects_head_dims_above_its_limit():
     lib = mlstm.load_library()
-    # d = 1024 is a valid forward head dimension, but beyond the backward's
-    # float32 LDS tiles; d = 1040 is beyond every entry point
-    assert lib.mlstm_parallel_bwd(*[FAKE] * 15, 1, 1, 64, 1024, 1, 0, None) == -4
-    assert lib.mlstm_parallel_bwd(*[FAKE] * 15, 1, 1, 64, 528, 0, 0, None) == -4
+    # the backward takes every forward head dimension; d = 1040 or one not a
+    # multiple of 16 is beyond every entry point
     assert lib.mlstm_parallel_bwd(*[FAKE] * 15, 1, 1, 64, 1040, 1, 0, None) == -4
+    assert lib.mlstm_parallel_bwd(*[FAKE] * 15, 1, 1, 64, 1040, 0, 0, None) == -4
+    assert lib.mlstm_parallel_bwd(*[FAKE] * 15, 1, 1, 64, 520, 0, 0, None) == -4
     # the one-wave MFMA kernel stops at 512; the selector is checked first
     assert lib.mlstm_causal_tiles(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, FAKE,
                                   1, 1, 64, 1024, 0, 5, None) == -8
