@@ -163,8 +163,9 @@ int mlstm_parallel_fwd_stream(const void* q, const void* k, const void* v,
  * needs mlstm_workspace_bytes(B, NH, T) of it (about 20.5 bytes per position
  * of B * NH * T, T padded to a multiple of 128: up to ~800 K positions) and
  * returns MLSTM_ERR_SCRATCH, before any device work, for a problem that needs
- * more (also where the single-launch path of mlstm_parallel_fwd, which uses
- * no workspace, would run).  All calls on one GPU share that GPU's array:
+ * more.  Where mlstm_parallel_fwd runs as a single launch (bf16, d <= 384,
+ * T <= 2048, T a multiple of 4) no workspace is used and any size is
+ * accepted.  All calls on one GPU share that GPU's array:
  * calls that overlap in time on one GPU (different streams, host threads)
  * race and must be serialized by the caller.  Nothing needs to be cleared between calls: each
  * call writes every workspace byte it reads.  Arguments, results and other

@@ -1,6 +1,8 @@
 // C ABI of libmlstm (declared in include/mlstm.h): argument validation,
-// workspace handling, and the two kernel launches of the stabilized parallel
-// mLSTM forward pass (xLSTM appendix A.3, Eqs. 79-86).
+// workspace handling, and the kernel launches of the stabilized parallel
+// mLSTM forward pass (xLSTM appendix A.3, Eqs. 79-86: one launch of a tile
+// kernel that scans its own gates, or the gate scan and then a tile kernel),
+// of its backward pass and of the recurrent step.
 #include "mlstm.h"
 #include "mlstm_internal.h"
 
@@ -308,7 +310,9 @@ int mlstm_parallel_fwd_noalloc(const void* q, const void* k, const void* v, cons
                                void* stream) {
   int st = check_forward_args(q, k, v, igate, fgate, h_out, m_out, n_out, B, NH, T, d, dtype);
   if (st != MLSTM_OK) return st;
-  if (mlstm::workspace_bytes(B * NH, T) > size_t(MLSTM_NOALLOC_SCRATCH_BYTES))
+  // the single-launch path needs no workspace, whatever the size
+  if (!fused_path(T, d, dtype) &&
+      mlstm::workspace_bytes(B * NH, T) > size_t(MLSTM_NOALLOC_SCRATCH_BYTES))
     return MLSTM_ERR_SCRATCH;
   st = check_forward_alias(q, k, v, igate, fgate, nullptr, h_out, nullptr, m_out, n_out, nullptr,
                            B, NH, T, d, dtype);
