@@ -440,12 +440,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
           }
         }
       } else {
+        // the tile's key factors and bound are read together, before any is
+        // used: one LDS round trip instead of one per register group
+        float4 e4[4];
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) e4[rq] = *reinterpret_cast<const float4*>(ge + 8 * rq + 4 * g);
         const double kb = *reinterpret_cast<const double*>(g_b + 8 * hh);
+        __builtin_amdgcn_sched_barrier(0);
         const float ei = __builtin_amdgcn_exp2f(float(r_i + kb));
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          const float4 e4 = *reinterpret_cast<const float4*>(ge + 8 * rq + 4 * g);
-          const float ee[4] = {e4.x, e4.y, e4.z, e4.w};
+          const float ee[4] = {e4[rq].x, e4[rq].y, e4[rq].z, e4[rq].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             st[4 * rq + e] *= ei * ee[e];
