@@ -214,10 +214,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const bool diag = (J * kBN == qw);
     const double* cb = reinterpret_cast<const double*>(buf + C::C_OFF);
     float cv[16];
+    // the tile's column terms are read together, before any is used
+    double2 cd[8];
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const double2 c01 = *reinterpret_cast<const double2*>(cb + 8 * rq + 4 * g);
-      const double2 c23 = *reinterpret_cast<const double2*>(cb + 8 * rq + 4 * g + 2);
+      cd[2 * rq] = *reinterpret_cast<const double2*>(cb + 8 * rq + 4 * g);
+      cd[2 * rq + 1] = *reinterpret_cast<const double2*>(cb + 8 * rq + 4 * g + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const double2 c01 = cd[2 * rq], c23 = cd[2 * rq + 1];
       const double cc[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
