@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace mlstm {
 namespace tilecommon {
 
@@ -81,6 +83,37 @@ __device__ inline void copy4(i32x4 rsrc, unsigned voffset, unsigned dst) {
                :
                : "s"(dst), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
+}
+
+// Row I of a run of rows, 16 bytes per active lane: global offset
+// vchunk + I * row_bytes in the range rsrc, LDS destination
+// lds_base + LDS_OFF + 16 * lane.  The row's offsets are formed inside the
+// instruction sequence, so that only the bases stay in registers: with the
+// offsets of every row of a tile formed up front, the compiler keeps them all
+// live and spills once the copies are spread over a loop of products.
+template <int I, int LDS_OFF>
+__device__ inline void copy16_row(i32x4 rsrc, unsigned vchunk, int row_bytes, unsigned lds_base) {
+  unsigned vtmp;
+  int stmp;
+  asm volatile(
+      "s_mul_i32 %1, %3, %5\n\t"
+      "v_add_u32 %0, %1, %2\n\t"
+      "s_add_u32 m0, %4, %6\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %7, 0 offen lds"
+      : "=&v"(vtmp), "=&s"(stmp)
+      : "v"(vchunk), "s"(row_bytes), "s"(lds_base), "n"(I), "n"(LDS_OFF), "s"(rsrc)
+      : "memory", "m0", "scc");
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order
+template <typename F, int... Is>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ inline i16x4 tr_read(const char* p) {

@@ -24,8 +24,14 @@
 // Data movement.  K, V (row-major, padded rows) and the column exponent terms
 // of tile J+1 are copied global -> LDS by the load-to-LDS path
 // (buffer_load_dwordx4 ... lds: no staging registers, no VALU) while tile J is
-// computed from the other buffer; one barrier per tile.  The copies go through
-// buffer resources whose range ends at the sequence end, so rows past it and
+// computed from the other buffer; one barrier per tile.  A copy holds its
+// wave at issue, and with one wave per SIMD nothing else feeds the matrix
+// core meanwhile, so a wave's 16 row copies are spread over the matrix
+// instructions of its first product, one every NS/16 of them, and each
+// copy's issue overlaps the product already in flight.  The first product
+// therefore runs on every tile in the loop, also where the wave's rows need
+// none of it (its result is then dropped).  The copies go through buffer
+// resources whose range ends at the sequence end, so rows past it and
 // head-dimension padding arrive as zeros.
 //
 // Exponents: log2(D'_ij / sqrt(d)) = R_i + C_j with the float64 terms of the
@@ -178,6 +184,39 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     if (w == 2 && lane < 2)
       dma4(make_rsrc(keyb + head * nb32 + J, 8), unsigned(4 * lane), buf + C::KB_OFF);
   };
+  // the same copies one row at a time, for spreading over the first product:
+  // row copy i (0 <= i < 16) is K row i (i < 8) or V row i - 8 of this
+  // wave's share; the tile's gate terms are copied by gate_copies
+  const unsigned vchunk = lane < dch ? unsigned(16 * lane) : kOutOfRange;
+  const int row_bytes = 2 * d;
+  // the wave's 8 rows of K and of V of tile J: one buffer range each
+  struct TileSrc { i32x4 k, v; };
+  auto tile_src = [&](int64_t J) {
+    const int64_t r0 = J * kBN + w * (kBN / kWaves);
+    const int64_t left = T - r0;
+    const int64_t nrec =
+        (left < 0 ? 0 : left < kBN / kWaves ? left : kBN / kWaves) * 2 * int64_t(d);
+    return TileSrc{rsrc_words(k + hoff + r0 * d, nrec), rsrc_words(v + hoff + r0 * d, nrec)};
+  };
+  auto row_copy = [&](const TileSrc& ts, char* buf, auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if (lane < C::CH) {
+      if constexpr (i < 8)
+        copy16_row<i & 7, (i & 7) * C::RSK>(ts.k, vchunk, row_bytes,
+                                             lds_addr(buf + w * (kBN / kWaves) * C::RSK));
+      else
+        copy16_row<i & 7, (i & 7) * C::RSV>(
+            ts.v, vchunk, row_bytes, lds_addr(buf + C::K_BYTES + w * (kBN / kWaves) * C::RSV));
+    }
+  };
+  auto gate_copies = [&](int64_t J, char* buf) {
+    const int64_t k0 = J * kBN;
+    if (w == 0 && lane < kBN / 2)
+      copy16(rsrc_words(colt + head * Tp + k0, kBN * 8), unsigned(16 * lane),
+             lds_addr(buf + C::C_OFF));
+    if (w == 2 && lane < 2)
+      copy4(rsrc_words(keyb + head * nb32 + J, 8), unsigned(4 * lane), lds_addr(buf + C::KB_OFF));
+  };
   // whether this wave's rows need tile J (copied into `buf`)
   auto wave_needs = [&](const char* buf, int64_t J) {
     if (J > wave_last) return false;
@@ -191,7 +230,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   const int j16 = l32 & 15;
   const int voff = (4 * g + (j16 >> 2)) * C::RSV + 32 * (l32 >> 4) + 8 * (j16 & 3);
 
-  auto compute = [&](const char* buf, int64_t J) {
+  // tile J from `buf`; during its first product the row copies of tile J + 1
+  // (sources `ts`) go into `nxt` when `more`; the rest only when `needs`
+  auto compute = [&](const char* buf, int64_t J, char* nxt, bool more, const TileSrc& ts,
+                     bool needs) {
     // S^T = K_J Q^T, K fragments read kPf steps ahead (the scheduling
     // barriers stop the compiler from hoisting every LDS read of the
     // unrolled loop, which would cost a register per read)
@@ -207,9 +249,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
         if (t + kPf < NS)
           kf[(t + kPf) % (kPf + 1)] = *reinterpret_cast<const bf16x8*>(kp + 32 * (t + kPf));
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kPf + 1)], qf[t], st, 0, 0, 0);
+        static_for<16>([&](auto ic) {
+          if ((decltype(ic)::value * NS) / 16 == t && more) row_copy(ts, nxt, ic);
+        });
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // A wave that needs none of the tile stops here.  (Issuing its copies
+    // back to back instead of running the first product would be a second
+    // copy site, and that makes the compiler spill the Q^T fragments.)
+    if (!needs) return;
     // lane (g, l32), register r holds S^T[key 8(r/4) + 4g + r%4][query l32]
     const bool diag = (J * kBN == qw);
     const double* cb = reinterpret_cast<const double*>(buf + C::C_OFF);
@@ -286,18 +335,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   // No plain global load is issued inside the loop: everything a tile needs
   // (K, V, C and the key tile's bound) arrives by the copies into LDS, so the
   // waits on those copies stay exact.
+  // one tile: its first product carries the row copies of the next tile
+  auto step = [&](const char* buf, int64_t J, char* nxt) {
+    const bool more = J + 1 <= last_tile;
+    const TileSrc ts = tile_src(J + 1);
+    if (more) gate_copies(J + 1, nxt);
+    compute(buf, J, nxt, more, ts, wave_needs(buf, J));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
   for (int64_t J = first_tile; J <= last_tile; J += 2) {
-    // even tile from smem0, prefetch into smem1
-    if (J + 1 <= last_tile) load_tile(J + 1, smem1);
-    if (wave_needs(smem0, J)) compute(smem0, J);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    step(smem0, J, smem1);  // even tile from smem0, prefetch into smem1
     if (J + 1 > last_tile) break;
-    // odd tile from smem1, prefetch into smem0
-    if (J + 2 <= last_tile) load_tile(J + 2, smem0);
-    if (wave_needs(smem1, J + 1)) compute(smem1, J + 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    step(smem1, J + 1, smem0);  // odd tile from smem1, prefetch into smem0
   }
 
   // ---- epilogue: n (Eq. 84), h~ = acc / n (Eqs. 85, 86), and with an
