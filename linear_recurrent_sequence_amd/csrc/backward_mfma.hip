@@ -27,7 +27,11 @@
 // bf16(s_ij E_ij / n_i) in the layout of the values pass's B fragments and
 // the values pass (kValuesStored) only reads it: dV is bitwise the same.  The
 // own rows' fragments are staged through LDS (one copy per row) before the
-// tile loop.
+// tile loop.  In the passes with first products, a wave's 16 row copies of
+// the next tile are spread over the matrix instructions of its first
+// products (a copy holds its wave at issue, and with one wave per SIMD that
+// would idle the matrix core); those products therefore run on every tile,
+// also where the wave's own rows take nothing from it.
 //
 // E_ij = D'_ij / sqrt(d) = 2^((A_i - A_j) + r_i + c_j) from the gate scan's
 // terms, as in the forward pass (0 above the diagonal and past the sequence
@@ -264,6 +268,49 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     }
   };
 
+  // The rows and keys passes (and the recomputing values pass) copy a tile's
+  // rows one at a time during the previous tile's first products: row copy
+  // i (0 <= i < 16) is row i of this wave's 8 rows of X1 (i < 8) or of X2.
+  struct TileSrc {
+    i32x4 x1, x2;
+  };
+  auto tile_src = [&](int J) {
+    const int r0 = J * kBN + w * (kBN / kBWaves);
+    const int left = T - r0;
+    const int64_t nrec =
+        int64_t(left < 0 ? 0 : left < kBN / kBWaves ? left : kBN / kBWaves) * 2 * d;
+    return TileSrc{rsrc_words(x1 + hoff + int64_t(r0) * d, nrec),
+                   rsrc_words(x2 + hoff + int64_t(r0) * d, nrec)};
+  };
+  auto row_copy = [&](const TileSrc& ts, char* buf, auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if (lane < C::CH) {
+      if constexpr (i < 8)
+        copy16_row<i & 7, (i & 7) * C::S1>(ts.x1, vchunk, 2 * d,
+                                            lds_addr(buf + C::X1_OFF + w * (kBN / kBWaves) * C::S1));
+      else
+        copy16_row<i & 7, (i & 7) * C::S2>(ts.x2, vchunk, 2 * d,
+                                            lds_addr(buf + C::X2_OFF + w * (kBN / kBWaves) * C::S2));
+    }
+  };
+  // the tile's gate terms and per-row scalars (as in load_tile)
+  auto small_copies = [&](int J, char* buf) {
+    const int x0 = J * kBN;
+    const int rows = T - x0 < kBN ? T - x0 : kBN;
+    const double* tsrc = MODE == kRowsPass ? colt : rowt;
+    if (w == 0 && lane < kBN / 2)
+      copy16(rsrc_words(tsrc + int64_t(head) * Tp + x0, kBN * 8), unsigned(16 * lane),
+             lds_addr(buf + C::GT));
+    if (MODE != kRowsPass) {
+      if (w == 1 && lane < kBN)
+        copy4(rsrc_words(inv_n + int64_t(head) * T + x0, int64_t(rows) * 4), unsigned(4 * lane),
+              lds_addr(buf + C::GN));
+      if (MODE == kKeysPass && w == 2 && lane < kBN)
+        copy4(rsrc_words(db + int64_t(head) * T + x0, int64_t(rows) * 4), unsigned(4 * lane),
+              lds_addr(buf + C::GD));
+    }
+  };
+
   // per-lane LDS offsets: rows of X1 / X2 for the first products, the
   // transposed gather of the accumulation operand
   const int off1 = C::X1_OFF + l32 * C::S1 + 16 * g;
@@ -276,7 +323,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     return ((int64_t(head) * tri + t) * kBWaves + w) * 2048;
   };
 
-  auto compute = [&](const char* buf, int J, const bf16x8 (&pin)[2]) {
+  // tile J from `buf`; during its first products the row copies of tile
+  // J + 1 (sources `ts`) go into `nxt` when `more`; the rest only when `needs`
+  auto compute = [&](const char* buf, int J, const bf16x8 (&pin)[2], char* nxt, bool more,
+                     const TileSrc& ts, bool needs) {
+    constexpr int NT = kTwo ? 2 * NS : NS;  // matrix instructions that carry the copies
     bf16x8 pb[2];
     if constexpr (MODE == kValuesStored) {
       pb[0] = pin[0];
@@ -294,6 +345,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
         if (t + kBPf < NS)
           kf[(t + kBPf) % (kBPf + 1)] = *reinterpret_cast<const bf16x8*>(p + 32 * (t + kBPf));
         y1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kBPf + 1)], f1[t], y1, 0, 0, 0);
+        static_for<16>([&](auto ic) {
+          if ((decltype(ic)::value * NT) / 16 == t && more) row_copy(ts, nxt, ic);
+        });
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -307,9 +361,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
         if (t + kBPf < NS)
           kf[(t + kBPf) % (kBPf + 1)] = *reinterpret_cast<const bf16x8*>(p + 32 * (t + kBPf));
         y2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kBPf + 1)], f2[t], y2, 0, 0, 0);
+        static_for<16>([&](auto ic) {
+          if ((decltype(ic)::value * NT) / 16 == NS + t && more) row_copy(ts, nxt, ic);
+        });
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // a wave whose rows need none of the tile stops after the first products
+    // (which carry the copies of the next tile)
+    if (!needs) return;
     // lane (g, l32), register r: own row l32, other row 8(r/4) + 4g + r%4 of the tile
     const bool diag = J * kBN == ow;
     const double* gt = reinterpret_cast<const double*>(buf + C::GT);
@@ -422,8 +482,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       if (J + 1 <= last) load_tile(J + 1, buf + C::GT);
     };
     auto compute_pair = [&](const char* buf, int J) {
-      if (wave_needs(J)) compute(buf, J, pin);
-      if (J + 1 <= last && wave_needs(J + 1)) compute(buf + C::GT, J + 1, pin1);
+      if (wave_needs(J)) compute(buf, J, pin, nullptr, false, TileSrc{}, true);
+      if (J + 1 <= last && wave_needs(J + 1))
+        compute(buf + C::GT, J + 1, pin1, nullptr, false, TileSrc{}, true);
     };
     auto next_pins = [&](int J) {
       pin[0] = pnext[0];
@@ -458,23 +519,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     }
   } else {
   load_tile(first, smem0);
-  load_pin(first, pin);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  auto step = [&](const char* buf, int J, char* nxt) {
+    const bool more = J + 1 <= last;
+    const TileSrc ts = tile_src(J + 1);
+    if (more) small_copies(J + 1, nxt);
+    compute(buf, J, pin, nxt, more, ts, wave_needs(J));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
   for (int J = first; J <= last; J += 2) {
-    load_pin(J + 1, pnext);
-    if (J + 1 <= last) load_tile(J + 1, smem1);
-    if (wave_needs(J)) compute(smem0, J, pin);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    step(smem0, J, smem1);  // even tile from smem0, the next into smem1
     if (J + 1 > last) break;
-    next_pin();
-    load_pin(J + 2, pnext);
-    if (J + 2 <= last) load_tile(J + 2, smem0);
-    if (wave_needs(J + 1)) compute(smem1, J + 1, pin);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    next_pin();
+    step(smem1, J + 1, smem0);  // odd tile from smem1, the next into smem0
   }
   }
 
