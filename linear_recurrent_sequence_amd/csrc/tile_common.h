@@ -57,7 +57,10 @@ __device__ inline void dma4(__amdgpu_buffer_rsrc_t rsrc, unsigned voffset, char*
 
 // The same copies issued through inline assembly, so that the compiler does
 // not wait for them before unrelated LDS reads; the kernel waits for them
-// (vmcnt) itself before each barrier.
+// (vmcnt) itself before each barrier.  They write M0 themselves, which the
+// compiler may not expect to change: a kernel that also uses the builtin
+// copies above (for which the compiler sets M0) issues all of those before
+// the first of these.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // buffer resource words: offsets at or past num_records bytes read as zeros
@@ -71,7 +74,17 @@ __device__ inline unsigned lds_addr(const char* p) {
 }
 // 16 bytes per active lane, global -> LDS at (wave-uniform) dst + 16 * lane.
 // M0 holds the LDS destination; one wait state separates its write from the copy.
+// Wave-uniform operands of the copies, forced into scalar registers: the "s"
+// constraint alone does not stop the compiler from placing a uniform value
+// that it computed in vector registers there.
+__device__ inline unsigned sreg(unsigned x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline i32x4 sreg(i32x4 x) {
+  return i32x4{__builtin_amdgcn_readfirstlane(x[0]), __builtin_amdgcn_readfirstlane(x[1]),
+               __builtin_amdgcn_readfirstlane(x[2]), __builtin_amdgcn_readfirstlane(x[3])};
+}
 __device__ inline void copy16(i32x4 rsrc, unsigned voffset, unsigned dst) {
+  rsrc = sreg(rsrc);
+  dst = sreg(dst);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(dst), "v"(voffset), "s"(rsrc)
@@ -79,6 +92,8 @@ __device__ inline void copy16(i32x4 rsrc, unsigned voffset, unsigned dst) {
 }
 // 4 bytes per active lane to dst + 4 * lane
 __device__ inline void copy4(i32x4 rsrc, unsigned voffset, unsigned dst) {
+  rsrc = sreg(rsrc);
+  dst = sreg(dst);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "s"(dst), "v"(voffset), "s"(rsrc)
@@ -93,6 +108,9 @@ __device__ inline void copy4(i32x4 rsrc, unsigned voffset, unsigned dst) {
 // live and spills once the copies are spread over a loop of products.
 template <int I, int LDS_OFF>
 __device__ inline void copy16_row(i32x4 rsrc, unsigned vchunk, int row_bytes, unsigned lds_base) {
+  rsrc = sreg(rsrc);
+  lds_base = sreg(lds_base);
+  row_bytes = int(sreg(unsigned(row_bytes)));
   unsigned vtmp;
   int stmp;
   asm volatile(

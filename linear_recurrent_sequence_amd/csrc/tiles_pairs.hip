@@ -31,7 +31,10 @@
 // Copies are buffer_load_dwordx4 ... lds (global -> LDS, no registers), one
 // padded row per instruction, issued through inline assembly so that the
 // compiler does not wait for them before unrelated LDS reads; the kernel
-// waits for its own copies (vmcnt) before each barrier.
+// waits for its own copies (vmcnt) before each barrier.  In the key loop a
+// wave's 8 rows of a tile share one buffer range and each copy forms its
+// row's offsets itself, so a copy costs three scalar instructions besides the
+// load rather than a buffer descriptor of its own.
 //
 // Exponents.  On a tile below the diagonal the exponent factors as
 // 2^(R_i + keyb_J) * e_j with e_j from the gate scan (one exponential per
@@ -172,14 +175,36 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
     if (lane < C::CH) copy16(rs, vchunk, dst);
   };
   // row i (0 <= i < RPW) of this wave's share of the 64-key tile of super-step s
+  // (prologue copies)
   auto copy_k = [&](int s, int i) {
     const int r = w + kWWaves * i;
     copy_row(k, s * kSK + r, lds_addr(lds + C::K_OFF + r * C::RSK));
   };
-  auto copy_v = [&](int s, int i) {
-    const int r = w + kWWaves * i;
-    copy_row(v, s * kSK + r, lds_addr(lds + C::V_OFF + r * C::RSV));
+  // In the key loop a wave's RPW rows w + 8 i of a 64-key tile share one
+  // buffer range, which ends before the first of them past the sequence end;
+  // each row's offsets are formed inside its copy (copy16_row).
+  const int row_step = kWWaves * 2 * d;  // bytes from one of a wave's rows to the next
+  auto wave_rows = [&](const u16* src, int s) {
+    const int r0 = s * kSK + w;
+    const int left = T - r0;
+    const int nv = left <= 0 ? 0 : (left + kWWaves - 1) / kWWaves;
+    return rsrc_words(src + hoff + int64_t(r0) * d,
+                      int64_t(nv < C::RPW ? nv : C::RPW) * row_step);
   };
+  // the wave's row copies i with (i n) / RPW == t (all of them for t < 0):
+  // its RPW row copies are spread over the n matrix instructions of a phase
+  auto rows_at = [&](int t, int n, i32x4 rs, unsigned lds_base, auto stride) {
+    static_for<C::RPW>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if ((t < 0 || (i * n) / C::RPW == t) && lane < C::CH)
+        copy16_row<i, i * kWWaves * decltype(stride)::value>(rs, vchunk, row_step, lds_base);
+    });
+  };
+  using KStride = std::integral_constant<int, C::RSK>;
+  using VStride = std::integral_constant<int, C::RSV>;
+  const unsigned lds_k = lds_addr(lds + C::K_OFF + w * C::RSK);
+  const unsigned lds_v = lds_addr(lds + C::V_OFF + w * C::RSV);
+
   // gate terms of super-step s: one small copy each for waves 0..2 (the
   // fused variant holds every key's terms in LDS from its prologue)
   auto copy_gates = [&](int s) {
@@ -398,12 +423,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
     };
     const bool need_own = member_needs(hh);
     const bool need_part = member_needs(hh ^ 1);
-    // the wave's RPW row copies are spread over the n matrix instructions of a phase
-    auto copies_at = [&](int t, int n, auto&& copy) {
-#pragma unroll
-      for (int i = 0; i < C::RPW; ++i)
-        if ((i * n) / C::RPW == t) copy(i);
-    };
+    const i32x4 rs_v = wave_rows(v, s);
     bf16x8 pown[2];
     if (need_own) {
       f32x16 st = f32x16{};
@@ -416,7 +436,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
         if (t + kWPf < C::NS)
           kf[(t + kWPf) % (kWPf + 1)] = *reinterpret_cast<const bf16x8*>(kaddr(t + kWPf));
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (kWPf + 1)], qf[t], st, 0, 0, 0);
-        copies_at(t, C::NS, [&](int i) { copy_v(s, i); });
+        rows_at(t, C::NS, rs_v, lds_v, VStride{});
         __builtin_amdgcn_sched_barrier(0);
       }
       // lane (g, l32), register r holds S^T[key 8(r/4) + 4g + r%4][query l32]
@@ -466,14 +486,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
       *reinterpret_cast<bf16x8*>(xmine + 16 * lane) = pown[0];
       *reinterpret_cast<bf16x8*>(xmine + 1024 + 16 * lane) = pown[1];
     } else {
-#pragma unroll
-      for (int i = 0; i < C::RPW; ++i) copy_v(s, i);
+      rows_at(-1, 1, rs_v, lds_v, VStride{});
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // ===== phase 2: V_s is resident; copies bring K_{s+1} and its gate terms =====
     const bool more = s < s_last_step;
+    const i32x4 rs_k = wave_rows(k, s + 1);
 
     // The products run even when neither key tile reaches the pair's rows
     // (their operands are then zero): a branch around them would make the
@@ -516,7 +536,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWThreads, kWThreads),
         const bf16x8 bop = c4 == 0 ? pown[0] : c4 == 1 ? pown[1] : c4 == 2 ? ppart[0] : ppart[1];
         acc[t >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16), bop,
                                                               acc[t >> 2], 0, 0, 0);
-        if (more) copies_at(t, NV, [&](int i) { copy_k(s + 1, i); });
+        if (more) rows_at(t, NV, rs_k, lds_k, KStride{});
         __builtin_amdgcn_sched_barrier(0);
       }
     }
