@@ -360,6 +360,40 @@ def test_tile_skipping_matches_all_tiles_and_oracle(s):
     check_full(_host(a[0]), _host(a[1]), _host(a[2]), x, "bf16")
 
 
+@pytest.mark.parametrize("s", [
+    spec(1, 2, 1500, 512, ig=("uniform", -40, 40), fg=("normal", -2, 3)),
+    spec(1, 1, 1000, 448, ig=("uniform", -20, 20), fg=("normal", 0, 4), fgate_floor=(0.01, -30.0)),
+    spec(2, 1, 333, 400, ig=("normal", 0, 2), fg=("normal", 0, 2)),
+], ids=_id)
+def test_single_wave_kernel_skipping_matches_all_tiles_and_oracle(s):
+    """Above d = 384 the one-wave-per-SIMD kernel runs.  Its first product
+    carries the next tile's copies, so it runs on every tile of the loop, also
+    where a wave skips the tile: skipping must still give the values of
+    visiting every tile, and both must pass the oracle's readings (ragged
+    tails, padded head dimensions, decay strong enough to skip tiles)."""
+    x = W.make(s, seed=15)
+    a = _staged(x, "mfma")
+    b = _staged(x, "mfma_all_tiles")
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta, tb)
+    check_full(_host(a[0]), _host(a[1]), _host(a[2]), x, "bf16")
+
+
+@pytest.mark.parametrize("s", [
+    spec(1, 2, 700, 64, ig=("uniform", -20, 20), fg=("normal", 0, 4), fgate_floor=(0.01, -30.0)),
+    spec(2, 1, 333, 208),
+    spec(1, 1, 97, 16),
+    spec(1, 1, 260, 32, ig=("normal", 0, 2), fg=("normal", 3, 1.5)),
+], ids=_id)
+def test_single_wave_kernel_at_small_head_dims(s):
+    """The one-wave-per-SIMD kernel selected explicitly at small head
+    dimensions (1 to 13 chunks of 16 bytes per row, so that a row copy leaves
+    most lanes idle) against the oracle."""
+    x = W.make(s, seed=16)
+    h, m, n = _staged(x, "mfma_single")
+    check_full(_host(h), _host(m), _host(n), x, "bf16")
+
+
 FUSED_CASES = [
     spec(1, 1, 4, 16), spec(1, 2, 64, 48), spec(1, 1, 68, 80), spec(2, 1, 132, 96),
     spec(2, 3, 300, 64, ig=("normal", 0, 2), fg=("normal", 3, 1.5)), spec(1, 2, 260, 128),
