@@ -296,8 +296,9 @@ def scan_at_size(torch, mlstm, dev, reps=20, warmup=5):
             "frac_of_hbm_16_per_position": round(sbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
-def layer_timing(torch, mlstm, workloads, dev, name, reps=50):
-    """Whole call and tile kernel alone on another layer shape (default kernels)."""
+def layer_timing(torch, mlstm, workloads, dev, name, reps=50, settle_s=0.5):
+    """Whole call and tile kernel alone on another layer shape (default
+    kernels), after settle_s seconds of untimed calls for the clock."""
     x = workloads.make(name, seed=0)
     spec = x["spec"]
     B, NH, T, d = spec["B"], spec["NH"], spec["T"], spec["d"]
@@ -311,8 +312,11 @@ def layer_timing(torch, mlstm, workloads, dev, name, reps=50):
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    for _ in range(5):
-        mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < settle_s:
+        for _ in range(5):
+            mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
+        torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(reps):
         mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
