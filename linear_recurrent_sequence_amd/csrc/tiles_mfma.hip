@@ -35,8 +35,13 @@
 // head-dimension padding arrive as zeros.
 //
 // Exponents: log2(D'_ij / sqrt(d)) = R_i + C_j with the float64 terms of the
-// gate scan, summed in float64 and rounded to float32 once per entry; C_j of
-// the tile's keys travels with the tile into LDS.
+// gate scan.  On a tile below the diagonal the exponent factors as
+// 2^(R_i + keyb_J) * e_j (R_i + keyb_J summed in float64 and rounded once; e_j
+// from the gate scan): one exponential per row and tile instead of one per
+// entry, which with one wave per SIMD would idle the matrix core.  On the
+// diagonal tile each entry takes its own exponential of R_i + C_j, summed in
+// float64 and rounded once, under the causal mask.  C_j, e_j and keyb_J of the
+// tile's keys travel with the tile into LDS.
 #include "mlstm_internal.h"
 #include "tile_common.h"
 
@@ -59,7 +64,8 @@ struct Cfg {
   static constexpr int V_BYTES = kBN * RSV;
   static constexpr int C_OFF = K_BYTES + V_BYTES;  // C_j of the tile's keys (float64)
   static constexpr int KB_OFF = C_OFF + kBN * 8;   // max of C_j over the key tile (float64)
-  static constexpr int BUF = (KB_OFF + 8 + 15) / 16 * 16;
+  static constexpr int E_OFF = (KB_OFF + 8 + 15) / 16 * 16;  // e_j of the tile's keys (float32)
+  static constexpr int BUF = E_OFF + kBN * 4;
 };
 
 template <int DP>
@@ -67,7 +73,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void tiles_mfma_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ m_in, const double* __restrict__ rowt,
-    const double* __restrict__ colt, u16* __restrict__ h_out, const double* __restrict__ rowb,
+    const double* __restrict__ colt, const float* __restrict__ colx, u16* __restrict__ h_out,
+    const double* __restrict__ rowb,
     const double* __restrict__ keyb, float* __restrict__ n_out, const u16* __restrict__ ogate,
     u16* __restrict__ htilde, float* __restrict__ b_out, int64_t T, int d, int64_t Tp,
     int64_t row_tiles, int64_t H, int skip) {
@@ -181,6 +188,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     }
     if (w == 0 && lane < kBN / 2)
       dma16(make_rsrc(colt + head * Tp + k0, kBN * 8), unsigned(16 * lane), buf + C::C_OFF);
+    if (w == 1 && lane < kBN / 4)
+      dma16(make_rsrc(colx + head * Tp + k0, kBN * 4), unsigned(16 * lane), buf + C::E_OFF);
     if (w == 2 && lane < 2)
       dma4(make_rsrc(keyb + head * nb32 + J, 8), unsigned(4 * lane), buf + C::KB_OFF);
   };
@@ -214,6 +223,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     if (w == 0 && lane < kBN / 2)
       copy16(rsrc_words(colt + head * Tp + k0, kBN * 8), unsigned(16 * lane),
              lds_addr(buf + C::C_OFF));
+    if (w == 1 && lane < kBN / 4)
+      copy16(rsrc_words(colx + head * Tp + k0, kBN * 4), unsigned(16 * lane),
+             lds_addr(buf + C::E_OFF));
     if (w == 2 && lane < 2)
       copy4(rsrc_words(keyb + head * nb32 + J, 8), unsigned(4 * lane), lds_addr(buf + C::KB_OFF));
   };
@@ -261,28 +273,52 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     if (!needs) return;
     // lane (g, l32), register r holds S^T[key 8(r/4) + 4g + r%4][query l32]
     const bool diag = (J * kBN == qw);
-    const double* cb = reinterpret_cast<const double*>(buf + C::C_OFF);
     float cv[16];
-    // the tile's column terms are read together, before any is used
-    double2 cd[8];
+    if (diag) {
+      // the diagonal tile: each entry's own exponential 2^(R_i + C_j) under
+      // the causal mask (Eq. 71); the tile's column terms are read together,
+      // before any is used
+      const double* cb = reinterpret_cast<const double*>(buf + C::C_OFF);
+      double2 cd[8];
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      cd[2 * rq] = *reinterpret_cast<const double2*>(cb + 8 * rq + 4 * g);
-      cd[2 * rq + 1] = *reinterpret_cast<const double2*>(cb + 8 * rq + 4 * g + 2);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      for (int rq = 0; rq < 4; ++rq) {
+        cd[2 * rq] = *reinterpret_cast<const double2*>(cb + 8 * rq + 4 * g);
+        cd[2 * rq + 1] = *reinterpret_cast<const double2*>(cb + 8 * rq + 4 * g + 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const double2 c01 = cd[2 * rq], c23 = cd[2 * rq + 1];
-      const double cc[4] = {c01.x, c01.y, c23.x, c23.y};
+      for (int rq = 0; rq < 4; ++rq) {
+        const double2 c01 = cd[2 * rq], c23 = cd[2 * rq + 1];
+        const double cc[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 8 * rq + 4 * g + e;
-        float ex = float(r_i + cc[e]);
-        if (diag && key > l32) ex = -INFINITY;  // above the diagonal (Eq. 71)
-        const float c = st[4 * rq + e] * __builtin_amdgcn_exp2f(ex);  // C~' (Eq. 82)
-        bsum += c;                                                 // b (Eq. 83)
-        cv[4 * rq + e] = c;
+        for (int e = 0; e < 4; ++e) {
+          const int key = 8 * rq + 4 * g + e;
+          const float ex = key > l32 ? -INFINITY : float(r_i + cc[e]);
+          const float c = st[4 * rq + e] * __builtin_amdgcn_exp2f(ex);  // C~' (Eq. 82)
+          bsum += c;                                                 // b (Eq. 83)
+          cv[4 * rq + e] = c;
+        }
+      }
+    } else {
+      // below the diagonal the exponent factors as 2^(R_i + keyb_J) * e_j:
+      // one exponential per row and tile; the tile's key factors and bound
+      // are read together, before any is used
+      const float* ge = reinterpret_cast<const float*>(buf + C::E_OFF);
+      float4 e4[4];
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) e4[rq] = *reinterpret_cast<const float4*>(ge + 8 * rq + 4 * g);
+      const double kb = *reinterpret_cast<const double*>(buf + C::KB_OFF);
+      __builtin_amdgcn_sched_barrier(0);
+      const float ei = __builtin_amdgcn_exp2f(float(r_i + kb));
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const float ee[4] = {e4[rq].x, e4[rq].y, e4[rq].z, e4[rq].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float c = st[4 * rq + e] * (ei * ee[e]);  // C~' (Eq. 82)
+          bsum += c;                                      // b (Eq. 83)
+          cv[4 * rq + e] = c;
+        }
       }
     }
     bf16x8 p[2];
@@ -395,7 +431,7 @@ hipError_t launch_dp(const void* q, const void* k, const void* v, const float* m
   const int64_t row_tiles = (T + kBM - 1) / kBM;
   hipLaunchKernelGGL(tiles_mfma_kernel<DP>, dim3(unsigned(row_tiles * H)), dim3(kThreads), 0,
                      stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), m, ws.rowt, ws.colt,
+                     static_cast<const u16*>(v), m, ws.rowt, ws.colt, ws.colx,
                      static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
                      static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), ep.b, T,
                      int(d), ws.Tp, row_tiles, H, int(skip));
