@@ -125,8 +125,8 @@ def cpu_baseline(x, budget_s):
 
 def single_launch(spec):
     """Whether mlstm_parallel_fwd runs this workload as one kernel launch (the
-    library's condition: bf16, d <= 384, T <= 2048 and divisible by 4)."""
-    return (spec["dtype"] == "bf16" and spec["d"] <= 384 and spec["T"] <= 2048
+    library's condition: bf16, d <= 512, T <= 2048 and divisible by 4)."""
+    return (spec["dtype"] == "bf16" and spec["d"] <= 512 and spec["T"] <= 2048
             and spec["T"] % 4 == 0)
 
 

@@ -134,7 +134,7 @@ enum { MLSTM_FORGET_SIGMOID = 0, MLSTM_FORGET_EXP = 1 };
  *   n_out     out  [B][NH][T] float32: the normalizer n (Eq. 84)
  *   B, NH, T  >= 1;  d a multiple of 16 in [16, 1024]
  *   dtype     MLSTM_FP32 or MLSTM_BF16
- * Runs on the null stream.  For bf16 with d <= 384 and T <= 2048, T a
+ * Runs on the null stream.  For bf16 with d <= 512 and T <= 2048, T a
  * multiple of 4, the pass is one kernel launch that needs no workspace: each
  * workgroup scans its head's gates itself (the gate-scan arithmetic in the
  * same order, so every output is bitwise that of the two stages).  Otherwise
@@ -163,7 +163,7 @@ int mlstm_parallel_fwd_stream(const void* q, const void* k, const void* v,
  * needs mlstm_workspace_bytes(B, NH, T) of it (about 20.5 bytes per position
  * of B * NH * T, T padded to a multiple of 128: up to ~800 K positions) and
  * returns MLSTM_ERR_SCRATCH, before any device work, for a problem that needs
- * more.  Where mlstm_parallel_fwd runs as a single launch (bf16, d <= 384,
+ * more.  Where mlstm_parallel_fwd runs as a single launch (bf16, d <= 512,
  * T <= 2048, T a multiple of 4) no workspace is used and any size is
  * accepted.  All calls on one GPU share that GPU's array:
  * calls that overlap in time on one GPU (different streams, host threads)

@@ -143,7 +143,8 @@ int run_tiles(const void* q, const void* k, const void* v, const float* m, const
 // Whether the whole pass runs as one launch of the tile kernel that scans its
 // gates itself (no workspace).
 bool fused_path(int64_t T, int64_t d, int dtype) {
-  return dtype == MLSTM_BF16 && mlstm::tiles_pairs_fused_supports(T, d);
+  return dtype == MLSTM_BF16 &&
+         (mlstm::tiles_pairs_fused_supports(T, d) || mlstm::tiles_mfma_fused_supports(T, d));
 }
 
 // Both stages on a given workspace (mlstm::workspace_bytes(B * NH, T) bytes,
@@ -155,8 +156,12 @@ int forward_on(void* ws, const void* q, const void* k, const void* v, const floa
                hipStream_t s, bool exp_forget) {
   const int64_t H = B * NH;
   if (fused_path(T, d, dtype))
-    return hip_status(mlstm::launch_tiles_pairs_fused(q, k, v, igate, fgate, h_out, m_out, n_out,
-                                                      ep, exp_forget, H, T, d, s));
+    return hip_status(
+        mlstm::tiles_pairs_fused_supports(T, d)
+            ? mlstm::launch_tiles_pairs_fused(q, k, v, igate, fgate, h_out, m_out, n_out, ep,
+                                              exp_forget, H, T, d, s)
+            : mlstm::launch_tiles_mfma_fused(q, k, v, igate, fgate, h_out, m_out, n_out, ep,
+                                             exp_forget, H, T, d, s));
   const Workspace w = mlstm::carve(ws, H, T);
   int st = hip_status(mlstm::launch_gate_scan(igate, fgate, m_out, w, H, T, d, exp_forget, s));
   if (st == MLSTM_OK)

@@ -120,6 +120,16 @@ hipError_t launch_tiles_mfma(const void* q, const void* k, const void* v, const 
                              const Epilogue& ep, bool skip, int64_t H, int64_t T, int64_t d,
                              hipStream_t stream);
 
+// Both stages in one launch of that kernel for 384 < d <= 512 (T <= 2048, T
+// divisible by 4): it scans its head's gates in its prologue (as the gate
+// scan does, bitwise) and keeps the terms it reads in LDS, with no workspace.
+bool tiles_mfma_fused_supports(int64_t T, int64_t d);
+hipError_t launch_tiles_mfma_fused(const void* q, const void* k, const void* v,
+                                   const float* igate, const float* fgate, void* h_out,
+                                   float* m_out, float* n_out, const Epilogue& ep,
+                                   bool exp_forget, int64_t H, int64_t T, int64_t d,
+                                   hipStream_t stream);
+
 // Stage 2, bf16 matrix-core tiles with two waves per SIMD (d <= 384), the
 // same results up to float32 rounding order.
 bool tiles_pairs_supports(int64_t d);

@@ -101,23 +101,30 @@ __device__ inline Elem dpp_elem(Elem x) {
 // of a row to the next row, lane 31 to rows 2 and 3, shift the wave right by 1
 constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
 
-// Ordered scan of one element per thread over the workgroup (thread order):
-// returns the composition of the elements of all earlier threads and stores
-// that of all threads in `total`.  Within a wave: an inclusive scan by row
-// shifts of 1, 2, 4, 8 lanes, then the row totals by the two row broadcasts
-// (DPP moves, no LDS); across the waves, in order through LDS.
-__device__ inline Elem block_scan(Elem x, Elem& total) {
-  __shared__ double s_a[kScanWaves];
-  __shared__ double s_b[kScanWaves];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  Elem incl = x;  // inclusive scan across the wave
+// Inclusive scan of one element per lane across a wave: row shifts of 1, 2,
+// 4, 8 lanes, then the row totals by the two row broadcasts (DPP moves, no
+// LDS).
+__device__ inline Elem wave_inclusive(Elem x) {
+  Elem incl = x;
   incl = combine(dpp_elem<kRowShr + 1, 0xF>(incl), incl);
   incl = combine(dpp_elem<kRowShr + 2, 0xF>(incl), incl);
   incl = combine(dpp_elem<kRowShr + 4, 0xF>(incl), incl);
   incl = combine(dpp_elem<kRowShr + 8, 0xF>(incl), incl);
   incl = combine(dpp_elem<kRowBcast15, 0xA>(incl), incl);
   incl = combine(dpp_elem<kRowBcast31, 0xC>(incl), incl);
+  return incl;
+}
+
+// Ordered scan of one element per thread over the workgroup (thread order):
+// returns the composition of the elements of all earlier threads and stores
+// that of all threads in `total`.  Within a wave by wave_inclusive; across
+// the waves, in order through LDS.
+__device__ inline Elem block_scan(Elem x, Elem& total) {
+  __shared__ double s_a[kScanWaves];
+  __shared__ double s_b[kScanWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const Elem incl = wave_inclusive(x);
   if (lane == 63) {
     s_a[wave] = incl.a;
     s_b[wave] = incl.b;
@@ -134,6 +141,42 @@ __device__ inline Elem block_scan(Elem x, Elem& total) {
   const Elem lexcl = dpp_elem<kWaveShr1, 0xF>(incl);
   __syncthreads();  // the shared totals may be rewritten by the next call
   return combine(before, lexcl);
+}
+
+// block_scan over kScanThreads elements run by a workgroup of half as many
+// threads: thread t holds the elements x0 and x1 of threads t and
+// t + kScanThreads / 2 of the full block and receives what block_scan gives
+// those two threads (before0, before1) and the total, bit for bit: the same
+// combinations in the same order.
+__device__ inline void block_scan_halves(Elem x0, Elem x1, Elem& before0, Elem& before1,
+                                         Elem& total) {
+  __shared__ double s_a[kScanWaves];
+  __shared__ double s_b[kScanWaves];
+  constexpr int kHalf = kScanWaves / 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;  // 0 .. kHalf - 1
+  const Elem incl0 = wave_inclusive(x0);
+  const Elem incl1 = wave_inclusive(x1);
+  if (lane == 63) {
+    s_a[wave] = incl0.a;
+    s_b[wave] = incl0.b;
+    s_a[wave + kHalf] = incl1.a;
+    s_b[wave + kHalf] = incl1.b;
+  }
+  __syncthreads();
+  Elem b0 = identity(), b1 = identity();
+  total = identity();
+  for (int w = 0; w < kScanWaves; ++w) {
+    const Elem e = {s_a[w], s_b[w]};
+    if (w < wave) b0 = combine(b0, e);
+    if (w < wave + kHalf) b1 = combine(b1, e);
+    total = combine(total, e);
+  }
+  const Elem lexcl0 = dpp_elem<kWaveShr1, 0xF>(incl0);
+  const Elem lexcl1 = dpp_elem<kWaveShr1, 0xF>(incl1);
+  __syncthreads();
+  before0 = combine(b0, lexcl0);
+  before1 = combine(b1, lexcl1);
 }
 
 // f~ and i~ of positions p0 .. p0 + 3 as stored (padding: f~ = 0, i~ = -inf)

@@ -41,6 +41,20 @@ __device__ inline void map_tile(int64_t wg, int64_t row_tiles, int64_t H, int64_
   }
 }
 
+// Gate inputs of a tile kernel that scans its head's gates in its prologue:
+// the pre-activations, the forget activation, ln(d)/2, and the m output of
+// the workgroup's rows.
+struct FusedGates {
+  const float* igate;
+  const float* fgate;
+  float* m_out;
+  double half_ln_d;
+  int exp_forget;
+};
+// s_waitcnt operand: vmcnt(N) for N < 64 (bits 3:0 and 15:14), no wait on
+// expcnt (bits 6:4) or lgkmcnt (bits 11:8)
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // a buffer resource: offsets at or past `num_records` bytes read as zeros
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t num_records) {
   const int n = num_records > 0x7FFFFFFF ? 0x7FFFFFFF : int(num_records);

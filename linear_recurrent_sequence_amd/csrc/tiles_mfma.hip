@@ -43,6 +43,7 @@
 // float64 and rounded once, under the causal mask.  C_j, e_j and keyb_J of the
 // tile's keys travel with the tile into LDS.
 #include "mlstm_internal.h"
+#include "scan_common.h"
 #include "tile_common.h"
 
 namespace mlstm {
@@ -53,6 +54,8 @@ using namespace tilecommon;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPf = 3;      // LDS fragment prefetch distance (MFMA steps)
+constexpr int kFusedMaxT = scan::kScanThreads * scan::kScanPer;  // one block scan
+constexpr int kQHalf = kBM / 2 / kWaves;  // Q rows per wave and tile buffer
 
 template <int DP>
 struct Cfg {
@@ -68,7 +71,7 @@ struct Cfg {
   static constexpr int BUF = E_OFF + kBN * 4;
 };
 
-template <int DP>
+template <int DP, bool FUSED>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(1, 1))) void tiles_mfma_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
@@ -77,11 +80,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     const double* __restrict__ rowb,
     const double* __restrict__ keyb, float* __restrict__ n_out, const u16* __restrict__ ogate,
     u16* __restrict__ htilde, float* __restrict__ b_out, int64_t T, int d, int64_t Tp,
-    int64_t row_tiles, int64_t H, int skip) {
+    int64_t row_tiles, int64_t H, int skip, FusedGates fg) {
   using C = Cfg<DP>;
   // two distinct buffers, so the loads into one never alias reads of the other
   __shared__ __attribute__((aligned(1024))) char smem0[C::BUF];
   __shared__ __attribute__((aligned(1024))) char smem1[C::BUF];
+  // FUSED: the gate terms the workgroup reads, from its own scan: e_j of
+  // every key before its last row, C_j of its diagonal keys, keyb of every
+  // 32-key tile, and rowb, R_i and m of its own rows
+  __shared__ __attribute__((aligned(16))) float f_e[FUSED ? kFusedMaxT : 1];
+  __shared__ __attribute__((aligned(16))) double f_cd[FUSED ? kBM : 1];
+  __shared__ double f_kb[FUSED ? kFusedMaxT / kBoundTile : 1];
+  __shared__ double f_rb[FUSED ? kBM / kBoundTile : 1];
+  __shared__ __attribute__((aligned(16))) double f_r[FUSED ? kBM : 1];
+  __shared__ __attribute__((aligned(16))) float f_m[FUSED ? kBM : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -98,14 +110,74 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 
   // Q^T fragments: B operand of S^T = K Q^T, reduction index = head dim.  The
   // workgroup's 128 query rows are staged in the two tile buffers (64 rows
-  // each, one copy per row, overlapping the first-tile search); rows past the
-  // sequence end and padded columns arrive as zeros.  Each wave then reads
-  // its 32 rows' fragments (loading them straight from memory, where each
-  // instruction touches 32 rows, was slower).
+  // each, one copy per row); rows past the sequence end and padded columns
+  // arrive as zeros.  Each wave then reads its 32 rows' fragments (loading
+  // them straight from memory, where each instruction touches 32 rows, was
+  // slower).  Without FUSED the prologue's copies (Q and the first tile) are
+  // the builtin ones, which the compiler sees: it can then issue the gate
+  // terms' loads of the prologue ahead of them (behind copies it cannot see,
+  // those loads would wait for the whole Q block).  With FUSED every copy
+  // goes through inline assembly, so the compiler never sets M0 itself.
   static_assert((kBM / 2) * C::RSK <= C::BUF, "64 staged rows fit in a tile buffer");
   bf16x8 qf[DP / 16];
-  {
-    const unsigned vchunk = lane < dch ? unsigned(16 * lane) : kOutOfRange;
+  const unsigned vchunk = lane < dch ? unsigned(16 * lane) : kOutOfRange;
+  // rows 64 h + kQHalf w + i (i < kQHalf) of the Q block into tile buffer h
+  auto copy_q_half = [&](int h) {
+    char* const dst = h == 0 ? smem0 : smem1;
+#pragma unroll
+    for (int i = 0; i < kQHalf; ++i) {
+      const int r = kQHalf * w + i;
+      const int64_t row = q0 + kBM / 2 * h + r;
+      if (lane < C::CH)
+        copy16(rsrc_words(q + hoff + row * d, row < T ? 2 * d : 0), vchunk,
+               lds_addr(dst + r * C::RSK));
+    }
+  };
+  const int64_t t_eff = T < q0 + kBM ? T : q0 + kBM;
+  // each wave's Q^T fragments from its staged rows (waves 0, 1 in buffer 0)
+  auto read_q_fragments = [&]() {
+    const char* qrow = (w < 2 ? smem0 : smem1) + (32 * (w & 1) + l32) * C::RSK + 16 * g;
+#pragma unroll
+    for (int s = 0; s < DP / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
+  };
+  // the wave's 8 rows of K and of V of tile J (FUSED: inline-assembly copies)
+  const int row_bytes = 2 * d;
+  struct TileSrc { i32x4 k, v; };
+  auto tile_src = [&](int64_t J) {
+    const int64_t r0 = J * kBN + w * (kBN / kWaves);
+    const int64_t left = T - r0;
+    const int64_t nrec =
+        (left < 0 ? 0 : left < kBN / kWaves ? left : kBN / kWaves) * 2 * int64_t(d);
+    return TileSrc{rsrc_words(k + hoff + r0 * d, nrec), rsrc_words(v + hoff + r0 * d, nrec)};
+  };
+  auto row_copy = [&](const TileSrc& ts, char* buf, auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if (lane < C::CH) {
+      if constexpr (i < 8)
+        copy16_row<i & 7, (i & 7) * C::RSK>(ts.k, vchunk, row_bytes,
+                                             lds_addr(buf + w * (kBN / kWaves) * C::RSK));
+      else
+        copy16_row<i & 7, (i & 7) * C::RSV>(
+            ts.v, vchunk, row_bytes, lds_addr(buf + C::K_BYTES + w * (kBN / kWaves) * C::RSV));
+    }
+  };
+  if constexpr (FUSED) {
+    // The gate pre-activations of positions [0, t_eff) go into buffer 1 ahead
+    // of the Q block's first half (buffer 0), so that they are waited for
+    // alone: a wave's loads complete in order.  Lengths are divisible by 4,
+    // so every head's gate row starts 16-byte aligned.
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const unsigned off = unsigned(1024 * (w + kWaves * c) + 16 * lane);
+      copy16(rsrc_words(fg.fgate + head * T, t_eff * 4), off,
+             lds_addr(smem1 + 1024 * (w + kWaves * c)));
+      copy16(rsrc_words(fg.igate + head * T, t_eff * 4), off,
+             lds_addr(smem1 + 4 * kFusedMaxT + 1024 * (w + kWaves * c)));
+    }
+  }
+  if constexpr (FUSED) {
+    copy_q_half(0);
+  } else {
 #pragma unroll 4
     for (int i = 0; i < kBM / kWaves; ++i) {
       const int r = (kBM / kWaves) * w + i;
@@ -115,7 +187,88 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
               (r < kBM / 2 ? smem0 : smem1) + (r % (kBM / 2)) * C::RSK);
     }
   }
-  const double r_i = rowt[head * Tp + qi];  // R_i, qi < Tp
+
+  // ---- FUSED: the scan of the gate-scan kernel (a 512-thread block over
+  // 2048 positions, 4 per thread) over positions [0, q0 + 128), thread tid
+  // running threads tid and tid + 256 of that block, so that the terms are
+  // bitwise the gate-scan kernel's.  The Q block's second half is copied once
+  // the gates have been read.
+  if constexpr (FUSED) {
+    using namespace scan;
+    constexpr int kHalfT = kScanThreads / 2;
+    static_assert(kHalfT == kThreads, "two scan threads per thread");
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(kQHalf));
+    __syncthreads();
+    float fr[2][kScanPer], iv[2][kScanPer];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int vt = tid + kHalfT * u;
+      const int64_t p0 = int64_t(kScanPer) * vt;
+      const float4 f4 = reinterpret_cast<const float4*>(smem1)[vt];
+      const float4 i4 = reinterpret_cast<const float4*>(smem1 + 4 * kFusedMaxT)[vt];
+      const float fa[kScanPer] = {f4.x, f4.y, f4.z, f4.w};
+      const float ia[kScanPer] = {i4.x, i4.y, i4.z, i4.w};
+#pragma unroll
+      for (int e = 0; e < kScanPer; ++e) {  // padding: no forgetting, no input
+        fr[u][e] = p0 + e < t_eff ? fa[e] : 0.0f;
+        iv[u][e] = p0 + e < t_eff ? ia[e] : -INFINITY;
+      }
+    }
+    __syncthreads();  // buffer 1 is refilled below
+    copy_q_half(1);
+    // a scan wave whose positions all lie at or past the workgroup's last
+    // row holds padding only: it skips the logarithms and the per-position
+    // terms, which nothing reads
+    double fb[2][kScanPer] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+    bool active[2];
+    Elem mine[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t p0 = int64_t(kScanPer) * (tid + kHalfT * u);
+      active[u] = kScanPer * 64 * (w + kWaves * u) < q0 + kBM;  // uniform across the wave
+      if (active[u]) to_log_forget(p0, t_eff, fg.exp_forget, fr[u], fb[u]);
+      mine[u] = thread_elem(fb[u], iv[u]);
+    }
+    // the Q block's first half has landed meanwhile (all but the wave's last
+    // kQHalf copies): waves 0, 1 read their Q^T fragments, and the first key
+    // tile is copied into buffer 0 while the scan runs (taken to be tile 0
+    // until the decay bounds say otherwise: a wave's copies land in order, so
+    // a later copy of the same rows is the one that stays)
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(kQHalf));
+    __syncthreads();
+    if (w < 2) read_q_fragments();
+    __syncthreads();
+    {
+      const TileSrc ts0 = tile_src(0);
+      static_for<16>([&](auto ic) { row_copy(ts0, smem0, ic); });
+    }
+    Elem before[2], total;
+    block_scan_halves(mine[0], mine[1], before[0], before[1], total);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t p0 = int64_t(kScanPer) * (tid + kHalfT * u);
+      Terms tm;
+      if (active[u]) position_terms(identity(), before[u], fb[u], iv[u], p0, t_eff, fg.half_ln_d, tm);
+      if (active[u] && p0 < q0 + kBM) {
+        *reinterpret_cast<float4*>(f_e + p0) = make_float4(tm.e[0], tm.e[1], tm.e[2], tm.e[3]);
+        if ((p0 & (kBoundTile - 1)) == 0) f_kb[p0 / kBoundTile] = tm.cmax;
+        if (p0 >= q0) {
+          const int o = int(p0 - q0);
+          *reinterpret_cast<double2*>(f_cd + o) = make_double2(tm.c[0], tm.c[1]);
+          *reinterpret_cast<double2*>(f_cd + o + 2) = make_double2(tm.c[2], tm.c[3]);
+          *reinterpret_cast<double2*>(f_r + o) = make_double2(tm.r[0], tm.r[1]);
+          *reinterpret_cast<double2*>(f_r + o + 2) = make_double2(tm.r[2], tm.r[3]);
+          *reinterpret_cast<float4*>(f_m + o) = make_float4(tm.m[0], tm.m[1], tm.m[2], tm.m[3]);
+          if ((o & (kBoundTile - 1)) == 0) f_rb[o / kBoundTile] = tm.rmax;
+#pragma unroll
+          for (int e = 0; e < kScanPer; ++e)
+            if (p0 + e < T) fg.m_out[head * T + p0 + e] = tm.m[e];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const double r_i = FUSED ? f_r[qi - q0] : rowt[head * Tp + qi];  // R_i, qi < Tp
 
   f32x16 acc[DP / 32];
 #pragma unroll
@@ -132,7 +285,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   // tile some wave needs, and inside the loop each wave skips the products
   // of tiles it does not need.
   const int64_t nb32 = Tp / kBoundTile;
-  const double rb_w = rowb[head * nb32 + qw / kBoundTile];
+  auto row_bound = [&](int64_t r) {  // rowb of the 32-row block of row r (of this workgroup)
+    return FUSED ? f_rb[(r - q0) / kBoundTile] : rowb[head * nb32 + r / kBoundTile];
+  };
+  auto key_bound = [&](int64_t J) {  // keyb of 32-key tile J
+    return FUSED ? f_kb[J] : keyb[head * nb32 + J];
+  };
+  const double rb_w = row_bound(qw);
   auto tile_needed = [&](double rb, double kb) { return rb + kb >= kSkipLog2; };
   int64_t first_tile = 0;
   if (skip) {
@@ -142,12 +301,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 #pragma unroll
     for (int u = 0; u < kWaves; ++u) {
       const int64_t qu = q0 + 32 * u;
-      rb_rows[u] = rowb[head * nb32 + qu / kBoundTile];
+      rb_rows[u] = row_bound(qu);
       last_w[u] = (4 * I + u < n_key_tiles - 1) ? 4 * I + u : n_key_tiles - 1;
     }
     int64_t mine = last_tile;  // the diagonal tile of wave 0 bounds the answer
     for (int64_t J = tid; J < last_tile; J += kThreads) {
-      const double kb = keyb[head * nb32 + J];
+      const double kb = key_bound(J);
       bool need = false;
 #pragma unroll
       for (int u = 0; u < kWaves; ++u)
@@ -169,9 +328,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     for (int u = 1; u < kWaves; ++u) first_tile = s_first[u] < first_tile ? s_first[u] : first_tile;
   }
 
-  // ---- global -> LDS copy of tile J: each wave copies 8 K rows and 8 V rows.
-  // The buffer range ends at the last key of the sequence, so rows past it
-  // arrive as zeros; head-dimension padding reads an out-of-range offset.
+  // ---- global -> LDS copies of tile J: each wave copies 8 K rows and 8 V
+  // rows.  The buffer ranges end at the last key of the sequence, so rows
+  // past it arrive as zeros; head-dimension padding reads an out-of-range
+  // offset.  load_tile (builtin copies) serves the first tile without FUSED.
   auto load_tile = [&](int64_t J, char* buf) {
     const int64_t k0 = J * kBN;
     const int64_t nrec = (T - k0 < kBN ? T - k0 : kBN) * int64_t(d) * 2;
@@ -193,32 +353,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     if (w == 2 && lane < 2)
       dma4(make_rsrc(keyb + head * nb32 + J, 8), unsigned(4 * lane), buf + C::KB_OFF);
   };
-  // the same copies one row at a time, for spreading over the first product:
-  // row copy i (0 <= i < 16) is K row i (i < 8) or V row i - 8 of this
-  // wave's share; the tile's gate terms are copied by gate_copies
-  const unsigned vchunk = lane < dch ? unsigned(16 * lane) : kOutOfRange;
-  const int row_bytes = 2 * d;
-  // the wave's 8 rows of K and of V of tile J: one buffer range each
-  struct TileSrc { i32x4 k, v; };
-  auto tile_src = [&](int64_t J) {
-    const int64_t r0 = J * kBN + w * (kBN / kWaves);
-    const int64_t left = T - r0;
-    const int64_t nrec =
-        (left < 0 ? 0 : left < kBN / kWaves ? left : kBN / kWaves) * 2 * int64_t(d);
-    return TileSrc{rsrc_words(k + hoff + r0 * d, nrec), rsrc_words(v + hoff + r0 * d, nrec)};
-  };
-  auto row_copy = [&](const TileSrc& ts, char* buf, auto ic) {
-    constexpr int i = decltype(ic)::value;
-    if (lane < C::CH) {
-      if constexpr (i < 8)
-        copy16_row<i & 7, (i & 7) * C::RSK>(ts.k, vchunk, row_bytes,
-                                             lds_addr(buf + w * (kBN / kWaves) * C::RSK));
-      else
-        copy16_row<i & 7, (i & 7) * C::RSV>(
-            ts.v, vchunk, row_bytes, lds_addr(buf + C::K_BYTES + w * (kBN / kWaves) * C::RSV));
-    }
-  };
+  // In the loop the same copies go one row at a time (row_copy, above), spread
+  // over the first product: row copy i (0 <= i < 16) is K row i (i < 8) or V
+  // row i - 8 of this wave's share (one buffer range each); the tile's gate
+  // terms are copied by gate_copies (FUSED: held in LDS instead).
   auto gate_copies = [&](int64_t J, char* buf) {
+    if (FUSED) return;
     const int64_t k0 = J * kBN;
     if (w == 0 && lane < kBN / 2)
       copy16(rsrc_words(colt + head * Tp + k0, kBN * 8), unsigned(16 * lane),
@@ -233,7 +373,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   auto wave_needs = [&](const char* buf, int64_t J) {
     if (J > wave_last) return false;
     if (!skip) return true;
-    const double kb = *reinterpret_cast<const double*>(buf + C::KB_OFF);
+    const double kb = FUSED ? f_kb[J] : *reinterpret_cast<const double*>(buf + C::KB_OFF);
     return tile_needed(rb_w, kb);
   };
 
@@ -278,7 +418,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       // the diagonal tile: each entry's own exponential 2^(R_i + C_j) under
       // the causal mask (Eq. 71); the tile's column terms are read together,
       // before any is used
-      const double* cb = reinterpret_cast<const double*>(buf + C::C_OFF);
+      const double* cb =
+          FUSED ? f_cd + (J * kBN - q0) : reinterpret_cast<const double*>(buf + C::C_OFF);
       double2 cd[8];
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
@@ -303,11 +444,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
       // below the diagonal the exponent factors as 2^(R_i + keyb_J) * e_j:
       // one exponential per row and tile; the tile's key factors and bound
       // are read together, before any is used
-      const float* ge = reinterpret_cast<const float*>(buf + C::E_OFF);
+      const float* ge = FUSED ? f_e + J * kBN : reinterpret_cast<const float*>(buf + C::E_OFF);
       float4 e4[4];
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) e4[rq] = *reinterpret_cast<const float4*>(ge + 8 * rq + 4 * g);
-      const double kb = *reinterpret_cast<const double*>(buf + C::KB_OFF);
+      const double kb = FUSED ? f_kb[J] : *reinterpret_cast<const double*>(buf + C::KB_OFF);
       __builtin_amdgcn_sched_barrier(0);
       const float ei = __builtin_amdgcn_exp2f(float(r_i + kb));
 #pragma unroll
@@ -356,21 +497,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
     }
   };
 
-  {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const char* qrow = (w < 2 ? smem0 : smem1) + (32 * (w & 1) + l32) * C::RSK + 16 * g;
-#pragma unroll
-    for (int s = 0; s < DP / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s);
-    __syncthreads();  // the buffers are refilled below
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (!FUSED || w >= 2) read_q_fragments();
+  __syncthreads();  // the buffers are refilled below
+  if constexpr (FUSED) {
+    if (first_tile != 0) {
+      const TileSrc ts = tile_src(first_tile);
+      static_for<16>([&](auto ic) { row_copy(ts, smem0, ic); });
+    }
+  } else {
+    load_tile(first_tile, smem0);
   }
-  load_tile(first_tile, smem0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // No plain global load is issued inside the loop: everything a tile needs
-  // (K, V, C and the key tile's bound) arrives by the copies into LDS, so the
-  // waits on those copies stay exact.
+  // (K, V and its gate terms) arrives by the copies into LDS or is there from
+  // the prologue's scan, so the waits on those copies stay exact.
   // one tile: its first product carries the row copies of the next tile
   auto step = [&](const char* buf, int64_t J, char* nxt) {
     const bool more = J + 1 <= last_tile;
@@ -390,7 +534,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   // output gate H = sigma(O~) (.) h~ (Eq. 78) from the float32 h~ ----
   bsum += __shfl_xor(bsum, 32, 64);
   if (qi < T) {
-    const float nn = fmaxf(fabsf(bsum), expf(-m_in[head * T + qi]));
+    const float nn = fmaxf(fabsf(bsum), expf(-(FUSED ? f_m[qi - q0] : m_in[head * T + qi])));
     if (g == 0) n_out[head * T + qi] = nn;
     if (g == 0 && b_out) b_out[head * T + qi] = bsum;
     const float inv = 1.0f / nn;
@@ -424,17 +568,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   }
 }
 
-template <int DP>
+template <int DP, bool FUSED>
 hipError_t launch_dp(const void* q, const void* k, const void* v, const float* m,
                      const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,
-                     bool skip, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+                     bool skip, int64_t H, int64_t T, int64_t d, const FusedGates& fg,
+                     hipStream_t stream) {
   const int64_t row_tiles = (T + kBM - 1) / kBM;
-  hipLaunchKernelGGL(tiles_mfma_kernel<DP>, dim3(unsigned(row_tiles * H)), dim3(kThreads), 0,
-                     stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                     static_cast<const u16*>(v), m, ws.rowt, ws.colt, ws.colx,
-                     static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
+  hipLaunchKernelGGL((tiles_mfma_kernel<DP, FUSED>), dim3(unsigned(row_tiles * H)),
+                     dim3(kThreads), 0, stream, static_cast<const u16*>(q),
+                     static_cast<const u16*>(k), static_cast<const u16*>(v), m, ws.rowt, ws.colt,
+                     ws.colx, static_cast<u16*>(h_out), ws.rowb, ws.keyb, n_out,
                      static_cast<const u16*>(ep.ogate), static_cast<u16*>(ep.htilde), ep.b, T,
-                     int(d), ws.Tp, row_tiles, H, int(skip));
+                     int(d), ws.Tp, row_tiles, H, int(skip), fg);
   return hipGetLastError();
 }
 
@@ -444,26 +589,58 @@ hipError_t launch_tiles_mfma(const void* q, const void* k, const void* v, const 
                              const Workspace& ws, void* h_out, float* n_out,
                              const Epilogue& ep, bool skip, int64_t H, int64_t T,
                              int64_t d, hipStream_t stream) {
+  const FusedGates none{};
+#define MLSTM_DP(n) launch_dp<32 * n, false>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, none, stream)
   // head dims are padded up to a multiple of 32 (zero columns add nothing)
   switch ((d + 31) / 32) {
-    case 1: return launch_dp<32>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 2: return launch_dp<64>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 3: return launch_dp<96>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 4: return launch_dp<128>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 5: return launch_dp<160>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 6: return launch_dp<192>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 7: return launch_dp<224>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 8: return launch_dp<256>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 9: return launch_dp<288>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 10: return launch_dp<320>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 11: return launch_dp<352>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 12: return launch_dp<384>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 13: return launch_dp<416>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 14: return launch_dp<448>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 15: return launch_dp<480>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
-    case 16: return launch_dp<512>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, stream);
+    case 1: return MLSTM_DP(1);
+    case 2: return MLSTM_DP(2);
+    case 3: return MLSTM_DP(3);
+    case 4: return MLSTM_DP(4);
+    case 5: return MLSTM_DP(5);
+    case 6: return MLSTM_DP(6);
+    case 7: return MLSTM_DP(7);
+    case 8: return MLSTM_DP(8);
+    case 9: return MLSTM_DP(9);
+    case 10: return MLSTM_DP(10);
+    case 11: return MLSTM_DP(11);
+    case 12: return MLSTM_DP(12);
+    case 13: return MLSTM_DP(13);
+    case 14: return MLSTM_DP(14);
+    case 15: return MLSTM_DP(15);
+    case 16: return MLSTM_DP(16);
     default: return hipErrorInvalidValue;
   }
+#undef MLSTM_DP
+}
+
+bool tiles_mfma_fused_supports(int64_t T, int64_t d) {
+  return d > 384 && d <= 512 && d % 16 == 0 && T >= 1 && T <= kFusedMaxT && T % 4 == 0;
+}
+
+hipError_t launch_tiles_mfma_fused(const void* q, const void* k, const void* v,
+                                   const float* igate, const float* fgate, void* h_out,
+                                   float* m_out, float* n_out, const Epilogue& ep,
+                                   bool exp_forget, int64_t H, int64_t T, int64_t d,
+                                   hipStream_t stream) {
+  if (!tiles_mfma_fused_supports(T, d)) return hipErrorInvalidValue;
+  Workspace none{};
+  none.Tp = padded_len(T);
+  FusedGates fg;
+  fg.igate = igate;
+  fg.fgate = fgate;
+  fg.m_out = m_out;
+  fg.half_ln_d = 0.5 * log(double(d));
+  fg.exp_forget = int(exp_forget);
+#define MLSTM_DP(n) launch_dp<32 * n, true>(q, k, v, nullptr, none, h_out, n_out, ep, true, H, T, d, fg, stream)
+  switch ((d + 31) / 32) {
+    case 13: return MLSTM_DP(13);
+    case 14: return MLSTM_DP(14);
+    case 15: return MLSTM_DP(15);
+    case 16: return MLSTM_DP(16);
+    default: return hipErrorInvalidValue;
+  }
+#undef MLSTM_DP
 }
 
 }  // namespace mlstm

@@ -65,10 +65,7 @@ constexpr int kSK = 64;   // keys per super-step (two 32-key tiles)
 constexpr int kWPf = 3;   // LDS fragment prefetch distance (MFMA steps)
 constexpr int kFusedMaxT = 2048;  // longest sequence of the fused gate scan (one scan chunk)
 constexpr int kQCopies = 16;      // row copies per wave of the workgroup's Q block
-// s_waitcnt operand: vmcnt(kQCopies) (bits 3:0 and 15:14), no wait on expcnt
-// (bits 6:4) or lgkmcnt (bits 11:8)
-constexpr int kWaitAllButQCopies =
-    (kQCopies & 15) | ((kQCopies >> 4) << 14) | (7 << 4) | (15 << 8);
+constexpr int kWaitAllButQCopies = wait_vmcnt(kQCopies);
 static_assert(kFusedMaxT == scan::kScanThreads * scan::kScanPer, "one block scan");
 
 // LDS layout: rows are padded so that the fragment reads are free of bank
@@ -108,16 +105,6 @@ struct WCfg {
   static constexpr int BYTES = FUSED ? F_M + kBM * 4 : X_OFF + kWWaves * 2048;
   static_assert(2 * kSK * RSK <= GC, "the staged Q block fits in the K and V regions");
   static_assert(BYTES <= 160 * 1024, "LDS budget");
-};
-
-// Gate inputs of the fused variant (FUSED): the pre-activations, the forget
-// activation, ln(d)/2, and the m output of the workgroup's rows.
-struct FusedGates {
-  const float* igate;
-  const float* fgate;
-  float* m_out;
-  double half_ln_d;
-  int exp_forget;
 };
 
 template <int DP, bool FUSED>

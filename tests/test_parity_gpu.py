@@ -401,18 +401,23 @@ FUSED_CASES = [
     spec(1, 1, 1, 16), spec(1, 2, 63, 48),  # lengths not divisible by 4: the two stages
     spec(1, 2, 2048, 64, ig=("uniform", -20, 20), fg=("normal", 0, 4), fgate_floor=(0.01, -30.0)),
     spec(1, 2, 1500, 128, ig=("uniform", -40, 40), fg=("normal", -2, 3)),
+    # 384 < d <= 512: the one-wave kernel with its own scan
+    spec(1, 1, 4, 400), spec(2, 1, 132, 416), spec(1, 2, 1000, 448), spec(2, 2, 2048, 512),
+    spec(1, 1, 260, 512, ig=("normal", 0, 2), fg=("normal", 3, 1.5)),
+    spec(1, 2, 2048, 480, ig=("uniform", -20, 20), fg=("normal", 0, 4), fgate_floor=(0.01, -30.0)),
+    spec(1, 1, 63, 512),  # a length not divisible by 4: the two stages
 ]
 
 
 @pytest.mark.parametrize("forget", ["sigmoid", "exp"])
 @pytest.mark.parametrize("s", FUSED_CASES, ids=_id)
 def test_fused_scan_equals_the_two_stage_pass_bitwise(s, forget):
-    """Up to 2048 positions (bf16, head dim up to 384, length divisible by 4)
+    """Up to 2048 positions (bf16, head dim up to 512, length divisible by 4)
     the one-shot entry points run a single tile kernel that scans the gates in
-    its prologue; the
-    scan there has the gate-scan kernel's block structure, so h, m and n must
-    be the bits of the two-stage pass (gate scan, then the same tile kernel
-    on the workspace)."""
+    its prologue.  The scan there has the gate-scan kernel's block structure
+    (run by 256 threads, two scan threads each, in the one-wave kernel above
+    d = 384), so h, m and n must be the bits of the two-stage pass (gate scan,
+    then the same tile kernel on the workspace)."""
     x = W.make(s, seed=71)
     if forget == "exp":  # log f = f~, small and negative
         x["fgate"] = (-0.02 * np.abs(x["fgate"])).astype(np.float32)
