@@ -533,11 +533,49 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
   // ---- epilogue: n (Eq. 84), h~ = acc / n (Eqs. 85, 86), and with an
   // output gate H = sigma(O~) (.) h~ (Eq. 78) from the float32 h~ ----
   bsum += __shfl_xor(bsum, 32, 64);
-  if (qi < T) {
-    const float nn = fmaxf(fabsf(bsum), expf(-(FUSED ? f_m[qi - q0] : m_in[head * T + qi])));
-    if (g == 0) n_out[head * T + qi] = nn;
-    if (g == 0 && b_out) b_out[head * T + qi] = bsum;
-    const float inv = 1.0f / nn;
+  const float m_q = qi < T ? (FUSED ? f_m[qi - q0] : m_in[head * T + qi]) : 0.0f;
+  const float nn = fmaxf(fabsf(bsum), expf(-m_q));
+  const float inv = 1.0f / nn;
+  if (qi < T && g == 0) {
+    n_out[head * T + qi] = nn;
+    if (b_out) b_out[head * T + qi] = bsum;
+  }
+  if (ogate == nullptr && htilde == nullptr) {
+    // bf16(h~) goes through LDS (the tile buffers are free now): the block's
+    // rows at the K rows' padded stride, rows 0..63 in buffer 0 and 64..127
+    // in buffer 1, columns in order; then the block's rows, contiguous in
+    // memory, are stored 1 KiB per instruction.  Rows past the sequence end
+    // fall outside the buffer range and are not written.
+    char* const obuf = (w < 2 ? smem0 : smem1) + (32 * (w & 1) + l32) * C::RSK;
+#pragma unroll
+    for (int b = 0; b < DP / 32; ++b) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int col = 32 * b + 8 * rq + 4 * g;
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[b][4 * rq + e] * inv);
+        *reinterpret_cast<bf16x4*>(obuf + 2 * col) = o;
+      }
+    }
+    __syncthreads();
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const int64_t rows = T - q0 < kBM ? T - q0 : kBM;
+    const auto rh = make_rsrc(h_out + hoff + q0 * d, rows * d * 2);
+    const int nstore = d / 4;  // 1 KiB stores of the 128 x d block
+#pragma unroll
+    for (int u = 0; u < (DP / 4 + kWaves - 1) / kWaves; ++u) {
+      const int n = w + kWaves * u;
+      if (n < nstore) {
+        const int gb = 1024 * n + 16 * lane;
+        const int r = gb / row_bytes;
+        const int c = (gb - r * row_bytes) >> 4;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(
+            (r < kBM / 2 ? smem0 : smem1) + (r % (kBM / 2)) * C::RSK + 16 * c);
+        __builtin_amdgcn_raw_buffer_store_b128(val, rh, gb, 0, 0);
+      }
+    }
+  } else if (qi < T) {
     const int64_t row = hoff + qi * d;
 #pragma unroll
     for (int b = 0; b < DP / 32; ++b) {
