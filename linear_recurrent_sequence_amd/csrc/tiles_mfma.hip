@@ -42,6 +42,15 @@
 // diagonal tile each entry takes its own exponential of R_i + C_j, summed in
 // float64 and rounded once, under the causal mask.  C_j, e_j and keyb_J of the
 // tile's keys travel with the tile into LDS.
+//
+// Fused gate scan (FUSED: 384 < d <= 512, at most 2048 positions, a multiple
+// of 4).  Each workgroup scans its head's gates from position 0 to its last
+// row in its prologue, as the gate-scan kernel does (its 512-thread block
+// scan run by these 256 threads, two scan threads each, in the same order,
+// so the terms are bitwise the same), and keeps in LDS what it reads later:
+// e_j of every key before its last row, C_j of its 128 diagonal keys, the key
+// tiles' bounds, and R_i, the row bounds and m of its own rows.  The whole
+// forward pass is then one launch with no workspace.
 #include "mlstm_internal.h"
 #include "scan_common.h"
 #include "tile_common.h"
