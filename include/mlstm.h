@@ -273,12 +273,14 @@ int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v,
  * on the vector ALUs (above d = 512 in head-dimension chunks, a correctness
  * path far slower than the matrix cores).  Results are bitwise
  * reproducible.  The library allocates a stream-ordered workspace: per-row
- * terms and, for bf16 on the matrix cores, the bf16 operand of the dV
- * product, 8 KiB per head, 128-key block and 32-query tile of the causal
- * triangle (142 MB for 32 heads of 2048), which the key pass stores so that
- * the dV pass need not recompute S; above 2 GiB (or the byte count in the
- * environment variable MLSTM_BWD_STORE_MAX, read at each call) the dV pass
- * recomputes it instead (bitwise the same dV).
+ * terms and, for bf16 on the matrix cores, the bf16 operands of the dV and
+ * dQ products, which the key pass stores so that the dV and dQ passes need
+ * not recompute S and G: 8 KiB per head, 128-key block and 32-query tile of
+ * the causal triangle for dV, 2 KiB per head and pair of 32-row tiles for dQ
+ * (278 MB for 32 heads of 2048).  Above 2 GiB (or the byte count in the
+ * environment variable MLSTM_BWD_STORE_MAX, read at each call) those passes
+ * recompute them instead: dV is then bitwise the same, dQ, dK and the gate
+ * gradients equal up to float32 rounding order.
  * Pointers 16-byte aligned; no output may alias an input.  Any d of the
  * forward pass (a multiple of 16 up to 1024).  Errors as for
  * mlstm_parallel_fwd.

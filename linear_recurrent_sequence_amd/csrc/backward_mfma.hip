@@ -22,12 +22,16 @@
 //   values pass (own = keys j, tiles of queries i):
 //     S = Q_I K^T;  dV^T += dH_I^T bf16(s_ij E_ij / n_i)     (Eq. 100)
 //
-// The values pass needs the S and E of the keys pass, on the same (key block,
-// query tile) pairs, so by default the keys pass stores the operand
-// bf16(s_ij E_ij / n_i) in the layout of the values pass's B fragments and
-// the values pass (kValuesStored) only reads it: dV is bitwise the same.  The
-// own rows' fragments are staged through LDS (one copy per row) before the
-// tile loop.  In the passes with first products, a wave's 16 row copies of
+// The values and rows passes need the S, G and E of the keys pass, so by
+// default the keys pass stores the operands bf16(s_ij E_ij / n_i) (in the
+// layout of the values pass's B fragments) and bf16(P) (key-major 32 x 32
+// blocks, which the rows pass reads transposed), and those passes
+// (kValuesStored, kRowsStored) only accumulate: dV is bitwise that of the
+// recomputing pass, dQ equal up to the float32 rounding order of S and G.  A
+// per-row kernel then forms 1/n_i, db_i and the row sums r_i of dD~ first
+// (the keys pass reads 1/n and db); r_i from its closed form
+// dh_i . h~_i + db_i b_i.  The own rows' fragments are staged through LDS (one
+// copy per row) before the tile loop.  In the passes with first products, a wave's 16 row copies of
 // the next tile are spread over the matrix instructions of its first
 // products (a copy holds its wave at issue, and with one wave per SIMD that
 // would idle the matrix core); those products therefore run on every tile,
@@ -39,9 +43,9 @@
 // ds_read_b64_tr_b16, in the key order of the accumulator layout.  The sums
 // r and c add float32 products of float32 values (no bf16 rounding); dQ, dK
 // and dV carry the bf16 rounding of P, as the forward's h~ carries that of
-// C~'.  The rows pass also forms the per-row scalars 1/n_i and db_i
-// (Eqs. 88-90, from dh_i . h~_i) for its own rows and stores them for the two
-// key passes.  The rows and keys passes hold two sets of own fragments and d / 2
+// C~'.  When it recomputes S, the rows pass also forms the per-row scalars
+// 1/n_i and db_i (Eqs. 88-90, from dh_i . h~_i) for its own rows and stores
+// them for the two key passes.  The rows and keys passes hold two sets of own fragments and d / 2
 // accumulator registers; above d = 384 that exceeds a wave's 512 registers,
 // so there each of those passes is split over two workgroups per row block
 // that recompute S and G and accumulate one half of the output columns each.
@@ -57,9 +61,9 @@ constexpr int kBThreads = 256;  // 4 waves, one per SIMD
 constexpr int kBWaves = kBThreads / 64;
 constexpr int kBPf = 2;         // LDS fragment prefetch distance (MFMA steps)
 
-// kValuesStored: the values pass on the operand bf16(C~'/n) that the keys pass
-// stored (no first product)
-enum { kRowsPass = 0, kKeysPass = 1, kValuesPass = 2, kValuesStored = 3 };
+// kValuesStored / kRowsStored: the values / rows pass on the operand that the
+// keys pass stored, bf16(C~'/n) / bf16(P) (no first products)
+enum { kRowsPass = 0, kKeysPass = 1, kValuesPass = 2, kValuesStored = 3, kRowsStored = 4 };
 
 // LDS layout of one buffer.  X1 is the tensor of the first product (K in the
 // rows pass, Q otherwise), X2 that of the second product (V, dH) or, in the
@@ -72,11 +76,13 @@ template <int DP, int MODE>
 struct BCfg {
   static_assert(DP % 64 == 0 && DP >= 64 && DP <= 512, "head dim of the matrix-core backward");
   static constexpr bool VAL = MODE == kValuesPass || MODE == kValuesStored;
+  static constexpr bool RST = MODE == kRowsStored;
   // output-column halves per row block (see the notes above)
-  static constexpr int SPLIT = (!VAL && DP > 384) ? 2 : 1;
+  static constexpr int SPLIT = (!VAL && !RST && DP > 384) ? 2 : 1;
   static constexpr int NB = DP / 32 / SPLIT;  // 32-column accumulator blocks per wave
   static constexpr int CH = DP / 8;  // 16-byte chunks per row
-  static constexpr int S1 = VAL ? 2 * DP + 16 : 2 * DP + 32;
+  // X1 of the stored rows pass (K) is read only transposed
+  static constexpr int S1 = RST ? 2 * DP + 64 : VAL ? 2 * DP + 16 : 2 * DP + 32;
   static constexpr int S2 = VAL ? 2 * DP + 64 : 2 * DP + 16;
   static constexpr int X1_OFF = 0;
   static constexpr int X2_OFF = MODE == kValuesStored ? 0 : kBN * S1;  // only dH: no X1
@@ -88,7 +94,10 @@ struct BCfg {
   // (tile J at 0, tile J + 1 at GT), so it waits and synchronises once per
   // 64 queries: its 24 matrix instructions per tile do not cover a load's
   // latency
-  static constexpr int BUF = MODE == kValuesStored ? 2 * GT : GEND;
+  // the stored rows pass: K rows, then bf16(P) of the workgroup's 4 query
+  // tiles against the key tile (8 KiB)
+  static constexpr int P_OFF = kBN * S1;
+  static constexpr int BUF = MODE == kValuesStored ? 2 * GT : RST ? P_OFF + 8192 : GEND;
   static constexpr int SA = VAL ? S2 : S1;          // transposed operand's stride
   static constexpr int A_OFF = VAL ? X2_OFF : X1_OFF;
   static_assert(2 * BUF <= 160 * 1024, "LDS budget");
@@ -104,6 +113,56 @@ __host__ __device__ inline int64_t store_tiles(int64_t T) {  // tiles of one hea
   return rt * nt - 2 * rt * (rt - 1);  // sum over I < rt of (nt - 4 I)
 }
 
+// The stored bf16(P) for the rows pass: for each head, key tile jk and query
+// tile j >= jk, a 2 KiB block of the 32 keys' 64-byte rows, blocks in the
+// order (jk, j) with j innermost.  Row r (key 32 jk + r) holds the tile's 32
+// queries in the order of the keys pass's fragments: position p = 16 c + 8 g + i
+// holds query q_of(p) = 16 c + 4 g + i + 4 (i / 4), so that each lane of the
+// keys pass stores 16 contiguous bytes per fragment.
+__host__ __device__ inline int64_t p_blocks(int64_t T) {  // blocks of one head
+  const int64_t nt = (T + kBN - 1) / kBN;
+  return nt * (nt + 1) / 2;
+}
+__device__ inline int64_t p_block(int64_t nt, int64_t jk, int64_t j) {
+  return jk * nt - jk * (jk - 1) / 2 + (j - jk);
+}
+__device__ inline int q_of(int p) {
+  return (p & ~15) + 4 * ((p >> 3) & 1) + (p & 7) + 4 * ((p >> 2) & 1);
+}
+
+// Per-row scalars of the stored-operand backward, one wave per row: 1/n_i;
+// db_i = sign(b_i) dn_i with dn_i = -(dh_i . h~_i) / n_i where |b_i| is above
+// the floor exp(-m_i), else 0 (Eqs. 88-90); and the row sum of dD~ (Eq. 95),
+// r_i = sum_j C~'_ij dC~'_ij = dh_i . h~_i + db_i b_i, which follows from
+// dC~'_ij = (dh_i . v_j) / n_i + db_i and sum_j C~'_ij v_j = n_i h~_i (Eqs. 83,
+// 86).  (The rows pass that recomputes S forms these itself.)
+__global__ __launch_bounds__(256) void bwd_prep_kernel(
+    const u16* __restrict__ h, const u16* __restrict__ dh, const float* __restrict__ m,
+    const float* __restrict__ n, const float* __restrict__ b, float* __restrict__ inv_n,
+    float* __restrict__ db, float* __restrict__ rsum, int64_t rows, int d) {
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float acc = 0.0f;
+  for (int c = 8 * lane; c < d; c += 512) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(dh + row * d + c);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(h + row * d + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += float(x[e]) * float(y[e]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) {
+    const float nn = n[row], bb = b[row];
+    const float dn = -acc / nn;
+    const bool above_floor = fabsf(bb) > expf(-m[row]);
+    const float dbv = above_floor ? (bb > 0.0f ? dn : (bb < 0.0f ? -dn : 0.0f)) : 0.0f;
+    inv_n[row] = 1.0f / nn;
+    db[row] = dbv;
+    rsum[row] = acc + dbv * bb;
+  }
+}
+
 // STORE (keys pass only): also store the values pass's operand.  Above
 // d = 384 both workgroups of a row block store the same bytes (they compute
 // the same S and E); a branch on the workgroup would cost the keys pass
@@ -116,10 +175,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     const float* __restrict__ n_in, const float* __restrict__ b_in, float* __restrict__ inv_n,
     float* __restrict__ db, const double* __restrict__ rowt, const double* __restrict__ colt,
     u16* __restrict__ out, float* __restrict__ sums, int T, int d, int Tp, int row_tiles, int H,
-    u16* __restrict__ vstore, int64_t tri) {
+    u16* __restrict__ vstore, int64_t tri, u16* __restrict__ pstore, int64_t ptri) {
   using C = BCfg<DP, MODE>;
   constexpr bool kTwo = MODE == kRowsPass || MODE == kKeysPass;  // a second first product (G)
-  constexpr bool kFirst = MODE != kValuesStored;                  // first products at all
+  constexpr bool kFirst = MODE != kValuesStored && MODE != kRowsStored;  // first products at all
+  constexpr bool kRows = MODE == kRowsPass || MODE == kRowsStored;   // own rows are queries
   constexpr int NS = DP / 16;                 // MFMA steps of a first-stage product
   constexpr int NV = 2 * C::NB;               // MFMA steps of the accumulation
   const int cb0 = C::NB * int(blockIdx.y);    // first 32-column block of this workgroup
@@ -142,7 +202,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   map_tile(blockIdx.x, row_tiles, H, I64, head64);
   // heaviest blocks first: the last query blocks for the rows pass, the first
   // key blocks for the key passes
-  const int I = MODE == kRowsPass ? int(I64) : row_tiles - 1 - int(I64);
+  const int I = kRows ? int(I64) : row_tiles - 1 - int(I64);
   const int head = int(head64);
   const int64_t hoff = int64_t(head) * T * d;
   const int ow = I * kBM + 32 * w;  // first own row of this wave
@@ -152,7 +212,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
 
   const u16* own1 = MODE == kRowsPass ? q : k;
   const u16* own2 = MODE == kRowsPass ? dh : v;
-  const u16* x1 = MODE == kRowsPass ? k : q;
+  const u16* x1 = kRows ? k : q;
   const u16* x2 = MODE == kRowsPass ? v : dh;
 
   // own fragments (B operands): row oi, head dims 16 s + 8 g + 0..7; rows past
@@ -188,8 +248,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
 
   // own gate terms: R_i, 1/n_i, db_i (rows pass) or C_j (key passes; -inf past
   // the sequence end)
-  const double own_t =
-      MODE == kRowsPass ? rowt[int64_t(head) * Tp + oi] : colt[int64_t(head) * Tp + oi];
+  const double own_t = !kFirst ? 0.0
+                      : MODE == kRowsPass ? rowt[int64_t(head) * Tp + oi]
+                                          : colt[int64_t(head) * Tp + oi];
   float own_in = 0.0f, own_db = 0.0f;
   if (MODE == kRowsPass) {
     // dn_i = -(dh_i . h~_i) / n_i (Eqs. 88-89); db_i = sign(b_i) dn_i where
@@ -233,9 +294,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   // tiles of the other axis: keys 0 .. the diagonal (rows pass) or queries
   // from the diagonal to the end (key passes); per wave, the tiles that hold
   // some causal pair with its own rows
-  const int first = MODE == kRowsPass ? 0 : 4 * I;
-  const int last = MODE == kRowsPass ? (4 * I + 3 < n_tiles - 1 ? 4 * I + 3 : n_tiles - 1) : n_tiles - 1;
-  auto wave_needs = [&](int J) { return MODE == kRowsPass ? J <= 4 * I + w : J >= 4 * I + w; };
+  const int first = kRows ? 0 : 4 * I;
+  const int last = kRows ? (4 * I + 3 < n_tiles - 1 ? 4 * I + 3 : n_tiles - 1) : n_tiles - 1;
+  auto wave_needs = [&](int J) { return kRows ? J <= 4 * I + w : J >= 4 * I + w; };
 
   auto load_tile = [&](int J, char* buf) {
     const int x0 = J * kBN;
@@ -248,9 +309,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       const int r = w * (kBN / kBWaves) + i;
       if (lane < C::CH) {
         const unsigned off = lane < dch ? unsigned(r * d * 2 + 16 * lane) : kOutOfRange;
-        if (kFirst) dma16(r1, off, buf + C::X1_OFF + r * C::S1);
-        dma16(r2, off, buf + C::X2_OFF + r * C::S2);
+        if (kFirst || MODE == kRowsStored) dma16(r1, off, buf + C::X1_OFF + r * C::S1);
+        if (MODE != kRowsStored) dma16(r2, off, buf + C::X2_OFF + r * C::S2);
       }
+    }
+    if constexpr (MODE == kRowsStored) {
+      // bf16(P) of key tile J against the query tiles 4 I .. 4 I + 3 (8 KiB,
+      // contiguous; blocks the waves do not need, and blocks past the head's
+      // last one, arrive as whatever precedes them, resp. zeros)
+      const auto rp = make_rsrc(pstore + int64_t(head) * ptri * 1024, ptri * 2048);
+      const unsigned base = unsigned(p_block(n_tiles, J, 4 * I) * 2048);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dma16(rp, base + unsigned(1024 * (2 * w + i) + 16 * lane),
+              buf + C::P_OFF + 1024 * (2 * w + i));
     }
     if (!kFirst) return;
     const double* tsrc = MODE == kRowsPass ? colt : rowt;
@@ -332,6 +404,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     if constexpr (MODE == kValuesStored) {
       pb[0] = pin[0];
       pb[1] = pin[1];
+    } else if constexpr (MODE == kRowsStored) {
+      // the B fragments P^T[keys][query q_of(l32)] from this wave's block of
+      // the stored tile, read transposed like the accumulation's A operand
+      // (the lane's accumulator column is query q_of(l32) of the wave)
+      const char* pp = buf + C::P_OFF + 2048 * w + (4 * g + (j16 >> 2)) * 64 + 32 * (l32 >> 4) +
+                       8 * (j16 & 3);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const i16x4 lo = tr_read(pp + 16 * c * 64);
+        const i16x4 hi = tr_read(pp + 16 * c * 64 + 8 * 64);
+        pb[c] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
     } else {
     // first products: Y1 = X1_J Own1^T (and Y2 = X2_J Own2^T)
     f32x16 y1 = f32x16{}, y2 = f32x16{};
@@ -425,6 +509,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       char* dst = reinterpret_cast<char*>(vstore) + slot(J);
       *reinterpret_cast<bf16x8*>(dst + 16 * lane) = vb[0];
       *reinterpret_cast<bf16x8*>(dst + 1024 + 16 * lane) = vb[1];
+      // bf16(P) into block (key tile 4 I + w, query tile J): row l32 (own
+      // key), fragment c at positions 16 c + 8 g .. + 7
+      char* pd = reinterpret_cast<char*>(pstore) +
+                 (int64_t(head) * ptri + p_block(n_tiles, 4 * I + w, J)) * 2048 + 64 * l32 + 16 * g;
+      *reinterpret_cast<bf16x8*>(pd) = pb[0];
+      *reinterpret_cast<bf16x8*>(pd + 32) = pb[1];
     }
     }
     // accumulation: step t = (column block b, half c of the tile's rows); the
@@ -517,6 +607,23 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       pin1[0] = pnext1[0];
       pin1[1] = pnext1[1];
     }
+  } else if constexpr (MODE == kRowsStored) {
+    // one tile per buffer: K rows and the stored P blocks of tile J + 1 land
+    // while tile J is accumulated
+    load_tile(first, smem0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int J = first; J <= last; J += 2) {
+      if (J + 1 <= last) load_tile(J + 1, smem1);
+      if (wave_needs(J)) compute(smem0, J, pin, nullptr, false, TileSrc{}, true);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (J + 1 > last) break;
+      if (J + 2 <= last) load_tile(J + 2, smem0);
+      if (wave_needs(J + 1)) compute(smem1, J + 1, pin, nullptr, false, TileSrc{}, true);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   } else {
   load_tile(first, smem0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -541,8 +648,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
     dsum += __shfl_xor(dsum, 32, 64);
     if (oi < T && g == 0 && blockIdx.y == 0) sums[int64_t(head) * T + oi] = dsum;
   }
-  if (oi < T) {
-    const int64_t row = hoff + int64_t(oi) * d;
+  // the output row of the lane's accumulator column (the stored rows pass
+  // holds the wave's queries in the stored blocks' order)
+  const int orow = MODE == kRowsStored ? ow + q_of(l32) : oi;
+  if (orow < T) {
+    const int64_t row = hoff + int64_t(orow) * d;
 #pragma unroll
     for (int b = 0; b < C::NB; ++b) {
 #pragma unroll
@@ -562,32 +672,43 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
 template <int DP, int MODE, bool STORE = false>
 void launch_pass(const void* q, const void* k, const void* v, const void* dh, const void* h,
                  const float* m, const float* n, const float* b, float* inv_n, float* db,
-                 const Workspace& ws, void* out, float* sums, void* vstore, int64_t H, int64_t T,
+                 const Workspace& ws, void* out, float* sums, void* store, int64_t H, int64_t T,
                  int64_t d, hipStream_t stream) {
   const int64_t row_tiles = (T + kBM - 1) / kBM;
-  static_assert(!STORE || MODE == kKeysPass, "only the keys pass stores the dV operand");
+  static_assert(!STORE || MODE == kKeysPass, "only the keys pass stores operands");
+  // the store holds the values pass's operand, then the rows pass's
+  u16* vstore = static_cast<u16*>(store);
+  u16* pstore = store ? vstore + H * store_tiles(T) * kBWaves * 1024 : nullptr;
   hipLaunchKernelGGL((bwd_mfma_kernel<DP, MODE, STORE>),
                      dim3(unsigned(row_tiles * H), unsigned(BCfg<DP, MODE>::SPLIT)), dim3(kBThreads),
                      0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                      static_cast<const u16*>(v), static_cast<const u16*>(dh),
                      static_cast<const u16*>(h), m, n, b, inv_n, db, ws.rowt, ws.colt,
                      static_cast<u16*>(out), sums, int(T), int(d), int(ws.Tp), int(row_tiles),
-                     int(H), static_cast<u16*>(vstore), store_tiles(T));
+                     int(H), vstore, store_tiles(T), pstore, p_blocks(T));
 }
 
 template <int DP>
 void launch_all(const void* q, const void* k, const void* v, const void* dh, const void* h,
                 const float* m, const float* n, const float* b, float* inv_n, float* db,
                 const Workspace& ws, void* dq, void* dk, void* dv, float* rsum, float* csum,
-                void* vstore, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
-  launch_pass<DP, kRowsPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, rsum, nullptr, H, T, d,
-                             stream);
-  if (vstore != nullptr) {
-    launch_pass<DP, kKeysPass, true>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dk, csum, vstore, H,
+                void* store, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+  if (store != nullptr) {
+    // the per-row scalars first; the keys pass forms S and G once and stores
+    // the operands of the values and rows passes, which only accumulate
+    const int64_t rows = H * T;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, stream,
+                       static_cast<const u16*>(h), static_cast<const u16*>(dh), m, n, b, inv_n, db,
+                       rsum, rows, int(d));
+    launch_pass<DP, kKeysPass, true>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dk, csum, store, H,
                                      T, d, stream);
-    launch_pass<DP, kValuesStored>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dv, nullptr, vstore, H,
+    launch_pass<DP, kValuesStored>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dv, nullptr, store, H,
                                    T, d, stream);
+    launch_pass<DP, kRowsStored>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, nullptr, store, H,
+                                 T, d, stream);
   } else {
+    launch_pass<DP, kRowsPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq, rsum, nullptr, H, T, d,
+                               stream);
     launch_pass<DP, kKeysPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dk, csum, nullptr, H, T, d,
                                stream);
     launch_pass<DP, kValuesPass>(q, k, v, dh, h, m, n, b, inv_n, db, ws, dv, nullptr, nullptr, H,
@@ -600,7 +721,7 @@ void launch_all(const void* q, const void* k, const void* v, const void* dh, con
 bool backward_mfma_supports(int64_t d) { return d % 16 == 0 && d >= 16 && d <= 512; }
 
 size_t backward_mfma_store_bytes(int64_t H, int64_t T) {
-  return size_t(H) * size_t(store_tiles(T)) * kBWaves * 2048;
+  return size_t(H) * (size_t(store_tiles(T)) * kBWaves + size_t(p_blocks(T))) * 2048;
 }
 
 hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* v,
