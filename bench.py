@@ -398,15 +398,16 @@ def backward_timing(torch, mlstm, workloads, x, dev, reps=20):
     ms = e0.elapsed_time(e1) / reps
     cf = workloads.counted_flops(B, NH, T, d)  # two causal contractions
     counted = 2.5 * cf  # five causal contractions: S, dh v^T, dQ, dK, dV
-    # executed: the matrix-core passes form S in the dQ and dK passes and
-    # dh v^T in both (7 contractions; 11 above d = 384, where those two passes
-    # split the output columns over two workgroups); the dV pass reads the
-    # operand the dK pass stored.  The vector passes recompute S and dh v^T
-    # once (7)
-    executed = ((3.5 if d <= 384 else 5.5) if mfma else 3.5) * cf
+    # executed: on the matrix cores the keys pass alone forms S and dh v^T and
+    # stores the operands of the dV and dQ passes, which only accumulate (5
+    # contractions; 7 above d = 384, where the keys pass splits the output
+    # columns over two workgroups that both form S and dh v^T).  The vector
+    # passes recompute S and dh v^T once (7)
+    executed = ((2.5 if d <= 384 else 3.5) if mfma else 3.5) * cf
     peak = PEAK_BF16_TFLOPS if mfma else 157.3
     return {"ms_per_call": round(ms, 4), "reps": reps,
-            "kernels": "bf16 matrix-core passes (dQ and r; dK, c and the stored dV operand; dV)" if mfma
+            "kernels": "bf16 matrix-core passes (per-row scalars; dK, c and the stored dV and dQ "
+                       "operands; dV; dQ)" if mfma
                        else "float32 vector passes",
             "counted_flops": counted,
             "counted_TFLOP/s": round(counted / (ms * 1e-3) / 1e12, 2),
