@@ -95,9 +95,13 @@ struct BCfg {
   // 64 queries: its 24 matrix instructions per tile do not cover a load's
   // latency
   // the stored rows pass: K rows, then bf16(P) of the workgroup's 4 query
-  // tiles against the key tile (8 KiB)
+  // tiles against the key tile (8 KiB); where four fit in LDS, two
+  // consecutive tiles per buffer (tile J at 0, tile J + 1 at RT), like the
+  // stored values pass
   static constexpr int P_OFF = kBN * S1;
-  static constexpr int BUF = MODE == kValuesStored ? 2 * GT : RST ? P_OFF + 8192 : GEND;
+  static constexpr int RT = P_OFF + 8192;
+  static constexpr bool RPAIR = RST && 4 * RT <= 160 * 1024;
+  static constexpr int BUF = MODE == kValuesStored ? 2 * GT : RPAIR ? 2 * RT : RST ? RT : GEND;
   static constexpr int SA = VAL ? S2 : S1;          // transposed operand's stride
   static constexpr int A_OFF = VAL ? X2_OFF : X1_OFF;
   static_assert(2 * BUF <= 160 * 1024, "LDS budget");
@@ -607,9 +611,35 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       pin1[0] = pnext1[0];
       pin1[1] = pnext1[1];
     }
+  } else if constexpr (MODE == kRowsStored && C::RPAIR) {
+    // pairs of tiles: (J, J + 1) from one buffer while (J + 2, J + 3) land in
+    // the other
+    auto load_pair = [&](int J, char* buf) {
+      load_tile(J, buf);
+      if (J + 1 <= last) load_tile(J + 1, buf + C::RT);
+    };
+    auto compute_pair = [&](const char* buf, int J) {
+      if (wave_needs(J)) compute(buf, J, pin, nullptr, false, TileSrc{}, true);
+      if (J + 1 <= last && wave_needs(J + 1))
+        compute(buf + C::RT, J + 1, pin, nullptr, false, TileSrc{}, true);
+    };
+    load_pair(first, smem0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int J = first; J <= last; J += 4) {
+      if (J + 2 <= last) load_pair(J + 2, smem1);
+      compute_pair(smem0, J);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (J + 2 > last) break;
+      if (J + 4 <= last) load_pair(J + 4, smem0);
+      compute_pair(smem1, J + 2);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   } else if constexpr (MODE == kRowsStored) {
-    // one tile per buffer: K rows and the stored P blocks of tile J + 1 land
-    // while tile J is accumulated
+    // one tile per buffer (the widest heads): K rows and the stored P blocks
+    // of tile J + 1 land while tile J is accumulated
     load_tile(first, smem0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
