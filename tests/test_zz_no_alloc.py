@@ -54,10 +54,12 @@ def test_noalloc_matches_the_stream_entry_point_on_consecutive_calls():
         assert torch.isfinite(out[0].float()).all()
 
 
-def test_noalloc_single_launch_needs_no_workspace_at_any_size():
+@pytest.mark.parametrize("d", [16, 512])
+def test_noalloc_single_launch_needs_no_workspace_at_any_size(d):
     """512 heads of 2048 need 21.5 MB of workspace in the two-launch form,
-    beyond the fixed array, but run as one launch with none."""
-    x = W.make(_spec(32, 16, 2048, 16), seed=70)
+    beyond the fixed array, but run as one launch with none (the pair kernel
+    at d = 16, the one-wave kernel at d = 512)."""
+    x = W.make(_spec(32, 16, 2048, d), seed=70)
     out, ref = _run_both(x)
     for name, a, b in zip(("h", "m", "n"), out, ref):
         assert torch.equal(a, b), name
