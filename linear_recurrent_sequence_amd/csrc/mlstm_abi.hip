@@ -144,7 +144,8 @@ int run_tiles(const void* q, const void* k, const void* v, const float* m, const
 // gates itself (no workspace).
 bool fused_path(int64_t T, int64_t d, int dtype) {
   return dtype == MLSTM_BF16 &&
-         (mlstm::tiles_pairs_fused_supports(T, d) || mlstm::tiles_mfma_fused_supports(T, d));
+         (mlstm::tiles_pipe_preferred(T, d) || mlstm::tiles_pairs_fused_supports(T, d) ||
+          mlstm::tiles_mfma_fused_supports(T, d));
 }
 
 // Both stages on a given workspace (mlstm::workspace_bytes(B * NH, T) bytes,
@@ -155,6 +156,9 @@ int forward_on(void* ws, const void* q, const void* k, const void* v, const floa
                float* n_out, int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
                hipStream_t s, bool exp_forget) {
   const int64_t H = B * NH;
+  if (fused_path(T, d, dtype) && mlstm::tiles_pipe_preferred(T, d))
+    return hip_status(mlstm::launch_tiles_pipe(q, k, v, igate, fgate, h_out, m_out, n_out, ep,
+                                               exp_forget, H, T, d, s));
   if (fused_path(T, d, dtype))
     return hip_status(
         mlstm::tiles_pairs_fused_supports(T, d)

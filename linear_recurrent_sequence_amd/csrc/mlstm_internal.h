@@ -149,6 +149,18 @@ hipError_t launch_tiles_pairs_fused(const void* q, const void* k, const void* v,
                                     bool exp_forget, int64_t H, int64_t T, int64_t d,
                                     hipStream_t stream);
 
+// Both stages in one launch with a software-pipelined key loop (bf16, d a
+// multiple of 64 up to 384, T <= 2048, T divisible by 4): four waves, one per
+// SIMD, each with 32 query rows and all columns; K and V staged through
+// registers into double-buffered LDS tiles.
+bool tiles_pipe_supports(int64_t T, int64_t d);
+// whether the one-launch forward pass takes this kernel (d <= 192)
+bool tiles_pipe_preferred(int64_t T, int64_t d);
+hipError_t launch_tiles_pipe(const void* q, const void* k, const void* v, const float* igate,
+                             const float* fgate, void* h_out, float* m_out, float* n_out,
+                             const Epilogue& ep, bool exp_forget, int64_t H, int64_t T,
+                             int64_t d, hipStream_t stream);
+
 // Stage 2, bf16 matrix-core tiles for wide heads (d <= 1024): four waves
 // share 32 query rows and split the head dimension in quarters.
 bool tiles_wide_supports(int64_t d);

@@ -409,15 +409,24 @@ FUSED_CASES = [
 ]
 
 
+def _pipelined(s):
+    """Whether the one-launch forward pass runs the software-pipelined kernel
+    (bf16, d a multiple of 64 up to 192, T <= 2048 divisible by 4)."""
+    return (s["dtype"] == "bf16" and s["d"] % 64 == 0 and s["d"] <= 192 and s["T"] <= 2048
+            and s["T"] % 4 == 0)
+
+
 @pytest.mark.parametrize("forget", ["sigmoid", "exp"])
 @pytest.mark.parametrize("s", FUSED_CASES, ids=_id)
 def test_fused_scan_equals_the_two_stage_pass_bitwise(s, forget):
     """Up to 2048 positions (bf16, head dim up to 512, length divisible by 4)
     the one-shot entry points run a single tile kernel that scans the gates in
     its prologue.  The scan there has the gate-scan kernel's block structure
-    (run by 256 threads, two scan threads each, in the one-wave kernel above
-    d = 384), so h, m and n must be the bits of the two-stage pass (gate scan,
-    then the same tile kernel on the workspace)."""
+    (run by 256 threads, two scan threads each, in the one-wave kernels), so
+    h, m and n must be the bits of the two-stage pass: gate scan, then the
+    tile kernel with the same arithmetic on the workspace (the two-wave pair
+    kernel for 192 < d <= 384; for d <= 192 the one-launch pass runs the
+    pipelined kernel, whose sums are those of the one-wave kernel)."""
     x = W.make(s, seed=71)
     if forget == "exp":  # log f = f~, small and negative
         x["fgate"] = (-0.02 * np.abs(x["fgate"])).astype(np.float32)
@@ -426,12 +435,56 @@ def test_fused_scan_equals_the_two_stage_pass_bitwise(s, forget):
         a = mlstm.parallel_fwd(q, k, v, ig, fg)
     else:
         a = mlstm.parallel_fwd_train(q, k, v, ig, fg, forget="exp")[:3]
-    b = mlstm.parallel_fwd_staged(q, k, v, ig, fg, kernel="mfma", forget=forget)
+    b = mlstm.parallel_fwd_staged(q, k, v, ig, fg, kernel="mfma_single" if _pipelined(s) else "mfma",
+                                  forget=forget)
     torch.cuda.synchronize()
     for name, ta, tb in zip("hmn", a, b):
         assert torch.equal(ta, tb), name
     if s["T"] <= 300:
         check_full(_host(a[0]), _host(a[1]), _host(a[2]), x, "bf16", forget=forget)
+
+
+PIPELINED_CASES = [
+    spec(1, 1, 4, 64), spec(1, 2, 100, 64), spec(2, 1, 512, 128), spec(1, 1, 252, 192),
+    spec(3, 1, 388, 64, ig=("normal", 0, 2), fg=("normal", 3, 1.5)),
+    spec(1, 2, 600, 128, ig=("uniform", -20, 20), fg=("normal", 0, 4), fgate_floor=(0.01, -30.0)),
+    spec(1, 1, 520, 192, ig=("uniform", -40, 40), fg=("normal", -2, 3)),
+    spec(8, 1, 136, 64),  # head count divisible by 8 (XCD-grouped schedule)
+]
+
+
+@pytest.mark.parametrize("s", PIPELINED_CASES, ids=_id)
+def test_pipelined_kernel_full(s):
+    """The software-pipelined kernel (one wave per SIMD, K and V staged
+    through registers, d <= 192) against the oracle on every row: ragged
+    tails, several row tiles, tiles skipped under strong decay."""
+    assert _pipelined(s)
+    x = W.make(s, seed=5)
+    h, m, n = run_gpu(x)
+    check_full(h, m, n, x, "bf16")
+
+
+def test_pipelined_kernel_epilogues():
+    """Output gate, stored h~ and the row sums b through the pipelined kernel:
+    the gated h is sigma(o~) h~ of the ungated pass's float32 h~, b matches
+    the oracle's (Eqs. 78, 83)."""
+    s = spec(2, 1, 300, 128)
+    x = W.make(s, seed=6)
+    q, k, v, ig, fg = _dev(x)
+    og = torch.from_numpy(W.round_bf16(np.random.default_rng(3).standard_normal(
+        x["q"].shape).astype(np.float32))).to("cuda").to(torch.bfloat16)
+    hg, ht, m, n = mlstm.parallel_fwd_gated(q, k, v, ig, fg, og, htilde=True)
+    h0, m0, n0 = mlstm.parallel_fwd(q, k, v, ig, fg)
+    ht2, m2, n2, b2 = mlstm.parallel_fwd_train(q, k, v, ig, fg)
+    torch.cuda.synchronize()
+    assert torch.equal(ht, h0) and torch.equal(m, m0) and torch.equal(n, n0)
+    assert torch.equal(ht2, h0) and torch.equal(n2, n0)
+    hr, mr, nr, br, rho, rho_num = oracle_full(x)
+    kap, kapn = conditions(nr, hr, rho, rho_num)
+    gate = 1.0 / (1.0 + np.exp(-_host(og)))
+    check(_host(hg), _host(m), _host(n), hr * gate, mr, nr, kap, kapn, TOL_H["bf16"], K_H["bf16"],
+          K_NUM["bf16"])
+    assert b_over_bar(_host(b2), br, nr, kap) <= 1.0
 
 
 def test_tile_skipping_long_context_full_size():
@@ -617,7 +670,10 @@ EXP_CASES = [
 def test_exp_forget_forward_matches_oracle(s):
     x = W.make(s, seed=22)
     q, k, v, ig, fg = _dev(x)
-    h, m, n = mlstm.parallel_fwd_staged(q, k, v, ig, fg, forget="exp")
+    # the two-stage pass with the tile kernel whose sums the one-launch pass
+    # reproduces (the one-wave kernel where the pipelined kernel runs)
+    kern = "mfma_single" if _pipelined(s) else "auto"
+    h, m, n = mlstm.parallel_fwd_staged(q, k, v, ig, fg, kernel=kern, forget="exp")
     ht, mt, nt, b = mlstm.parallel_fwd_train(q, k, v, ig, fg, forget="exp")
     hs, ms, ns = mlstm.parallel_fwd_staged(q, k, v, ig, fg)  # sigmoid: must differ
     torch.cuda.synchronize()
@@ -986,8 +1042,11 @@ def _inputs_into(bufs, x):
 def test_graph_capture_replays_match_eager():
     """mlstm_parallel_fwd (stream-ordered workspace) and the staged entry
     points (caller workspace) captured into HIP graphs: every replay, with new
-    inputs copied in and eager work in between, equals the eager call bitwise."""
+    inputs copied in and eager work in between, equals the eager call bitwise
+    (the staged pass runs the one-wave kernel, whose sums the pipelined
+    kernel of the one-launch pass reproduces at this head dimension)."""
     s = spec(2, 2, 300, 64)
+    assert _pipelined(s)
     xs = [W.make(s, seed=40 + i) for i in range(3)]
     q, k, v, ig, fg = _dev(xs[0])
     bufs = (q, k, v, ig, fg)
@@ -1001,7 +1060,7 @@ def test_graph_capture_replays_match_eager():
     with torch.cuda.stream(side):  # warm up on the capture stream
         mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
         mlstm.gate_scan(ig, fg, 64, ws, m=m2)
-        mlstm.causal_tiles(q, k, v, m2, ws, out=(h2, n2))
+        mlstm.causal_tiles(q, k, v, m2, ws, kernel="mfma_single", out=(h2, n2))
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
@@ -1009,7 +1068,7 @@ def test_graph_capture_replays_match_eager():
         mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n))
     with torch.cuda.graph(g2):
         mlstm.gate_scan(ig, fg, 64, ws, m=m2)
-        mlstm.causal_tiles(q, k, v, m2, ws, out=(h2, n2))
+        mlstm.causal_tiles(q, k, v, m2, ws, kernel="mfma_single", out=(h2, n2))
     for x in xs + xs[:1]:
         _inputs_into(bufs, x)
         g1.replay()
