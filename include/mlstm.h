@@ -72,11 +72,16 @@ enum {
   MLSTM_KERNEL_MFMA_WIDE = 5       /* bf16 only: the wide-head MFMA kernel, for any d */
 };
 /*
- * The bf16 MFMA path has three tile kernels.  For d <= 384 it runs 8 waves
+ * The bf16 MFMA path has three tile kernels, and a fourth on the one-launch
+ * path.  For d <= 384 it runs 8 waves
  * per workgroup, two per SIMD: the two waves that share a SIMD share 32 query
  * rows, each forms C~' for its own 32 of every 64 keys and accumulates half
  * of the output columns, so one wave's copies and exponentials overlap the
- * other's matrix-core work.  For 384 < d <= 512 (and with
+ * other's matrix-core work.  On the one-launch path with d a multiple of 64
+ * up to 192 it runs 4 waves, one per SIMD, each with 32 query rows and all
+ * columns, and software-pipelines the key loop (the Q K^T product of one key
+ * tile beside the C~' V product of the previous one, K and V staged through
+ * registers); its sums are those of the one-wave kernel below.  For 384 < d <= 512 (and with
  * MLSTM_KERNEL_MFMA_SINGLE) it runs 4 waves, one per SIMD, each with 32 query
  * rows and all columns.  For d > 512 (and with MLSTM_KERNEL_MFMA_WIDE) four
  * waves share 32 query rows, each holding a quarter of the head dimension:
@@ -137,7 +142,9 @@ enum { MLSTM_FORGET_SIGMOID = 0, MLSTM_FORGET_EXP = 1 };
  * Runs on the null stream.  For bf16 with d <= 512 and T <= 2048, T a
  * multiple of 4, the pass is one kernel launch that needs no workspace: each
  * workgroup scans its head's gates itself (the gate-scan arithmetic in the
- * same order, so every output is bitwise that of the two stages).  Otherwise
+ * same order, so every output is bitwise that of the two stages with the same
+ * tile arithmetic: the one-wave kernel where the pipelined kernel runs, the
+ * kernel MLSTM_KERNEL_AUTO picks otherwise).  Otherwise
  * the gate scan and the tile kernel run as two launches on a
  * library-allocated, stream-ordered workspace.
  * Returns MLSTM_OK or a negative status.
