@@ -503,7 +503,12 @@ def main():
     staged_tile_ms = e0.elapsed_time(e1) / reps
     if single:
         tile_ms = timed_kernel_ms
-        kernel_name = f"tiles_pairs_kernel<{(d + 63) // 64 * 64}, gate scan fused>"
+        if d % 64 == 0 and d <= 192:
+            kernel_name = f"tiles_pipe_kernel<{d}> (gate scan fused)"
+        elif d <= 384:
+            kernel_name = f"tiles_pairs_kernel<{(d + 63) // 64 * 64}, gate scan fused>"
+        else:
+            kernel_name = f"tiles_mfma_kernel<{(d + 31) // 32 * 32}, gate scan fused>"
     else:
         tile_ms = staged_tile_ms
         kernel_name = "causal tile kernel of the two-launch form"
@@ -574,7 +579,9 @@ def main():
             "bound": "mfma", "kernel": kernel_name, "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_from_counters() if single else None,
+            # the committed counter record covers the 125M-shaped layer's kernel only
+            "traffic": (traffic_from_counters()
+                        if single and args.workload == "xlstm125m_layer" else None),
             "avg_launch_ms": round(tile_ms, 5),
         },
         "staged": {"gate_scan_avg_launch_ms": round(scan_ms, 5),
