@@ -122,9 +122,15 @@ int run_tiles(const void* q, const void* k, const void* v, const float* m, const
                         kernel == MLSTM_KERNEL_MFMA_SINGLE || kernel == MLSTM_KERNEL_MFMA_WIDE ||
                         (kernel == MLSTM_KERNEL_AUTO && dtype == MLSTM_BF16);
   const bool skip = kernel != MLSTM_KERNEL_MFMA_ALL_TILES;
-  if (!use_mfma)
+  if (!use_mfma) {
+    // float32 inputs: the float32 matrix-core kernel where it applies, unless
+    // the vector kernel is asked for
+    if (kernel == MLSTM_KERNEL_AUTO && dtype == MLSTM_FP32 && mlstm::tiles_f32_supports(d))
+      return hip_status(mlstm::launch_tiles_f32(q, k, v, m, w, h_out, n_out, ep, true, H, T, d,
+                                                stream));
     return hip_status(mlstm::launch_tiles_vector(q, k, v, m, w, h_out, n_out, ep, H, T, d,
                                                  dtype == MLSTM_BF16, stream));
+  }
   if (kernel == MLSTM_KERNEL_MFMA_SINGLE) {
     if (d > 512) return MLSTM_ERR_HEAD_DIM;
     return hip_status(mlstm::launch_tiles_mfma(q, k, v, m, w, h_out, n_out, ep, skip, H, T, d,

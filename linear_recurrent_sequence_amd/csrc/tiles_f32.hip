@@ -1,0 +1,401 @@
+// Stage 2, float32 matrix-core variant: Eqs. 81-86 of the xLSTM appendix
+// ("Parallel mLSTM Backward Pass" opens with the stabilized forward pass) over
+// causal 32 x 32 tiles for float32 inputs, both contractions on the gfx950
+// float32 matrix instruction v_mfma_f32_32x32x2_f32 (float32 products and
+// sums, nothing rounded to a narrower type).
+//
+// Work decomposition.  A workgroup of 4 waves (one per SIMD) owns 128 query
+// rows of one head, 32 per wave, and walks the key axis in 32-key tiles up
+// to its diagonal.  A wave holds its rows' Q^T fragments (the B operand of
+// S^T = K Q^T) and all d output columns of O^T = V^T C~'^T: d / 2 + d / 2
+// registers per lane, which caps this kernel at d = 384.
+//
+// Reduction order.  The instruction sums over 2 indices k = lane / 32.  In
+// step 4u + v of the first product, lane (g, l) takes head dim 8u + 4g + v,
+// so a lane's operands of four steps are 16 contiguous bytes of one row (one
+// LDS read each for K, resident registers for Q).  In the second product the
+// reduction index is the key: step s pairs key 8(s/4) + 4g + s%4 with lane
+// half g, which is exactly the key of register s of the first product's
+// 32 x 32 result in that lane, so C~'^T feeds the B operand from registers
+// with no data movement, and V^T is read one float per lane per step.
+//
+// Data movement.  One K tile and one V tile live in LDS: during the first
+// product of tile J the copies bring V_J, during the second they bring
+// K_{J+1} (global -> LDS loads, spread over the matrix instructions); two
+// barriers per tile.  The Q block is staged through the same region, half
+// at a time.  Buffer ranges end at the sequence end, so rows past it read as
+// zeros.
+//
+// Exponents: each entry's exponential 2^fl32(R_i + C_j) (Eqs. 79, 81, 82),
+// the sum formed in float64 from the gate scan's terms and rounded once, as
+// in the float32 vector kernel; the causal mask of Eq. 71 on the diagonal
+// tile.  A tile whose exponent bound is below kSkipLog2 for a wave's rows
+// contributes exactly zero and is not multiplied.
+#include "mlstm_internal.h"
+#include "tile_common.h"
+
+namespace mlstm {
+namespace {
+
+using namespace tilecommon;
+
+constexpr int kFThreads = 256;
+constexpr int kFWaves = kFThreads / 64;
+constexpr int kFPf = 4;  // LDS operand prefetch distance (reads)
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// K rows (and the staged Q rows) at 4 d + 16 bytes: a K read takes 16 bytes
+// of each of 32 rows, 16 (d / 4 + 1) bytes apart, an odd number of 16-byte
+// slots for d % 32 == 0: every 16 lanes hit 16 distinct slots.  V rows at
+// 4 d + 32 bytes: the two half-waves read 128 bytes of rows 4 apart, whose
+// offsets differ by 128 modulo 256 bytes: all 64 banks once.
+template <int DP>
+struct FCfg {
+  static_assert(DP % 32 == 0 && DP >= 32 && DP <= 384, "head dim of the float32 MFMA kernel");
+  static_assert(DP <= 256 || DP % 64 == 0, "above 256 the columns split in halves of 32-col blocks");
+  static constexpr int RB = 4 * DP;       // bytes of a row in memory
+  static constexpr int CH = DP / 4;       // 16-byte chunks per row
+  static constexpr int NCP = (CH + 63) / 64;  // copy instructions per row
+  static constexpr int RSK = RB + 16;
+  static constexpr int RSV = 4 * 32 * (DP / 32 / (DP <= 256 ? 1 : 2)) + 32;
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = kBN * RSK;
+  static constexpr int BYTES = V_OFF + kBN * RSV;
+  static constexpr int NU = DP / 8;       // 16-byte operand groups of the first product
+  // output columns: above d = 256 two workgroups per row block take half of
+  // the 32-column blocks each (both form S, whose registers and the Q^T
+  // operands' would otherwise not fit beside all the accumulators)
+  static constexpr int NSPLIT = DP <= 256 ? 1 : 2;
+  static constexpr int NB = DP / 32 / NSPLIT;  // 32-column output blocks of a workgroup
+  static constexpr int VC = 32 * NB;           // V columns a workgroup copies and reads
+  static constexpr int RVB = 4 * VC;           // bytes of those columns in a row
+  static constexpr int NCV = (RVB / 16 + 63) / 64;  // copy instructions per V row
+  // Q^T operand groups held in accumulation registers (read there directly
+  // by the matrix instructions): as many as fit beside the accumulators of
+  // O^T and the 16 of S^T
+  static constexpr int NQA = (256 - 16 * NB - 16) / 4 < NU ? (256 - 16 * NB - 16) / 4 : NU;
+  static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int DP>
+__global__ __attribute__((amdgpu_flat_work_group_size(kFThreads, kFThreads),
+                          amdgpu_waves_per_eu(1, 1))) void tiles_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ m_in, const double* __restrict__ rowt,
+    const double* __restrict__ colt, const double* __restrict__ rowb,
+    const double* __restrict__ keyb, float* __restrict__ h_out, float* __restrict__ n_out,
+    const float* __restrict__ ogate, float* __restrict__ htilde, float* __restrict__ b_out,
+    int T, int Tp, int row_tiles, int H, int skip) {
+  using C = FCfg<DP>;
+  __shared__ __attribute__((aligned(1024))) char lds[C::BYTES];
+  __shared__ int s_first[kFWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;    // half-wave: the reduction index of every step
+  const int l32 = lane & 31;  // query column (first product's B, every result)
+  const int cs = int(blockIdx.x) % C::NSPLIT;  // this workgroup's half of the columns
+  int64_t I64, head64;
+  map_tile(blockIdx.x / C::NSPLIT, row_tiles, H, I64, head64);
+  const int I = int(I64), head = int(head64);
+  const int64_t hoff = int64_t(head) * T * DP;
+  const int q0 = I * kBM;
+  const int qw = q0 + 32 * w;
+  const int qi = qw + l32;
+  const int nb32 = Tp / kBoundTile;
+
+  // ---- copies: row r of a run of rows starting at `r0`, into LDS rows of
+  // stride RS; 16 bytes per lane, lanes [0, CH) in pieces of 64
+  const unsigned vchunk = unsigned(16 * lane);
+  auto rows_src = [&](const float* base, int r0, int nrows) {
+    const int left = T - r0;
+    const int n = left <= 0 ? 0 : (left < nrows ? left : nrows);
+    return rsrc_words(base + hoff + int64_t(r0) * DP, int64_t(n) * C::RB);
+  };
+  // copy c of a wave's 8 rows of a K tile (row c / NCP, piece c % NCP)
+  auto k_copy = [&](auto cc, const i32x4& rs, unsigned lds_base) {
+    constexpr int c = decltype(cc)::value;
+    constexpr int r = c / C::NCP, p = c % C::NCP;
+    if (lane < C::CH - 64 * p)
+      copy16_row<r, r * C::RSK + 1024 * p>(rs, vchunk + 1024u * p, C::RB, lds_base);
+  };
+  // the same for V, this workgroup's VC columns of each row
+  const unsigned vcol = unsigned(cs * C::RVB);
+  auto v_copy = [&](auto cc, const i32x4& rs, unsigned lds_base) {
+    constexpr int c = decltype(cc)::value;
+    constexpr int r = c / C::NCV, p = c % C::NCV;
+    if (lane < C::RVB / 16 - 64 * p)
+      copy16_row<r, r * C::RSV + 1024 * p>(rs, vcol + vchunk + 1024u * p, C::RB, lds_base);
+  };
+  constexpr int kCopies = 8 * C::NCP;   // K copies per wave and tile
+  constexpr int kVCopies = 8 * C::NCV;  // V copies per wave and tile
+  const unsigned lds_k = lds_addr(lds + C::K_OFF + 8 * w * C::RSK);
+  const unsigned lds_v = lds_addr(lds + C::V_OFF + 8 * w * C::RSV);
+
+  // ---- prologue: each wave stages its own 32 Q rows in its own LDS region,
+  // a quarter of the head dimension at a time (rows of d bytes at a stride of
+  // d + 16), and reads its Q^T operand groups of that quarter; no barrier
+  // (each wave waits for its own copies and reads)
+  f32x4 qf[C::NU];
+  {
+    constexpr int RSQ = DP + 16;
+    constexpr int NQ = C::NU / 4;  // operand groups per quarter
+    const i32x4 rs = rows_src(q, qw, 32);
+    const unsigned base = lds_addr(lds + 32 * w * RSQ);
+    const char* const qrow = lds + (32 * w + l32) * RSQ + 16 * g;
+    static_for<4>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      static_for<32>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if (lane < DP / 16) copy16_row<i, i * RSQ>(rs, vchunk + unsigned(h * DP), C::RB, base);
+      });
+      __builtin_amdgcn_s_waitcnt(0);
+      static_for<NQ>([&](auto jc) {
+        constexpr int u = h * NQ + decltype(jc)::value;
+        const char* const src = qrow + 32 * (u - h * NQ);
+        if constexpr (u < C::NQA) {  // each read waited for inside its own statement
+          float a0, a1, a2, a3;
+          asm volatile(
+              "ds_read_b32 %0, %4\n\tds_read_b32 %1, %4 offset:4\n\t"
+              "ds_read_b32 %2, %4 offset:8\n\tds_read_b32 %3, %4 offset:12\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=a"(a0), "=a"(a1), "=a"(a2), "=a"(a3)
+              : "v"(lds_addr(src))
+              : "memory");
+          qf[u] = f32x4{a0, a1, a2, a3};
+        } else
+          qf[u] = *reinterpret_cast<const f32x4*>(src);
+      });
+      __builtin_amdgcn_s_waitcnt(0);  // the region is refilled next
+    });
+    static_assert(32 * kFWaves * RSQ <= C::BYTES, "the staged Q quarters fit");
+  }
+  __syncthreads();  // every wave's staging is done before the tile region is filled
+
+  const int n_key_tiles = (T + kBN - 1) / kBN;
+  const int last_tile = (4 * I + 3 < n_key_tiles - 1) ? 4 * I + 3 : n_key_tiles - 1;
+  const int wave_last = (4 * I + w < n_key_tiles - 1) ? 4 * I + w : n_key_tiles - 1;
+  const double r_i = rowt[int64_t(head) * Tp + qi];  // R_i (qi < Tp)
+  const double rb_w = rowb[int64_t(head) * nb32 + qw / kBoundTile];
+  auto tile_needed = [&](double rb, double kb) { return rb + kb >= kSkipLog2; };
+  auto key_bound = [&](int J) { return keyb[int64_t(head) * nb32 + J]; };
+
+  // ---- decay-aware start: the first tile some wave needs
+  int first = 0;
+  if (skip) {
+    double rb_rows[kFWaves];
+    int last_w[kFWaves];
+#pragma unroll
+    for (int u = 0; u < kFWaves; ++u) {
+      rb_rows[u] = rowb[int64_t(head) * nb32 + (q0 + 32 * u) / kBoundTile];
+      last_w[u] = (4 * I + u < n_key_tiles - 1) ? 4 * I + u : n_key_tiles - 1;
+    }
+    int mine = last_tile;
+    for (int J0 = 0; J0 < last_tile; J0 += kFThreads) {
+      const int J = J0 + tid;
+      bool need = false;
+      if (J < last_tile) {
+        const double kb = key_bound(J);
+#pragma unroll
+        for (int u = 0; u < kFWaves; ++u)
+          need = need || (J <= last_w[u] && tile_needed(rb_rows[u], kb));
+      }
+      const uint64_t hits = __builtin_amdgcn_ballot_w64(need);
+      if (hits != 0) {
+        mine = J0 + 64 * w + int(__builtin_ctzll(hits));
+        break;
+      }
+    }
+    if (lane == 0) s_first[w] = mine;
+    __syncthreads();
+    first = s_first[0];
+#pragma unroll
+    for (int u = 1; u < kFWaves; ++u) first = s_first[u] < first ? s_first[u] : first;
+    first = __builtin_amdgcn_readfirstlane(first);
+  }
+
+  // the first K tile
+  {
+    const i32x4 rs = rows_src(k, first * kBN + 8 * w, 8);
+    static_for<kCopies>([&](auto cc) { k_copy(cc, rs, lds_k); });
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  f32x16 acc[C::NB];
+#pragma unroll
+  for (int b = 0; b < C::NB; ++b) acc[b] = f32x16{};
+  float bsum = 0.0f;
+
+  // per-lane LDS offsets of the operand reads
+  const char* const kp = lds + C::K_OFF + l32 * C::RSK + 16 * g;
+  // V: step s reads row 8 (s / 4) + 4 g + s % 4, column 32 b + l32
+  const char* const vp = lds + C::V_OFF + 4 * g * C::RSV + 4 * l32;
+  constexpr int NSV = 16 * C::NB;  // steps of the second product
+
+  for (int J = first; J <= last_tile; ++J) {
+    const bool need = __builtin_amdgcn_readfirstlane(
+                          int(J <= wave_last && (!skip || tile_needed(rb_w, key_bound(J))))) != 0;
+    // ===== phase 1: K_J resident; the copies bring V_J =====
+    const i32x4 rs_v = rows_src(v, J * kBN + 8 * w, 8);
+    float cv[16];
+    if (need) {
+      // the tile's C_j of this lane's keys 8 rq + 4 g + e, loaded during the
+      // last quarter of the product
+      const double* cj = colt + int64_t(head) * Tp + J * kBN + 4 * g;
+      double2 cd[8];
+      f32x16 st = f32x16{};
+      f32x4 kf[kFPf + 1];
+#pragma unroll
+      for (int u = 0; u < kFPf && u < C::NU; ++u) kf[u] = *reinterpret_cast<const f32x4*>(kp + 32 * u);
+      static_for<C::NU>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (u + kFPf < C::NU)
+          kf[(u + kFPf) % (kFPf + 1)] = *reinterpret_cast<const f32x4*>(kp + 32 * (u + kFPf));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          st = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[u % (kFPf + 1)][e], qf[u][e], st, 0, 0, 0);
+        static_for<kVCopies>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          if constexpr ((c * C::NU) / kVCopies == u) v_copy(cc, rs_v, lds_v);
+        });
+        if constexpr (u == (3 * C::NU) / 4) {
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            cd[2 * rq] = *reinterpret_cast<const double2*>(cj + 8 * rq);
+            cd[2 * rq + 1] = *reinterpret_cast<const double2*>(cj + 8 * rq + 2);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // C~' = S (.) D' (Eq. 82) with each entry's own exponential; lane (g,
+      // l32), register r holds S^T[key 8 (r / 4) + 4 g + r % 4][query l32]
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const double cc4[4] = {cd[2 * rq].x, cd[2 * rq].y, cd[2 * rq + 1].x, cd[2 * rq + 1].y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = J * kBN + 8 * rq + 4 * g + e;
+          // causal mask (Eq. 71); keys past T carry C_j = -inf
+          const float ex = key > qi ? -INFINITY : float(r_i + cc4[e]);
+          const float c = st[4 * rq + e] * exp2f(ex);
+          bsum += c;  // b (Eq. 83)
+          cv[4 * rq + e] = c;
+        }
+      }
+    } else {
+      static_for<kVCopies>([&](auto cc) { v_copy(cc, rs_v, lds_v); });
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ===== phase 2: V_J resident; the copies bring K_{J+1} =====
+    const bool more = J < last_tile;
+    const i32x4 rs_k = rows_src(k, (J + 1) * kBN + 8 * w, 8);
+    if (need) {
+      // O^T += V_J^T C~'^T: step t = (column block b, key step s)
+      auto vaddr = [&](int t) {
+        const int b = t >> 4, s = t & 15;
+        return vp + (8 * (s >> 2) + (s & 3)) * C::RSV + 128 * b;
+      };
+      float vf[kFPf + 1];
+#pragma unroll
+      for (int t = 0; t < kFPf; ++t) vf[t] = *reinterpret_cast<const float*>(vaddr(t));
+      static_for<NSV>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        if constexpr (t + kFPf < NSV)
+          vf[(t + kFPf) % (kFPf + 1)] = *reinterpret_cast<const float*>(vaddr(t + kFPf));
+        acc[t >> 4] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[t % (kFPf + 1)], cv[t & 15],
+                                                            acc[t >> 4], 0, 0, 0);
+        if (more) {
+          static_for<kCopies>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            if constexpr ((c * NSV) / kCopies == t) k_copy(cc, rs_k, lds_k);
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else if (more) {
+      static_for<kCopies>([&](auto cc) { k_copy(cc, rs_k, lds_k); });
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // ---- epilogue: b of the two half-waves (keys 4g + ...), n (Eq. 84),
+  // h~ = acc / n (Eqs. 85, 86), output gate (Eq. 78)
+  bsum += __shfl_xor(bsum, 32, 64);
+  if (qi < T) {
+    const float nn = fmaxf(fabsf(bsum), expf(-m_in[int64_t(head) * T + qi]));
+    if (g == 0 && cs == 0) {
+      n_out[int64_t(head) * T + qi] = nn;
+      if (b_out) b_out[int64_t(head) * T + qi] = bsum;
+    }
+    const int64_t row = hoff + int64_t(qi) * DP;
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        // register 4 rq + e of block b: column 32 b + 8 rq + 4 g + e of the
+        // workgroup's columns
+        const int col = C::VC * cs + 32 * b + 8 * rq + 4 * g;
+        f32x4 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] = acc[b][4 * rq + e] / nn;
+        if (htilde) *reinterpret_cast<f32x4*>(htilde + row + col) = hv;
+        if (ogate) {
+          const f32x4 og = *reinterpret_cast<const f32x4*>(ogate + row + col);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hv[e] *= 1.0f / (1.0f + __expf(-og[e]));
+        }
+        *reinterpret_cast<f32x4*>(h_out + row + col) = hv;
+      }
+    }
+  }
+}
+
+template <int DP>
+hipError_t launch_f(const void* q, const void* k, const void* v, const float* m,
+                    const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep, bool skip,
+                    int64_t H, int64_t T, hipStream_t stream) {
+  const int64_t row_tiles = (T + kBM - 1) / kBM;
+  hipLaunchKernelGGL((tiles_f32_kernel<DP>), dim3(unsigned(row_tiles * H * FCfg<DP>::NSPLIT)),
+                     dim3(kFThreads), 0,
+                     stream, static_cast<const float*>(q), static_cast<const float*>(k),
+                     static_cast<const float*>(v), m, ws.rowt, ws.colt, ws.rowb, ws.keyb,
+                     static_cast<float*>(h_out), n_out, static_cast<const float*>(ep.ogate),
+                     static_cast<float*>(ep.htilde), ep.b, int(T), int(ws.Tp), int(row_tiles),
+                     int(H), int(skip));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool tiles_f32_supports(int64_t d) {
+  return d % 32 == 0 && d >= 32 && (d <= 256 || (d % 64 == 0 && d <= 384));
+}
+
+hipError_t launch_tiles_f32(const void* q, const void* k, const void* v, const float* m,
+                            const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,
+                            bool skip, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+  if (!tiles_f32_supports(d)) return hipErrorInvalidValue;
+#define MLSTM_DP(n) launch_f<32 * n>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, stream)
+  switch (d / 32) {
+    case 1: return MLSTM_DP(1);
+    case 2: return MLSTM_DP(2);
+    case 3: return MLSTM_DP(3);
+    case 4: return MLSTM_DP(4);
+    case 5: return MLSTM_DP(5);
+    case 6: return MLSTM_DP(6);
+    case 7: return MLSTM_DP(7);
+    case 8: return MLSTM_DP(8);
+    case 10: return MLSTM_DP(10);
+    case 12: return MLSTM_DP(12);
+    default: return hipErrorInvalidValue;
+  }
+#undef MLSTM_DP
+}
+
+}  // namespace mlstm

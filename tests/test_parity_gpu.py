@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from linear_recurrent_sequence_amd import workloads as W
-from parity import K_H, K_NUM, b_over_bar, check, conditions, head_normwise, m_error, row_relative
+from parity import K_H, K_N, K_NUM, b_over_bar, check, conditions, head_normwise, m_error, row_relative
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -114,6 +114,68 @@ def test_fp32_ragged_full(s):
     x = W.make(s, seed=2)
     h, m, n = run_gpu(x)
     check_full(h, m, n, x, "fp32")
+
+
+F32_MFMA_CASES = [
+    spec(1, 1, 4, 32, "fp32"), spec(1, 2, 129, 96, "fp32"), spec(2, 1, 260, 192, "fp32"),
+    spec(1, 1, 200, 256, "fp32"), spec(1, 1, 161, 320, "fp32"), spec(1, 2, 140, 384, "fp32"),
+    spec(1, 2, 500, 64, "fp32", ig=("uniform", -20, 20), fg=("normal", 0, 4),
+         fgate_floor=(0.01, -30.0)),
+    spec(1, 1, 333, 128, "fp32", ig=("uniform", -40, 40), fg=("normal", -2, 3)),
+    spec(8, 1, 100, 32, "fp32"),  # head count divisible by 8 (XCD-grouped schedule)
+]
+
+
+@pytest.mark.parametrize("s", F32_MFMA_CASES, ids=_id)
+def test_fp32_matrix_core_kernel_full(s):
+    """Float32 inputs with d a multiple of 32 up to 256 (and 320, 384, where
+    two workgroups per row block take half of the columns each) run on the
+    float32 matrix instruction: against the oracle on every row (ragged
+    tails, several row tiles, tiles skipped under strong decay), and against
+    the float32 vector kernel (the same exponents, other summation orders)."""
+    x = W.make(s, seed=3)
+    h, m, n = run_gpu(x)
+    check_full(h, m, n, x, "fp32")
+    hv, mv, nv = run_gpu(x, kernel="vector")
+    assert np.array_equal(m, mv)
+    # both within their bars of the oracle, so within twice the bar of each
+    # other, on the rows where those bars are the flat ones
+    hr, _, nr, _, rho, rho_num = oracle_full(x)
+    kap, kapn = conditions(nr, hr, rho, rho_num)
+    well = kap <= K_N
+    assert (np.abs(n - nv) / nv)[well].max() <= 2e-5
+    keep = (kap <= K_H["fp32"]) & (kapn <= K_NUM["fp32"])
+    assert row_relative(h, hv)[keep].max() <= 2 * TOL_H["fp32"]
+
+
+def test_fp32_matrix_core_kernel_epilogues():
+    """Output gate, stored h~ and b through the float32 matrix-core kernel
+    (Eqs. 78, 83), at a head dim that splits the columns."""
+    s = spec(1, 2, 150, 384, "fp32")
+    x = W.make(s, seed=4)
+    q, k, v, ig, fg = _dev(x)
+    og = torch.from_numpy(np.random.default_rng(5).standard_normal(
+        x["q"].shape).astype(np.float32)).to("cuda")
+    hg, ht, m, n = mlstm.parallel_fwd_gated(q, k, v, ig, fg, og, htilde=True)
+    h0, m0, n0 = mlstm.parallel_fwd(q, k, v, ig, fg)
+    h2, m2, n2, b2 = mlstm.parallel_fwd_train(q, k, v, ig, fg)
+    torch.cuda.synchronize()
+    assert torch.equal(ht, h0) and torch.equal(n, n0) and torch.equal(h2, h0)
+    hr, mr, nr, br, rho, rho_num = oracle_full(x)
+    kap, kapn = conditions(nr, hr, rho, rho_num)
+    gate = 1.0 / (1.0 + np.exp(-_host(og)))
+    check(_host(hg), _host(m), _host(n), hr * gate, mr, nr, kap, kapn, TOL_H["fp32"],
+          K_H["fp32"], K_NUM["fp32"])
+    assert b_over_bar(_host(b2), br, nr, kap) <= 1.0
+
+
+def test_fp32_matrix_core_kernel_exp_forget():
+    s = spec(1, 2, 257, 128, "fp32", fg=("normal", -0.05, 0.03))
+    x = W.make(s, seed=6)
+    q, k, v, ig, fg = _dev(x)
+    h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg, forget="exp")
+    torch.cuda.synchronize()
+    check_full(_host(h), _host(m), _host(n), x, "fp32", forget="exp")
 
 
 def test_tiny_fp32_workload():
