@@ -51,6 +51,8 @@ def parse():
                    help="skip the tile-skipping comparison on the 16K stress workload")
     p.add_argument("--no-wide", action="store_true",
                    help="skip the 1.3B-shaped layers (sub-heads of 512, true heads of 1024)")
+    p.add_argument("--no-fp32", action="store_true",
+                   help="skip the 125M-shaped layer with float32 inputs")
     p.add_argument("--cpu-budget-s", type=float, default=15.0,
                    help="approximate CPU seconds for the oracle sample")
     p.add_argument("--oracle-budget-s", type=float, default=6.0,
@@ -341,6 +343,56 @@ def layer_timing(torch, mlstm, workloads, dev, name, reps=50, settle_s=0.5):
             "tile_frac": round(flops / (tile_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+PEAK_FP32_TFLOPS = 157.3  # MI355X dense float32 matrix (and vector) peak
+
+
+def fp32_layer_timing(torch, mlstm, workloads, dev, reps=20):
+    """The 125M-shaped layer (8 x 4 heads, T = 2048, d = 384) with float32
+    inputs: whole call (gate scan, then the float32 matrix-core tile kernel),
+    the tile kernel alone, and the float32 vector kernel on the same inputs."""
+    spec = dict(B=8, NH=4, T=2048, d=384, dtype="fp32", igate=("normal", 0.0, 1.0),
+                fgate=("normal", 3.0, 1.0), name="xlstm125m_layer_fp32")
+    x = workloads.make(spec, seed=0)
+    B, NH, T, d = 8, 4, 2048, 384
+    q, k, v = (torch.from_numpy(x[n]).to(dev).contiguous() for n in ("q", "k", "v"))
+    ig = torch.from_numpy(x["igate"]).to(dev).contiguous()
+    fg = torch.from_numpy(x["fgate"]).to(dev).contiguous()
+    h = torch.empty_like(q)
+    m = torch.empty((B, NH, T), dtype=torch.float32, device=dev)
+    n = torch.empty_like(m)
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, r):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(r):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / r
+
+    call_ms = timed(lambda: mlstm.parallel_fwd(q, k, v, ig, fg, out=(h, m, n)), reps)
+    ws = mlstm.alloc_workspace(B, NH, T, dev)
+    mlstm.gate_scan(ig, fg, d, ws, m=m)
+    tile_ms = timed(lambda: mlstm.causal_tiles(q, k, v, m, ws, out=(h, n)), reps)
+    vec_ms = timed(lambda: mlstm.causal_tiles(q, k, v, m, ws, kernel="vector", out=(h, n)), 2)
+    flops = workloads.counted_flops(B, NH, T, d)
+    return {"workload": spec["name"], "B": B, "NH": NH, "T": T, "d": d, "dtype": "f32",
+            "kernel": "tiles_f32_kernel<384> (output columns split over two workgroups)",
+            "ms_per_call": round(call_ms, 4),
+            "TFLOP/s": round(flops / (call_ms * 1e-3) / 1e12, 2),
+            "tile_avg_launch_ms": round(tile_ms, 4),
+            "tile_TFLOP/s": round(flops / (tile_ms * 1e-3) / 1e12, 2),
+            "peak_fp32": PEAK_FP32_TFLOPS,
+            "tile_frac": round(flops / (tile_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+            "executed_frac": round(1.5 * flops / (tile_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+            "vector_kernel_ms": round(vec_ms, 3)}
+
+
 def recurrent_decode(torch, mlstm, dev, B, NH, d, reps=50):
     """Time mlstm_recurrent_step (bf16 q/k/v, float32 state updated in place)."""
     g = torch.Generator(device="cpu").manual_seed(0)
@@ -541,6 +593,8 @@ def main():
             xw = workloads.make("xlstm1p3b_layer_d1024", seed=0)
             wide[1]["backward"] = backward_timing(torch, mlstm, workloads, xw, dev, reps=2)
 
+    f32 = None if args.no_fp32 else fp32_layer_timing(torch, mlstm, workloads, dev)
+
     # recurrent (generation) step on the same layer shape: the 8 x 4 heads'
     # state (19 MB) stays in the 256 MB last-level cache between steps; a
     # batch of 256 (604 MB of state) has to stream it from HBM
@@ -602,6 +656,8 @@ def main():
         line["tile_skipping"] = skip_rec
     if wide is not None:
         line["other_layers"] = wide
+    if f32 is not None:
+        line["fp32_layer"] = f32
     line["recurrent_step"] = rec
     if bwd is not None:
         line["backward"] = bwd
