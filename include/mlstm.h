@@ -65,7 +65,7 @@ enum { MLSTM_FP32 = 0, MLSTM_BF16 = 1 };
 /* tile-kernel selector for mlstm_causal_tiles */
 enum {
   MLSTM_KERNEL_AUTO = 0,   /* bf16 -> matrix-core kernel; fp32 -> float32 matrix-core kernel
-                              (d a multiple of 32 up to 256, or 320, 384), else vector kernel */
+                              (d a multiple of 32 up to 256, or 320, 384, 512), else vector kernel */
   MLSTM_KERNEL_MFMA = 1,   /* bf16 only: bf16 MFMA tiles (the production path) */
   MLSTM_KERNEL_VECTOR = 2, /* any dtype: float32 vector-ALU tiles, no bf16 rounding of C~' */
   MLSTM_KERNEL_MFMA_ALL_TILES = 3, /* as MLSTM_KERNEL_MFMA, but visiting every causal tile */
@@ -92,7 +92,7 @@ enum {
  * matrix instruction v_mfma_f32_32x32x2_f32: 4 waves, one per SIMD, each with
  * 32 query rows and their Q^T operands in registers, C~' kept in float32 and
  * fed from the first product's registers to the second; above d = 256 two
- * workgroups per 128 query rows take half of the output columns each.  Other
+ * (at d = 512 four) workgroups per 128 query rows split the output columns.  Other
  * float32 head dimensions, and MLSTM_KERNEL_VECTOR, run the float32 vector
  * kernel.
  */

@@ -170,7 +170,8 @@ hipError_t launch_tiles_wide(const void* q, const void* k, const void* v, const 
                              hipStream_t stream);
 
 // Stage 2, float32 matrix-core tiles (v_mfma_f32_32x32x2_f32) for float32
-// inputs, d a multiple of 32 up to 384; `skip` as for the bf16 kernels.
+// inputs, d a multiple of 32 up to 256, or 320, 384, 512; `skip` as for the
+// bf16 kernels.
 bool tiles_f32_supports(int64_t d);
 hipError_t launch_tiles_f32(const void* q, const void* k, const void* v, const float* m,
                             const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,

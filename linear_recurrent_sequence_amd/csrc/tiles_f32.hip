@@ -7,8 +7,10 @@
 // Work decomposition.  A workgroup of 4 waves (one per SIMD) owns 128 query
 // rows of one head, 32 per wave, and walks the key axis in 32-key tiles up
 // to its diagonal.  A wave holds its rows' Q^T fragments (the B operand of
-// S^T = K Q^T) and all d output columns of O^T = V^T C~'^T: d / 2 + d / 2
-// registers per lane, which caps this kernel at d = 384.
+// S^T = K Q^T) and the output columns of O^T = V^T C~'^T: all of them up
+// to d = 256 (d / 2 + d / 2 registers per lane); above, two workgroups per
+// row block (four at d = 512) take a share of the 32-column output blocks
+// each and all of them form S.
 //
 // Reduction order.  The instruction sums over 2 indices k = lane / 32.  In
 // step 4u + v of the first product, lane (g, l) takes head dim 8u + 4g + v,
@@ -52,13 +54,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // offsets differ by 128 modulo 256 bytes: all 64 banks once.
 template <int DP>
 struct FCfg {
-  static_assert(DP % 32 == 0 && DP >= 32 && DP <= 384, "head dim of the float32 MFMA kernel");
-  static_assert(DP <= 256 || DP % 64 == 0, "above 256 the columns split in halves of 32-col blocks");
+  static_assert(DP % 32 == 0 && DP >= 32 && DP <= 512, "head dim of the float32 MFMA kernel");
+  static_assert(DP <= 256 || (DP <= 384 && DP % 64 == 0) || DP == 512,
+                "above 256 the columns split into halves (d = 320, 384) or quarters (d = 512)");
   static constexpr int RB = 4 * DP;       // bytes of a row in memory
   static constexpr int CH = DP / 4;       // 16-byte chunks per row
   static constexpr int NCP = (CH + 63) / 64;  // copy instructions per row
   static constexpr int RSK = RB + 16;
-  static constexpr int RSV = 4 * 32 * (DP / 32 / (DP <= 256 ? 1 : 2)) + 32;
+  static constexpr int RSV = 4 * 32 * (DP / 32 / (DP <= 256 ? 1 : DP <= 384 ? 2 : 4)) + 32;
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = kBN * RSK;
   static constexpr int BYTES = V_OFF + kBN * RSV;
@@ -66,7 +69,7 @@ struct FCfg {
   // output columns: above d = 256 two workgroups per row block take half of
   // the 32-column blocks each (both form S, whose registers and the Q^T
   // operands' would otherwise not fit beside all the accumulators)
-  static constexpr int NSPLIT = DP <= 256 ? 1 : 2;
+  static constexpr int NSPLIT = DP <= 256 ? 1 : DP <= 384 ? 2 : 4;
   static constexpr int NB = DP / 32 / NSPLIT;  // 32-column output blocks of a workgroup
   static constexpr int VC = 32 * NB;           // V columns a workgroup copies and reads
   static constexpr int RVB = 4 * VC;           // bytes of those columns in a row
@@ -374,7 +377,7 @@ hipError_t launch_f(const void* q, const void* k, const void* v, const float* m,
 }  // namespace
 
 bool tiles_f32_supports(int64_t d) {
-  return d % 32 == 0 && d >= 32 && (d <= 256 || (d % 64 == 0 && d <= 384));
+  return d % 32 == 0 && d >= 32 && (d <= 256 || (d % 64 == 0 && d <= 384) || d == 512);
 }
 
 hipError_t launch_tiles_f32(const void* q, const void* k, const void* v, const float* m,
@@ -393,6 +396,7 @@ hipError_t launch_tiles_f32(const void* q, const void* k, const void* v, const f
     case 8: return MLSTM_DP(8);
     case 10: return MLSTM_DP(10);
     case 12: return MLSTM_DP(12);
+    case 16: return MLSTM_DP(16);
     default: return hipErrorInvalidValue;
   }
 #undef MLSTM_DP

@@ -119,6 +119,7 @@ def test_fp32_ragged_full(s):
 F32_MFMA_CASES = [
     spec(1, 1, 4, 32, "fp32"), spec(1, 2, 129, 96, "fp32"), spec(2, 1, 260, 192, "fp32"),
     spec(1, 1, 200, 256, "fp32"), spec(1, 1, 161, 320, "fp32"), spec(1, 2, 140, 384, "fp32"),
+    spec(1, 1, 150, 512, "fp32"),
     spec(1, 2, 500, 64, "fp32", ig=("uniform", -20, 20), fg=("normal", 0, 4),
          fgate_floor=(0.01, -30.0)),
     spec(1, 1, 333, 128, "fp32", ig=("uniform", -40, 40), fg=("normal", -2, 3)),
@@ -128,8 +129,8 @@ F32_MFMA_CASES = [
 
 @pytest.mark.parametrize("s", F32_MFMA_CASES, ids=_id)
 def test_fp32_matrix_core_kernel_full(s):
-    """Float32 inputs with d a multiple of 32 up to 256 (and 320, 384, where
-    two workgroups per row block take half of the columns each) run on the
+    """Float32 inputs with d a multiple of 32 up to 256 (and 320, 384, 512,
+    where two or four workgroups per row block split the columns) run on the
     float32 matrix instruction: against the oracle on every row (ragged
     tails, several row tiles, tiles skipped under strong decay), and against
     the float32 vector kernel (the same exponents, other summation orders)."""
