@@ -30,6 +30,8 @@
 // (backward_mfma.hip, whose rows pass also forms the per-row scalars); the
 // gate-gradient scan is shared.
 #include <cstdlib>
+#include <cstring>
+#include <type_traits>
 
 #include "mlstm_internal.h"
 
@@ -539,7 +541,7 @@ hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* f
                         const Tin* dh, const Workspace& ws, float* inv_n, float* db, float* rsum,
                         float* csum, void* vstore, Tin* dq, Tin* dk, Tin* dv, float* digate,
                         float* dfgate, int64_t H, int64_t T, int64_t d, bool exp_forget, bool mfma,
-                        hipStream_t stream) {
+                        bool f32_tiles, hipStream_t stream) {
   if (mfma) {  // the rows pass forms the per-row scalars itself
     const hipError_t e = launch_backward_mfma_tiles(q, k, v, dh, h, m, n, b, inv_n, db, ws, dq,
                                                     dk, dv, rsum, csum, vstore, H, T, d, stream);
@@ -549,7 +551,13 @@ hipError_t launch_typed(const Tin* q, const Tin* k, const Tin* v, const float* f
     hipLaunchKernelGGL(bwd_rows_prep_kernel<Tin>, dim3(unsigned((rows + 3) / 4)), dim3(256), 0,
                        stream, h, dh, m, n, b, inv_n, db, rows, int(d));
     const int64_t tiles = (T + kBT - 1) / kBT;
-    if (d <= kBMaxD) {
+    if (f32_tiles) {  // float32 inputs only
+      if constexpr (std::is_same<Tin, float>::value) {
+        const hipError_t e = launch_backward_f32_tiles(q, k, v, dh, inv_n, db, ws, dq, dk, dv,
+                                                       rsum, csum, H, T, d, stream);
+        if (e != hipSuccess) return e;
+      }
+    } else if (d <= kBMaxD) {
       hipLaunchKernelGGL(bwd_rows_kernel<Tin>, dim3(unsigned(tiles * H)), dim3(256), 0, stream,
                          q, k, v, dh, inv_n, db, ws.rowt, ws.colt, dq, rsum, T, int(d), ws.Tp,
                          tiles);
@@ -616,14 +624,19 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const fl
                              b, static_cast<const B16*>(dh), ws, inv_n, db, rsum, csum, vstore,
                              static_cast<B16*>(dq), static_cast<B16*>(dk), static_cast<B16*>(dv),
                              digate, dfgate, H, T, d, exp_forget, backward_mfma_supports(d),
-                             stream);
+                             false, stream);
   }
+  // float32 inputs: the matrix-core passes where they apply, unless the
+  // environment variable MLSTM_BWD_F32=vector asks for the vector passes
+  const char* sel = std::getenv("MLSTM_BWD_F32");
+  const bool f32_tiles =
+      backward_f32_supports(d) && !(sel != nullptr && std::strcmp(sel, "vector") == 0);
   return launch_typed<float>(static_cast<const float*>(q), static_cast<const float*>(k),
                              static_cast<const float*>(v), fgate, static_cast<const float*>(h), m,
                              n, b, static_cast<const float*>(dh), ws, inv_n, db, rsum, csum,
                              nullptr, static_cast<float*>(dq), static_cast<float*>(dk),
                              static_cast<float*>(dv), digate, dfgate, H, T, d, exp_forget, false,
-                             stream);
+                             f32_tiles, stream);
 }
 
 }  // namespace mlstm

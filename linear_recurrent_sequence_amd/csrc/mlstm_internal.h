@@ -217,6 +217,17 @@ hipError_t launch_backward_mfma_tiles(const void* q, const void* k, const void* 
                                       float* rsum, float* csum, void* vstore, int64_t H,
                                       int64_t T, int64_t d, hipStream_t stream);
 
+// The row and column passes of the backward on the float32 matrix
+// instruction (float32 inputs, d a multiple of 32 up to 384): dQ and the row
+// sums r of dD~, dK and the column sums c, dV, from the per-row scalars 1/n
+// and db.
+bool backward_f32_supports(int64_t d);
+hipError_t launch_backward_f32_tiles(const float* q, const float* k, const float* v,
+                                     const float* dh, const float* inv_n, const float* db,
+                                     const Workspace& ws, float* dq, float* dk, float* dv,
+                                     float* rsum, float* csum, int64_t H, int64_t T, int64_t d,
+                                     hipStream_t stream);
+
 // Recurrent step (generation), stabilized states in float32: C [H][d][d],
 // n [H][d], m [H].  C_out may equal C_in; n_out / m_out must not overlap
 // n_in / m_in.  den_out [H] is optional.  hipErrorInvalidValue for an

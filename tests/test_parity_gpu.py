@@ -1052,6 +1052,61 @@ def test_backward_stored_operands_against_the_recomputing_passes(shape, monkeypa
 
 
 # ---------------------------------------------------------------------------
+# backward on the float32 matrix instruction (float32 inputs, d a multiple of
+# 32 up to 384); d = 352 and 384 put the partial products in the spare tile
+# buffer (three barriers per tile)
+# ---------------------------------------------------------------------------
+
+BWD_F32_CASES = [
+    spec(1, 1, 1, 32, "fp32"), spec(1, 2, 77, 64, "fp32"), spec(1, 1, 100, 96, "fp32"),
+    spec(2, 1, 161, 128, "fp32", ig=("normal", 0, 2), fg=("normal", 1, 2)),
+    spec(8, 1, 70, 64, "fp32"),  # head count divisible by 8 (XCD-grouped schedule)
+    spec(1, 1, 130, 256, "fp32"), spec(1, 1, 99, 320, "fp32"), spec(1, 1, 140, 352, "fp32"),
+    spec(1, 2, 200, 384, "fp32"), spec(1, 1, 33, 224, "fp32"),
+    spec(1, 2, 150, 160, "fp32", ig=("uniform", -20, 20), fg=("normal", 0, 4),
+         fgate_floor=(0.01, -30.0)),
+]
+
+
+def _grads_gpu(x, dh_np):
+    q, k, v, ig, fg = _dev(x)
+    dh = torch.from_numpy(dh_np).to("cuda").to(q.dtype).contiguous()
+    h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg)
+    grads = mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, dh)
+    torch.cuda.synchronize()
+    return [_host(t) for t in grads]
+
+
+@pytest.mark.parametrize("s", BWD_F32_CASES, ids=_id)
+def test_backward_f32_matrix_core_matches_oracle(s, monkeypatch):
+    """Against the oracle's Eqs. 87-105, and against the float32 vector passes
+    on the same inputs (same per-entry formulas and exponents, the products
+    summed in another order): both to the float32 bar."""
+    x = W.make(s, seed=43)
+    dh_np = np.random.default_rng(44).standard_normal(x["q"].shape).astype(np.float32)
+    monkeypatch.delenv("MLSTM_BWD_F32", raising=False)
+    got, ref, fwd = _backward_case(x, dh_np)
+    _check_backward(got, ref, fwd, "fp32")
+    monkeypatch.setenv("MLSTM_BWD_F32", "vector")
+    vec = _grads_gpu(x, dh_np)
+    _check_backward(got, vec, fwd, "fp32")
+    again = _grads_gpu(x, dh_np)
+    monkeypatch.delenv("MLSTM_BWD_F32")
+    assert all(np.array_equal(a, b) for a, b in zip(vec, again))
+    assert all(np.array_equal(a, b) for a, b in zip(got, _grads_gpu(x, dh_np))), "deterministic"
+
+
+def test_backward_f32_matrix_core_full_size_sampled_heads():
+    """The 125M-shaped layer (B=8, NH=4, T=2048, d=384) in float32: two heads
+    against the oracle."""
+    base = W.WORKLOADS["xlstm125m_layer"]
+    x = W.make(dict(base, dtype="fp32"), seed=0)
+    dh_np = np.random.default_rng(45).standard_normal(x["q"].shape).astype(np.float32)
+    got, ref, fwd = _backward_case(x, dh_np, heads=[(0, 0), (7, 3)])
+    _check_backward(got, ref, fwd, "fp32")
+
+
+# ---------------------------------------------------------------------------
 # large shapes: a 65536-position head (512 row tiles, 2048 key tiles) and a
 # thousand small heads (grid and index arithmetic at size)
 # ---------------------------------------------------------------------------
