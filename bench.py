@@ -381,6 +381,13 @@ def fp32_layer_timing(torch, mlstm, workloads, dev, reps=20):
     tile_ms = timed(lambda: mlstm.causal_tiles(q, k, v, m, ws, out=(h, n)), reps)
     vec_ms = timed(lambda: mlstm.causal_tiles(q, k, v, m, ws, kernel="vector", out=(h, n)), 2)
     flops = workloads.counted_flops(B, NH, T, d)
+    bwd = backward_timing(torch, mlstm, workloads, x, dev, reps=5)
+    # the float32 vector passes of the backward on the same inputs
+    os.environ["MLSTM_BWD_F32"] = "vector"
+    try:
+        bwd_vec = backward_timing(torch, mlstm, workloads, x, dev, reps=1)
+    finally:
+        del os.environ["MLSTM_BWD_F32"]
     return {"workload": spec["name"], "B": B, "NH": NH, "T": T, "d": d, "dtype": "f32",
             "kernel": "tiles_f32_kernel<384> (output columns split over two workgroups)",
             "ms_per_call": round(call_ms, 4),
@@ -390,7 +397,8 @@ def fp32_layer_timing(torch, mlstm, workloads, dev, reps=20):
             "peak_fp32": PEAK_FP32_TFLOPS,
             "tile_frac": round(flops / (tile_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
             "executed_frac": round(1.5 * flops / (tile_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
-            "vector_kernel_ms": round(vec_ms, 3)}
+            "vector_kernel_ms": round(vec_ms, 3),
+            "backward": bwd, "backward_vector_passes_ms": bwd_vec["ms_per_call"]}
 
 
 def recurrent_decode(torch, mlstm, dev, B, NH, d, reps=50):
@@ -435,7 +443,8 @@ def backward_timing(torch, mlstm, workloads, x, dev, reps=20):
     h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg)
     dh = torch.randn(q.shape, generator=torch.Generator().manual_seed(1)).to(dev).to(dt)
     mfma = spec["dtype"] == "bf16" and d <= 512
-    if not mfma:
+    f32mm = spec["dtype"] == "fp32" and d % 32 == 0 and 32 <= d <= 384
+    if not (mfma or f32mm):
         reps = 3
     for _ in range(2):
         mlstm.parallel_bwd(q, k, v, ig, fg, h, m, n, b, dh)
@@ -454,17 +463,19 @@ def backward_timing(torch, mlstm, workloads, x, dev, reps=20):
     # stores the operands of the dV and dQ passes, which only accumulate (5
     # contractions; 7 above d = 384, where the keys pass splits the output
     # columns over two workgroups that both form S and dh v^T).  The vector
-    # passes recompute S and dh v^T once (7)
-    executed = ((2.5 if d <= 384 else 3.5) if mfma else 3.5) * cf
-    peak = PEAK_BF16_TFLOPS if mfma else 157.3
+    # passes recompute S and dh v^T once (7).  The float32 matrix-core passes
+    # each form their own S (rows, keys, values) and dh v^T (rows, keys): 8
+    executed = ((2.5 if d <= 384 else 3.5) if mfma else 4.0 if f32mm else 3.5) * cf
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_TFLOPS
     return {"ms_per_call": round(ms, 4), "reps": reps,
             "kernels": "bf16 matrix-core passes (per-row scalars; dK, c and the stored dV and dQ "
                        "operands; dV; dQ)" if mfma
-                       else "float32 vector passes",
+                       else "float32 matrix-core passes (per-row scalars; dQ, r; dK, c; dV)"
+                       if f32mm else "float32 vector passes",
             "counted_flops": counted,
             "counted_TFLOP/s": round(counted / (ms * 1e-3) / 1e12, 2),
             "executed_TFLOP/s": round(executed / (ms * 1e-3) / 1e12, 2),
-            "bound": "mfma" if mfma else "alu", "peak": peak,
+            "bound": "mfma" if (mfma or f32mm) else "alu", "peak": peak,
             "frac": round(counted / (ms * 1e-3) / 1e12 / peak, 4)}
 
 

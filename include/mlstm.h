@@ -283,10 +283,13 @@ int mlstm_parallel_fwd_train(const void* q, const void* k, const void* v,
  * on the matrix cores (bf16 operands, float32 accumulation; the operand
  * E (.) dC~' of the dQ and dK products and C~'/n of the dV product are
  * rounded to bf16, the row and column sums of dD~ behind the gate gradients
- * are not); for float32, and for bf16 above d = 512, everything is float32
- * on the vector ALUs (above d = 512 in head-dimension chunks, a correctness
- * path far slower than the matrix cores).  Results are bitwise
- * reproducible.  The library allocates a stream-ordered workspace: per-row
+ * are not); for float32 with d a multiple of 32 up to 384 they run on the
+ * float32 matrix instruction (float32 operands and sums throughout; the
+ * environment variable MLSTM_BWD_F32=vector, read at each call, selects the
+ * vector passes instead); for the other float32 head dims, and for bf16
+ * above d = 512, everything is float32 on the vector ALUs (above d = 512 in
+ * head-dimension chunks, a correctness path far slower than the matrix
+ * cores).  Results are bitwise reproducible.  The library allocates a stream-ordered workspace: per-row
  * terms and, for bf16 on the matrix cores, the bf16 operands of the dV and
  * dQ products, which the key pass stores so that the dV and dQ passes need
  * not recompute S and G: 8 KiB per head, 128-key block and 32-query tile of
