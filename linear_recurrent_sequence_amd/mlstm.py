@@ -14,6 +14,7 @@ Returns h~ (same dtype as q), m and n (float32), as defined by Eqs. 80, 84 and
 stabilized forward pass).
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -96,6 +97,12 @@ def _require(name, t, shape, dtype, device=None):
     ``dtype`` (and, if ``device`` is given, on that GPU).  Every tensor handed
     to the C ABI goes through here first: a host pointer, a wrong element type
     or a short buffer would otherwise reach the kernels."""
+    # the common case in one expression (each tensor attribute read costs the
+    # host time of a small kernel launch); the messages below on failure
+    if (isinstance(t, torch.Tensor) and t.dtype == dtype and t.shape == shape
+            and t.is_contiguous() and (device is None or t.device == device)):
+        if device is None or device.type == "cuda":
+            return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
     if tuple(t.shape) != tuple(shape):
@@ -136,13 +143,30 @@ def _check_inputs(q, k, v, igate, fgate):
         _require(name, t, q.shape, q.dtype)
     for name, t in named[3:]:
         _require(name, t, (B, NH, T), torch.float32)
+    dev = q.device
+    if dev.type == "cuda" and k.device == dev and v.device == dev and igate.device == dev \
+            and fgate.device == dev:
+        return B, NH, T, d
     for name, t in named:  # devices last: a malformed tensor is named first
-        _require_device(name, t, q.device)
+        _require_device(name, t, dev)
     return B, NH, T, d
 
 
 def _stream_ptr(device):
+    """The current HIP stream of ``device`` (torch's raw-stream query where
+    this build has it: it skips building a Stream object)."""
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return ctypes.c_void_p(raw(device.index if device.index is not None
+                                   else torch.cuda.current_device()))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _on(device):
+    """torch.cuda.device(device), or nothing when it is already current."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
 
 
 def parallel_fwd(q, k, v, igate, fgate, out=None):
@@ -161,7 +185,7 @@ def parallel_fwd(q, k, v, igate, fgate, out=None):
         _require("h", h, q.shape, q.dtype, q.device)
         _require("m", m, (B, NH, T), torch.float32, q.device)
         _require("n", n, (B, NH, T), torch.float32, q.device)
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         st = lib.mlstm_parallel_fwd_stream(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
             h.data_ptr(), m.data_ptr(), n.data_ptr(), B, NH, T, d, _dtype_code(q),
@@ -182,7 +206,7 @@ def parallel_fwd_noalloc(q, k, v, igate, fgate, out):
     _require("h", h, q.shape, q.dtype, q.device)
     _require("m", m, (B, NH, T), torch.float32, q.device)
     _require("n", n, (B, NH, T), torch.float32, q.device)
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         st = lib.mlstm_parallel_fwd_noalloc(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
             h.data_ptr(), m.data_ptr(), n.data_ptr(), B, NH, T, d, _dtype_code(q),
@@ -205,7 +229,7 @@ def parallel_fwd_gated(q, k, v, igate, fgate, ogate, htilde=False):
     ht = torch.empty_like(q) if htilde else None
     m = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
     n = torch.empty((B, NH, T), dtype=torch.float32, device=q.device)
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         st = lib.mlstm_parallel_fwd_gated(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
             ogate.data_ptr(), h.data_ptr(), ht.data_ptr() if htilde else None, m.data_ptr(),
@@ -240,7 +264,7 @@ def gate_scan(igate, fgate, d, workspace, m=None, forget="sigmoid"):
         m = torch.empty((B, NH, T), dtype=torch.float32, device=igate.device)
     else:
         _require("m", m, (B, NH, T), torch.float32, igate.device)
-    with torch.cuda.device(igate.device):
+    with _on(igate.device):
         st = lib.mlstm_gate_scan(igate.data_ptr(), fgate.data_ptr(), m.data_ptr(),
                                  workspace.data_ptr(), workspace.numel(), B, NH, T, d,
                                  _forget_code(forget), _stream_ptr(igate.device))
@@ -263,7 +287,7 @@ def causal_tiles(q, k, v, m, workspace, kernel="auto", out=None):
         h, n = out
         _require("h", h, q.shape, q.dtype, q.device)
         _require("n", n, (B, NH, T), torch.float32, q.device)
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         st = lib.mlstm_causal_tiles(q.data_ptr(), k.data_ptr(), v.data_ptr(), m.data_ptr(),
                                     workspace.data_ptr(), workspace.numel(), h.data_ptr(),
                                     n.data_ptr(), B, NH, T, d, _dtype_code(q), KERNELS[kernel],
@@ -318,7 +342,7 @@ def recurrent_step(q, k, v, igate, fgate, state, out_state=None, den=False, forg
         _require(name, t, shp, torch.float32, q.device)
     h = torch.empty_like(q)
     dn = torch.empty((B, NH), dtype=torch.float32, device=q.device) if den else None
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         st = lib.mlstm_recurrent_step(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
             C.data_ptr(), n.data_ptr(), m.data_ptr(), Co.data_ptr(), no.data_ptr(), mo.data_ptr(),
@@ -335,7 +359,7 @@ def parallel_fwd_train(q, k, v, igate, fgate, forget="sigmoid"):
     B, NH, T, d = _check_inputs(q, k, v, igate, fgate)
     h = torch.empty_like(q)
     m, n, b = (torch.empty((B, NH, T), dtype=torch.float32, device=q.device) for _ in range(3))
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         st = lib.mlstm_parallel_fwd_train(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
             h.data_ptr(), m.data_ptr(), n.data_ptr(), b.data_ptr(), B, NH, T, d, _dtype_code(q),
@@ -355,7 +379,7 @@ def parallel_bwd(q, k, v, igate, fgate, h, m, n, b, dh, forget="sigmoid"):
         _require(name, t, (B, NH, T), torch.float32, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dig, dfg = torch.empty_like(igate), torch.empty_like(fgate)
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         st = lib.mlstm_parallel_bwd(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), igate.data_ptr(), fgate.data_ptr(),
             h.data_ptr(), m.data_ptr(), n.data_ptr(), b.data_ptr(), dh.data_ptr(),
