@@ -1052,6 +1052,53 @@ def test_backward_stored_operands_against_the_recomputing_passes(shape, monkeypa
 
 
 # ---------------------------------------------------------------------------
+# float32 head dims outside the float32 matrix-core kernel, T <= 2048: the
+# vector kernel scans its head's gates itself (one launch, no workspace)
+# ---------------------------------------------------------------------------
+
+VECTOR_FUSED_CASES = [
+    spec(1, 1, 64, 16, "fp32"), spec(1, 1, 1, 16, "fp32"), spec(2, 3, 77, 48, "fp32"),
+    spec(1, 2, 2048, 16, "fp32"), spec(1, 1, 301, 80, "fp32", ig=("normal", 0, 2)),
+    spec(1, 1, 130, 544, "fp32"), spec(1, 1, 65, 1024, "fp32"),
+    spec(1, 2, 500, 112, "fp32", ig=("uniform", -20, 20), fg=("normal", 0, 4),
+         fgate_floor=(0.01, -30.0)),
+]
+
+
+@pytest.mark.parametrize("s", VECTOR_FUSED_CASES, ids=_id)
+def test_vector_kernel_fused_scan_matches_two_launches(s):
+    """Bitwise the same h, m, n as the gate-scan launch followed by the vector
+    kernel (the same scan arithmetic in the same order), and the oracle's
+    readings."""
+    x = W.make(s, seed=46)
+    h, m, n = run_gpu(x)
+    h2, m2, n2 = run_gpu(x, kernel="vector")
+    assert np.array_equal(m, m2) and np.array_equal(n, n2) and np.array_equal(h, h2)
+    check_full(h, m, n, x, "fp32")
+
+
+@pytest.mark.parametrize("forget", ["sigmoid", "exp"])
+def test_vector_kernel_fused_scan_exp_forget_and_b(forget):
+    s = spec(1, 2, 99, 48, "fp32", fg=("normal", -0.05, 0.03) if forget == "exp" else
+             ("normal", 3.0, 1.0))
+    x = W.make(s, seed=47)
+    q, k, v, ig, fg = _dev(x)
+    h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg, forget=forget)
+    h2, m2, n2 = mlstm.parallel_fwd_staged(q, k, v, ig, fg, kernel="vector", forget=forget)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h2) and torch.equal(m, m2) and torch.equal(n, n2)
+    hr, mr, nr, br, rho, _ = oracle_full(x, forget)
+    assert b_over_bar(_host(b), br, nr, rho / nr) <= 1.0
+
+
+def test_vector_kernel_just_past_the_fused_scan():
+    """T = 2049 takes the two launches again (the fused scan covers 2048)."""
+    x = W.make(spec(1, 1, 2049, 16, "fp32"), seed=48)
+    h, m, n = run_gpu(x)
+    check_full(h, m, n, x, "fp32")
+
+
+# ---------------------------------------------------------------------------
 # backward on the float32 matrix instruction (float32 inputs, d a multiple of
 # 32 up to 384); d = 352 and 384 put the partial products in the spare tile
 # buffer (three barriers per tile)
@@ -1065,6 +1112,7 @@ BWD_F32_CASES = [
     spec(1, 2, 200, 384, "fp32"), spec(1, 1, 33, 224, "fp32"),
     spec(1, 2, 150, 160, "fp32", ig=("uniform", -20, 20), fg=("normal", 0, 4),
          fgate_floor=(0.01, -30.0)),
+    spec(1, 1, 3000, 64, "fp32"),  # 94 tiles of 32 rows, ragged tail
 ]
 
 
