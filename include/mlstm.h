@@ -152,9 +152,8 @@ enum { MLSTM_FORGET_SIGMOID = 0, MLSTM_FORGET_EXP = 1 };
  * same order, so every output is bitwise that of the two stages with the same
  * tile arithmetic: the one-wave kernel where the pipelined kernel runs, the
  * kernel MLSTM_KERNEL_AUTO picks otherwise).  So is the pass for float32
- * inputs with T <= 2048 and a d that the float32 matrix-core kernel does not
- * take (d not a multiple of 32, 288, 352, 416 .. 480 and above 512): the
- * float32 vector kernel scans its head's gates itself, bitwise as its two
+ * inputs with T <= 2048: the float32 tile kernel (matrix-core where it takes
+ * d, vector otherwise) scans its head's gates itself, bitwise as its two
  * stages would.  Otherwise the gate scan and the tile kernel run as two
  * launches on a library-allocated, stream-ordered workspace.
  * Returns MLSTM_OK or a negative status.
@@ -181,8 +180,8 @@ int mlstm_parallel_fwd_stream(const void* q, const void* k, const void* v,
  * of B * NH * T, T padded to a multiple of 128: up to ~800 K positions) and
  * returns MLSTM_ERR_SCRATCH, before any device work, for a problem that needs
  * more.  Where mlstm_parallel_fwd runs as a single launch (bf16, d <= 512,
- * T <= 2048, T a multiple of 4; float32 on the vector kernel, T <= 2048) no
- * workspace is used and any size is accepted.  All calls on one GPU share that GPU's array:
+ * T <= 2048, T a multiple of 4; float32, T <= 2048) no workspace is used
+ * and any size is accepted.  All calls on one GPU share that GPU's array:
  * calls that overlap in time on one GPU (different streams, host threads)
  * race and must be serialized by the caller.  Nothing needs to be cleared between calls: each
  * call writes every workspace byte it reads.  Arguments, results and other

@@ -153,13 +153,18 @@ bool vector_fused_path(int64_t T, int64_t d, int dtype) {
          mlstm::tiles_vector_fused_supports(T, d);
 }
 
+// float32 inputs on the float32 matrix-core kernel, same sequence bound
+bool f32_fused_path(int64_t T, int64_t d, int dtype) {
+  return dtype == MLSTM_FP32 && mlstm::tiles_f32_fused_supports(T, d);
+}
+
 // Whether the whole pass runs as one launch of the tile kernel that scans its
 // gates itself (no workspace).
 bool fused_path(int64_t T, int64_t d, int dtype) {
   return (dtype == MLSTM_BF16 &&
           (mlstm::tiles_pipe_preferred(T, d) || mlstm::tiles_pairs_fused_supports(T, d) ||
            mlstm::tiles_mfma_fused_supports(T, d))) ||
-         vector_fused_path(T, d, dtype);
+         vector_fused_path(T, d, dtype) || f32_fused_path(T, d, dtype);
 }
 
 // Both stages on a given workspace (mlstm::workspace_bytes(B * NH, T) bytes,
@@ -170,6 +175,9 @@ int forward_on(void* ws, const void* q, const void* k, const void* v, const floa
                float* n_out, int64_t B, int64_t NH, int64_t T, int64_t d, int dtype,
                hipStream_t s, bool exp_forget) {
   const int64_t H = B * NH;
+  if (f32_fused_path(T, d, dtype))
+    return hip_status(mlstm::launch_tiles_f32_fused(q, k, v, igate, fgate, h_out, m_out, n_out,
+                                                    ep, exp_forget, H, T, d, s));
   if (vector_fused_path(T, d, dtype))
     return hip_status(mlstm::launch_tiles_vector_fused(q, k, v, igate, fgate, h_out, m_out, n_out,
                                                        ep, exp_forget, H, T, d, false, s));

@@ -183,6 +183,14 @@ hipError_t launch_tiles_vector(const void* q, const void* k, const void* v, cons
                                const Epilogue& ep, int64_t H, int64_t T, int64_t d,
                                bool is_bf16, hipStream_t stream);
 
+// Both stages in one launch on the float32 matrix-core kernel (T <= 2048, a
+// d it takes): the kernel scans its head's gates in its prologue.
+bool tiles_f32_fused_supports(int64_t T, int64_t d);
+hipError_t launch_tiles_f32_fused(const void* q, const void* k, const void* v, const float* igate,
+                                  const float* fgate, void* h_out, float* m_out, float* n_out,
+                                  const Epilogue& ep, bool exp_forget, int64_t H, int64_t T,
+                                  int64_t d, hipStream_t stream);
+
 // Both stages in one launch on the vector tiles (T <= 2048, any d of the
 // vector kernel): the kernel scans its head's gates in its prologue.
 bool tiles_vector_fused_supports(int64_t T, int64_t d);

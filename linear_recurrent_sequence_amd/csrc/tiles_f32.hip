@@ -33,7 +33,16 @@
 // in the float32 vector kernel; the causal mask of Eq. 71 on the diagonal
 // tile.  A tile whose exponent bound is below kSkipLog2 for a wave's rows
 // contributes exactly zero and is not multiplied.
+//
+// On sequences of at most 2048 positions the kernel can also scan its head's
+// gates itself (the whole pass in one launch, no workspace), as the bf16
+// single-launch kernels do: its 256 threads run the gate-scan kernel's
+// 512-thread block scan over positions [0, q0 + 128), two scan threads each,
+// so every term is bitwise that of the two-launch path; C_j and the key-tile
+// bounds of those positions, R_i, m and the row-block bounds of the
+// workgroup's rows stay in LDS.
 #include "mlstm_internal.h"
+#include "scan_common.h"
 #include "tile_common.h"
 
 namespace mlstm {
@@ -44,6 +53,7 @@ using namespace tilecommon;
 constexpr int kFThreads = 256;
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kFPf = 4;  // LDS operand prefetch distance (reads)
+constexpr int kFFusedMaxT = scan::kScanThreads * scan::kScanPer;  // one block scan: 2048
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -81,7 +91,7 @@ struct FCfg {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int DP>
+template <int DP, bool FUSED>
 __global__ __attribute__((amdgpu_flat_work_group_size(kFThreads, kFThreads),
                           amdgpu_waves_per_eu(1, 1))) void tiles_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
@@ -89,10 +99,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kFThreads, kFThreads),
     const double* __restrict__ colt, const double* __restrict__ rowb,
     const double* __restrict__ keyb, float* __restrict__ h_out, float* __restrict__ n_out,
     const float* __restrict__ ogate, float* __restrict__ htilde, float* __restrict__ b_out,
-    int T, int Tp, int row_tiles, int H, int skip) {
+    int T, int Tp, int row_tiles, int H, int skip, FusedGates fg) {
   using C = FCfg<DP>;
   __shared__ __attribute__((aligned(1024))) char lds[C::BYTES];
   __shared__ int s_first[kFWaves];
+  // fused gate scan: C_j and key-tile bounds of positions [0, q0 + 128);
+  // R_i, m and the row-block bounds of the workgroup's 128 rows
+  __shared__ double f_c[FUSED ? kFFusedMaxT : 1];
+  __shared__ double f_kb[FUSED ? kFFusedMaxT / kBoundTile : 1];
+  __shared__ double f_r[FUSED ? kBM : 1];
+  __shared__ double f_rb[FUSED ? kBM / kBoundTile : 1];
+  __shared__ float f_m[FUSED ? kBM : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,6 +154,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kFThreads, kFThreads),
   const unsigned lds_k = lds_addr(lds + C::K_OFF + 8 * w * C::RSK);
   const unsigned lds_v = lds_addr(lds + C::V_OFF + 8 * w * C::RSV);
 
+  // ---- fused gate scan, first part: the gate loads, in flight during the Q
+  // staging below.  Positions at or past t_eff are padding (no forgetting, no
+  // input): they follow every position this workgroup reads.
+  const int t_eff = T < q0 + kBM ? T : q0 + kBM;
+  float g_fr[2][scan::kScanPer], g_iv[2][scan::kScanPer];
+  bool g_active[2];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int p0 = scan::kScanPer * (tid + (scan::kScanThreads / 2) * u);
+      g_active[u] = scan::kScanPer * 64 * (w + 4 * u) < t_eff;  // uniform across the wave
+#pragma unroll
+      for (int e = 0; e < scan::kScanPer; ++e) {
+        g_fr[u][e] = 0.0f;
+        g_iv[u][e] = -INFINITY;
+      }
+      if (g_active[u])
+        scan::load_raw(fg.fgate + int64_t(head) * T, fg.igate + int64_t(head) * T, p0, t_eff,
+                       (T & 3) == 0, g_fr[u], g_iv[u]);
+    }
+  }
+
   // ---- prologue: each wave stages its own 32 Q rows in its own LDS region,
   // a quarter of the head dimension at a time (rows of d bytes at a stride of
   // d + 16), and reads its Q^T operand groups of that quarter; no barrier
@@ -177,13 +216,64 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kFThreads, kFThreads),
   }
   __syncthreads();  // every wave's staging is done before the tile region is filled
 
+  // ---- fused gate scan, second part: the block scan and the terms
+  if constexpr (FUSED) {
+    using namespace scan;
+    double fb[2][kScanPer];
+    Elem mine[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int p0 = kScanPer * (tid + (kScanThreads / 2) * u);
+#pragma unroll
+      for (int e = 0; e < kScanPer; ++e) fb[u][e] = 0.0;
+      if (g_active[u]) to_log_forget(p0, t_eff, fg.exp_forget, g_fr[u], fb[u]);
+      mine[u] = thread_elem(fb[u], g_iv[u]);
+    }
+    Elem before[2], total;
+    block_scan_halves(mine[0], mine[1], before[0], before[1], total);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!g_active[u]) continue;
+      const int p0 = kScanPer * (tid + (kScanThreads / 2) * u);
+      Terms tm;
+      position_terms(identity(), before[u], fb[u], g_iv[u], p0, t_eff, fg.half_ln_d, tm);
+      if ((p0 & (kBoundTile - 1)) == 0) {
+        f_kb[p0 / kBoundTile] = tm.cmax;
+        if (p0 >= q0) f_rb[(p0 - q0) / kBoundTile] = tm.rmax;
+      }
+#pragma unroll
+      for (int e = 0; e < kScanPer; ++e) {
+        const int p = p0 + e;
+        if (p < t_eff) {
+          f_c[p] = tm.c[e];
+          if (p >= q0) {
+            f_r[p - q0] = tm.r[e];
+            f_m[p - q0] = tm.m[e];
+            if (cs == 0) fg.m_out[int64_t(head) * T + p] = tm.m[e];
+          }
+        } else if (p >= q0 && p < q0 + kBM) {  // rows past the sequence end
+          f_r[p - q0] = 0.0;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
   const int n_key_tiles = (T + kBN - 1) / kBN;
   const int last_tile = (4 * I + 3 < n_key_tiles - 1) ? 4 * I + 3 : n_key_tiles - 1;
   const int wave_last = (4 * I + w < n_key_tiles - 1) ? 4 * I + w : n_key_tiles - 1;
-  const double r_i = rowt[int64_t(head) * Tp + qi];  // R_i (qi < Tp)
-  const double rb_w = rowb[int64_t(head) * nb32 + qw / kBoundTile];
+  // R_i (qi < Tp) and this wave's row-block bound
+  const double r_i = FUSED ? (qi < t_eff ? f_r[qi - q0] : 0.0) : rowt[int64_t(head) * Tp + qi];
+  auto row_bound = [&](int u) {  // bound of the workgroup's 32-row block u
+    if constexpr (FUSED) return q0 + 32 * u < t_eff ? f_rb[u] : 0.0;
+    else return rowb[int64_t(head) * nb32 + (q0 + 32 * u) / kBoundTile];
+  };
+  const double rb_w = row_bound(w);
   auto tile_needed = [&](double rb, double kb) { return rb + kb >= kSkipLog2; };
-  auto key_bound = [&](int J) { return keyb[int64_t(head) * nb32 + J]; };
+  auto key_bound = [&](int J) {
+    if constexpr (FUSED) return f_kb[J];
+    else return keyb[int64_t(head) * nb32 + J];
+  };
 
   // ---- decay-aware start: the first tile some wave needs
   int first = 0;
@@ -192,7 +282,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kFThreads, kFThreads),
     int last_w[kFWaves];
 #pragma unroll
     for (int u = 0; u < kFWaves; ++u) {
-      rb_rows[u] = rowb[int64_t(head) * nb32 + (q0 + 32 * u) / kBoundTile];
+      rb_rows[u] = row_bound(u);
       last_w[u] = (4 * I + u < n_key_tiles - 1) ? 4 * I + u : n_key_tiles - 1;
     }
     int mine = last_tile;
@@ -267,8 +357,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kFThreads, kFThreads),
         if constexpr (u == (3 * C::NU) / 4) {
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq) {
-            cd[2 * rq] = *reinterpret_cast<const double2*>(cj + 8 * rq);
-            cd[2 * rq + 1] = *reinterpret_cast<const double2*>(cj + 8 * rq + 2);
+            if constexpr (FUSED) {
+              const int o = J * kBN + 4 * g + 8 * rq;  // < q0 + 128: formed by the scan
+              cd[2 * rq] = make_double2(f_c[o], f_c[o + 1]);
+              cd[2 * rq + 1] = make_double2(f_c[o + 2], f_c[o + 3]);
+            } else {
+              cd[2 * rq] = *reinterpret_cast<const double2*>(cj + 8 * rq);
+              cd[2 * rq + 1] = *reinterpret_cast<const double2*>(cj + 8 * rq + 2);
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -331,7 +427,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kFThreads, kFThreads),
   // h~ = acc / n (Eqs. 85, 86), output gate (Eq. 78)
   bsum += __shfl_xor(bsum, 32, 64);
   if (qi < T) {
-    const float nn = fmaxf(fabsf(bsum), expf(-m_in[int64_t(head) * T + qi]));
+    const float m_i = FUSED ? f_m[qi - q0] : m_in[int64_t(head) * T + qi];
+    const float nn = fmaxf(fabsf(bsum), expf(-m_i));
     if (g == 0 && cs == 0) {
       n_out[int64_t(head) * T + qi] = nn;
       if (b_out) b_out[int64_t(head) * T + qi] = bsum;
@@ -359,32 +456,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kFThreads, kFThreads),
   }
 }
 
-template <int DP>
+template <int DP, bool FUSED>
 hipError_t launch_f(const void* q, const void* k, const void* v, const float* m,
                     const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep, bool skip,
-                    int64_t H, int64_t T, hipStream_t stream) {
+                    int64_t H, int64_t T, const FusedGates& fg, hipStream_t stream) {
   const int64_t row_tiles = (T + kBM - 1) / kBM;
-  hipLaunchKernelGGL((tiles_f32_kernel<DP>), dim3(unsigned(row_tiles * H * FCfg<DP>::NSPLIT)),
-                     dim3(kFThreads), 0,
+  hipLaunchKernelGGL((tiles_f32_kernel<DP, FUSED>),
+                     dim3(unsigned(row_tiles * H * FCfg<DP>::NSPLIT)), dim3(kFThreads), 0,
                      stream, static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), m, ws.rowt, ws.colt, ws.rowb, ws.keyb,
                      static_cast<float*>(h_out), n_out, static_cast<const float*>(ep.ogate),
                      static_cast<float*>(ep.htilde), ep.b, int(T), int(ws.Tp), int(row_tiles),
-                     int(H), int(skip));
+                     int(H), int(skip), fg);
   return hipGetLastError();
 }
 
-}  // namespace
-
-bool tiles_f32_supports(int64_t d) {
-  return d % 32 == 0 && d >= 32 && (d <= 256 || (d % 64 == 0 && d <= 384) || d == 512);
-}
-
-hipError_t launch_tiles_f32(const void* q, const void* k, const void* v, const float* m,
-                            const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,
-                            bool skip, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
-  if (!tiles_f32_supports(d)) return hipErrorInvalidValue;
-#define MLSTM_DP(n) launch_f<32 * n>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, stream)
+template <bool FUSED>
+hipError_t launch_any(const void* q, const void* k, const void* v, const float* m,
+                      const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,
+                      bool skip, int64_t H, int64_t T, int64_t d, const FusedGates& fg,
+                      hipStream_t stream) {
+#define MLSTM_DP(n) \
+  launch_f<32 * n, FUSED>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, fg, stream)
   switch (d / 32) {
     case 1: return MLSTM_DP(1);
     case 2: return MLSTM_DP(2);
@@ -400,6 +493,39 @@ hipError_t launch_tiles_f32(const void* q, const void* k, const void* v, const f
     default: return hipErrorInvalidValue;
   }
 #undef MLSTM_DP
+}
+
+}  // namespace
+
+bool tiles_f32_supports(int64_t d) {
+  return d % 32 == 0 && d >= 32 && (d <= 256 || (d % 64 == 0 && d <= 384) || d == 512);
+}
+
+hipError_t launch_tiles_f32(const void* q, const void* k, const void* v, const float* m,
+                            const Workspace& ws, void* h_out, float* n_out, const Epilogue& ep,
+                            bool skip, int64_t H, int64_t T, int64_t d, hipStream_t stream) {
+  if (!tiles_f32_supports(d)) return hipErrorInvalidValue;
+  return launch_any<false>(q, k, v, m, ws, h_out, n_out, ep, skip, H, T, d, FusedGates{}, stream);
+}
+
+bool tiles_f32_fused_supports(int64_t T, int64_t d) {
+  return tiles_f32_supports(d) && T >= 1 && T <= kFFusedMaxT;
+}
+
+hipError_t launch_tiles_f32_fused(const void* q, const void* k, const void* v, const float* igate,
+                                  const float* fgate, void* h_out, float* m_out, float* n_out,
+                                  const Epilogue& ep, bool exp_forget, int64_t H, int64_t T,
+                                  int64_t d, hipStream_t stream) {
+  if (!tiles_f32_fused_supports(T, d)) return hipErrorInvalidValue;
+  FusedGates fg;
+  fg.igate = igate;
+  fg.fgate = fgate;
+  fg.m_out = m_out;
+  fg.half_ln_d = 0.5 * log(double(d));  // as the gate-scan kernel forms it
+  fg.exp_forget = int(exp_forget);
+  Workspace none{};
+  none.Tp = padded_len(T);  // for the row count arithmetic only; nothing is read
+  return launch_any<true>(q, k, v, nullptr, none, h_out, n_out, ep, true, H, T, d, fg, stream);
 }
 
 }  // namespace mlstm

@@ -36,11 +36,14 @@ def _host(t):
 
 
 def run_gpu(x, kernel="auto"):
+    """mlstm_parallel_fwd (kernel "auto"), or the two stages with the given
+    tile kernel ("auto_staged": the two stages with the kernel auto picks)"""
     q, k, v, ig, fg = _dev(x)
     if kernel == "auto":
         h, m, n = mlstm.parallel_fwd(q, k, v, ig, fg)
     else:
-        h, m, n = mlstm.parallel_fwd_staged(q, k, v, ig, fg, kernel=kernel)
+        h, m, n = mlstm.parallel_fwd_staged(q, k, v, ig, fg,
+                                            kernel="auto" if kernel == "auto_staged" else kernel)
     torch.cuda.synchronize()
     return _host(h), _host(m), _host(n)
 
@@ -1089,6 +1092,48 @@ def test_vector_kernel_fused_scan_exp_forget_and_b(forget):
     assert torch.equal(h, h2) and torch.equal(m, m2) and torch.equal(n, n2)
     hr, mr, nr, br, rho, _ = oracle_full(x, forget)
     assert b_over_bar(_host(b), br, nr, rho / nr) <= 1.0
+
+
+F32_FUSED_CASES = [
+    spec(1, 1, 1, 32, "fp32"), spec(2, 3, 77, 64, "fp32"), spec(1, 2, 2048, 128, "fp32"),
+    spec(1, 1, 301, 256, "fp32", ig=("normal", 0, 2)), spec(1, 2, 500, 384, "fp32"),
+    spec(1, 1, 130, 512, "fp32"), spec(8, 1, 200, 96, "fp32"),
+    spec(1, 2, 700, 160, "fp32", ig=("uniform", -20, 20), fg=("normal", 0, 4),
+         fgate_floor=(0.01, -30.0)),
+]
+
+
+@pytest.mark.parametrize("s", F32_FUSED_CASES, ids=_id)
+def test_fp32_matrix_core_fused_scan_matches_two_launches(s):
+    """The float32 matrix-core kernel scanning its own gates (one launch):
+    bitwise the gate-scan launch followed by the same kernel, and the
+    oracle's readings."""
+    x = W.make(s, seed=49)
+    h, m, n = run_gpu(x)
+    h2, m2, n2 = run_gpu(x, kernel="auto_staged")
+    assert np.array_equal(m, m2) and np.array_equal(n, n2) and np.array_equal(h, h2)
+    check_full(h, m, n, x, "fp32")
+
+
+@pytest.mark.parametrize("forget", ["sigmoid", "exp"])
+def test_fp32_matrix_core_fused_scan_epilogues(forget):
+    s = spec(1, 2, 199, 384, "fp32", fg=("normal", -0.05, 0.03) if forget == "exp" else
+             ("normal", 3.0, 1.0))
+    x = W.make(s, seed=50)
+    q, k, v, ig, fg = _dev(x)
+    h, m, n, b = mlstm.parallel_fwd_train(q, k, v, ig, fg, forget=forget)
+    h2, m2, n2 = mlstm.parallel_fwd_staged(q, k, v, ig, fg, forget=forget)
+    og = torch.from_numpy(W.make_ogate(s, seed=51)).to("cuda")
+    hg, ht, mg, ng = mlstm.parallel_fwd_gated(q, k, v, ig, fg, og, htilde=True) \
+        if forget == "sigmoid" else (None, None, None, None)
+    torch.cuda.synchronize()
+    assert torch.equal(h, h2) and torch.equal(m, m2) and torch.equal(n, n2)
+    hr, mr, nr, br, rho, _ = oracle_full(x, forget)
+    assert b_over_bar(_host(b), br, nr, rho / nr) <= 1.0
+    if hg is not None:
+        assert torch.equal(ht, h)
+        ref = _host(ht) / (1.0 + np.exp(-W.make_ogate(s, seed=51)))
+        assert np.allclose(_host(hg), ref, rtol=1e-5, atol=1e-6)
 
 
 def test_vector_kernel_just_past_the_fused_scan():
