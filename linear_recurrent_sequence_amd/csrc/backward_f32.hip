@@ -195,11 +195,26 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
         tt[4 * rq + 3] = b.y;
       }
       if constexpr (!ROWS) {
+        const int64_t base = int64_t(head) * T + 32 * J + 4 * g;
+        if ((T & 3) == 0 && 32 * J + 32 <= T) {  // whole tile inside, rows 16-byte aligned
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = 32 * J + 8 * (r >> 2) + 4 * g + (r & 3);
-          tin[r] = i < T ? inv_n[int64_t(head) * T + i] : 0.0f;
-          if constexpr (MODE == kKeysPass) tdb[r] = i < T ? db[int64_t(head) * T + i] : 0.0f;
+          for (int rq = 0; rq < 4; ++rq) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(inv_n + base + 8 * rq);
+            f32x4 b = f32x4{};
+            if constexpr (MODE == kKeysPass) b = *reinterpret_cast<const f32x4*>(db + base + 8 * rq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              tin[4 * rq + e] = a[e];
+              tdb[4 * rq + e] = b[e];
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = 32 * J + 8 * (r >> 2) + 4 * g + (r & 3);
+            tin[r] = i < T ? inv_n[int64_t(head) * T + i] : 0.0f;
+            if constexpr (MODE == kKeysPass) tdb[r] = i < T ? db[int64_t(head) * T + i] : 0.0f;
+          }
         }
       }
     }
