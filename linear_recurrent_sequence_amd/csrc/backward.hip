@@ -70,14 +70,26 @@ __global__ __launch_bounds__(256) void bwd_rows_prep_kernel(
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
+  // the row's scalars are loaded with its vectors, so that their latencies overlap
+  const float nn = n[row], bb = b[row], mm = m[row];
   float acc = 0.0f;
-  for (int c = lane; c < d; c += 64) acc += load_elem(dh + row * d + c) * load_elem(h + row * d + c);
+  if constexpr (std::is_same<Tin, float>::value) {  // 16 bytes per lane (d % 16 == 0)
+    for (int c = 4 * lane; c < d; c += 256) {
+      const float4 x = *reinterpret_cast<const float4*>(dh + row * d + c);
+      const float4 y = *reinterpret_cast<const float4*>(h + row * d + c);
+      acc += x.x * y.x;
+      acc += x.y * y.y;
+      acc += x.z * y.z;
+      acc += x.w * y.w;
+    }
+  } else {
+    for (int c = lane; c < d; c += 64) acc += load_elem(dh + row * d + c) * load_elem(h + row * d + c);
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (lane == 0) {
-    const float nn = n[row], bb = b[row];
     const float dn = -acc / nn;
-    const bool above_floor = fabsf(bb) > expf(-m[row]);
+    const bool above_floor = fabsf(bb) > expf(-mm);
     inv_n[row] = 1.0f / nn;
     db[row] = above_floor ? (bb > 0.0f ? dn : (bb < 0.0f ? -dn : 0.0f)) : 0.0f;
   }

@@ -147,6 +147,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
+  // the row's scalars are loaded with its vectors, so that their latencies overlap
+  const float nn = n[row], bb = b[row], mm = m[row];
   float acc = 0.0f;
   for (int c = 8 * lane; c < d; c += 512) {
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(dh + row * d + c);
@@ -157,9 +159,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (lane == 0) {
-    const float nn = n[row], bb = b[row];
     const float dn = -acc / nn;
-    const bool above_floor = fabsf(bb) > expf(-m[row]);
+    const bool above_floor = fabsf(bb) > expf(-mm);
     const float dbv = above_floor ? (bb > 0.0f ? dn : (bb < 0.0f ? -dn : 0.0f)) : 0.0f;
     inv_n[row] = 1.0f / nn;
     db[row] = dbv;
