@@ -36,10 +36,10 @@
 // the rows and keys passes the tile read by both products is double
 // buffered and the next one is copied during the first products; the tile
 // read only by the first products is copied during the second.  Where three
-// tiles and the 32 KiB of partials do not fit in LDS (d = 384), the partials
-// go to the spare buffer of the double-buffered tile, and both copies run
-// during the second product.  The values pass reads Q in the first product
-// and dH in the second, one buffer each.
+// tiles and the 32 KiB of partials do not fit in LDS (d = 352, 384), the
+// partials go to the buffer of the tile that only the first products read,
+// once every wave has read it (one more barrier per tile).  The values pass
+// reads Q in the first product and dH in the second, one buffer each.
 #include "mlstm_internal.h"
 #include "tile_common.h"
 
@@ -73,7 +73,8 @@ struct BCfg {
   static constexpr int XCH = (TWO ? 2 : 1) * 4 * 4 * 1024;  // partials of the 4 waves
   static constexpr bool ALIAS = TWO && 3 * TILE + XCH > 160 * 1024;
   // rows / keys: X1 (read by both products) in buffers 0 and 1, X2 (first
-  // products only), the partials; values: X1 = Q, X3 = dH, the partials
+  // products only), the partials (in the X2 buffer when ALIAS); values:
+  // X1 = Q, X3 = dH, the partials
   static constexpr int X2_OFF = 2 * TILE;
   static constexpr int X3_OFF = TILE;
   static constexpr int XCH_OFF = TWO ? 3 * TILE : 2 * TILE;
@@ -178,7 +179,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
   for (int J = t_first; J <= t_last; ++J) {
     const bool more = J < t_last;
     const int cur = x1_off(J);
-    char* const xch = lds + (C::ALIAS ? x1_off(J + 1) : C::XCH_OFF);
+    char* const xch = lds + (C::ALIAS ? C::X2_OFF : C::XCH_OFF);
 
     // terms of the tile's rows 32 J + 8 rq + 4 g + e (register 4 rq + e)
     double tt[16];
@@ -225,7 +226,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
       const char* const r2 = lds + C::X2_OFF + l32 * C::RS + 16 * g + 4 * D0;
       // copies during phase 1: the next X1 tile (rows / keys, unaliased) or
       // the current dH tile (values)
-      constexpr bool kCopy1 = C::TWO ? !C::ALIAS : true;
+      constexpr bool kCopy1 = true;
       const int ctile = C::TWO ? J + 1 : J;
       const bool cdo = C::TWO ? more : true;
       const i32x4 rs_c = rows_src(C::TWO ? x1 : x2, ctile);
@@ -262,6 +263,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
         __builtin_amdgcn_sched_barrier(0);
       });
       // partials to LDS: tensor t, wave w, register group rq: 16 bytes per lane
+      // (aliased: into the X2 tile, once every wave has read it)
+      if constexpr (C::ALIAS) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       char* const xw = xch + 4096 * w + 16 * lane;
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
@@ -326,12 +329,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
         const int bt = t >> 4, st2 = t & 15;
         return cp + (8 * (st2 >> 2) + (st2 & 3)) * C::RS + 4 * 32 * 4 * bt;
       };
-      // copies during phase 2: X2 of the next tile (and X1 too when aliased);
-      // the next Q (values)
+      // copies during phase 2: X2 of the next tile; the next Q (values)
       const i32x4 rs_a = rows_src(C::TWO ? x2 : x1, J + 1);
       const unsigned dst_a = tile_base(C::TWO ? C::X2_OFF : 0);
-      const i32x4 rs_b = rows_src(x1, J + 1);
-      const unsigned dst_b = tile_base(x1_off(J + 1));
       float af[kBPf2 + 1];
 #pragma unroll
       for (int t = 0; t < kBPf2; ++t) af[t] = *reinterpret_cast<const float*>(caddr(t));
@@ -345,13 +345,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kBThreads, kBThreads),
         if (more) {
           static_for<C::kCopies>([&](auto cc) {
             constexpr int c = decltype(cc)::value;
-            if constexpr (C::ALIAS) {
-              // both tiles' copies over the steps, interleaved
-              if constexpr ((2 * c * NS2) / (2 * C::kCopies) == t) copy(cc, rs_a, dst_a);
-              if constexpr (((2 * c + 1) * NS2) / (2 * C::kCopies) == t) copy(cc, rs_b, dst_b);
-            } else {
-              if constexpr ((c * NS2) / C::kCopies == t) copy(cc, rs_a, dst_a);
-            }
+            if constexpr ((c * NS2) / C::kCopies == t) copy(cc, rs_a, dst_a);
           });
         }
         __builtin_amdgcn_sched_barrier(0);
